@@ -1,0 +1,214 @@
+/*
+ * csa2.h -- C ABI of libcsa2, the MI355X (gfx950) sparse FP4-KV decode path.
+ *
+ * The library implements, as hand-written HIP kernels, the hot path of the
+ * DeepSeek-V4.1-Flash global KV cache described on these web pages:
+ *   [P1] discuss.pytorch.kr, "DeepSeek-V4.1-Flash, KV cache 890 bytes per token"
+ *        (sections "Causal Encoder-Decoder", "CSA2", "Hierarchical Sparse
+ *        Indexer", "FP4 KV cache", "why the KV cache became the bottleneck")
+ *   [P3] llmfeed.kr news summary, section "scale and structure"
+ *   [P4] ingu627.github.io asymmetric-serving blog, sections 2 and 3
+ *
+ * Conventions (every entry point):
+ *   - Pointers marked "device" are device memory owned by the caller.  The
+ *     library never allocates device memory and keeps no pointer after a call
+ *     returns.  Scratch memory comes in through a caller-owned workspace whose
+ *     size the matching *_workspace_size call reports.
+ *   - A workspace must be all zero before its first use (csa2_workspace_clear
+ *     does that).  Every call leaves the parts it used zero again, so one
+ *     workspace can serve a sequence of calls on one stream.  Calls that
+ *     overlap in time on one workspace race; give concurrent streams their
+ *     own workspaces.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Host-side argument validation happens before any
+ *     launch; a rejected call launches nothing and returns a status.
+ *   - Launch failures return CSA2_ERR_HIP.  No exception crosses the ABI.
+ *   - Device data is trusted only as far as stated: selected indices that are
+ *     negative or >= the sequence length, and page ids outside
+ *     [0, num_blocks), are skipped rather than read.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA2_ABI_VERSION 1
+
+typedef enum {
+  CSA2_OK = 0,
+  CSA2_ERR_INVALID_ARG = 1,  /* null pointer, bad size or unsupported combination */
+  CSA2_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement      */
+  CSA2_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required        */
+  CSA2_ERR_HIP = 4           /* a HIP launch or runtime call failed               */
+} csa2_status;
+
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
+
+/* CSA2 layer modes that run the indexer ([P1] "CSA2", mode table).  Reuse
+ * mode runs no indexer: pass an earlier call's indices to the attention of
+ * another layer. */
+typedef enum { CSA2_FULL = 0, CSA2_REINDEX = 1 } csa2_mode;
+
+typedef void *csa2_stream; /* hipStream_t */
+
+/* One KV layer's paged pool (structure of arrays, all device, caller-owned).
+ * Token slot r = block * block_tokens + slot holds:
+ *   codes   [num_blocks * block_tokens][latent_dim / 2]  E2M1 nibbles, byte j =
+ *           channel 2j (low nibble) | channel 2j+1 (high nibble)
+ *   scales  [num_blocks * block_tokens][latent_dim / 16] E4M3FN, one per 16 channels
+ *   rope    [num_blocks * block_tokens][rope_dim] bf16, or NULL when rope_dim == 0
+ *   idx_keys[num_blocks * block_tokens][idx_dim] of idx_dtype, or NULL for a
+ *           layer that never selects
+ * block_tokens must be 64; latent_dim must be 512; rope_dim 0 or 64; idx_dim 64. */
+typedef struct {
+  uint8_t *codes;
+  uint8_t *scales;
+  uint16_t *rope;
+  void *idx_keys;
+  int32_t num_blocks;
+  int32_t block_tokens;
+  int32_t latent_dim;
+  int32_t rope_dim;
+  int32_t idx_dim;
+  int32_t idx_dtype; /* csa2_dtype */
+} csa2_kv_layer;
+
+/* Batch view.  Position p of sequence b lives in slot
+ * block_table[b * max_blocks_per_seq + p / 64] * 64 + p % 64. */
+typedef struct {
+  const int32_t *block_table; /* device [batch][max_blocks_per_seq]                 */
+  int32_t max_blocks_per_seq;
+  const int32_t *seq_lens;    /* device [batch]: visible tokens of each sequence     */
+  int32_t batch;
+  int32_t max_seq_len;        /* host upper bound of seq_lens (sizes the launches);
+                                 0 means max_blocks_per_seq * 64                      */
+} csa2_seqs;
+
+int csa2_abi_version(void);
+const char *csa2_status_string(csa2_status status);
+
+/* Zero `bytes` of a workspace on `stream` (a fill kernel, no memset node). */
+csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream);
+
+/* ---- FP4 format ([P1] "FP4 KV cache": E2M1 elements, one E4M3 scale per 16
+ * channels, no global scale).  For each row and 16-channel group g:
+ *   s_g = E4M3(fl32(amax_g / 6)) rounded to nearest even, saturating at 448;
+ *   element = nearest E2M1 grid point to |x| / s_g (ties to the even code,
+ *   saturating at 6) with the sign of x; s_g == 0 zeroes the group.
+ * x: device fp32 [rows][channels]; codes: device [rows][channels/2];
+ * scales: device [rows][channels/16].  channels must be a positive multiple
+ * of 16; rows >= 0 (0 is a no-op).  Bit-exact and deterministic. */
+csa2_status csa2_fp4_pack(const float *x, int64_t rows, int32_t channels, uint8_t *codes,
+                          uint8_t *scales, csa2_stream stream);
+
+/* Inverse of the pack: y[r][c] = E2M1(nibble) * E4M3(scale) (exact in fp32). */
+csa2_status csa2_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int32_t channels, float *y, csa2_stream stream);
+
+/* ---- Decode-time append ([P1] "FP4 KV cache" format; the paged layout is
+ * this library's).  For every sequence b, packs latent[b] (device fp32
+ * [batch][latent_dim]) into the slot of position seq_lens[b] and copies
+ * rope[b] (device bf16 [batch][rope_dim], or NULL) and idx_key[b] (device
+ * [batch][idx_dim] of idx_dtype, or NULL) beside it.  The caller increments
+ * seq_lens afterwards.  A position whose page is not mapped (page index beyond
+ * max_blocks_per_seq or page id outside the pool) is skipped. */
+csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
+                           const uint16_t *rope, const void *idx_key, csa2_stream stream);
+
+/* ---- CED projection with fused pack ([P1] "Causal Encoder-Decoder":
+ * C_l = H W_l^KV, Z_l = H W_l^Z for every decoder layer l).
+ *   h:     device bf16 [tokens][hidden]
+ *   w_kv:  device bf16 [n_layers][512][hidden]  (out x in, W_l^KV transposed)
+ *   w_z:   device bf16 [n_layers][64][hidden] or NULL
+ *   codes: device [n_layers][tokens][256], scales: device [n_layers][tokens][32]
+ *          (C_l packed from its fp32 accumulators exactly as csa2_fp4_pack)
+ *   z:     device bf16 [n_layers][tokens][64] (round to nearest even) or NULL
+ *   c_f32: device fp32 [n_layers][tokens][512] copy of the accumulators, or NULL
+ * hidden must be a positive multiple of 64; tokens >= 0. */
+csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,
+                                const uint16_t *w_kv, const uint16_t *w_z, uint8_t *codes,
+                                uint8_t *scales, uint16_t *z, float *c_f32, csa2_stream stream);
+
+/* ---- Indexer scores alone (the scoring step of [P1] "CSA2"):
+ * scores[b][t] = sum_d q_idx[b][d] * k_idx[b, t][d] for t < seq_lens[b]
+ * (fp32 accumulation); entries t >= seq_lens[b] up to max_seq_len are written
+ * as -inf.  q_idx: device fp32 [batch][idx_dim]; scores: device fp32
+ * [batch][max_seq_len]. */
+csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx,
+                              float *scores, csa2_stream stream);
+
+/* ---- Top-K of given scores: for each row b the top_k largest of
+ * scores[b][0 .. lens[b]) (ties: lower position wins), written to
+ * indices[b][0..top_k) in unspecified order and padded with -1 when
+ * lens[b] < top_k.  scores: device fp32 [batch][row_stride], finite;
+ * lens: device int32 [batch]; max_len: host bound of lens (<= row_stride). */
+csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top_k, size_t *bytes);
+csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *lens, int32_t batch,
+                      int32_t max_len, int32_t top_k, int32_t *indices, void *ws, size_t ws_bytes,
+                      csa2_stream stream);
+
+/* ---- Index selection ([P1] "CSA2" Full / Reindex modes and "Hierarchical
+ * Sparse Indexer").
+ * FULL: scores every visible position of each sequence with q_idx[b] and
+ *   writes the top_k positions to indices[b] (unordered, -1 padded).  When
+ *   pool_out is not NULL it also gives each aligned run of pool_block_tokens
+ *   positions the maximum score inside it and writes the ids of the best
+ *   pool_blocks runs (ties: lower id) to pool_out[b] (unordered, -1 padded).
+ *   In that hierarchical case indices[b] is selected among the pool's
+ *   positions, which holds the same set as over all positions except at
+ *   exact ties of the K-th score (pool_blocks >= top_k is required).
+ * REINDEX: scores only the positions of pool_in[b] (block ids from an
+ *   earlier FULL call over the same keys) with this layer's q_idx and
+ *   writes the top_k of them to indices[b].
+ * keys: the layer whose idx_keys are scored; q_idx: device fp32
+ * [batch][idx_dim]; indices: device int32 [batch][top_k].
+ * top_k in [1, 4096]; pool_block_tokens must be 8 and pool_blocks in
+ * [1, 4096]. */
+csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len, int32_t top_k,
+                                             int32_t pool_blocks, int32_t pool_block_tokens,
+                                             size_t *bytes);
+csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx,
+                              int32_t top_k, int32_t mode, const int32_t *pool_in, int32_t *pool_out,
+                              int32_t pool_blocks, int32_t pool_block_tokens, int32_t *indices,
+                              void *ws, size_t ws_bytes, csa2_stream stream);
+
+/* ---- Sparse FP4 decode attention ([P1] "CSA2": all heads share one latent;
+ * "FP4 KV cache": entries are dequantized before attention; [P4] section 2:
+ * 64 heads, 1 KV head).  For each sequence b and head h, over the valid
+ * selected positions S = {indices[b][i] : 0 <= indices[b][i] < seq_lens[b]}:
+ *   logit_s = softmax_scale * (q[b,h,0:512] . c_s + q[b,h,512:512+rope] . rope_s)
+ *   out[b][h] = sum_s softmax(logit)_s * c_s ,  lse[b][h] = log sum_s exp(logit_s)
+ * where c_s is the dequantized latent (K = V).  An empty S gives out = 0 and
+ * lse = -inf.  q: device bf16 [batch][heads][latent_dim + rope_dim];
+ * indices: device int32 [batch][top_k]; out: device fp32 [batch][heads][512];
+ * lse: device fp32 [batch][heads] or NULL.  heads must be a positive multiple
+ * of 16 (at most 128); top_k in [1, 4096].  The logits and the softmax run in
+ * fp32; q and rope enter the matrix cores as fp16. */
+csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim,
+                                     size_t *bytes);
+csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_seqs *seqs,
+                                        const uint16_t *q, int32_t heads, const int32_t *indices,
+                                        int32_t top_k, float softmax_scale, float *out, float *lse,
+                                        void *ws, size_t ws_bytes, csa2_stream stream);
+
+/* ---- Host-side page allocator (no device memory): a free list of block ids
+ * [0, num_blocks).  Not thread-safe; one instance per owner. */
+typedef struct csa2_block_pool csa2_block_pool;
+csa2_block_pool *csa2_block_pool_create(int32_t num_blocks);
+/* Takes n ids (n >= 0) into ids_out; fails without taking any when fewer are free. */
+csa2_status csa2_block_alloc(csa2_block_pool *pool, int32_t n, int32_t *ids_out);
+/* Returns n ids; fails without returning any on an out-of-range or already free id. */
+csa2_status csa2_block_free(csa2_block_pool *pool, int32_t n, const int32_t *ids);
+int32_t csa2_block_pool_num_free(const csa2_block_pool *pool);
+void csa2_block_pool_destroy(csa2_block_pool *pool);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

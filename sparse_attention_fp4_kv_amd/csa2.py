@@ -1,0 +1,346 @@
+"""Thin Python binding of libcsa2 (include/csa2.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+torch supplies device memory and the current stream.  The raw C entry points
+are available under their C names on ``lib()``; the helpers below take torch
+tensors, allocate outputs with torch and raise ``Csa2Error`` on any status
+other than CSA2_OK.  Importing this module never needs a GPU; calling into the
+library needs the built libcsa2.so and fails loudly when it is missing.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcsa2.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+FULL, REINDEX = 0, 1
+PAGE = 64
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_status_string(status)} (status {status})")
+
+
+class KvLayer(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("rope", ctypes.c_void_p),
+        ("idx_keys", ctypes.c_void_p),
+        ("num_blocks", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+        ("latent_dim", ctypes.c_int32),
+        ("rope_dim", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32),
+        ("idx_dtype", ctypes.c_int32),
+    ]
+
+
+class Seqs(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("seq_lens", ctypes.c_void_p),
+        ("batch", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_PKV = ctypes.POINTER(KvLayer)
+_PSQ = ctypes.POINTER(Seqs)
+
+# C name -> (restype, argtypes), exactly as declared in include/csa2.h
+SIGNATURES = {
+    "csa2_abi_version": (ctypes.c_int, []),
+    "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "csa2_workspace_clear": (ctypes.c_int, [_P, _SZ, _P]),
+    "csa2_fp4_pack": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
+    "csa2_fp4_unpack": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P]),
+    "csa2_kv_append": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P, _P]),
+    "csa2_ced_kv_project": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "csa2_index_scores": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P]),
+    "csa2_topk_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "csa2_topk": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "csa2_index_select_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "csa2_index_select": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
+    "csa2_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "csa2_sparse_fp4_decode_attn": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "csa2_block_pool_create": (_P, [_I32]),
+    "csa2_block_alloc": (ctypes.c_int, [_P, _I32, _P]),
+    "csa2_block_free": (ctypes.c_int, [_P, _I32, _P]),
+    "csa2_block_pool_num_free": (_I32, [_P]),
+    "csa2_block_pool_destroy": (None, [_P]),
+}
+
+_LIB = None
+
+
+def lib():
+    """The loaded libcsa2 with every declared signature attached."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libcsa2.so is not built ({LIB_PATH}); run `python -m sparse_attention_fp4_kv_amd.build_lib`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _status_string(s):
+    try:
+        return lib().csa2_status_string(int(s)).decode()
+    except Exception:  # library not loadable: still report the number
+        return "status"
+
+
+def _check(status, where):
+    if status != OK:
+        raise Csa2Error(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _require(t, dtype, name, device=True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if device and not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+
+
+# ----------------------------------------------------------------- structures
+class PagedLayer:
+    """One KV layer's paged pool, allocated with torch on the current device.
+
+    codes [num_blocks*64][256] u8, scales [num_blocks*64][32] u8,
+    rope [num_blocks*64][rope_dim] bf16 bits (int16) or None,
+    idx_keys [num_blocks*64][64] fp32 / bf16 bits (int16) or None.
+    """
+
+    def __init__(self, num_blocks, rope_dim=0, idx_dtype=None, device="cuda"):
+        rows = num_blocks * PAGE
+        self.num_blocks = num_blocks
+        self.codes = torch.zeros((rows, 256), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros((rows, 32), dtype=torch.uint8, device=device)
+        self.rope = torch.zeros((rows, rope_dim), dtype=torch.int16, device=device) if rope_dim else None
+        self.rope_dim = rope_dim
+        self.idx_dtype = idx_dtype
+        if idx_dtype == "f32":
+            self.idx_keys = torch.zeros((rows, 64), dtype=torch.float32, device=device)
+        elif idx_dtype == "bf16":
+            self.idx_keys = torch.zeros((rows, 64), dtype=torch.int16, device=device)
+        else:
+            self.idx_keys = None
+
+    def struct(self):
+        return KvLayer(
+            codes=self.codes.data_ptr(), scales=self.scales.data_ptr(),
+            rope=self.rope.data_ptr() if self.rope is not None else None,
+            idx_keys=self.idx_keys.data_ptr() if self.idx_keys is not None else None,
+            num_blocks=self.num_blocks, block_tokens=PAGE, latent_dim=512, rope_dim=self.rope_dim,
+            idx_dim=64, idx_dtype=F32 if self.idx_dtype == "f32" else BF16)
+
+
+class Batch:
+    """Block tables and lengths of a batch (device int32 tensors)."""
+
+    def __init__(self, block_table, seq_lens, max_seq_len=0):
+        _require(block_table, torch.int32, "block_table")
+        _require(seq_lens, torch.int32, "seq_lens")
+        self.block_table = block_table
+        self.seq_lens = seq_lens
+        self.max_seq_len = int(max_seq_len)
+
+    @property
+    def batch(self):
+        return self.block_table.shape[0]
+
+    def struct(self):
+        return Seqs(block_table=self.block_table.data_ptr(), max_blocks_per_seq=self.block_table.shape[1],
+                    seq_lens=self.seq_lens.data_ptr(), batch=self.block_table.shape[0],
+                    max_seq_len=self.max_seq_len)
+
+
+def workspace(nbytes, device="cuda"):
+    """A zeroed workspace of at least nbytes (256-byte aligned by torch's allocator)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------- entry points
+def csa2_workspace_clear(ws):
+    _check(lib().csa2_workspace_clear(_ptr(ws), ws.numel(), _stream()), "csa2_workspace_clear")
+
+
+def csa2_fp4_pack(x):
+    """x: fp32 [rows, C] -> (codes u8 [rows, C/2], scales u8 [rows, C/16])."""
+    _require(x, torch.float32, "x")
+    rows, C = x.shape
+    codes = torch.empty((rows, C // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, C // 16), dtype=torch.uint8, device=x.device)
+    _check(lib().csa2_fp4_pack(_ptr(x), rows, C, _ptr(codes), _ptr(scales), _stream()), "csa2_fp4_pack")
+    return codes, scales
+
+
+def csa2_fp4_pack_into(x, codes, scales):
+    _require(x, torch.float32, "x")
+    rows, C = x.shape
+    _check(lib().csa2_fp4_pack(_ptr(x), rows, C, _ptr(codes), _ptr(scales), _stream()), "csa2_fp4_pack")
+
+
+def csa2_fp4_unpack(codes, scales):
+    rows, half = codes.shape
+    y = torch.empty((rows, 2 * half), dtype=torch.float32, device=codes.device)
+    _check(lib().csa2_fp4_unpack(_ptr(codes), _ptr(scales), rows, 2 * half, _ptr(y), _stream()), "csa2_fp4_unpack")
+    return y
+
+
+def csa2_kv_append(layer, batch, latent, rope=None, idx_key=None):
+    kv, sq = layer.struct(), batch.struct()
+    _check(lib().csa2_kv_append(ctypes.byref(kv), ctypes.byref(sq), _ptr(latent), _ptr(rope), _ptr(idx_key),
+                                _stream()), "csa2_kv_append")
+
+
+def csa2_ced_kv_project(h, w_kv, w_z=None, c_f32=False):
+    """h bf16 bits [T, hidden] (int16); w_kv [L, 512, hidden]; w_z [L, 64, hidden] or None."""
+    T, hidden = h.shape
+    L = w_kv.shape[0]
+    dev = h.device
+    codes = torch.empty((L, T, 256), dtype=torch.uint8, device=dev)
+    scales = torch.empty((L, T, 32), dtype=torch.uint8, device=dev)
+    z = torch.empty((L, T, 64), dtype=torch.int16, device=dev) if w_z is not None else None
+    c = torch.empty((L, T, 512), dtype=torch.float32, device=dev) if c_f32 else None
+    _check(lib().csa2_ced_kv_project(_ptr(h), T, hidden, L, _ptr(w_kv), _ptr(w_z), _ptr(codes), _ptr(scales), _ptr(z),
+                                     _ptr(c), _stream()), "csa2_ced_kv_project")
+    return codes, scales, z, c
+
+
+def csa2_index_scores(layer, batch, q_idx, max_len):
+    scores = torch.empty((batch.batch, max_len), dtype=torch.float32, device=q_idx.device)
+    kv, sq = layer.struct(), batch.struct()
+    _check(lib().csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), _ptr(q_idx), _ptr(scores), _stream()),
+           "csa2_index_scores")
+    return scores
+
+
+def topk_workspace_bytes(batch, max_len, top_k):
+    n = ctypes.c_size_t()
+    _check(lib().csa2_topk_workspace_size(batch, max_len, top_k, ctypes.byref(n)), "csa2_topk_workspace_size")
+    return n.value
+
+
+def csa2_topk(scores, lens, top_k, ws=None):
+    _require(scores, torch.float32, "scores")
+    B, M = scores.shape
+    if ws is None:
+        ws = workspace(topk_workspace_bytes(B, M, top_k), scores.device)
+    idx = torch.empty((B, top_k), dtype=torch.int32, device=scores.device)
+    _check(lib().csa2_topk(_ptr(scores), M, _ptr(lens), B, M, top_k, _ptr(idx), _ptr(ws), ws.numel(), _stream()),
+           "csa2_topk")
+    return idx
+
+
+def index_select_workspace_bytes(batch, max_len, top_k, pool_blocks=0):
+    n = ctypes.c_size_t()
+    _check(lib().csa2_index_select_workspace_size(batch, max_len, top_k, pool_blocks, 8 if pool_blocks else 0,
+                                                  ctypes.byref(n)), "csa2_index_select_workspace_size")
+    return n.value
+
+
+def csa2_index_select(layer, batch, q_idx, top_k, mode=FULL, pool_in=None, pool_blocks=0, want_pool=False,
+                      ws=None, indices=None, pool_out=None):
+    """Full (optionally hierarchical: want_pool) or Reindex selection -> (indices, pool_out or None)."""
+    B = batch.batch
+    dev = q_idx.device
+    max_len = batch.max_seq_len or batch.block_table.shape[1] * PAGE
+    pooled = mode == REINDEX or want_pool
+    if ws is None:
+        ws = workspace(index_select_workspace_bytes(B, max_len, top_k, pool_blocks if pooled else 0), dev)
+    if indices is None:
+        indices = torch.empty((B, top_k), dtype=torch.int32, device=dev)
+    if want_pool and pool_out is None:
+        pool_out = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
+    kv, sq = layer.struct(), batch.struct()
+    _check(lib().csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), _ptr(q_idx), top_k, mode, _ptr(pool_in),
+                                   _ptr(pool_out) if want_pool else None, pool_blocks, 8 if pooled else 0,
+                                   _ptr(indices), _ptr(ws), ws.numel(), _stream()), "csa2_index_select")
+    return indices, (pool_out if want_pool else None)
+
+
+def attn_workspace_bytes(batch, heads, top_k):
+    n = ctypes.c_size_t()
+    _check(lib().csa2_attn_workspace_size(batch, heads, top_k, 512, ctypes.byref(n)), "csa2_attn_workspace_size")
+    return n.value
+
+
+def csa2_sparse_fp4_decode_attn(layer, batch, q, indices, softmax_scale, ws=None, out=None, lse=None):
+    """q bf16 bits [B, H, 512+rope] (int16); indices int32 [B, K] -> (out fp32 [B, H, 512], lse fp32 [B, H])."""
+    B, H, _ = q.shape
+    K = indices.shape[1]
+    dev = q.device
+    if ws is None:
+        ws = workspace(attn_workspace_bytes(B, H, K), dev)
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    kv, sq = layer.struct(), batch.struct()
+    _check(lib().csa2_sparse_fp4_decode_attn(ctypes.byref(kv), ctypes.byref(sq), _ptr(q), H, _ptr(indices), K,
+                                             float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                             _stream()), "csa2_sparse_fp4_decode_attn")
+    return out, lse
+
+
+class BlockPool:
+    """Host-side page allocator (csa2_block_pool_*)."""
+
+    def __init__(self, num_blocks):
+        self._h = lib().csa2_block_pool_create(num_blocks)
+        if not self._h:
+            raise Csa2Error(ERR_INVALID_ARG, "csa2_block_pool_create")
+
+    def alloc(self, n):
+        arr = (ctypes.c_int32 * max(n, 1))()
+        _check(lib().csa2_block_alloc(self._h, n, arr), "csa2_block_alloc")
+        return [arr[i] for i in range(n)]
+
+    def free(self, ids):
+        arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+        _check(lib().csa2_block_free(self._h, len(ids), arr), "csa2_block_free")
+
+    @property
+    def num_free(self):
+        return lib().csa2_block_pool_num_free(self._h)
+
+    def close(self):
+        if self._h:
+            lib().csa2_block_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

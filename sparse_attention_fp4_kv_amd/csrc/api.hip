@@ -1,0 +1,291 @@
+// C ABI of libcsa2: argument validation, launch dispatch, workspace sizing
+// and the host-side page allocator.  Every public entry point validates its
+// arguments before launching anything and never lets a C++ exception out.
+#include "../../include/csa2.h"
+
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace csa2;
+
+namespace {
+
+constexpr int kMaxTopK = 4096;
+constexpr int kMaxPoolBlocks = 4096;
+
+hipStream_t as_stream(csa2_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_HIP; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks a layer and produces its device view.  need_kv: codes/scales are read;
+// need_keys: idx_keys are read.
+csa2_status check_layer(const csa2_kv_layer *l, bool need_kv, bool need_keys, KvLayerDev *out) {
+  if (l == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (l->block_tokens != 64 || l->latent_dim != 512 || l->num_blocks < 0) return CSA2_ERR_INVALID_ARG;
+  if (l->rope_dim != 0 && l->rope_dim != 64) return CSA2_ERR_INVALID_ARG;
+  if (need_kv) {
+    if (l->codes == nullptr || l->scales == nullptr) return CSA2_ERR_INVALID_ARG;
+    if (!aligned(l->codes, 16) || !aligned(l->scales, 16)) return CSA2_ERR_INVALID_ARG;
+    if (l->rope_dim != 0 && (l->rope == nullptr || !aligned(l->rope, 16))) return CSA2_ERR_INVALID_ARG;
+  }
+  if (need_keys) {
+    if (l->idx_keys == nullptr || l->idx_dim != 64 || !aligned(l->idx_keys, 16)) return CSA2_ERR_INVALID_ARG;
+    if (l->idx_dtype != CSA2_F32 && l->idx_dtype != CSA2_BF16) return CSA2_ERR_INVALID_ARG;
+  }
+  out->codes = l->codes;
+  out->scales = l->scales;
+  out->rope = l->rope_dim ? l->rope : nullptr;
+  out->idx_keys = l->idx_keys;
+  out->num_blocks = l->num_blocks;
+  out->rope_dim = l->rope_dim;
+  out->idx_f32 = l->idx_dtype == CSA2_F32 ? 1 : 0;
+  return CSA2_OK;
+}
+
+csa2_status check_seqs(const csa2_seqs *s, SeqsDev *out) {
+  if (s == nullptr || s->batch < 0 || s->max_blocks_per_seq < 0 || s->max_seq_len < 0) return CSA2_ERR_INVALID_ARG;
+  if (s->batch > 0 && (s->block_table == nullptr || s->seq_lens == nullptr)) return CSA2_ERR_INVALID_ARG;
+  const int64_t cap = (int64_t)s->max_blocks_per_seq * 64;
+  const int64_t ml = s->max_seq_len ? s->max_seq_len : cap;
+  if (ml > cap || ml > (int64_t)0x7FFFFFFF - 64) return CSA2_ERR_INVALID_ARG;
+  out->block_table = s->block_table;
+  out->seq_lens = s->seq_lens;
+  out->max_blocks = s->max_blocks_per_seq;
+  out->batch = s->batch;
+  out->max_len = (int)ml;
+  return CSA2_OK;
+}
+
+}  // namespace
+
+struct csa2_block_pool {
+  std::vector<int32_t> free_ids;   // stack of free ids
+  std::vector<uint8_t> is_free;    // per id
+};
+
+extern "C" {
+
+int csa2_abi_version(void) { return CSA2_ABI_VERSION; }
+
+const char *csa2_status_string(csa2_status s) {
+  switch (s) {
+    case CSA2_OK: return "ok";
+    case CSA2_ERR_INVALID_ARG: return "invalid argument";
+    case CSA2_ERR_UNSUPPORTED: return "unsupported";
+    case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA2_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream) {
+  if (bytes == 0) return CSA2_OK;
+  if (ws == nullptr || !aligned(ws, 4) || bytes % 4 != 0) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_fill_zero(ws, bytes, as_stream(stream)));
+}
+
+csa2_status csa2_fp4_pack(const float *x, int64_t rows, int32_t channels, uint8_t *codes, uint8_t *scales,
+                          csa2_stream stream) {
+  if (rows < 0 || channels <= 0 || channels % 16 != 0) return CSA2_ERR_INVALID_ARG;
+  if (rows == 0) return CSA2_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8)) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_fp4_pack(x, rows, channels, codes, scales, as_stream(stream)));
+}
+
+csa2_status csa2_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int32_t channels, float *y,
+                            csa2_stream stream) {
+  if (rows < 0 || channels <= 0 || channels % 16 != 0) return CSA2_ERR_INVALID_ARG;
+  if (rows == 0) return CSA2_OK;
+  if (y == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(codes, 8)) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_fp4_unpack(codes, scales, rows, channels, y, as_stream(stream)));
+}
+
+csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
+                           const uint16_t *rope, const void *idx_key, csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(layer, true, false, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (S.batch == 0) return CSA2_OK;
+  if (latent == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (rope != nullptr && L.rope_dim == 0) return CSA2_ERR_INVALID_ARG;
+  if (L.rope_dim != 0 && rope == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (idx_key != nullptr && (layer->idx_keys == nullptr || layer->idx_dim != 64 ||
+                             (layer->idx_dtype != CSA2_F32 && layer->idx_dtype != CSA2_BF16)))
+    return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_kv_append(L, S, latent, rope, idx_key, as_stream(stream)));
+}
+
+csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,
+                                const uint16_t *w_kv, const uint16_t *w_z, uint8_t *codes, uint8_t *scales,
+                                uint16_t *z, float *c_f32, csa2_stream stream) {
+  if (tokens < 0 || n_layers < 0 || hidden <= 0 || hidden % 64 != 0) return CSA2_ERR_INVALID_ARG;
+  if (tokens > (int64_t)1 << 31 || n_layers > 4096) return CSA2_ERR_INVALID_ARG;
+  if (tokens == 0 || n_layers == 0) return CSA2_OK;
+  if (h == nullptr || w_kv == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_INVALID_ARG;
+  if ((z == nullptr) != (w_z == nullptr)) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(w_kv, 16) || (w_z && !aligned(w_z, 16)) || !aligned(codes, 8) ||
+      (z && !aligned(z, 16)) || (c_f32 && !aligned(c_f32, 16)))
+    return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_ced_project(h, tokens, hidden, n_layers, w_kv, w_z, codes, scales, z, c_f32,
+                                     as_stream(stream)));
+}
+
+csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx, float *scores,
+                              csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(keys, false, true, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (S.batch == 0 || S.max_len == 0) return CSA2_OK;
+  if (q_idx == nullptr || scores == nullptr) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_index_scores(L, S, q_idx, scores, as_stream(stream)));
+}
+
+csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top_k, size_t *bytes) {
+  if (bytes == nullptr || batch < 0 || max_len < 0 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  *bytes = topk_workspace_bytes(batch, max_len, top_k);
+  return CSA2_OK;
+}
+
+csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *lens, int32_t batch, int32_t max_len,
+                      int32_t top_k, int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream) {
+  if (batch < 0 || max_len < 0 || top_k < 1 || top_k > kMaxTopK || row_stride < max_len) return CSA2_ERR_INVALID_ARG;
+  if (batch == 0) return CSA2_OK;
+  if (scores == nullptr || lens == nullptr || indices == nullptr) return CSA2_ERR_INVALID_ARG;
+  const size_t need = topk_workspace_bytes(batch, max_len, top_k);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_topk_scores(scores, row_stride, lens, batch, max_len, top_k, indices, ws, as_stream(stream)));
+}
+
+csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len, int32_t top_k, int32_t pool_blocks,
+                                             int32_t pool_block_tokens, size_t *bytes) {
+  if (bytes == nullptr || batch < 0 || max_seq_len < 0 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (pool_blocks < 0 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
+  if (pool_blocks > 0 && pool_block_tokens != 8) return CSA2_ERR_INVALID_ARG;
+  *bytes = index_select_workspace_bytes(batch, max_seq_len, top_k, pool_blocks);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx, int32_t top_k,
+                              int32_t mode, const int32_t *pool_in, int32_t *pool_out, int32_t pool_blocks,
+                              int32_t pool_block_tokens, int32_t *indices, void *ws, size_t ws_bytes,
+                              csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(keys, false, true, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (mode != CSA2_FULL && mode != CSA2_REINDEX) return CSA2_ERR_INVALID_ARG;
+  const bool pooled = (mode == CSA2_REINDEX) || pool_out != nullptr;
+  if (pooled) {
+    if (pool_block_tokens != 8 || pool_blocks < 1 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
+    if (pool_blocks < top_k && mode == CSA2_FULL) return CSA2_ERR_INVALID_ARG;  // pool must hold the top-K
+  }
+  if (mode == CSA2_REINDEX && (pool_in == nullptr || pool_out != nullptr)) return CSA2_ERR_INVALID_ARG;
+  if (mode == CSA2_FULL && pool_in != nullptr) return CSA2_ERR_INVALID_ARG;
+  if (S.batch == 0) return CSA2_OK;
+  if (q_idx == nullptr || indices == nullptr) return CSA2_ERR_INVALID_ARG;
+  const size_t need = index_select_workspace_bytes(S.batch, S.max_len, top_k, pooled ? pool_blocks : 0);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  hipError_t e;
+  if (mode == CSA2_FULL)
+    e = launch_index_select_full(L, S, q_idx, top_k, pool_out, pool_out ? pool_blocks : 0, indices, ws,
+                                 as_stream(stream));
+  else
+    e = launch_index_select_reindex(L, S, q_idx, top_k, pool_in, pool_blocks, indices, ws, as_stream(stream));
+  return from_hip(e);
+}
+
+csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim, size_t *bytes) {
+  if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
+      top_k > kMaxTopK || latent_dim != 512)
+    return CSA2_ERR_INVALID_ARG;
+  *bytes = attn_workspace_bytes(batch, heads, top_k);
+  return CSA2_OK;
+}
+
+csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_seqs *seqs, const uint16_t *q,
+                                        int32_t heads, const int32_t *indices, int32_t top_k, float softmax_scale,
+                                        float *out, float *lse, void *ws, size_t ws_bytes, csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(layer, true, false, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return CSA2_ERR_INVALID_ARG;
+  if (S.batch == 0) return CSA2_OK;
+  if (q == nullptr || indices == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16))
+    return CSA2_ERR_INVALID_ARG;
+  const size_t need = attn_workspace_bytes(S.batch, heads, top_k);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, out, lse, ws, as_stream(stream)));
+}
+
+csa2_block_pool *csa2_block_pool_create(int32_t num_blocks) {
+  if (num_blocks < 0) return nullptr;
+  csa2_block_pool *p = new (std::nothrow) csa2_block_pool;
+  if (p == nullptr) return nullptr;
+  try {
+    p->free_ids.resize(num_blocks);
+    p->is_free.assign(num_blocks, 1);
+  } catch (...) {
+    delete p;
+    return nullptr;
+  }
+  // pop order: lowest id first
+  for (int32_t i = 0; i < num_blocks; ++i) p->free_ids[i] = num_blocks - 1 - i;
+  return p;
+}
+
+csa2_status csa2_block_alloc(csa2_block_pool *pool, int32_t n, int32_t *ids_out) {
+  if (pool == nullptr || n < 0 || (n > 0 && ids_out == nullptr)) return CSA2_ERR_INVALID_ARG;
+  if ((size_t)n > pool->free_ids.size()) return CSA2_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = pool->free_ids.back();
+    pool->free_ids.pop_back();
+    pool->is_free[id] = 0;
+    ids_out[i] = id;
+  }
+  return CSA2_OK;
+}
+
+csa2_status csa2_block_free(csa2_block_pool *pool, int32_t n, const int32_t *ids) {
+  if (pool == nullptr || n < 0 || (n > 0 && ids == nullptr)) return CSA2_ERR_INVALID_ARG;
+  const int32_t nb = (int32_t)pool->is_free.size();
+  // validate everything first (no partial frees), including duplicates within ids
+  std::vector<uint8_t> seen;
+  try {
+    seen.assign(nb, 0);
+  } catch (...) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= nb || pool->is_free[id] || seen[id]) return CSA2_ERR_INVALID_ARG;
+    seen[id] = 1;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    pool->is_free[ids[i]] = 1;
+    pool->free_ids.push_back(ids[i]);
+  }
+  return CSA2_OK;
+}
+
+int32_t csa2_block_pool_num_free(const csa2_block_pool *pool) {
+  return pool == nullptr ? -1 : (int32_t)pool->free_ids.size();
+}
+
+void csa2_block_pool_destroy(csa2_block_pool *pool) { delete pool; }
+
+}  // extern "C"

@@ -1,0 +1,390 @@
+// Sparse FP4 decode attention over the selected entries of a paged cache.
+//
+// Sources: discuss.pytorch.kr DeepSeek-V4.1-Flash summary, section "CSA2"
+// (one small latent shared by all heads; each layer attends over its top-K
+// selected entries) and section "FP4 KV cache" (the cache is dequantized
+// before attention); ingu627 asymmetric-serving blog, section 2 (64 heads,
+// one KV head).  For each sequence b and head h over the valid selected set S:
+//   logit_s = scale * (q[h,:512] . c_s + q[h,512:] . rope_s)
+//   out[h]  = sum_s softmax(logit)_s c_s,   lse[h] = log sum_s exp(logit_s)
+// with c_s the dequantized 512-channel latent (K = V).
+//
+// Design (ours):
+//   * One workgroup (4 waves) serves up to 64 heads of one sequence, so each
+//     dequantized entry feeds every head: QK^T and PV are MFMA contractions
+//     with M = heads (v_mfma_f32_16x16x32_f16, fp32 accumulation).
+//   * Entries are processed in tiles of 32.  A tile's FP4 codes are gathered
+//     straight into registers (8 lanes per 256-byte row), dequantized with the
+//     hardware E2M1 -> fp16 convert plus one packed multiply by the E4M3 scale
+//     (exact), and written to LDS twice: row-major (QK^T operand, channels
+//     contiguous) and transposed (PV operand, entries contiguous).
+//   * Online softmax in fp32 (exp2 domain).  P enters the PV contraction as
+//     fp16 hi + lo parts (two MFMAs), which keeps the output within ~1e-5
+//     relative of an fp32 P; a single fp16 P is not accurate enough for
+//     latents with x20 outlier channels.
+//   * Split-K over entries across workgroups for small batches; partial
+//     (m, l, O) are merged by an lse-weighted combine kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr int kT = 32;                 // entries per tile
+constexpr int kQkLd = kLatent + 64 + 8;  // row-major tile row (f16): 512 latent + 64 rope + pad
+constexpr int kVLd = kT + 8;           // transposed tile row (f16): 32 entries + pad
+constexpr int kPLd = kT + 8;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  KvLayerDev L;
+  SeqsDev S;
+  const uint16_t *q;      // [B][H][512 + rope]
+  const int32_t *idx;     // [B][K]
+  int heads;              // H
+  int top_k;
+  int splits;             // workgroups per (b, head group) along the entries
+  int tiles_per_split;
+  float scale_log2;       // softmax scale * log2(e)
+  float *out;             // [B][H][512]  (splits == 1)
+  float *lse;             // [B][H] or null
+  float *part_o;          // [B][H][splits][512]  (splits > 1)
+  float *part_ml;         // [B][H][splits][2]
+};
+
+template <int MT>
+struct Smem {
+  f16 cq[kT][kQkLd];             // row-major dequantized tile (+ rope)
+  f16 cv[kLatent][kVLd];         // transposed dequantized tile
+  float s[16 * MT][kT];          // logits of the tile
+  f16 p_hi[16 * MT][kPLd];
+  f16 p_lo[16 * MT][kPLd];
+  float m_run[16 * MT], l_run[16 * MT], alpha[16 * MT];
+  int64_t slot[kT];
+};
+
+__device__ __forceinline__ f16x8 lds_f16x8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+
+__device__ __forceinline__ f16x8 bf16x8_to_f16x8(uint4 v) {
+  f16x8 r;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = (f16)__uint_as_float(w[i] << 16);
+    r[2 * i + 1] = (f16)__uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  return r;
+}
+
+template <int MT>
+__global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
+  constexpr int HG = 16 * MT;                  // heads in this workgroup
+  __shared__ Smem<MT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int h0 = hg * HG;
+  const int qw = kLatent + a.L.rope_dim;       // q row width
+  const int n = min(max(a.S.seq_lens[b], 0), a.S.max_len);
+  const int ks_total = qw / 32;                // 16 or 18 k-steps of 32 channels
+
+  // ---- QK^T work of this wave: one M-tile (16 heads) and 1 or 2 N-tiles of 16 entries
+  int qk_mt, qk_nt0, qk_ntn;
+  if constexpr (MT == 4) { qk_mt = wave; qk_nt0 = 0; qk_ntn = 2; }
+  else if constexpr (MT == 2) { qk_mt = wave >> 1; qk_nt0 = wave & 1; qk_ntn = 1; }
+  else { qk_mt = 0; qk_nt0 = wave & 1; qk_ntn = wave < 2 ? 1 : 0; }
+
+  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*ks + 8*(lane/16) .. +7
+  f16x8 qf[18];
+  {
+    const uint16_t *qrow = a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * qw + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      if (ks < ks_total) qf[ks] = bf16x8_to_f16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks));
+      else qf[ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  // ---- PV accumulators: wave owns channels [128*wave, 128*wave+128) for all HG heads
+  f32x4 acc[MT][8];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (tid < HG) {
+    sm.m_run[tid] = -INFINITY;
+    sm.l_run[tid] = 0.0f;
+  }
+
+  const int tile_begin = split * a.tiles_per_split;
+  const int n_tiles_all = (a.top_k + kT - 1) / kT;
+  const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles_all);
+  const int32_t *idx_row = a.idx + (size_t)b * a.top_k;
+
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int e0 = tile * kT;
+    // 1. resolve the physical slots of this tile's entries
+    if (tid < kT) {
+      const int i = e0 + tid;
+      int64_t slot = -1;
+      if (i < a.top_k) {
+        const int p = idx_row[i];
+        if (p >= 0 && p < n) {
+          const int page = p / kPage;
+          if (page < a.S.max_blocks) {
+            const int blk = a.S.block_table[(size_t)b * a.S.max_blocks + page];
+            if (blk >= 0 && blk < a.L.num_blocks) slot = (int64_t)blk * kPage + p % kPage;
+          }
+        }
+      }
+      sm.slot[tid] = slot;
+    }
+    __syncthreads();
+    // 2. gather + dequantize: thread -> entry tid/8, channels 64*(tid%8) .. +63
+    {
+      const int e = tid >> 3, cb = tid & 7;
+      const int64_t slot = sm.slot[e];
+      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = make_uint4(0, 0, 0, 0);
+      uint32_t sc4 = 0;
+      uint4 rp = make_uint4(0, 0, 0, 0);
+      if (slot >= 0) {
+        const uint4 *cp = reinterpret_cast<const uint4 *>(a.L.codes + slot * (kLatent / 2) + 32 * cb);
+        c0 = cp[0];
+        c1 = cp[1];
+        sc4 = *reinterpret_cast<const uint32_t *>(a.L.scales + slot * (kLatent / kGroup) + 4 * cb);
+        if (a.L.rope_dim) rp = *reinterpret_cast<const uint4 *>(a.L.rope + slot * 64 + 8 * cb);
+      }
+      const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int wi = 0; wi < 8; ++wi) {
+        const f16 s = (f16)e4m3_decode((sc4 >> (8 * (wi >> 1))) & 0xFFu);
+        const f16x8 v = deq8(words[wi], s);
+        *reinterpret_cast<f16x8 *>(&sm.cq[e][64 * cb + 8 * wi]) = v;
+      }
+      if (a.L.rope_dim) *reinterpret_cast<f16x8 *>(&sm.cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
+    }
+    __syncthreads();
+    // 3. transposed copy for PV: thread -> channels 2*tid, 2*tid+1 over the 32 entries
+    {
+      const int c = 2 * tid;
+      uint32_t colw[kT];
+#pragma unroll
+      for (int e = 0; e < kT; ++e) colw[e] = *reinterpret_cast<const uint32_t *>(&sm.cq[e][c]);
+#pragma unroll
+      for (int g = 0; g < kT / 8; ++g) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = colw[8 * g + 2 * j], y = colw[8 * g + 2 * j + 1];
+          lo[j] = (x & 0xFFFFu) | (y << 16);
+          hi[j] = (x >> 16) | (y & 0xFFFF0000u);
+        }
+        *reinterpret_cast<uint4 *>(&sm.cv[c][8 * g]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4 *>(&sm.cv[c + 1][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      }
+    }
+    // 4. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
+    for (int j = 0; j < qk_ntn; ++j) {
+      const int nt = qk_nt0 + j;
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      const f16 *brow = &sm.cq[16 * nt + (lane & 15)][8 * (lane >> 4)];
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks < ks_total) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], lds_f16x8(brow + 32 * ks), s, 0, 0, 0);
+      }
+      // lane holds S[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
+      const int ent = 16 * nt + (lane & 15);
+      const bool valid = sm.slot[ent] >= 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sm.s[16 * qk_mt + 4 * (lane >> 4) + r][ent] = valid ? s[r] * a.scale_log2 : -INFINITY;
+    }
+    __syncthreads();
+    // 5. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
+    {
+      constexpr int TPH = 256 / HG;   // threads per head (16, 8 or 4)
+      constexpr int EPT = kT / TPH;   // entries per thread (2, 4 or 8)
+      const int h = tid / TPH, part = tid % TPH;
+      float v[EPT];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        v[i] = sm.s[h][part * EPT + i];
+        mx = fmaxf(mx, v[i]);
+      }
+#pragma unroll
+      for (int off = 1; off < TPH; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_old = sm.m_run[h];
+      const float m_new = fmaxf(m_old, mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        const float p = (m_new == -INFINITY) ? 0.f : exp2f(v[i] - m_new);
+        sum += p;
+        const f16 ph = (f16)p;
+        const f16 pl = (f16)(p - (float)ph);
+        sm.p_hi[h][part * EPT + i] = ph;
+        sm.p_lo[h][part * EPT + i] = pl;
+      }
+#pragma unroll
+      for (int off = 1; off < TPH; off <<= 1) sum += __shfl_xor(sum, off);
+      __syncthreads();  // every thread has read m_run before it changes
+      if (part == 0) {
+        const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_old - m_new);
+        sm.alpha[h] = al;
+        sm.m_run[h] = m_new;
+        sm.l_run[h] = sm.l_run[h] * al + sum;
+      }
+    }
+    __syncthreads();
+    // 6. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
+    {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float al = sm.alpha[16 * mt + 4 * (lane >> 4) + r];
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) acc[mt][nt][r] *= al;
+        }
+      }
+      f16x8 ph[MT], pl[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        ph[mt] = lds_f16x8(&sm.p_hi[16 * mt + (lane & 15)][8 * (lane >> 4)]);
+        pl[mt] = lds_f16x8(&sm.p_lo[16 * mt + (lane & 15)][8 * (lane >> 4)]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const f16x8 bv = lds_f16x8(&sm.cv[128 * wave + 16 * nt + (lane & 15)][8 * (lane >> 4)]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[mt], bv, acc[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- write the result (final when unsplit, else a partial for the combine)
+  if (a.splits == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * mt + 4 * (lane >> 4) + r;
+        const float l = sm.l_run[h];
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        float *orow = a.out + ((size_t)b * a.heads + h0 + h) * kLatent + 128 * wave + (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = acc[mt][nt][r] * inv;
+      }
+    if (a.lse != nullptr && tid < HG) {
+      const float l = sm.l_run[tid];
+      a.lse[(size_t)b * a.heads + h0 + tid] = l > 0.f ? (sm.m_run[tid] + log2f(l)) / kLog2e : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * mt + 4 * (lane >> 4) + r;
+        float *orow = a.part_o + (((size_t)b * a.heads + h0 + h) * a.splits + split) * kLatent + 128 * wave +
+                      (lane & 15);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = acc[mt][nt][r];
+      }
+    if (tid < HG) {
+      float *ml = a.part_ml + (((size_t)b * a.heads + h0 + tid) * a.splits + split) * 2;
+      ml[0] = sm.m_run[tid];
+      ml[1] = sm.l_run[tid];
+    }
+  }
+}
+
+// One workgroup of 128 threads per (b, h): merges the splits' partials.
+__global__ void __launch_bounds__(128) attn_combine_kernel(const float *__restrict__ part_o,
+                                                           const float *__restrict__ part_ml, int splits,
+                                                           float *__restrict__ out, float *__restrict__ lse) {
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *ml = part_ml + (size_t)bh * splits * 2;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, ml[2 * s]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < splits; ++s) {
+      const float ms = ml[2 * s];
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - m);
+      l += w * ml[2 * s + 1];
+      const float4 po = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + s) * kLatent)[tid];
+      o.x += w * po.x;
+      o.y += w * po.y;
+      o.z += w * po.z;
+      o.w += w * po.w;
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[tid] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (lse != nullptr && tid == 0) lse[bh] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
+}
+
+int heads_per_group(int heads) { return heads % 64 == 0 ? 64 : (heads % 32 == 0 ? 32 : 16); }
+
+int choose_splits(int batch, int heads, int top_k) {
+  const int groups = batch * (heads / heads_per_group(heads));
+  const int tiles = (top_k + kT - 1) / kT;
+  int splits = (512 + groups - 1) / groups;
+  if (splits > tiles) splits = tiles;
+  if (splits > 64) splits = 64;
+  if (splits < 1) splits = 1;
+  return splits;
+}
+
+}  // namespace
+
+size_t attn_workspace_bytes(int batch, int heads, int top_k) {
+  const int splits = choose_splits(batch, heads, top_k);
+  if (splits == 1) return 256;
+  const size_t o = (size_t)batch * heads * splits * kLatent * sizeof(float);
+  const size_t ml = (size_t)batch * heads * splits * 2 * sizeof(float);
+  return ((o + 255) & ~(size_t)255) + ((ml + 255) & ~(size_t)255);
+}
+
+hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
+                              const int32_t *indices, int top_k, float scale, float *out, float *lse, void *ws,
+                              hipStream_t st) {
+  if (S.batch == 0) return hipSuccess;
+  const int hgsz = heads_per_group(heads);
+  const int splits = choose_splits(S.batch, heads, top_k);
+  const int tiles = (top_k + kT - 1) / kT;
+  AttnArgs a;
+  a.L = L;
+  a.S = S;
+  a.q = q;
+  a.idx = indices;
+  a.heads = heads;
+  a.top_k = top_k;
+  a.splits = splits;
+  a.tiles_per_split = (tiles + splits - 1) / splits;
+  a.scale_log2 = scale * kLog2e;
+  a.out = out;
+  a.lse = lse;
+  const size_t o_bytes = (size_t)S.batch * heads * splits * kLatent * sizeof(float);
+  a.part_o = static_cast<float *>(ws);
+  a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o_bytes + 255) & ~(size_t)255));
+  const dim3 grid(splits, heads / hgsz, S.batch);
+  if (hgsz == 64) sparse_attn_kernel<4><<<grid, dim3(256), 0, st>>>(a);
+  else if (hgsz == 32) sparse_attn_kernel<2><<<grid, dim3(256), 0, st>>>(a);
+  else sparse_attn_kernel<1><<<grid, dim3(256), 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  attn_combine_kernel<<<dim3(S.batch * heads), dim3(128), 0, st>>>(a.part_o, a.part_ml, splits, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

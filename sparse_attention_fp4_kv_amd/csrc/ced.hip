@@ -1,0 +1,191 @@
+// CED global-KV projection with the FP4 pack fused into the epilogue.
+//
+// Source: discuss.pytorch.kr DeepSeek-V4.1-Flash summary, section "Causal
+// Encoder-Decoder": every decoder layer l takes its global KV from the last
+// encoder hidden state through its own weights, C_l = H W_l^KV and
+// Z_l = H W_l^Z.  The FP4 format of C is the one in section "FP4 KV cache".
+//
+// Design (ours): all layers form one GEMM
+//   out[t][n] = sum_k H[t][k] * W[n][k],  n = l * 576 + c  (c < 512: C_l, else Z_l)
+// with H [tokens][hidden] and the weights in out x in orientation, so both
+// operands are read along k (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// A workgroup computes a 128 x 128 output tile with 4 waves (64 x 64 each,
+// 2 x 2 MFMA tiles of 32 x 32), k-steps of 64 staged through LDS with a
+// register prefetch of the next step.  The epilogue parks the fp32 tile in
+// LDS and packs each 16-channel group of C straight to E2M1 + E4M3 (the same
+// rounding rules as the standalone pack) and rounds Z to bf16, so C never
+// reaches HBM in fp32 (unless the optional debug copy is asked for).
+#include "common.h"
+#include "kernels.h"
+
+namespace csa2 {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int kLdA = BK + 8;   // bf16 per LDS row (pad breaks bank conflicts)
+constexpr int kLdC = BN + 4;   // fp32 per epilogue row
+constexpr int kNPerLayer = kLatent + kIdxDim;  // 576
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+struct CedArgs {
+  const uint16_t *h;
+  const uint16_t *w_kv;
+  const uint16_t *w_z;
+  int64_t tokens;
+  int hidden;
+  int n_layers;
+  uint8_t *codes;
+  uint8_t *scales;
+  uint16_t *z;
+  float *c_f32;
+};
+
+// Row n of the combined weight matrix, or null for a Z row without weights.
+__device__ __forceinline__ const uint16_t *weight_row(const CedArgs &a, int n) {
+  const int l = n / kNPerLayer, c = n % kNPerLayer;
+  if (c < kLatent) return a.w_kv + ((size_t)l * kLatent + c) * a.hidden;
+  if (a.w_z == nullptr) return nullptr;
+  return a.w_z + ((size_t)l * kIdxDim + (c - kLatent)) * a.hidden;
+}
+
+union SmemCed {
+  struct {
+    uint16_t a[2][BM][kLdA];
+    uint16_t b[2][BN][kLdA];
+  } ab;
+  float c[BM][kLdC];
+};
+
+__global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
+  __shared__ __attribute__((aligned(16))) SmemCed sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int n_total = a.n_layers * kNPerLayer;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+
+  // global -> register staging: thread loads rows (tid / 8) + 32 * i, 16-byte column chunk tid % 8
+  const int ld_row = tid >> 3, ld_col = 8 * (tid & 7);
+  const uint16_t *a_src[4];
+  const uint16_t *b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = m0 + ld_row + 32 * i;
+    a_src[i] = m < a.tokens ? a.h + m * a.hidden + ld_col : nullptr;
+    const int n = n0 + ld_row + 32 * i;
+    b_src[i] = n < n_total ? weight_row(a, n) : nullptr;
+    if (b_src[i]) b_src[i] += ld_col;
+  }
+  uint4 ra[4], rb[4];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+      rb[i] = b_src[i] ? *reinterpret_cast<const uint4 *>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4 *>(&sm.ab.a[buf][ld_row + 32 * i][ld_col]) = ra[i];
+      *reinterpret_cast<uint4 *>(&sm.ab.b[buf][ld_row + 32 * i][ld_col]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int k_steps = a.hidden / BK;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int ks = 0; ks < k_steps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < k_steps) fetch((ks + 1) * BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = *reinterpret_cast<const bf16x8 *>(&sm.ab.a[buf][wm + 32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
+        fb[i] = *reinterpret_cast<const bf16x8 *>(&sm.ab.b[buf][wn + 32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < k_steps) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: fp32 tile -> LDS -> pack / round / store
+  // lane holds out[wm + 32i + 8*(e/4) + 4*(lane/32) + e%4][wn + 32j + lane%32]
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sm.c[wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][wn + 32 * j + (lane & 31)] = acc[i][j][e];
+  __syncthreads();
+  // 128 rows x 8 groups of 16 columns = 1024 groups, 4 per thread
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int g = tid + 256 * it;
+    const int r = g >> 3, cg = g & 7;
+    const int64_t t = m0 + r;
+    const int n = n0 + 16 * cg;
+    if (t >= a.tokens || n >= n_total) continue;
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = sm.c[r][16 * cg + i];
+    const int l = n / kNPerLayer, c = n % kNPerLayer;
+    const size_t row = (size_t)l * a.tokens + t;
+    if (c < kLatent) {
+      uint32_t w0, w1;
+      const uint32_t sc = pack_group16(v, &w0, &w1);
+      reinterpret_cast<uint2 *>(a.codes + row * (kLatent / 2))[c / kGroup] = make_uint2(w0, w1);
+      a.scales[row * (kLatent / kGroup) + c / kGroup] = (uint8_t)sc;
+      if (a.c_f32 != nullptr) {
+        float4 *dst = reinterpret_cast<float4 *>(a.c_f32 + row * kLatent + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+      }
+    } else if (a.z != nullptr && a.w_z != nullptr) {
+      uint32_t packed[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
+        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+        packed[i] = lo | (hi << 16);
+      }
+      uint4 *dst = reinterpret_cast<uint4 *>(a.z + row * kIdxDim + (c - kLatent));
+      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int n_layers, const uint16_t *w_kv,
+                              const uint16_t *w_z, uint8_t *codes, uint8_t *scales, uint16_t *z, float *c_f32,
+                              hipStream_t st) {
+  if (tokens == 0 || n_layers == 0) return hipSuccess;
+  CedArgs a{h, w_kv, w_z, tokens, hidden, n_layers, codes, scales, z, c_f32};
+  const int n_total = n_layers * kNPerLayer;
+  const dim3 grid((n_total + BN - 1) / BN, (unsigned)((tokens + BM - 1) / BM));
+  ced_kernel<<<grid, dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

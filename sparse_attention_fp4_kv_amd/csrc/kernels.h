@@ -1,0 +1,64 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the HIP
+// kernels.  Not installed; the public interface is include/csa2.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+// Device view of one KV layer's paged pool (validated copy of csa2_kv_layer).
+struct KvLayerDev {
+  uint8_t *codes;
+  uint8_t *scales;
+  uint16_t *rope;
+  void *idx_keys;
+  int num_blocks;
+  int rope_dim;  // 0 or 64
+  int idx_f32;   // 1: fp32 keys, 0: bf16 keys
+};
+
+// Device view of a batch (validated copy of csa2_seqs).
+struct SeqsDev {
+  const int32_t *block_table;
+  const int32_t *seq_lens;
+  int max_blocks;
+  int batch;
+  int max_len;  // host bound of seq_lens
+};
+
+hipError_t launch_fp4_pack(const float *x, int64_t rows, int channels, uint8_t *codes, uint8_t *scales,
+                           hipStream_t st);
+hipError_t launch_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int channels, float *y,
+                             hipStream_t st);
+hipError_t launch_kv_append(const KvLayerDev &L, const SeqsDev &S, const float *latent, const uint16_t *rope,
+                            const void *idx_key, hipStream_t st);
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+
+// ---- indexer / top-K (indexer.hip)
+size_t topk_workspace_bytes(int batch, int max_items, int top_k);
+hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, float *scores,
+                               hipStream_t st);
+hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t *lens, int batch, int max_len,
+                              int top_k, int32_t *indices, void *ws, hipStream_t st);
+size_t index_select_workspace_bytes(int batch, int max_len, int top_k, int pool_blocks);
+hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
+                                    int32_t *pool_out, int pool_blocks, int32_t *indices, void *ws,
+                                    hipStream_t st);
+hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
+                                       const int32_t *pool_in, int pool_blocks, int32_t *indices, void *ws,
+                                       hipStream_t st);
+
+// ---- attention (attention.hip)
+size_t attn_workspace_bytes(int batch, int heads, int top_k);
+hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
+                              const int32_t *indices, int top_k, float scale, float *out, float *lse, void *ws,
+                              hipStream_t st);
+
+// ---- CED projection (ced.hip)
+hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int n_layers, const uint16_t *w_kv,
+                              const uint16_t *w_z, uint8_t *codes, uint8_t *scales, uint16_t *z, float *c_f32,
+                              hipStream_t st);
+
+}  // namespace csa2

@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU parity tests: cache construction from the seeded
+inputs and the comparison rules.
+
+Comparison rules (fixed before any kernel was written):
+  * packing, pools of equal scores, integer work: bit-exact;
+  * top-K sets: equal, except positions whose oracle score lies within
+    1e-5 * max(|S_K|, rms(scores)) of the K-th oracle score S_K;
+  * attention: max |out - oracle| <= 2e-3 (fp32 accumulation), lse <= 1e-3.
+"""
+
+import numpy as np
+import torch
+
+import oracle
+from sparse_attention_fp4_kv_amd import csa2, workloads as wl
+
+ATTN_TOL = 2e-3
+LSE_TOL = 1e-3
+TOPK_REL = 1e-5
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    t = torch.from_numpy(a).to(dev())
+    return t if dtype is None else t.to(dtype)
+
+
+def build_tables(st, seq_lens, permuted, extra_blocks=0):
+    tables, nb = wl.block_tables(st, seq_lens, permuted, extra_blocks)
+    return tables, nb
+
+
+def fill_layer(layer, tables, seq_lens, latents=None, keys=None, ropes=None):
+    """Write per-sequence arrays into the paged pool at the table's physical rows.
+
+    latents[b]: fp32 [n_b][512] (packed on the GPU); keys[b]: fp32 or bf16 bits
+    [n_b][64]; ropes[b]: bf16 bits [n_b][64].
+    """
+    for b, n in enumerate(seq_lens):
+        if n == 0:
+            continue
+        rows = oracle.paged.physical_rows(tables[b], np.arange(n))
+        rows_t = torch.from_numpy(rows).to(dev())
+        if latents is not None:
+            codes, scales = csa2.csa2_fp4_pack(to_dev(latents[b]))
+            layer.codes[rows_t] = codes
+            layer.scales[rows_t] = scales
+        if keys is not None:
+            layer.idx_keys[rows_t] = to_dev(keys[b])
+        if ropes is not None:
+            layer.rope[rows_t] = to_dev(ropes[b])
+    torch.cuda.synchronize()
+
+
+def make_batch(tables, seq_lens, max_len=0):
+    return csa2.Batch(to_dev(tables.astype(np.int32)), to_dev(np.asarray(seq_lens, dtype=np.int32)), max_len)
+
+
+def topk_tolerance(scores):
+    scores = np.asarray(scores, dtype=np.float64)
+    return lambda sk: TOPK_REL * max(abs(sk), float(np.sqrt(np.mean(scores ** 2))) if scores.size else 0.0)
+
+
+def check_topk(gpu_row, score_of, k, where=""):
+    """gpu_row: int array [k] (-1 padded); score_of: dict position -> oracle score (all candidates)."""
+    gpu = [int(i) for i in gpu_row if i >= 0]
+    assert len(gpu) == len(set(gpu)), f"{where}: duplicate indices"
+    assert all(i in score_of for i in gpu), f"{where}: index outside the candidates"
+    pos = np.array(list(score_of.keys()), dtype=np.int64)
+    sc = np.array([score_of[p] for p in pos], dtype=np.float64)
+    ref = oracle.indexer.topk(sc, k, positions=pos)
+    ref_set = set(int(i) for i in ref if i >= 0)
+    assert len(gpu) == len(ref_set), f"{where}: {len(gpu)} selected, oracle {len(ref_set)}"
+    assert int(np.sum(np.asarray(gpu_row) < 0)) == k - len(ref_set), f"{where}: wrong -1 padding"
+    diff = ref_set.symmetric_difference(gpu)
+    if diff:
+        sk = min(score_of[i] for i in ref_set)
+        tol = topk_tolerance(sc)(sk)
+        bad = [i for i in diff if abs(score_of[i] - sk) > tol]
+        assert not bad, f"{where}: {len(diff)} differing indices, {len(bad)} beyond tolerance (S_K={sk})"
+    return len(diff)
+
+
+def oracle_attention_rows(latent, ropes, q_bits, sel, n, sigma):
+    """Oracle attention of one sequence: latent fp32 [n][512], sel positions, rope bits or None."""
+    valid = oracle.attention.valid_slots(sel, n)
+    codes, scales = oracle.fp4.fp4_pack(latent[valid]) if len(valid) else (np.zeros((0, 256), np.uint8),
+                                                                          np.zeros((0, 32), np.uint8))
+    c = oracle.fp4.fp4_unpack(codes, scales)
+    rope = oracle.ced.bf16_bits_to_f64(ropes[valid]) if ropes is not None else None
+    return oracle.attention.sparse_attention(q_bits, c, sigma, rope_sel=rope)

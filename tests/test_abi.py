@@ -1,0 +1,88 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and its host-side validation and page allocator behave as
+documented (no GPU work is launched by any call here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_fp4_kv_amd import csa2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HAVE_LIB = os.path.exists(csa2.LIB_PATH)
+needs_lib = pytest.mark.skipif(not HAVE_LIB, reason="libcsa2.so not built")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_lists_the_entry_points():
+    names = header_functions()
+    for must in ("csa2_fp4_pack", "csa2_fp4_unpack", "csa2_kv_append", "csa2_ced_kv_project", "csa2_index_select",
+                 "csa2_topk", "csa2_sparse_fp4_decode_attn", "csa2_block_pool_create"):
+        assert must in names
+    assert set(names) == set(csa2.SIGNATURES)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(csa2.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(raw, name), name
+    assert csa2.lib().csa2_abi_version() == 1
+    assert csa2.lib().csa2_status_string(3) == b"workspace missing or too small"
+
+
+@needs_lib
+def test_validation_rejects_before_launch():
+    L = csa2.lib()
+    s = None
+    assert L.csa2_fp4_pack(None, 4, 15, None, None, s) == csa2.ERR_INVALID_ARG
+    assert L.csa2_fp4_pack(None, -1, 16, None, None, s) == csa2.ERR_INVALID_ARG
+    assert L.csa2_fp4_pack(None, 0, 16, None, None, s) == csa2.OK  # empty is a no-op
+    assert L.csa2_fp4_pack(None, 4, 16, None, None, s) == csa2.ERR_INVALID_ARG
+    assert L.csa2_ced_kv_project(None, 4, 100, 1, None, None, None, None, None, None, s) == csa2.ERR_INVALID_ARG
+    n = ctypes.c_size_t()
+    assert L.csa2_topk_workspace_size(1, 100, 0, ctypes.byref(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_topk_workspace_size(1, 100, 4097, ctypes.byref(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_topk_workspace_size(2, 1000, 64, ctypes.byref(n)) == csa2.OK and n.value > 0
+    assert L.csa2_attn_workspace_size(1, 20, 64, 512, ctypes.byref(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_attn_workspace_size(1, 64, 2048, 512, ctypes.byref(n)) == csa2.OK
+    # a layer with the wrong page size is rejected
+    kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=16, num_blocks=1, block_tokens=32, latent_dim=512,
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16)
+    sq = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=1, max_seq_len=64)
+    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, 16, s) == csa2.ERR_INVALID_ARG
+    kv.block_tokens = 64
+    sq.max_seq_len = 65  # beyond max_blocks_per_seq * 64
+    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, 16, s) == csa2.ERR_INVALID_ARG
+    sq.max_seq_len = 64
+    # too-small workspace
+    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, 8, csa2.FULL, None, None, 0, 0, 16, 256, 1,
+                               s) == csa2.ERR_WORKSPACE
+    # Reindex without a pool
+    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, 8, csa2.REINDEX, None, None, 16, 8, 16, 256,
+                               1 << 30, s) == csa2.ERR_INVALID_ARG
+
+
+@needs_lib
+def test_block_pool():
+    p = csa2.BlockPool(5)
+    a = p.alloc(3)
+    assert a == [0, 1, 2] and p.num_free == 2
+    with pytest.raises(csa2.Csa2Error):
+        p.alloc(3)  # not enough: nothing taken
+    assert p.num_free == 2
+    with pytest.raises(csa2.Csa2Error):
+        p.free([1, 1])  # duplicate
+    with pytest.raises(csa2.Csa2Error):
+        p.free([4])  # already free
+    assert p.num_free == 2
+    p.free([1])
+    assert p.num_free == 3 and p.alloc(1) == [1]
+    p.close()

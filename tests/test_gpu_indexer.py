@@ -1,0 +1,128 @@
+"""GPU parity of indexer scores, exact top-K, Full / hierarchical / Reindex selection."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_fp4_kv_amd import csa2, workloads as wl
+
+from _util import build_tables, check_topk, fill_layer, make_batch, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _keys_layer(seq_lens, dtype, permuted, seed):
+    st = wl.Streams(seed)
+    tables, nb = build_tables(st, seq_lens, permuted)
+    keys = [wl.idx_keys(st, b, n, dtype) for b, n in enumerate(seq_lens)]
+    layer = csa2.PagedLayer(nb, idx_dtype=dtype, device="cuda")
+    fill_layer(layer, tables, seq_lens, keys=keys)
+    return st, tables, keys, layer
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scores_match_oracle(dtype):
+    seq_lens = [1000, 64, 1, 4096 + 13]
+    st, tables, keys, layer = _keys_layer(seq_lens, dtype, True, 40)
+    q = wl.q_idx(st, 0, len(seq_lens))
+    max_len = max(seq_lens)
+    batch = make_batch(tables, seq_lens, max_len)
+    s = csa2.csa2_index_scores(layer, batch, to_dev(q), max_len)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    for b, n in enumerate(seq_lens):
+        ref = oracle.indexer.index_scores(q[b], oracle.indexer.keys_to_f64(keys[b], dtype))
+        err = np.max(np.abs(s[b, :n] - ref) / (1e-6 + np.abs(ref).max()))
+        assert err < 1e-6, (b, err)
+        assert np.all(np.isneginf(s[b, n:]))
+
+
+def test_topk_exact_on_given_scores_with_ties():
+    """Integer scores with heavy ties: the index sets must match the oracle exactly."""
+    rng = np.random.default_rng(7)
+    lens = np.array([0, 1, 37, 300, 2047, 2048, 2049, 5000, 70000], dtype=np.int32)
+    M = int(lens.max())
+    sc = rng.integers(-20, 21, size=(len(lens), M)).astype(np.float32)
+    sc[3, :] = 5.0   # all equal
+    sc[5, ::2] = -0.0  # signed zeros must tie with +0
+    for K in (1, 7, 256, 2048, 4096):
+        idx = csa2.csa2_topk(to_dev(sc), to_dev(lens), K)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        for b, n in enumerate(lens):
+            ref = oracle.indexer.topk(sc[b, :n].astype(np.float64), K)
+            assert set(idx[b].tolist()) == set(ref.tolist()), (K, b)
+            assert np.sum(idx[b] < 0) == max(0, K - n)
+
+
+def test_topk_random_scores_repeatable_workspace():
+    rng = np.random.default_rng(8)
+    lens = np.array([65536, 30000, 4096], dtype=np.int32)
+    sc = rng.standard_normal((3, 65536)).astype(np.float32)
+    ws = csa2.workspace(csa2.topk_workspace_bytes(3, 65536, 2048))
+    for rep in range(3):  # the workspace is left zeroed by each call
+        idx = csa2.csa2_topk(to_dev(sc), to_dev(lens), 2048, ws=ws)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        for b, n in enumerate(lens):
+            ref = oracle.indexer.topk(sc[b, :n].astype(np.float64), 2048)
+            assert set(idx[b].tolist()) == set(ref.tolist()), (rep, b)
+
+
+@pytest.mark.parametrize("dtype,permuted", [("f32", False), ("bf16", True)])
+def test_full_select(dtype, permuted):
+    seq_lens = [4096, 65536 + 17, 100, 3000]
+    st, tables, keys, layer = _keys_layer(seq_lens, dtype, permuted, 41)
+    q = wl.q_idx(st, 0, len(seq_lens))
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    for K in (256, 2048):
+        idx, _ = csa2.csa2_index_select(layer, batch, to_dev(q), K, csa2.FULL)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        for b, n in enumerate(seq_lens):
+            s = oracle.indexer.index_scores(q[b], oracle.indexer.keys_to_f64(keys[b], dtype))
+            check_topk(idx[b], dict(enumerate(s)), K, where=f"K={K} b={b}")
+
+
+def test_hierarchical_pool_and_reindex():
+    seq_lens = [200000, 16384, 50, 70001]
+    P, K = 2048, 2048
+    st, tables, keys, layer = _keys_layer(seq_lens, "bf16", True, 42)
+    q0 = wl.q_idx(st, 0, len(seq_lens))
+    q1 = wl.q_idx(st, 1, len(seq_lens))
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    idx, pool = csa2.csa2_index_select(layer, batch, to_dev(q0), K, csa2.FULL, pool_blocks=P, want_pool=True)
+    torch.cuda.synchronize()
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    # Reindex stage fed with the oracle's pool, so a difference is the Reindex kernel's
+    o_pools = []
+    for b, n in enumerate(seq_lens):
+        kf = oracle.indexer.keys_to_f64(keys[b], "bf16")
+        s0 = oracle.indexer.index_scores(q0[b], kf)
+        bs = oracle.indexer.block_scores_fast(s0)
+        nb = len(bs)
+        check_topk(pool[b], dict(enumerate(bs)), P, where=f"pool b={b}")
+        check_topk(idx[b], dict(enumerate(s0)), K, where=f"full-in-pool b={b}")
+        o_pools.append(oracle.indexer.pool_blocks(s0, P))
+        assert np.sum(pool[b] >= 0) == min(P, nb)
+    o_pool_t = to_dev(np.stack(o_pools).astype(np.int32))
+    idx1, _ = csa2.csa2_index_select(layer, batch, to_dev(q1), K, csa2.REINDEX, pool_in=o_pool_t, pool_blocks=P)
+    torch.cuda.synchronize()
+    idx1 = idx1.cpu().numpy()
+    for b, n in enumerate(seq_lens):
+        kf = oracle.indexer.keys_to_f64(keys[b], "bf16")
+        pos = oracle.indexer.pool_positions(o_pools[b], n)
+        s1 = oracle.indexer.index_scores(q1[b], kf[pos])
+        check_topk(idx1[b], dict(zip(pos.tolist(), s1)), K, where=f"reindex b={b}")
+
+
+def test_select_rejects_bad_args():
+    seq_lens = [64]
+    st, tables, keys, layer = _keys_layer(seq_lens, "bf16", False, 43)
+    batch = make_batch(tables, seq_lens, 64)
+    q = to_dev(wl.q_idx(st, 0, 1))
+    with pytest.raises(csa2.Csa2Error):
+        csa2.csa2_index_select(layer, batch, q, 0, csa2.FULL)
+    with pytest.raises(csa2.Csa2Error):  # pool smaller than K
+        csa2.csa2_index_select(layer, batch, q, 64, csa2.FULL, pool_blocks=4, want_pool=True)
