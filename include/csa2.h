@@ -92,6 +92,15 @@ typedef struct {
 int csa2_abi_version(void);
 const char *csa2_status_string(csa2_status status);
 
+/* Profiling aid (not for concurrent use from several host threads): arms a
+ * one-shot timer on the next launch of the named kernel -- hipEventRecord of
+ * start_event (a hipEvent_t) just before it and of stop_event just after it,
+ * on the stream it is launched on.  Names: "index_scan" (the Full-mode key
+ * scan), "pool_score", "topk_given", "topk_compact", "sparse_attn",
+ * "attn_combine", "ced_project", "fp4_pack", "kv_append", "index_scores".
+ * kernel == NULL disarms.  Returns CSA2_ERR_INVALID_ARG for an unknown name. */
+csa2_status csa2_time_next_launch(const char *kernel, void *start_event, void *stop_event);
+
 /* Zero `bytes` of a workspace on `stream` (a fill kernel, no memset node). */
 csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream);
 
@@ -113,8 +122,10 @@ csa2_status csa2_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t
 /* ---- Decode-time append ([P1] "FP4 KV cache" format; the paged layout is
  * this library's).  For every sequence b, packs latent[b] (device fp32
  * [batch][latent_dim]) into the slot of position seq_lens[b] and copies
- * rope[b] (device bf16 [batch][rope_dim], or NULL) and idx_key[b] (device
- * [batch][idx_dim] of idx_dtype, or NULL) beside it.  The caller increments
+ * rope[b] (device bf16 [batch][rope_dim]) and idx_key[b] (device
+ * [batch][idx_dim] of idx_dtype) beside it.  Any of the three may be NULL
+ * (not all): a key-only pool appends just idx_key; a layer with a rope
+ * side-band needs rope whenever latent is given.  The caller increments
  * seq_lens afterwards.  A position whose page is not mapped (page index beyond
  * max_blocks_per_seq or page id outside the pool) is skipped. */
 csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
@@ -144,9 +155,10 @@ csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
 
 /* ---- Top-K of given scores: for each row b the top_k largest of
  * scores[b][0 .. lens[b]) (ties: lower position wins), written to
- * indices[b][0..top_k) in unspecified order and padded with -1 when
+ * indices[b][0..top_k) in increasing position order and padded with -1 when
  * lens[b] < top_k.  scores: device fp32 [batch][row_stride], finite;
- * lens: device int32 [batch]; max_len: host bound of lens (<= row_stride). */
+ * lens: device int32 [batch]; max_len: host bound of lens (<= row_stride,
+ * at most 8,388,608). */
 csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top_k, size_t *bytes);
 csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *lens, int32_t batch,
                       int32_t max_len, int32_t top_k, int32_t *indices, void *ws, size_t ws_bytes,
@@ -155,20 +167,21 @@ csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *le
 /* ---- Index selection ([P1] "CSA2" Full / Reindex modes and "Hierarchical
  * Sparse Indexer").
  * FULL: scores every visible position of each sequence with q_idx[b] and
- *   writes the top_k positions to indices[b] (unordered, -1 padded).  When
+ *   writes the top_k positions to indices[b] (ascending, -1 padded).  When
  *   pool_out is not NULL it also gives each aligned run of pool_block_tokens
  *   positions the maximum score inside it and writes the ids of the best
- *   pool_blocks runs (ties: lower id) to pool_out[b] (unordered, -1 padded).
- *   In that hierarchical case indices[b] is selected among the pool's
- *   positions, which holds the same set as over all positions except at
- *   exact ties of the K-th score (pool_blocks >= top_k is required).
+ *   pool_blocks runs (ties: lower id) to pool_out[b] (ascending, -1 padded).
+ *   indices[b] is the exact top_k over all positions in both cases.
  * REINDEX: scores only the positions of pool_in[b] (block ids from an
  *   earlier FULL call over the same keys) with this layer's q_idx and
- *   writes the top_k of them to indices[b].
+ *   writes the top_k of them to indices[b], in the order pool_in[b] lists
+ *   the blocks (increasing when pool_in comes from FULL).  Ids that are
+ *   negative or past the sequence are skipped; a repeated id is scored
+ *   twice, so its positions may repeat.
  * keys: the layer whose idx_keys are scored; q_idx: device fp32
  * [batch][idx_dim]; indices: device int32 [batch][top_k].
  * top_k in [1, 4096]; pool_block_tokens must be 8 and pool_blocks in
- * [1, 4096]. */
+ * [1, 2048]; max_seq_len at most 8,388,608.  Results are deterministic. */
 csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len, int32_t top_k,
                                              int32_t pool_blocks, int32_t pool_block_tokens,
                                              size_t *bytes);

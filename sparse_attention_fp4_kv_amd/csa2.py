@@ -64,6 +64,7 @@ _PSQ = ctypes.POINTER(Seqs)
 SIGNATURES = {
     "csa2_abi_version": (ctypes.c_int, []),
     "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "csa2_time_next_launch": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
     "csa2_workspace_clear": (ctypes.c_int, [_P, _SZ, _P]),
     "csa2_fp4_pack": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "csa2_fp4_unpack": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P]),
@@ -190,6 +191,18 @@ def workspace(nbytes, device="cuda"):
 
 
 # ----------------------------------------------------------------- entry points
+def csa2_time_next_launch(kernel, start_event=None, stop_event=None):
+    """Arm a one-shot HIP-event timing of the next launch of `kernel` (torch.cuda.Event pair)."""
+    if kernel is None:
+        _check(lib().csa2_time_next_launch(None, None, None), "csa2_time_next_launch")
+        return
+    for ev in (start_event, stop_event):
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record()
+    _check(lib().csa2_time_next_launch(kernel.encode(), ctypes.c_void_p(start_event.cuda_event),
+                                       ctypes.c_void_p(stop_event.cuda_event)), "csa2_time_next_launch")
+
+
 def csa2_workspace_clear(ws):
     _check(lib().csa2_workspace_clear(_ptr(ws), ws.numel(), _stream()), "csa2_workspace_clear")
 

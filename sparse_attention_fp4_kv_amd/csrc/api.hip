@@ -3,6 +3,7 @@
 // arguments before launching anything and never lets a C++ exception out.
 #include "../../include/csa2.h"
 
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -13,7 +14,8 @@ using namespace csa2;
 namespace {
 
 constexpr int kMaxTopK = 4096;
-constexpr int kMaxPoolBlocks = 4096;
+constexpr int kMaxPoolBlocks = 2048;  // pool positions must fit one 16,384-candidate select
+constexpr int64_t kMaxSelectLen = 4096LL * 2048;  // 8M positions per row
 
 hipStream_t as_stream(csa2_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -51,7 +53,7 @@ csa2_status check_seqs(const csa2_seqs *s, SeqsDev *out) {
   if (s->batch > 0 && (s->block_table == nullptr || s->seq_lens == nullptr)) return CSA2_ERR_INVALID_ARG;
   const int64_t cap = (int64_t)s->max_blocks_per_seq * 64;
   const int64_t ml = s->max_seq_len ? s->max_seq_len : cap;
-  if (ml > cap || ml > (int64_t)0x7FFFFFFF - 64) return CSA2_ERR_INVALID_ARG;
+  if (ml > cap || ml > kMaxSelectLen) return CSA2_ERR_INVALID_ARG;
   out->block_table = s->block_table;
   out->seq_lens = s->seq_lens;
   out->max_blocks = s->max_blocks_per_seq;
@@ -60,7 +62,31 @@ csa2_status check_seqs(const csa2_seqs *s, SeqsDev *out) {
   return CSA2_OK;
 }
 
+// One-shot launch timer armed by csa2_time_next_launch.
+struct ArmedTimer {
+  int id = -1;
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool started = false;
+};
+ArmedTimer g_timer;
+
+const char *const kKernelNames[kKernCount] = {"index_scan",  "pool_score",   "topk_given", "topk_compact",
+                                              "sparse_attn", "attn_combine", "ced_project", "fp4_pack",
+                                              "kv_append",   "index_scores"};
+
 }  // namespace
+
+namespace csa2 {
+void timer_before(KernelId id, hipStream_t st) {
+  if (g_timer.id != (int)id || g_timer.started) return;
+  if (hipEventRecord(g_timer.start, st) == hipSuccess) g_timer.started = true;
+}
+void timer_after(KernelId id, hipStream_t st) {
+  if (g_timer.id != (int)id || !g_timer.started) return;
+  (void)hipEventRecord(g_timer.stop, st);
+  g_timer = ArmedTimer();
+}
+}  // namespace csa2
 
 struct csa2_block_pool {
   std::vector<int32_t> free_ids;   // stack of free ids
@@ -80,6 +106,24 @@ const char *csa2_status_string(csa2_status s) {
     case CSA2_ERR_HIP: return "HIP error";
   }
   return "unknown status";
+}
+
+csa2_status csa2_time_next_launch(const char *kernel, void *start_event, void *stop_event) {
+  if (kernel == nullptr) {
+    g_timer = ArmedTimer();
+    return CSA2_OK;
+  }
+  if (start_event == nullptr || stop_event == nullptr) return CSA2_ERR_INVALID_ARG;
+  for (int i = 0; i < kKernCount; ++i) {
+    if (std::strcmp(kernel, kKernelNames[i]) == 0) {
+      g_timer.id = i;
+      g_timer.start = static_cast<hipEvent_t>(start_event);
+      g_timer.stop = static_cast<hipEvent_t>(stop_event);
+      g_timer.started = false;
+      return CSA2_OK;
+    }
+  }
+  return CSA2_ERR_INVALID_ARG;
 }
 
 csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream) {
@@ -110,13 +154,13 @@ csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, co
                            const uint16_t *rope, const void *idx_key, csa2_stream stream) {
   KvLayerDev L;
   SeqsDev S;
-  csa2_status st = check_layer(layer, true, false, &L);
+  csa2_status st = check_layer(layer, latent != nullptr, false, &L);
   if (st != CSA2_OK) return st;
   if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
   if (S.batch == 0) return CSA2_OK;
-  if (latent == nullptr) return CSA2_ERR_INVALID_ARG;
-  if (rope != nullptr && L.rope_dim == 0) return CSA2_ERR_INVALID_ARG;
-  if (L.rope_dim != 0 && rope == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (latent == nullptr && rope == nullptr && idx_key == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (rope != nullptr && (L.rope_dim == 0 || layer->rope == nullptr)) return CSA2_ERR_INVALID_ARG;
+  if (latent != nullptr && L.rope_dim != 0 && rope == nullptr) return CSA2_ERR_INVALID_ARG;
   if (idx_key != nullptr && (layer->idx_keys == nullptr || layer->idx_dim != 64 ||
                              (layer->idx_dtype != CSA2_F32 && layer->idx_dtype != CSA2_BF16)))
     return CSA2_ERR_INVALID_ARG;
@@ -151,14 +195,16 @@ csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
 }
 
 csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top_k, size_t *bytes) {
-  if (bytes == nullptr || batch < 0 || max_len < 0 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (bytes == nullptr || batch < 0 || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 || top_k > kMaxTopK)
+    return CSA2_ERR_INVALID_ARG;
   *bytes = topk_workspace_bytes(batch, max_len, top_k);
   return CSA2_OK;
 }
 
 csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *lens, int32_t batch, int32_t max_len,
                       int32_t top_k, int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream) {
-  if (batch < 0 || max_len < 0 || top_k < 1 || top_k > kMaxTopK || row_stride < max_len) return CSA2_ERR_INVALID_ARG;
+  if (batch < 0 || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 || top_k > kMaxTopK || row_stride < max_len)
+    return CSA2_ERR_INVALID_ARG;
   if (batch == 0) return CSA2_OK;
   if (scores == nullptr || lens == nullptr || indices == nullptr) return CSA2_ERR_INVALID_ARG;
   const size_t need = topk_workspace_bytes(batch, max_len, top_k);
@@ -168,7 +214,9 @@ csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *le
 
 csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len, int32_t top_k, int32_t pool_blocks,
                                              int32_t pool_block_tokens, size_t *bytes) {
-  if (bytes == nullptr || batch < 0 || max_seq_len < 0 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (bytes == nullptr || batch < 0 || max_seq_len < 0 || max_seq_len > kMaxSelectLen || top_k < 1 ||
+      top_k > kMaxTopK)
+    return CSA2_ERR_INVALID_ARG;
   if (pool_blocks < 0 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
   if (pool_blocks > 0 && pool_block_tokens != 8) return CSA2_ERR_INVALID_ARG;
   *bytes = index_select_workspace_bytes(batch, max_seq_len, top_k, pool_blocks);
@@ -189,7 +237,6 @@ csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
   const bool pooled = (mode == CSA2_REINDEX) || pool_out != nullptr;
   if (pooled) {
     if (pool_block_tokens != 8 || pool_blocks < 1 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
-    if (pool_blocks < top_k && mode == CSA2_FULL) return CSA2_ERR_INVALID_ARG;  // pool must hold the top-K
   }
   if (mode == CSA2_REINDEX && (pool_in == nullptr || pool_out != nullptr)) return CSA2_ERR_INVALID_ARG;
   if (mode == CSA2_FULL && pool_in != nullptr) return CSA2_ERR_INVALID_ARG;

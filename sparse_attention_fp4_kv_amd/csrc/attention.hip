@@ -36,6 +36,7 @@ constexpr int kQkLd = kLatent + 64 + 8;  // row-major tile row (f16): 512 latent
 constexpr int kVLd = kT + 8;           // transposed tile row (f16): 32 entries + pad
 constexpr int kPLd = kT + 8;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSplits = 32;         // split-K workgroups per (sequence, head group)
 
 struct AttnArgs {
   KvLayerDev L;
@@ -94,15 +95,19 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   else if constexpr (MT == 2) { qk_mt = wave >> 1; qk_nt0 = wave & 1; qk_ntn = 1; }
   else { qk_mt = 0; qk_nt0 = wave & 1; qk_ntn = wave < 2 ? 1 : 0; }
 
-  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*ks + 8*(lane/16) .. +7
+  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*ks + 8*(lane/16) .. +7.
+  // All loads are issued before any conversion (no branch between them).
   f16x8 qf[18];
   {
     const uint16_t *qrow = a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * qw + 8 * (lane >> 4);
+    uint4 raw[18];
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      if (ks < ks_total) qf[ks] = bf16x8_to_f16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * ks));
-      else qf[ks] = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < 16; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
+    const int rk = ks_total > 16 ? 1 : 0;  // rope k-steps re-read the last latent step when absent
+#pragma unroll
+    for (int ks = 16; ks < 18; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * (rk ? ks : 15));
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
   }
 
   // ---- PV accumulators: wave owns channels [128*wave, 128*wave+128) for all HG heads
@@ -145,15 +150,20 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     {
       const int e = tid >> 3, cb = tid & 7;
       const int64_t slot = sm.slot[e];
-      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = make_uint4(0, 0, 0, 0);
+      const int64_t rs = slot < 0 ? 0 : slot;  // invalid entries read slot 0 and are zeroed below
+      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0, rp = c0;
       uint32_t sc4 = 0;
-      uint4 rp = make_uint4(0, 0, 0, 0);
-      if (slot >= 0) {
-        const uint4 *cp = reinterpret_cast<const uint4 *>(a.L.codes + slot * (kLatent / 2) + 32 * cb);
+      if (a.L.num_blocks > 0) {  // uniform; an empty pool has no slot 0
+        const uint4 *cp = reinterpret_cast<const uint4 *>(a.L.codes + rs * (kLatent / 2) + 32 * cb);
         c0 = cp[0];
         c1 = cp[1];
-        sc4 = *reinterpret_cast<const uint32_t *>(a.L.scales + slot * (kLatent / kGroup) + 4 * cb);
-        if (a.L.rope_dim) rp = *reinterpret_cast<const uint4 *>(a.L.rope + slot * 64 + 8 * cb);
+        sc4 = *reinterpret_cast<const uint32_t *>(a.L.scales + rs * (kLatent / kGroup) + 4 * cb);
+        if (a.L.rope_dim) rp = *reinterpret_cast<const uint4 *>(a.L.rope + rs * 64 + 8 * cb);
+      }
+      if (slot < 0) {
+        c0 = c1 = make_uint4(0, 0, 0, 0);
+        sc4 = 0;
+        rp = make_uint4(0, 0, 0, 0);
       }
       const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
@@ -189,9 +199,19 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const int nt = qk_nt0 + j;
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
       const f16 *brow = &sm.cq[16 * nt + (lane & 15)][8 * (lane >> 4)];
+      // B fragments read 4 k-steps ahead of the MFMA that consumes them
+      f16x8 bq[16];
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        if (ks < ks_total) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], lds_f16x8(brow + 32 * ks), s, 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) bq[ks] = lds_f16x8(brow + 32 * ks);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        if (ks + 4 < 16) bq[ks + 4] = lds_f16x8(brow + 32 * (ks + 4));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], bq[ks], s, 0, 0, 0);
+      }
+      if (ks_total > 16) {
+#pragma unroll
+        for (int ks = 16; ks < 18; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], lds_f16x8(brow + 32 * ks), s, 0, 0, 0);
       }
       // lane holds S[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
       const int ent = 16 * nt + (lane & 15);
@@ -310,23 +330,31 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(const float *__restri
                                                            float *__restrict__ out, float *__restrict__ lse) {
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const float *ml = part_ml + (size_t)bh * splits * 2;
+  // all loads are unconditional (kMaxSplits-bounded unrolled loop): empty
+  // splits (m = -inf, l = 0, O = 0) get weight 0
+  const float2 *ml = reinterpret_cast<const float2 *>(part_ml + (size_t)bh * splits * 2);
+  float2 mls[kMaxSplits];
+  float4 po[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int sc = s < splits ? s : 0;
+    mls[s] = ml[sc];
+    po[s] = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + sc) * kLatent)[tid];
+  }
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, ml[2 * s]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < splits) m = fmaxf(m, mls[s].x);
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
   float l = 0.f;
-  if (m != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float ms = ml[2 * s];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - m);
-      l += w * ml[2 * s + 1];
-      const float4 po = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + s) * kLatent)[tid];
-      o.x += w * po.x;
-      o.y += w * po.y;
-      o.z += w * po.z;
-      o.w += w * po.w;
-    }
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const float w = (s < splits && mls[s].x != -INFINITY) ? exp2f(mls[s].x - m) : 0.f;
+    l += w * mls[s].y;
+    o.x += w * po[s].x;
+    o.y += w * po[s].y;
+    o.z += w * po[s].z;
+    o.w += w * po[s].w;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[tid] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
@@ -338,9 +366,9 @@ int heads_per_group(int heads) { return heads % 64 == 0 ? 64 : (heads % 32 == 0 
 int choose_splits(int batch, int heads, int top_k) {
   const int groups = batch * (heads / heads_per_group(heads));
   const int tiles = (top_k + kT - 1) / kT;
-  int splits = (512 + groups - 1) / groups;
+  int splits = (256 + groups - 1) / groups;  // about one workgroup per CU
   if (splits > tiles) splits = tiles;
-  if (splits > 64) splits = 64;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   if (splits < 1) splits = 1;
   return splits;
 }
@@ -378,12 +406,16 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   a.part_o = static_cast<float *>(ws);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o_bytes + 255) & ~(size_t)255));
   const dim3 grid(splits, heads / hgsz, S.batch);
+  timer_before(kKernSparseAttn, st);
   if (hgsz == 64) sparse_attn_kernel<4><<<grid, dim3(256), 0, st>>>(a);
   else if (hgsz == 32) sparse_attn_kernel<2><<<grid, dim3(256), 0, st>>>(a);
   else sparse_attn_kernel<1><<<grid, dim3(256), 0, st>>>(a);
+  timer_after(kKernSparseAttn, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
+  timer_before(kKernAttnCombine, st);
   attn_combine_kernel<<<dim3(S.batch * heads), dim3(128), 0, st>>>(a.part_o, a.part_ml, splits, out, lse);
+  timer_after(kKernAttnCombine, st);
   return hipGetLastError();
 }
 

@@ -184,7 +184,9 @@ hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int
   CedArgs a{h, w_kv, w_z, tokens, hidden, n_layers, codes, scales, z, c_f32};
   const int n_total = n_layers * kNPerLayer;
   const dim3 grid((n_total + BN - 1) / BN, (unsigned)((tokens + BM - 1) / BM));
+  timer_before(kKernCedProject, st);
   ced_kernel<<<grid, dim3(256), 0, st>>>(a);
+  timer_after(kKernCedProject, st);
   return hipGetLastError();
 }
 

@@ -3,27 +3,43 @@
 // Sources: discuss.pytorch.kr DeepSeek-V4.1-Flash summary, section "CSA2"
 // (Full / Reindex / Reuse modes: Full and Reindex score cached indexer keys
 // with their own query and select the top-K; Reuse selects nothing) and
-// section "Hierarchical Sparse Indexer" (the first Full layer also gives each
+// section "Hierarchical Sparse Indexer" (the first Full layer scores every
+// visible position, selects its own top-K and, in the same pass, gives each
 // block of 8 positions the maximum score inside it and keeps the best 2048
-// blocks, at most 16,384 positions, as the candidate pool that the later
+// blocks -- at most 16,384 positions -- as the candidate pool that the later
 // Reindex layers score).
 //
-// Design (ours; the pages give no kernel):
-//   Stage A  streams the keys once.  A wave scores one aligned run of 8
-//            positions per load (8 lanes per key, 16 B per lane, so 1 KB of
-//            bf16 keys per wave instruction), turns each score into an
-//            order-preserving 32-bit key, and counts the keys' top 11 bits in
-//            an LDS histogram that is merged into one of 8 global replicas
-//            (fewer atomics on one address).  The last workgroup of a row
-//            (atomic counter, no spinning) sums the replicas and finds the
-//            threshold bin T holding the K-th largest key.
-//   Stage B  re-reads the 4-byte keys: keys above bin T are selected outright
-//            (wave-aggregated atomic slots); keys in bin T become candidates
-//            (key, position) with composite (key << 32) | ~position.  The last
-//            workgroup of the row finishes with an exact radix select over
-//            the candidates' remaining 53 composite bits in LDS, so equal
-//            scores go to the lower position, then pads with -1.
-//   Scores are fp32 dot products (fp32 or bf16 keys, fp32 query).
+// Design (ours; the pages give no kernel).  A score is an fp32 dot product
+// (fp32 or bf16 keys, fp32 query) mapped to an order-preserving 32-bit key;
+// item order is (key descending, position ascending), so ties go to the lower
+// position.  No global atomics, fences or inter-workgroup waits are used: on
+// gfx950 they cost more than a kernel boundary.
+//   producers  Each workgroup owns a fixed slice of a row (2048 positions of a
+//              full scan, 2048 given scores, or 16 pool blocks), keeps its keys
+//              in LDS and stores all of them.  It then emits its best items as
+//              a candidate segment, cut exactly with two 11-bit radix levels to
+//              a budget of about 3x its expected share of the top-K, plus the
+//              segment's edge: every item it did not emit has a key below the
+//              edge.  The full scan streams the keys with non-temporal 16-byte
+//              loads, 16 in flight per lane, after one page-table lookup per
+//              64 positions; loads are never guarded by branches (unmapped
+//              pages read slot 0 and are masked).  In hierarchical mode it
+//              emits two segments: block maxima and positions.
+//   select     One 512-thread workgroup per row and output loads the segments
+//              into LDS in position order and finds the exact threshold with
+//              32-bit radix levels (11/11/10 key bits, then position bits only
+//              for ties at the boundary; each threshold search runs in one
+//              wave).  A segment whose edge exceeds the threshold's key may
+//              hold more winners: those segments are re-read in full from the
+//              stored keys (items at or above the threshold key only) and the
+//              threshold is recomputed, which is then exact.  If that would
+//              not fit in LDS, the select runs over every stored item of the
+//              row.  Outputs are written in increasing position order and
+//              padded with -1, so results are deterministic.
+//   Hierarchical Full: the block select (pool) and the position select (the
+//   layer's own top-K over all positions) run as two workgroups side by side.
+//   Reindex: 16-block producer workgroups score the pool with the layer's own
+//   query; the select runs as above.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,67 +47,127 @@ namespace csa2 {
 
 namespace {
 
-constexpr int kBins = 2048;      // top 11 key bits
-constexpr int kReplicas = 8;     // global histogram copies per row
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kBins = 2048;                    // 11-bit radix digits
+constexpr int kScanPos = 2048;                 // positions per producer workgroup
+constexpr int kScanPages = kScanPos / kPage;   // 32
+constexpr int kBlk = 8;                        // positions per pool block
+constexpr int kScanBlocks = kScanPos / kBlk;   // 256
+constexpr int kCandCap = 12288;                // candidates one select workgroup holds in LDS
+constexpr int kSelThreads = 512;
+constexpr int kSelIPT = kCandCap / kSelThreads;  // 24
+constexpr int kPoolBlocksPerWg = 16;           // pool producer: 16 blocks = 128 items
+constexpr int kPoolItemsPerWg = kPoolBlocksPerWg * kBlk;
+constexpr int kMaxPoolItems = 2048 * kBlk;     // 16,384
+constexpr int kMaxSeg = 4096;                  // segments per row (8M positions, host-validated)
+constexpr int kSegPerThread = kMaxSeg / kSelThreads;  // 8
 
-enum ItemMode { kPos = 0, kBlockMax = 1, kPool = 2, kGiven = 3 };
+enum SelMode { kFullPos = 0, kFullHier = 1, kReindex = 2, kGiven = 3 };
 
-struct RowState {
-  uint32_t ctrA, ctrB, thr, above, nsel, ncand, total, pad;
+struct SegInfo {
+  uint32_t count;  // candidates emitted
+  uint32_t edge;   // every item the segment did not emit has a key < edge
 };
 
-struct TopkWs {
-  RowState *rows;   // [B]
-  uint32_t *hist;   // [B][kReplicas][kBins]
-  uint32_t *keys;   // [B][cap]
-  uint64_t *cand;   // [B][cap]
-  int64_t cap;
+// Per-row workspace views.
+struct SelWs {
+  uint32_t *keys;    // [B][cap_keys]      position keys (scan) or keys of given scores
+  uint32_t *bkeys;   // [B][cap_blocks]    block-max keys (hierarchical scan)
+  uint2 *pool_full;  // [B][kMaxPoolItems] (key, position) of every pool item (Reindex)
+  uint2 *cand_pos;   // [B][kCandCap]      position candidates
+  uint2 *cand_blk;   // [B][kCandCap]      block candidates
+  SegInfo *seg_pos;  // [B][max_seg]
+  SegInfo *seg_blk;  // [B][max_seg]
+  int64_t cap_keys, cap_blocks;
+  int max_seg;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-TopkWs carve(void *ws, int batch, int64_t cap) {
+struct WsShape {
+  int64_t cap_keys, cap_blocks;
+  int max_seg;
+  bool pool;
+};
+
+WsShape ws_shape(int max_len, int pool_blocks) {
+  WsShape s;
+  s.cap_keys = round_up(max_len > 0 ? max_len : 1, kScanPos);
+  s.cap_blocks = round_up((s.cap_keys + kBlk - 1) / kBlk, kScanBlocks);
+  const int seg_scan = (int)(s.cap_keys / kScanPos);
+  const int seg_pool = (pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
+  s.max_seg = seg_scan > seg_pool ? seg_scan : seg_pool;
+  s.pool = pool_blocks > 0;
+  return s;
+}
+
+size_t ws_bytes_for(int batch, const WsShape &s) {
+  const size_t B = (size_t)batch;
+  return align256(4 * B * s.cap_keys) + align256(4 * B * s.cap_blocks) +
+         (s.pool ? align256(8 * B * kMaxPoolItems) : 0) + 2 * align256(8 * B * kCandCap) +
+         2 * align256(sizeof(SegInfo) * B * s.max_seg);
+}
+
+SelWs carve(void *ws, int batch, const WsShape &s) {
+  const size_t B = (size_t)batch;
   char *p = static_cast<char *>(ws);
-  TopkWs w;
-  w.rows = reinterpret_cast<RowState *>(p);
-  p += align256(sizeof(RowState) * batch);
-  w.hist = reinterpret_cast<uint32_t *>(p);
-  p += align256(sizeof(uint32_t) * (size_t)batch * kReplicas * kBins);
+  SelWs w;
   w.keys = reinterpret_cast<uint32_t *>(p);
-  p += align256(sizeof(uint32_t) * (size_t)batch * cap);
-  w.cand = reinterpret_cast<uint64_t *>(p);
-  w.cap = cap;
+  p += align256(4 * B * s.cap_keys);
+  w.bkeys = reinterpret_cast<uint32_t *>(p);
+  p += align256(4 * B * s.cap_blocks);
+  w.pool_full = nullptr;
+  if (s.pool) {
+    w.pool_full = reinterpret_cast<uint2 *>(p);
+    p += align256(8 * B * kMaxPoolItems);
+  }
+  w.cand_pos = reinterpret_cast<uint2 *>(p);
+  p += align256(8 * B * kCandCap);
+  w.cand_blk = reinterpret_cast<uint2 *>(p);
+  p += align256(8 * B * kCandCap);
+  w.seg_pos = reinterpret_cast<SegInfo *>(p);
+  p += align256(sizeof(SegInfo) * B * s.max_seg);
+  w.seg_blk = reinterpret_cast<SegInfo *>(p);
+  w.cap_keys = s.cap_keys;
+  w.cap_blocks = s.cap_blocks;
+  w.max_seg = s.max_seg;
   return w;
 }
 
-size_t ws_bytes(int batch, int64_t cap) {
-  return align256(sizeof(RowState) * batch) + align256(sizeof(uint32_t) * (size_t)batch * kReplicas * kBins) +
-         align256(sizeof(uint32_t) * (size_t)batch * cap) + align256(sizeof(uint64_t) * (size_t)batch * cap);
+// Candidate budget of a segment: about 3x its expected share of `need`
+// winners (at least 8), at most its size and its share of the LDS capacity.
+__device__ __forceinline__ int seg_budget(int need, int nseg, int ips) {
+  nseg = nseg > 0 ? nseg : 1;
+  int c = (3 * need + nseg - 1) / nseg;
+  if (c < 8) c = 8;
+  if (c > ips) c = ips;
+  const int lim = kCandCap / nseg;
+  return c < lim ? c : lim;
 }
 
 // ------------------------------------------------------------------ scoring
-// Lane l of a wave works on position l/8 of an aligned run of 8 and on dims
-// 8*(l%8) .. 8*(l%8)+7; the 8 partial sums of a position are combined with
-// three xor shuffles, so every lane ends with its position's score.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 struct KeyLoad {
-  uint4 a, b;  // bf16 keys use a only
+  u32x4 a, b;  // bf16 keys use a only
 };
 
+// Lane l works on position l/8 of an aligned run of 8 and on dims 8*(l%8) ..
+// +7 of its key; the 8 partial sums of a position are combined with three xor
+// shuffles, so every lane ends with its position's score.
 template <bool F32>
 __device__ __forceinline__ KeyLoad load_unit(const void *keys, int64_t slot0, int lane) {
   KeyLoad r;
   if constexpr (F32) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(keys) +
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(keys) +
                                                      (slot0 + (lane >> 3)) * kIdxDim + 8 * (lane & 7));
-    r.a = p[0];
-    r.b = p[1];
+    r.a = __builtin_nontemporal_load(p);
+    r.b = __builtin_nontemporal_load(p + 1);
   } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(keys) +
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(keys) +
                                                      (slot0 + (lane >> 3)) * kIdxDim + 8 * (lane & 7));
-    r.a = p[0];
-    r.b = make_uint4(0, 0, 0, 0);
+    r.a = __builtin_nontemporal_load(p);
+    r.b = u32x4{0, 0, 0, 0};
   }
   return r;
 }
@@ -100,23 +176,23 @@ template <bool F32>
 __device__ __forceinline__ float unit_score(const KeyLoad &k, const float (&q)[8]) {
   float s;
   if constexpr (F32) {
-    s = q[0] * __uint_as_float(k.a.x);
-    s = fmaf(q[1], __uint_as_float(k.a.y), s);
-    s = fmaf(q[2], __uint_as_float(k.a.z), s);
-    s = fmaf(q[3], __uint_as_float(k.a.w), s);
-    s = fmaf(q[4], __uint_as_float(k.b.x), s);
-    s = fmaf(q[5], __uint_as_float(k.b.y), s);
-    s = fmaf(q[6], __uint_as_float(k.b.z), s);
-    s = fmaf(q[7], __uint_as_float(k.b.w), s);
+    s = q[0] * __uint_as_float(k.a[0]);
+    s = fmaf(q[1], __uint_as_float(k.a[1]), s);
+    s = fmaf(q[2], __uint_as_float(k.a[2]), s);
+    s = fmaf(q[3], __uint_as_float(k.a[3]), s);
+    s = fmaf(q[4], __uint_as_float(k.b[0]), s);
+    s = fmaf(q[5], __uint_as_float(k.b[1]), s);
+    s = fmaf(q[6], __uint_as_float(k.b[2]), s);
+    s = fmaf(q[7], __uint_as_float(k.b[3]), s);
   } else {
-    s = q[0] * __uint_as_float(k.a.x << 16);
-    s = fmaf(q[1], __uint_as_float(k.a.x & 0xFFFF0000u), s);
-    s = fmaf(q[2], __uint_as_float(k.a.y << 16), s);
-    s = fmaf(q[3], __uint_as_float(k.a.y & 0xFFFF0000u), s);
-    s = fmaf(q[4], __uint_as_float(k.a.z << 16), s);
-    s = fmaf(q[5], __uint_as_float(k.a.z & 0xFFFF0000u), s);
-    s = fmaf(q[6], __uint_as_float(k.a.w << 16), s);
-    s = fmaf(q[7], __uint_as_float(k.a.w & 0xFFFF0000u), s);
+    s = q[0] * __uint_as_float(k.a[0] << 16);
+    s = fmaf(q[1], __uint_as_float(k.a[0] & 0xFFFF0000u), s);
+    s = fmaf(q[2], __uint_as_float(k.a[1] << 16), s);
+    s = fmaf(q[3], __uint_as_float(k.a[1] & 0xFFFF0000u), s);
+    s = fmaf(q[4], __uint_as_float(k.a[2] << 16), s);
+    s = fmaf(q[5], __uint_as_float(k.a[2] & 0xFFFF0000u), s);
+    s = fmaf(q[6], __uint_as_float(k.a[3] << 16), s);
+    s = fmaf(q[7], __uint_as_float(k.a[3] & 0xFFFF0000u), s);
   }
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
@@ -124,373 +200,821 @@ __device__ __forceinline__ float unit_score(const KeyLoad &k, const float (&q)[8
   return s;
 }
 
-// Physical slot of position t0 (a multiple of 8) of row b, or -1 when its
-// page is not mapped.
-__device__ __forceinline__ int64_t slot_of(const SeqsDev &S, int num_blocks, int b, int64_t t0) {
-  const int64_t page = t0 / kPage;
-  if (page >= S.max_blocks) return -1;
-  const int blk = S.block_table[(int64_t)b * S.max_blocks + page];
-  if (blk < 0 || blk >= num_blocks) return -1;
-  return (int64_t)blk * kPage + (t0 % kPage);
-}
-
 __device__ __forceinline__ int row_len(const SeqsDev &S, int b) {
   const int n = S.seq_lens[b];
   return n < 0 ? 0 : (n > S.max_len ? S.max_len : n);
 }
 
-// ------------------------------------------------------------------ scans
-// hist: kBins counts in LDS.  Finds the bin d with
-//   sum(hist[d+1..]) < need <= sum(hist[d..])
-// and returns d and sum(hist[d+1..]).  When all bins together hold fewer than
-// `need`, returns d = 0 and sum(hist[1..]).  Called by all kThreads threads;
-// red is LDS scratch of 2 * kThreads + 4 words.
-__device__ void find_threshold_bin(const uint32_t *hist, uint32_t need, uint32_t *red, uint32_t &bin,
-                                   uint32_t &above) {
-  const int t = threadIdx.x;
-  constexpr int per = kBins / kThreads;  // thread t owns bins [per*t, per*t + per)
-  uint32_t mine = 0;
+// Physical block of page `page` of row b, or -1 when it is not mapped.
+__device__ __forceinline__ int page_block(const SeqsDev &S, int num_blocks, int b, int64_t page) {
+  if (page < 0 || page >= S.max_blocks) return -1;
+  const int blk = S.block_table[(int64_t)b * S.max_blocks + page];
+  return (blk >= 0 && blk < num_blocks) ? blk : -1;
+}
+
+// ------------------------------------------------------------------ block-wide helpers
+// Exclusive prefix sum of one value per thread across a workgroup of NT
+// threads.  Returns the prefix; *total gets the sum.  scratch: NT/64 words.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch, uint32_t *total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
 #pragma unroll
-  for (int j = 0; j < per; ++j) mine += hist[per * t + j];
-  red[t] = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) scratch[wave] = incl;
   __syncthreads();
-  if (t < 64) {
-    uint32_t v[4];
-    uint32_t lane_sum = 0;
+  uint32_t wave_base = 0, tot = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[j] = red[4 * t + j];
-      lane_sum += v[j];
-    }
-    uint32_t incl = lane_sum;  // inclusive suffix sum over lanes t..63
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t s = scratch[w];
+    if (w < wave) wave_base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return wave_base + incl - v;
+}
+
+// Threshold digit of a 2048-bin histogram in LDS, computed by wave 0 alone:
+// the bin d with sum(hist[d+1..]) < need <= sum(hist[d..]).  Result in
+// res[0] = d, res[1] = sum(hist[d+1..]), res[2] = found (0 when all bins hold
+// fewer than `need`; then d = 0 and res[1] = total - hist[0]).  Every thread
+// must call it (it ends with a barrier).
+__device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t need, uint32_t *res) {
+  const int t = threadIdx.x;
+  if (t < 64) {
+    constexpr int per = kBins / 64;  // lane l owns bins [32l, 32l+32)
+    const u32x4 *h4 = reinterpret_cast<const u32x4 *>(&hist[per * t]);
+    u32x4 v[per / 4];
+#pragma unroll
+    for (int j = 0; j < per / 4; ++j) v[j] = h4[j];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < per / 4; ++j) mine += v[j][0] + v[j][1] + v[j][2] + v[j][3];
+    uint32_t incl = mine;  // sum over lanes t..63
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t o = __shfl_down(incl, off);
       if (t + off < 64) incl += o;
     }
-    uint32_t run = incl - lane_sum;
+    const uint32_t above_me = incl - mine;  // sum over lanes above t
+    const uint64_t hit = __ballot(above_me < need && incl >= need);
+    if (hit) {
+      // the boundary bin is one of lane src's: lanes 0..31 take its bins from
+      // the top down and a prefix sum over lanes gives each bin's count above
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const uint32_t base = __shfl(above_me, src);
+      const int bin = per * src + (per - 1) - (t & (per - 1));
+      const uint32_t h = t < per ? hist[bin] : 0u;
+      uint32_t cum = h;
 #pragma unroll
-    for (int j = 3; j >= 0; --j) {
-      red[kThreads + 4 * t + j] = run;  // sum of the threads above thread 4t+j
-      run += v[j];
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(cum, off);
+        if (t >= off) cum += o;
+      }
+      const uint64_t q = __ballot(t < per && base + cum - h < need && base + cum >= need);
+      if (t == __ffsll((unsigned long long)q) - 1) {
+        res[0] = (uint32_t)bin;
+        res[1] = base + cum - h;
+        res[2] = 1u;
+      }
+    } else if (t == 0) {
+      res[0] = 0u;
+      res[1] = incl - hist[0];
+      res[2] = 0u;
     }
-    if (t == 0) {
-      red[2 * kThreads] = 0u;
-      red[2 * kThreads + 1] = 0xFFFFFFFFu;
-      red[2 * kThreads + 2] = incl;  // total
-    }
-  }
-  __syncthreads();
-  uint32_t run = red[kThreads + t];
-#pragma unroll
-  for (int j = per - 1; j >= 0; --j) {
-    const uint32_t h = hist[per * t + j];
-    if (run < need && run + h >= need) {
-      red[2 * kThreads] = (uint32_t)(per * t + j);
-      red[2 * kThreads + 1] = run;
-    }
-    run += h;
-  }
-  __syncthreads();
-  bin = red[2 * kThreads];
-  above = red[2 * kThreads + 1];
-  if (above == 0xFFFFFFFFu) {
-    bin = 0;
-    above = red[2 * kThreads + 2] - hist[0];
   }
   __syncthreads();
 }
 
-// ------------------------------------------------------------------ stage A
-struct StageA {
+// Ordered compaction over a workgroup of NT threads.  Wave w owns items
+// [64 IPT w, 64 IPT (w + 1)); its lane l holds items 64 IPT w + 64 j + l
+// (j < IPT), so item order is (wave, j, lane) order.  Bit j of flags keeps
+// item j of this lane; emit(j, slot) is called for every kept item with its
+// slot base + (kept items before it).  Returns the number kept.  red: NT/64
+// words of LDS.
+template <int NT, int IPT, class Emit>
+__device__ __forceinline__ uint32_t ordered_emit(uint32_t flags, uint32_t *red, uint32_t base, Emit emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = __lanemask_lt();
+  uint64_t bal[IPT];
+  uint32_t wtot = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    bal[j] = __ballot((flags >> j) & 1u);
+    wtot += (uint32_t)__popcll(bal[j]);
+  }
+  if (lane == 0) red[wave] = wtot;
+  __syncthreads();
+  uint32_t wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = red[w];
+    wbase += w < wave ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  uint32_t run = base + wbase;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    if ((flags >> j) & 1u) emit(j, run + (uint32_t)__popcll(bal[j] & below));
+    run += (uint32_t)__popcll(bal[j]);
+  }
+  return tot;
+}
+
+// ------------------------------------------------------------------ producer: emission
+// Emits the best items of a producer workgroup (keys in LDS, key 0 = no item)
+// as an ordered candidate segment of at most `cap` items: whole 11-bit key
+// bins from the top, then the best 11-bit sub-bins of the boundary bin.
+// Thread t owns items [IPT*t, IPT*t + IPT); pos_of(i) is item i's position.
+template <int NT, int IPT, class PosOf>
+__device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
+                                             uint32_t *hist, uint32_t *red, PosOf pos_of) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int i0 = 64 * IPT * wave + lane;  // this lane's items: i0 + 64 j
+  uint32_t k[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) k[j] = keys_l[i0 + 64 * j];
+  for (int i = t; i < kBins; i += NT) hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < IPT; ++j)
+    if (k[j]) atomicAdd(&hist[k[j] >> 21], 1u);
+  __syncthreads();
+  find_threshold(hist, (uint32_t)cap + 1u, red + 16);
+  const uint32_t d1 = red[16], above = red[17];
+  const bool cut = red[18] != 0u;
+  uint32_t d2 = 0, edge = 0;
+  if (cut) {
+    // level 2 inside the boundary bin d1: room for cap - above of its items
+    const uint32_t room = (uint32_t)cap - above;
+    __syncthreads();
+    for (int i = t; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < IPT; ++j)
+      if (k[j] && (k[j] >> 21) == d1) atomicAdd(&hist[(k[j] >> 10) & 0x7FFu], 1u);
+    __syncthreads();
+    find_threshold(hist, room + 1u, red + 16);
+    d2 = red[16];  // found: bin d1 holds more than `room` items
+    const uint64_t e = ((uint64_t)d1 << 21) + ((uint64_t)(d2 + 1u) << 10);
+    edge = e > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)e;
+  }
+  uint32_t flags = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const uint32_t key = k[j];
+    const bool em =
+        key != 0u && (!cut || (key >> 21) > d1 || ((key >> 21) == d1 && ((key >> 10) & 0x7FFu) > d2));
+    flags |= em ? (1u << j) : 0u;
+  }
+  const uint32_t total = ordered_emit<NT, IPT>(flags, red, 0u, [&](int j, uint32_t slot) {
+    cand_seg[slot] = make_uint2(k[j], pos_of(i0 + 64 * j));
+  });
+  if (t == 0) *info = SegInfo{total, edge};
+}
+
+// ------------------------------------------------------------------ producer: full scan
+struct ScanArgs {
   KvLayerDev L;
   SeqsDev S;
-  const float *q_idx;     // [B][64]
-  const int32_t *pool;    // kPool: [B][pool_blocks]
-  int pool_blocks;
-  const float *scores;    // kGiven: [B][stride]
-  int64_t stride;
-  const int32_t *lens;    // kGiven: [B]
-  int units_per_wg;       // units of 8 items (kBlockMax: 8 positions -> 1 item)
-  uint32_t need;
-  TopkWs w;
+  const float *q_idx;
+  int K, P;  // top-K, pool blocks (hierarchical)
+  SelWs w;
 };
 
-__device__ __forceinline__ void hist_add(uint32_t *h, uint32_t key) {
-  if (key != 0u) atomicAdd(&h[key >> 21], 1u);
-}
-
-// After the workgroup's keys and histogram are in memory: count the
-// workgroup done; the last one of the row sums the replicas (reading and
-// zeroing them with atomic exchanges) and stores the threshold bin.
-__device__ void stage_a_finish(const StageA &a, int b, uint32_t *sh_hist, uint32_t *red) {
-  __shared__ uint32_t is_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&a.w.rows[b].ctrA, 1u);
-    is_last = (old == gridDim.x - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  uint32_t *g = a.w.hist + (size_t)b * kReplicas * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) {
-    uint32_t s = 0;
-#pragma unroll
-    for (int r = 0; r < kReplicas; ++r) s += atomicExch(&g[r * kBins + i], 0u);
-    sh_hist[i] = s;
-  }
-  __syncthreads();
-  uint32_t bin, above;
-  find_threshold_bin(sh_hist, a.need, red, bin, above);
-  if (threadIdx.x == 0) {
-    RowState &rs = a.w.rows[b];
-    rs.thr = bin;
-    rs.above = above;
-    rs.total = red[2 * kThreads + 2];
-    rs.ctrA = 0u;
-  }
-}
-
-template <int MODE, bool F32>
-__global__ void __launch_bounds__(kThreads) stage_a_kernel(StageA a) {
-  __shared__ uint32_t sh_hist[kBins];
-  __shared__ uint32_t red[2 * kThreads + 4];
-  const int b = blockIdx.y;
+template <bool F32, bool HIER>
+__global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
+  __shared__ int32_t pg[kScanPages];
+  __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
+  __shared__ __attribute__((aligned(16))) uint32_t bkey[kScanBlocks];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ uint32_t red[256 / 64 + 24];
+  const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = 0u;
+  const int n = row_len(a.S, b);
+  const int64_t base = (int64_t)wg * kScanPos;
+  if (base >= n) return;  // segments past the row are never read
+  const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
+  if (tid < kScanPages) pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
+  float q[8];
+  {
+    const float *qp = a.q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = qp[e];
+  }
   __syncthreads();
-
-  uint32_t *keys_out = a.w.keys + (size_t)b * a.w.cap;
-  const int64_t u_begin = (int64_t)blockIdx.x * a.units_per_wg;
-
-  if constexpr (MODE == kGiven) {
-    const int64_t n = a.lens[b] < 0 ? 0 : min((int64_t)a.lens[b], a.w.cap);
-    const int64_t i_begin = u_begin * 8, i_end = i_begin + (int64_t)a.units_per_wg * 8;
-    for (int64_t i = i_begin + tid; i < i_end && i < n; i += kThreads) {
-      const uint32_t key = score_key(a.scores[(size_t)b * a.stride + i]);
-      keys_out[i] = key;
-      hist_add(sh_hist, key);
-    }
-  } else {
-    const int n = row_len(a.S, b);
-    int64_t n_units;  // units of this row
-    if constexpr (MODE == kPool) n_units = a.pool_blocks;
-    else n_units = (n + 7) / 8;
-    const int64_t u_end = min(u_begin + a.units_per_wg, n_units);
-    float q[8];
-    {
-      const float *qp = a.q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
+  // wave w streams pages 8w .. 8w+7, two pages (16 loads of 1 KB) at a time
+#pragma unroll 1
+  for (int pp = 0; pp < 8; pp += 2) {
+    KeyLoad kl[16];
+    int pid[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = qp[e];
-    }
-    constexpr int kUnroll = 4;
-    for (int64_t u0 = u_begin + wave; u0 < u_end; u0 += kWaves * kUnroll) {
-      KeyLoad kl[kUnroll];
-      int64_t t0[kUnroll];
-      bool ok[kUnroll];
+    for (int h = 0; h < 2; ++h) pid[h] = pg[8 * wave + pp + h];
+    if (can_load) {
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int64_t u = u0 + (int64_t)j * kWaves;
-        ok[j] = false;
-        t0[j] = -1;
-        if (u < u_end) {
-          if constexpr (MODE == kPool) {
-            const int pb = a.pool[(size_t)b * a.pool_blocks + u];
-            t0[j] = pb < 0 ? -1 : (int64_t)pb * 8;
-          } else {
-            t0[j] = u * 8;
-          }
-          if (t0[j] >= 0 && t0[j] < n) {
-            const int64_t slot0 = slot_of(a.S, a.L.num_blocks, b, t0[j]);
-            if (slot0 >= 0) {
-              ok[j] = true;
-              kl[j] = load_unit<F32>(a.L.idx_keys, slot0, lane);
-            }
-          }
-        }
+      for (int u = 0; u < 16; ++u) {
+        const int id = pid[u >> 3] < 0 ? 0 : pid[u >> 3];  // unmapped: read slot 0, masked below
+        kl[u] = load_unit<F32>(a.L.idx_keys, (int64_t)id * kPage + 8 * (u & 7), lane);
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int64_t u = u0 + (int64_t)j * kWaves;
-        if (u >= u_end) continue;  // uniform across the wave
-        float s = 0.0f;
-        if (ok[j]) s = unit_score<F32>(kl[j], q);
-        const bool pos_ok = ok[j] && (t0[j] + (lane >> 3) < n);
-        if constexpr (MODE == kBlockMax) {
-          float m = pos_ok ? s : -INFINITY;
-          m = fmaxf(m, __shfl_xor(m, 8));
-          m = fmaxf(m, __shfl_xor(m, 16));
-          m = fmaxf(m, __shfl_xor(m, 32));
-          if (lane == 0) {
-            const uint32_t key = ok[j] ? score_key(m) : 0u;
-            keys_out[u] = key;
-            hist_add(sh_hist, key);
-          }
-        } else {
-          // items of a row: positions < n (kPos) or all pool_blocks * 8 slots (kPool)
-          const bool in_row = MODE == kPool || u * 8 + (lane >> 3) < n;
-          if ((lane & 7) == 0 && in_row) {
-            const uint32_t key = pos_ok ? score_key(s) : 0u;
-            keys_out[u * 8 + (lane >> 3)] = key;
-            hist_add(sh_hist, key);
-          }
-        }
+      for (int u = 0; u < 16; ++u) kl[u] = KeyLoad{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int page = 8 * wave + pp + (u >> 3);
+      const int lp = page * kPage + 8 * (u & 7) + (lane >> 3);  // local position
+      const bool ok = pid[u >> 3] >= 0 && base + lp < n;
+      const float s = unit_score<F32>(kl[u], q);
+      if ((lane & 7) == 0) pkey[lp] = ok ? score_key(s) : 0u;
+      if constexpr (HIER) {
+        float m = ok ? s : -INFINITY;
+        m = fmaxf(m, __shfl_xor(m, 8));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lane == 0) bkey[lp >> 3] = (pid[u >> 3] >= 0 && base + (lp & ~7) < n) ? score_key(m) : 0u;
       }
     }
   }
   __syncthreads();
-  // merge the workgroup histogram into replica blockIdx.x % kReplicas
-  uint32_t *g = a.w.hist + ((size_t)b * kReplicas + (blockIdx.x % kReplicas)) * kBins;
-  for (int i = tid; i < kBins; i += kThreads) {
-    const uint32_t c = sh_hist[i];
-    if (c) atomicAdd(&g[i], c);
+  // store every key (the select re-reads segments that overflow their budget)
+  {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(pkey);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.w.keys + (size_t)b * a.w.cap_keys + base);
+    dst[tid] = src[tid];
+    dst[tid + 256] = src[tid + 256];
+    if constexpr (HIER) a.w.bkeys[(size_t)b * a.w.cap_blocks + base / kBlk + tid] = bkey[tid];
   }
-  stage_a_finish(a, b, sh_hist, red);
+  const int nseg = (n + kScanPos - 1) / kScanPos;
+  {
+    const int cap = seg_budget(a.K, nseg, kScanPos);
+    emit_segment<256, 8>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                         a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
+                         [&](int i) { return (uint32_t)(base + i); });
+  }
+  if constexpr (HIER) {
+    __syncthreads();
+    const int cap = seg_budget(a.P, nseg, kScanBlocks);
+    emit_segment<256, 1>(bkey, cap, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap,
+                         a.w.seg_blk + (size_t)b * a.w.max_seg + wg, hist, red,
+                         [&](int i) { return (uint32_t)(base / kBlk + i); });
+  }
 }
 
-// ------------------------------------------------------------------ stage B
-struct StageB {
-  SeqsDev S;
-  int mode;               // ItemMode
-  const int32_t *pool;    // kPool
-  int pool_blocks;
-  const int32_t *lens;    // kGiven
-  int items_per_wg;
-  uint32_t need;
-  int32_t *out;           // [B][need]
-  TopkWs w;
+// ------------------------------------------------------------------ producer: given scores
+struct GivenArgs {
+  const float *scores;
+  int64_t stride;
+  const int32_t *lens;
+  int max_len;
+  int K;
+  SelWs w;
 };
 
-__device__ __forceinline__ int64_t items_of_row(const StageB &a, int b) {
-  if (a.mode == kGiven) return a.lens[b] < 0 ? 0 : min((int64_t)a.lens[b], a.w.cap);
+__global__ void __launch_bounds__(256) given_kernel(GivenArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ uint32_t red[256 / 64 + 24];
+  const int b = blockIdx.y, wg = blockIdx.x, tid = threadIdx.x;
+  const int n = min(max(a.lens[b], 0), a.max_len);
+  const int64_t base = (int64_t)wg * kScanPos;
+  if (base >= n) return;
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // loads first, clamped inside the row
+    const int64_t p = base + 8 * tid + j;
+    v[j] = a.scores[(size_t)b * a.stride + (p < n ? p : n - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pkey[8 * tid + j] = (base + 8 * tid + j < n) ? score_key(v[j]) : 0u;
+  __syncthreads();
+  uint32_t *kout = a.w.keys + (size_t)b * a.w.cap_keys + base;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kout[8 * tid + j] = pkey[8 * tid + j];
+  const int nseg = (n + kScanPos - 1) / kScanPos;
+  const int cap = seg_budget(a.K, nseg, kScanPos);
+  emit_segment<256, 8>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
+                       [&](int i) { return (uint32_t)(base + i); });
+}
+
+// ------------------------------------------------------------------ producer: pool scoring
+struct PoolArgs {
+  KvLayerDev L;
+  SeqsDev S;
+  const float *q_idx;
+  const int32_t *pool;  // [B][pool_blocks]
+  int pool_blocks;
+  int K;
+  SelWs w;
+};
+
+// Workgroup w scores pool blocks [16w, 16w+16) of its row (wave v: blocks
+// 4v .. 4v+3), stores every (key, position) and emits a budgeted segment.
+template <bool F32>
+__global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
+  __shared__ int64_t slot0[kPoolBlocksPerWg];
+  __shared__ int32_t tok0[kPoolBlocksPerWg];
+  __shared__ uint32_t key_l[256];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ uint32_t red[256 / 64 + 24];
+  const int b = blockIdx.y, wg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = row_len(a.S, b);
-  if (a.mode == kPos) return n;
-  if (a.mode == kBlockMax) return (n + 7) / 8;
-  return (int64_t)a.pool_blocks * 8;
-}
-
-__device__ __forceinline__ int32_t position_of(const StageB &a, int b, int64_t i) {
-  if (a.mode == kPool) return a.pool[(size_t)b * a.pool_blocks + (i >> 3)] * 8 + (int32_t)(i & 7);
-  return (int32_t)i;
-}
-
-// Wave-aggregated append: every lane with `pred` gets a distinct slot.
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t *counter) {
-  const uint64_t m = __ballot(pred);
-  const uint32_t cnt = (uint32_t)__popcll(m);
-  const int lane = threadIdx.x & 63;
-  const int leader = m ? __ffsll((unsigned long long)m) - 1 : 0;
-  uint32_t base = 0;
-  if (cnt && lane == leader) base = atomicAdd(counter, cnt);
-  base = __shfl(base, leader);
-  const uint64_t below = lane ? (m & ((~0ull) >> (64 - lane))) : 0ull;
-  return base + (uint32_t)__popcll(below);
-}
-
-__global__ void __launch_bounds__(kThreads) stage_b_kernel(StageB a) {
-  __shared__ uint32_t sh_hist[kBins];
-  __shared__ uint32_t red[2 * kThreads + 4];
-  __shared__ uint32_t is_last, emitted;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  RowState &rs = a.w.rows[b];
-  const uint32_t thr = rs.thr;
-  const int64_t items = items_of_row(a, b);
-  const uint32_t *keys = a.w.keys + (size_t)b * a.w.cap;
-  uint64_t *cand = a.w.cand + (size_t)b * a.w.cap;
-  int32_t *out = a.out + (size_t)b * a.need;
-
-  const int64_t i_begin = (int64_t)blockIdx.x * a.items_per_wg;
-  const int64_t i_end = i_begin + a.items_per_wg;
-  for (int64_t i0 = i_begin; i0 < i_end; i0 += kThreads) {
-    const int64_t i = i0 + tid;
-    const uint32_t key = (i < items && i < i_end) ? keys[i] : 0u;
-    const uint32_t bin = key >> 21;
-    const bool sure = key != 0u && bin > thr;
-    const bool maybe = key != 0u && bin == thr;
-    const uint32_t s_slot = wave_append(sure, &rs.nsel);
-    if (sure) out[s_slot] = position_of(a, b, i);
-    const uint32_t c_slot = wave_append(maybe, &rs.ncand);
-    if (maybe) cand[c_slot] = ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)position_of(a, b, i));
-  }
-
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&rs.ctrB, 1u);
-    is_last = (old == gridDim.x - 1) ? 1u : 0u;
-    emitted = 0u;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  const uint32_t above = rs.above;
-  const uint32_t nc = rs.ncand;
-  const uint32_t total = rs.total;
-  const uint32_t take = (total < a.need ? total : a.need) - above;  // candidates to keep
-  auto emit = [&](uint64_t c) {
-    const uint32_t slot = above + atomicAdd(&emitted, 1u);
-    out[slot] = (int32_t)(~(uint32_t)(c & 0xFFFFFFFFull));
-  };
-  if (take >= nc) {
-    for (uint32_t i = tid; i < nc; i += kThreads) emit(cand[i]);
-  } else {
-    uint64_t prefix = (uint64_t)thr << 53;
-    uint64_t mask = 0x7FFull << 53;
-    uint32_t need = take;
-    const int shifts[5] = {42, 32, 21, 10, 0};
-    const int widths[5] = {11, 10, 11, 11, 10};
-    for (int lv = 0; lv < 5; ++lv) {
-      const int sh = shifts[lv];
-      const uint64_t dm = (1ull << widths[lv]) - 1ull;
-      for (int i = tid; i < kBins; i += kThreads) sh_hist[i] = 0u;
-      __syncthreads();
-      for (uint32_t i = tid; i < nc; i += kThreads) {
-        const uint64_t c = cand[i];
-        if ((c & mask) == prefix) atomicAdd(&sh_hist[(c >> sh) & dm], 1u);
-      }
-      __syncthreads();
-      uint32_t d, above_d;
-      find_threshold_bin(sh_hist, need, red, d, above_d);
-      for (uint32_t i = tid; i < nc; i += kThreads) {
-        const uint64_t c = cand[i];
-        if ((c & mask) == prefix && ((c >> sh) & dm) > d) emit(c);
-      }
-      need -= above_d;
-      prefix |= (uint64_t)d << sh;
-      mask |= dm << sh;
-      const uint32_t at_d = sh_hist[d];
-      __syncthreads();
-      if (at_d == need) {
-        for (uint32_t i = tid; i < nc; i += kThreads) {
-          const uint64_t c = cand[i];
-          if ((c & mask) == prefix) emit(c);
+  if (tid < kPoolBlocksPerWg) {
+    const int j = wg * kPoolBlocksPerWg + tid;
+    int64_t s0 = -1;
+    int t0 = -1;
+    if (j < a.pool_blocks) {
+      const int pb = a.pool[(size_t)b * a.pool_blocks + j];
+      if (pb >= 0 && (int64_t)pb * kBlk < n) {
+        const int blk = page_block(a.S, a.L.num_blocks, b, ((int64_t)pb * kBlk) / kPage);
+        if (blk >= 0) {
+          s0 = (int64_t)blk * kPage + ((int64_t)pb * kBlk) % kPage;
+          t0 = pb * kBlk;
         }
-        break;
+      }
+    }
+    slot0[tid] = s0;
+    tok0[tid] = t0;
+  }
+  key_l[tid] = 0u;  // items 128..255 stay empty
+  float q[8];
+  {
+    const float *qp = a.q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = qp[e];
+  }
+  __syncthreads();
+  KeyLoad kl[4];
+  if (a.L.num_blocks > 0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s0 = slot0[4 * wave + u];
+      kl[u] = load_unit<F32>(a.L.idx_keys, s0 < 0 ? 0 : s0, lane);  // unmapped: slot 0, masked below
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kl[u] = KeyLoad{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int blk = 4 * wave + u;
+    const int t0 = tok0[blk];
+    const float s = unit_score<F32>(kl[u], q);
+    const bool ok = t0 >= 0 && t0 + (lane >> 3) < n;
+    if ((lane & 7) == 0) key_l[blk * kBlk + (lane >> 3)] = ok ? score_key(s) : 0u;
+  }
+  __syncthreads();
+  auto pos_of = [&](int i) { return (uint32_t)(tok0[i >> 3] + (i & 7)); };
+  if (tid < kPoolItemsPerWg) {
+    const uint32_t k = key_l[tid];
+    a.w.pool_full[(size_t)b * kMaxPoolItems + (size_t)wg * kPoolItemsPerWg + tid] =
+        make_uint2(k, k ? pos_of(tid) : 0u);
+  }
+  const int nseg = (a.pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
+  const int cap = seg_budget(a.K, nseg, kPoolItemsPerWg);
+  emit_segment<256, 1>(key_l, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red, pos_of);
+}
+
+// ------------------------------------------------------------------ select
+struct SelArgs {
+  SelWs w;
+  SeqsDev S;
+  const int32_t *lens;   // kGiven
+  int max_len;           // kGiven
+  int mode;
+  int K;                 // indices per row
+  int P;                 // pool blocks per row (kFullHier: output size; kReindex: input size)
+  int32_t *pool_out;     // kFullHier
+  int32_t *out;          // [B][K]
+};
+
+struct SelSmem {
+  uint32_t ck[kCandCap];      // candidate keys
+  uint32_t cp[kCandCap];      // candidate positions
+  uint32_t hist[kBins];
+  uint32_t seg_cnt[kMaxSeg];  // candidates a segment contributes
+  uint32_t seg_off[kMaxSeg];  // where they start in ck/cp
+  uint32_t red[kSelThreads / 64 + 24];
+};
+
+// Threshold of a selection: an item (key k, position p) is selected when
+//   (k >> ksh) >  (kt >> ksh), or
+//   (k >> ksh) == (kt >> ksh) and (!tie || ~p >= pinv).
+struct Thresh {
+  uint32_t kt, pinv;
+  int ksh;
+  bool tie;
+};
+
+__device__ __forceinline__ bool selected(uint32_t k, uint32_t p, const Thresh &th) {
+  const uint32_t a = k >> th.ksh, b = th.kt >> th.ksh;
+  return a > b || (a == b && (!th.tie || (~p) >= th.pinv));
+}
+
+// Smallest key any selected item can have.
+__device__ __forceinline__ uint32_t thresh_key_floor(const Thresh &th) { return (th.kt >> th.ksh) << th.ksh; }
+
+// Exact threshold for the top `need` (1 <= need <= #valid) of n items given by
+// key(i, valid) and pos(i): radix levels over the 32-bit key (digits of 11,
+// 11 and 10 bits), then, only when more items than remain share the boundary
+// key, over ~position among those items (lower positions win).  Each level
+// builds a histogram of its digit in LDS and picks the boundary digit with
+// one wave.
+template <class Key, class Pos>
+__device__ __forceinline__ Thresh find_thresh(SelSmem &sm, int64_t n, uint32_t need, Key key, Pos pos) {
+  const int t = threadIdx.x;
+  Thresh th{0u, 0u, 0, false};
+  uint32_t rem = need, pre = 0, ppre = 0;
+#pragma unroll 1
+  for (int lv = 0; lv < 6; ++lv) {
+    const bool posl = lv >= 3;
+    const int l = posl ? lv - 3 : lv;
+    const int sh = l == 0 ? 21 : (l == 1 ? 10 : 0);
+    const int hi = l == 0 ? 32 : (l == 1 ? 21 : 10);
+    const uint32_t dm = l == 2 ? 0x3FFu : 0x7FFu;
+    const uint32_t hp = hi >= 32 ? 0u : ((posl ? ppre : pre) >> hi);
+    for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int64_t i0 = t; i0 < n; i0 += 4 * kSelThreads) {
+      uint32_t kk[4];
+      bool vv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // reads first
+        const int64_t i = i0 + u * kSelThreads;
+        vv[u] = false;
+        kk[u] = i < n ? key(i, vv[u]) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u * kSelThreads;
+        const uint32_t v = posl ? (vv[u] ? ~pos(i) : 0u) : kk[u];
+        const bool ok = vv[u] && (!posl || kk[u] == pre) && (hi >= 32 || (v >> hi) == hp);
+        if (ok) atomicAdd(&sm.hist[(v >> sh) & dm], 1u);
+      }
+    }
+    __syncthreads();
+    find_threshold(sm.hist, rem, sm.red + 16);
+    const uint32_t d = sm.red[16];
+    rem -= sm.red[17];
+    const bool done = sm.hist[d] == rem;
+    __syncthreads();
+    if (!posl) {
+      pre |= d << sh;
+      th.kt = pre;
+      th.ksh = sh;
+      if (done) return th;
+      if (l == 2) th.tie = true;  // every key bit fixed: ties resolved by position
+    } else {
+      ppre |= d << sh;
+      th.pinv = ppre & ~((1u << sh) - 1u);
+      if (done) return th;
+    }
+  }
+  return th;
+}
+
+// Ordered compaction of the selected items (or of all valid ones) of n items
+// to out[0 .. out_cap); returns the count written.
+template <int IPT, class Key, class Pos>
+__device__ __forceinline__ uint32_t compact(SelSmem &sm, int64_t n, bool all, const Thresh &th, Key key, Pos pos,
+                                            int32_t *out, uint32_t out_cap) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t written = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += (int64_t)kSelThreads * IPT) {
+    const int64_t i0 = c0 + (int64_t)64 * IPT * wave + lane;  // this lane's items: i0 + 64 j
+    uint32_t flags = 0;
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int64_t i = i0 + 64 * j;
+      bool valid = false;
+      uint32_t k = 0;
+      if (i < n) k = key(i, valid);
+      if (valid && (all || selected(k, pos(i), th))) flags |= 1u << j;
+    }
+    written += ordered_emit<kSelThreads, IPT>(flags, sm.red, written, [&](int j, uint32_t slot) {
+      if (slot < out_cap) out[slot] = (int32_t)pos(i0 + 64 * j);  // cap: a repeated pool block
+    });
+  }
+  return written < out_cap ? written : out_cap;
+}
+
+// A row's candidate stream: nseg segments of ips items; segment s emitted
+// info[s].count candidates at cand[s * cap ..]; every item of segment s is
+// also stored: keys at full_keys[s * ips + i] (position s * ips + i) or
+// (key, position) pairs at full_pairs[s * ips + i].
+struct Stream {
+  const uint2 *cand;
+  const SegInfo *info;
+  const uint32_t *full_keys;
+  const uint2 *full_pairs;
+  int nseg, ips, cap;
+  int64_t items;  // stored items of the row (nseg * ips or fewer)
+};
+
+__device__ __forceinline__ uint2 stored_item(const Stream &s, int64_t i) {
+  if (s.full_pairs) return s.full_pairs[i];
+  return make_uint2(s.full_keys[i], (uint32_t)i);
+}
+
+// Exclusive prefix of v across one wave; *total gets the wave's sum.
+__device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t *total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  *total = __shfl(incl, 63);
+  return incl - v;
+}
+
+// One wave walks every stored item of segment s in position order and counts
+// (FILL false) or writes to ck/cp from dst on (FILL true) those with a
+// non-zero key >= floor_key.  Key segments hold ips = 256 or 2048 keys (one
+// 16-byte load per lane per 256), pair segments ips = 128 pairs.
+template <bool FILL>
+__device__ __forceinline__ uint32_t wave_segment(SelSmem &sm, const Stream &st, int s, uint32_t floor_key, uint32_t dst) {
+  const int lane = threadIdx.x & 63;
+  uint32_t run = 0;
+  if (st.full_pairs) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(st.full_pairs + (size_t)s * st.ips);
+    const int steps = st.ips / 128;
+    for (int u = 0; u < steps; ++u) {
+      const u32x4 v = src[64 * u + lane];  // pairs 2*lane and 2*lane + 1 of this step
+      const bool t0 = v[0] != 0u && v[0] >= floor_key, t1 = v[2] != 0u && v[2] >= floor_key;
+      uint32_t tot;
+      uint32_t o = run + wave_exclusive_scan((uint32_t)t0 + (uint32_t)t1, &tot);
+      if constexpr (FILL) {
+        if (t0) {
+          sm.ck[dst + o] = v[0];
+          sm.cp[dst + o] = v[1];
+          ++o;
+        }
+        if (t1) {
+          sm.ck[dst + o] = v[2];
+          sm.cp[dst + o] = v[3];
+        }
+      }
+      run += tot;
+    }
+  } else {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(st.full_keys + (size_t)s * st.ips);
+    const int steps = st.ips / 256;  // 1 or 8
+    for (int u0 = 0; u0 < steps; u0 += 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int du = 0; du < 4; ++du) v[du] = src[64 * (u0 + du < steps ? u0 + du : u0) + lane];  // loads first
+#pragma unroll
+    for (int du = 0; du < 4; ++du) {
+      const int u = u0 + du;
+      if (u >= steps) break;
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c += (v[du][e] != 0u && v[du][e] >= floor_key) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t o = run + wave_exclusive_scan(c, &tot);
+      if constexpr (FILL) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (v[du][e] != 0u && v[du][e] >= floor_key) {
+            sm.ck[dst + o] = v[du][e];
+            sm.cp[dst + o] = (uint32_t)((int64_t)s * st.ips + 256 * u + 4 * lane + e);
+            ++o;
+          }
+      }
+      run += tot;
+    }
+    }
+  }
+  return run;
+}
+
+// Copies every segment's emitted candidates to ck/cp at seg_off (segments in
+// order, so positions stay ordered) with one load per slot: segment s owns
+// slots [s * cap, s * cap + cap) of cand, of which the first seg_cnt[s] are
+// filled.  When ovf_l is given, segments whose bit is set there are left out.
+__device__ __forceinline__ void copy_candidates(SelSmem &sm, const Stream &st, int nseg, const uint32_t *ovf_l) {
+  const int t = threadIdx.x;
+  const int slots = nseg * st.cap;  // <= kCandCap
+  const float inv_cap = 1.0f / (float)st.cap;
+  constexpr int kBatch = 12;
+#pragma unroll 1
+  for (int u0 = 0; u0 < kSelIPT; u0 += kBatch) {
+    if (t + kSelThreads * u0 >= slots) break;
+    uint2 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = t + kSelThreads * (u0 + u);
+      v[u] = st.cand[j < slots ? j : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = t + kSelThreads * (u0 + u);
+      if (j < slots) {
+        int sg = (int)((float)j * inv_cap);  // j / cap, corrected below
+        int i = j - sg * st.cap;
+        if (i < 0) {
+          --sg;
+          i += st.cap;
+        } else if (i >= st.cap) {
+          ++sg;
+          i -= st.cap;
+        }
+        const bool skip = ovf_l && ((ovf_l[sg >> 5] >> (sg & 31)) & 1u);
+        if (!skip && (uint32_t)i < sm.seg_cnt[sg]) {
+          const uint32_t d = sm.seg_off[sg] + (uint32_t)i;
+          sm.ck[d] = v[u].x;
+          sm.cp[d] = v[u].y;
+        }
       }
     }
   }
-  __syncthreads();
-  const uint32_t filled = above + emitted;
-  for (uint32_t i = filled + tid; i < a.need; i += kThreads) out[i] = -1;
-  __syncthreads();
-  if (tid == 0) {
-    rs.ctrB = 0u;
-    rs.thr = 0u;
-    rs.above = 0u;
-    rs.nsel = 0u;
-    rs.ncand = 0u;
-    rs.total = 0u;
+}
+
+// The select over every stored item of a row, for rows whose candidates do
+// not fit in LDS (heavily clustered or tied scores).
+__device__ __forceinline__ uint32_t select_all_stored(SelSmem &sm, const Stream &st, int need, int32_t *out) {
+  const int t = threadIdx.x;
+  auto gkey = [&](int64_t i, bool &valid) {
+    const uint32_t k = stored_item(st, i).x;
+    valid = k != 0u;
+    return k;
+  };
+  auto gpos = [&](int64_t i) { return stored_item(st, i).y; };
+  uint32_t v = 0;
+  for (int64_t i = t; i < st.items; i += kSelThreads) v += stored_item(st, i).x != 0u;
+  uint32_t tot;
+  block_exclusive_scan<kSelThreads>(v, sm.red, &tot);
+  const bool all = (int64_t)tot <= need;
+  Thresh th{0u, 0u, 0, false};
+  if (!all) th = find_thresh(sm, st.items, (uint32_t)need, gkey, gpos);
+  return compact<2>(sm, st.items, all, th, gkey, gpos, out, (uint32_t)need);
+}
+
+// Top `need` of a row from its stream, in increasing position order (stream
+// order for a pool), -1 padded.
+__device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int need, int32_t *out) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int nseg = st.nseg < kMaxSeg ? st.nseg : kMaxSeg;
+  // --- segment infos: thread t owns segments kSegPerThread * t .. + kSegPerThread - 1 (loads first)
+  SegInfo si[kSegPerThread];
+#pragma unroll
+  for (int j = 0; j < kSegPerThread; ++j) {
+    const int s = kSegPerThread * t + j;
+    si[j] = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)];
   }
+  uint32_t cnt = 0, emax = 0;
+#pragma unroll
+  for (int j = 0; j < kSegPerThread; ++j) {
+    const int s = kSegPerThread * t + j;
+    if (s < nseg) {
+      cnt += si[j].count;
+      emax = emax > si[j].edge ? emax : si[j].edge;
+    }
+  }
+  uint32_t C;
+  {
+    uint32_t off = block_exclusive_scan<kSelThreads>(cnt, sm.red, &C);
+#pragma unroll
+    for (int j = 0; j < kSegPerThread; ++j) {
+      const int s = kSegPerThread * t + j;
+      if (s < nseg) {
+        sm.seg_cnt[s] = si[j].count;
+        sm.seg_off[s] = off;
+        off += si[j].count;
+      }
+    }
+  }
+  // largest edge over the row
+  {
+    uint32_t e = emax;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_xor(e, o);
+      e = e > x ? e : x;
+    }
+    if (lane == 0) sm.red[16 + wave] = e;
+  }
+  __syncthreads();
+  uint32_t max_edge = 0;
+  for (int w = 0; w < kSelThreads / 64; ++w) max_edge = max_edge > sm.red[16 + w] ? max_edge : sm.red[16 + w];
+  copy_candidates(sm, st, nseg, nullptr);
+  __syncthreads();
+
+  auto lkey = [&](int64_t i, bool &valid) {
+    const uint32_t k = sm.ck[i];
+    valid = k != 0u;
+    return k;
+  };
+  auto lpos = [&](int64_t i) { return sm.cp[i]; };
+  // Pass 0 selects among the emitted candidates.  Items a segment left out
+  // are below its edge, so when no edge is above the selection's key floor
+  // that selection is exact.  Otherwise the segments with such an edge are
+  // re-read in full (items at or above the floor only) and pass 1 selects
+  // among the larger set, which is then exact: its threshold can only rise.
+  uint32_t n_c = C, written = 0;
+  for (int pass = 0;; ++pass) {
+    Thresh th{0u, 0u, 0, false};
+    const bool all = n_c <= (uint32_t)need;
+    if (!all) th = find_thresh(sm, (int64_t)n_c, (uint32_t)need, lkey, lpos);
+    const uint32_t floor_key = all ? 0u : thresh_key_floor(th);
+    if (pass == 1 || (all ? max_edge == 0u : max_edge <= floor_key)) {
+      written = compact<8>(sm, n_c, all, th, lkey, lpos, out, (uint32_t)need);
+      break;
+    }
+    // --- overflowing segments: a bitmap in hist (kMaxSeg bits)
+    uint32_t *ovf_l = sm.hist;
+    auto is_ovf = [&](int s) { return (ovf_l[s >> 5] >> (s & 31)) & 1u; };
+    __syncthreads();
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSegPerThread; ++j) {  // edges re-read: keeps registers free on the common path
+      const int s = kSegPerThread * t + j;
+      const uint32_t edge = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)].edge;
+      if (s < nseg && edge > floor_key) mine |= 1u << j;
+    }
+    // thread t's bits land at bit kSegPerThread * (t % tpw) of word t / tpw
+    {
+      constexpr int tpw = 32 / kSegPerThread;
+      uint32_t word = mine << (kSegPerThread * (t % tpw));
+#pragma unroll
+      for (int o = 1; o < tpw; o <<= 1) word |= __shfl_xor(word, o);
+      if (t % tpw == 0) ovf_l[t / tpw] = word;
+    }
+    __syncthreads();
+    // --- count, one wave per overflowing segment (wave w: segments w, w+16, ...)
+    for (int s = wave; s < nseg; s += kSelThreads / 64)
+      if (is_ovf(s)) {
+        const uint32_t c = wave_segment<false>(sm, st, s, floor_key, 0u);
+        if (lane == 0) sm.seg_cnt[s] = c;
+      }
+    __syncthreads();
+    uint32_t cnt2 = 0;
+#pragma unroll
+    for (int j = 0; j < kSegPerThread; ++j) {
+      const int s = kSegPerThread * t + j;
+      if (s < nseg) cnt2 += sm.seg_cnt[s];
+    }
+    uint32_t C2;
+    uint32_t off2 = block_exclusive_scan<kSelThreads>(cnt2, sm.red, &C2);
+    if (C2 > (uint32_t)kCandCap) {
+      written = select_all_stored(sm, st, need, out);
+      break;
+    }
+#pragma unroll
+    for (int j = 0; j < kSegPerThread; ++j) {
+      const int s = kSegPerThread * t + j;
+      if (s < nseg) {
+        sm.seg_off[s] = off2;
+        off2 += sm.seg_cnt[s];
+      }
+    }
+    __syncthreads();
+    copy_candidates(sm, st, nseg, ovf_l);
+    for (int s = wave; s < nseg; s += kSelThreads / 64)
+      if (is_ovf(s)) wave_segment<true>(sm, st, s, floor_key, sm.seg_off[s]);
+    __syncthreads();
+    n_c = C2;
+  }
+  __syncthreads();
+  for (int i = (int)written + t; i < need; i += kSelThreads) out[i] = -1;
+}
+
+// grid (1 or 2, B): x == 0 selects positions (indices), x == 1 the pool blocks.
+__global__ void __launch_bounds__(kSelThreads) select_kernel(SelArgs a) {
+  __shared__ SelSmem sm;
+  const int b = blockIdx.y;
+  const bool re = a.mode == kReindex, blk = blockIdx.x != 0;
+  const int n = re ? 0 : (a.mode == kGiven ? min(max(a.lens[b], 0), a.max_len) : row_len(a.S, b));
+  Stream st;
+  st.cand = (blk ? a.w.cand_blk : a.w.cand_pos) + (size_t)b * kCandCap;
+  st.info = (blk ? a.w.seg_blk : a.w.seg_pos) + (size_t)b * a.w.max_seg;
+  st.full_keys = re ? nullptr : (blk ? a.w.bkeys + (size_t)b * a.w.cap_blocks : a.w.keys + (size_t)b * a.w.cap_keys);
+  st.full_pairs = re ? a.w.pool_full + (size_t)b * kMaxPoolItems : nullptr;
+  st.nseg = re ? (a.P + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg : (n + kScanPos - 1) / kScanPos;
+  st.ips = re ? kPoolItemsPerWg : (blk ? kScanBlocks : kScanPos);
+  st.items = re ? (int64_t)a.P * kBlk : (blk ? (n + kBlk - 1) / kBlk : n);
+  const int need = blk ? a.P : a.K;
+  int32_t *out = blk ? a.pool_out + (size_t)b * a.P : a.out + (size_t)b * a.K;
+  st.cap = seg_budget(need, st.nseg, st.ips);
+  select_stream(sm, st, need, out);
 }
 
 // ------------------------------------------------------------------ scores only
 template <bool F32>
-__global__ void __launch_bounds__(kThreads) scores_kernel(KvLayerDev L, SeqsDev S, const float *q_idx, float *scores,
-                                                          int units_per_wg) {
+__global__ void __launch_bounds__(256) scores_kernel(KvLayerDev L, SeqsDev S, const float *q_idx, float *scores,
+                                                     int units_per_wg) {
   const int b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = row_len(S, b);
@@ -501,56 +1025,33 @@ __global__ void __launch_bounds__(kThreads) scores_kernel(KvLayerDev L, SeqsDev 
   const float *qp = q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
 #pragma unroll
   for (int e = 0; e < 8; ++e) q[e] = qp[e];
-  for (int64_t u = u_begin + wave; u < u_end; u += kWaves) {
+  for (int64_t u = u_begin + wave; u < u_end; u += 4) {
     const int64_t t0 = u * 8;
-    bool ok = false;
-    KeyLoad kl;
-    if (t0 < n) {
-      const int64_t slot0 = slot_of(S, L.num_blocks, b, t0);
-      if (slot0 >= 0) {
-        ok = true;
-        kl = load_unit<F32>(L.idx_keys, slot0, lane);
-      }
-    }
-    float s = ok ? unit_score<F32>(kl, q) : 0.0f;
+    const int blk = (t0 < n && L.num_blocks > 0) ? page_block(S, L.num_blocks, b, t0 / kPage) : -1;
+    const KeyLoad kl = load_unit<F32>(L.idx_keys, blk < 0 ? 0 : (int64_t)blk * kPage + t0 % kPage, lane);
+    const float s = unit_score<F32>(kl, q);
     const int64_t t = t0 + (lane >> 3);
-    if ((lane & 7) == 0 && t < S.max_len) scores[(size_t)b * S.max_len + t] = (ok && t < n) ? s : -INFINITY;
+    if ((lane & 7) == 0 && t < S.max_len) scores[(size_t)b * S.max_len + t] = (blk >= 0 && t < n) ? s : -INFINITY;
   }
 }
 
-template <int MODE>
-hipError_t run_stage_a(const StageA &a, int64_t units_per_row, int batch, hipStream_t st) {
-  const int64_t gx = (units_per_row + a.units_per_wg - 1) / a.units_per_wg;
-  if (gx <= 0 || batch <= 0) return hipSuccess;
-  const dim3 grid((unsigned)gx, (unsigned)batch);
-  if (a.L.idx_f32) stage_a_kernel<MODE, true><<<grid, dim3(kThreads), 0, st>>>(a);
-  else stage_a_kernel<MODE, false><<<grid, dim3(kThreads), 0, st>>>(a);
+hipError_t run_select(const SelArgs &a, int outputs, int batch, hipStream_t st) {
+  timer_before(kKernTopkCompact, st);
+  select_kernel<<<dim3(outputs, batch), dim3(kSelThreads), 0, st>>>(a);
+  timer_after(kKernTopkCompact, st);
   return hipGetLastError();
 }
-
-hipError_t run_stage_b(const StageB &a, int64_t items_per_row, int batch, hipStream_t st) {
-  const int64_t gx = (items_per_row + a.items_per_wg - 1) / a.items_per_wg;
-  if (gx <= 0 || batch <= 0) return hipSuccess;
-  stage_b_kernel<<<dim3((unsigned)gx, (unsigned)batch), dim3(kThreads), 0, st>>>(a);
-  return hipGetLastError();
-}
-
-constexpr int kPosUnitsPerWg = 128;   // 1024 positions per workgroup in a full scan
-constexpr int kPoolUnitsPerWg = 16;   // 16 pool blocks (128 positions) per workgroup
-constexpr int kItemsPerWgB = 2048;    // stage B items per workgroup
 
 }  // namespace
 
 size_t topk_workspace_bytes(int batch, int max_items, int top_k) {
   (void)top_k;
-  return ws_bytes(batch, max_items > 0 ? max_items : 1);
+  return ws_bytes_for(batch, ws_shape(max_items, 0));
 }
 
 size_t index_select_workspace_bytes(int batch, int max_len, int top_k, int pool_blocks) {
   (void)top_k;
-  int64_t cap = max_len;
-  if ((int64_t)pool_blocks * 8 > cap) cap = (int64_t)pool_blocks * 8;
-  return ws_bytes(batch, cap > 0 ? cap : 1);
+  return ws_bytes_for(batch, ws_shape(max_len, pool_blocks));
 }
 
 hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, float *scores,
@@ -560,75 +1061,88 @@ hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, const floa
   const int64_t gx = (units + per - 1) / per;
   if (gx <= 0 || S.batch <= 0) return hipSuccess;
   const dim3 grid((unsigned)gx, (unsigned)S.batch);
-  if (L.idx_f32) scores_kernel<true><<<grid, dim3(kThreads), 0, st>>>(L, S, q_idx, scores, per);
-  else scores_kernel<false><<<grid, dim3(kThreads), 0, st>>>(L, S, q_idx, scores, per);
+  timer_before(kKernIndexScores, st);
+  if (L.idx_f32) scores_kernel<true><<<grid, dim3(256), 0, st>>>(L, S, q_idx, scores, per);
+  else scores_kernel<false><<<grid, dim3(256), 0, st>>>(L, S, q_idx, scores, per);
+  timer_after(kKernIndexScores, st);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t *lens, int batch, int max_len,
                               int top_k, int32_t *indices, void *ws, hipStream_t st) {
-  TopkWs w = carve(ws, batch, max_len > 0 ? max_len : 1);
-  StageA a{};
-  a.scores = scores;
-  a.stride = stride;
-  a.lens = lens;
-  a.units_per_wg = 256;  // 2048 scores per workgroup
-  a.need = (uint32_t)top_k;
-  a.w = w;
-  hipError_t e = run_stage_a<kGiven>(a, ((int64_t)max_len + 7) / 8, batch, st);
+  if (batch <= 0) return hipSuccess;
+  const WsShape sh = ws_shape(max_len, 0);
+  SelWs w = carve(ws, batch, sh);
+  GivenArgs g{scores, stride, lens, max_len, top_k, w};
+  const int gx = (int)(sh.cap_keys / kScanPos);
+  timer_before(kKernTopkGiven, st);
+  given_kernel<<<dim3(gx, batch), dim3(256), 0, st>>>(g);
+  timer_after(kKernTopkGiven, st);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  StageB bb{};
-  bb.mode = kGiven;
-  bb.lens = lens;
-  bb.items_per_wg = kItemsPerWgB;
-  bb.need = (uint32_t)top_k;
-  bb.out = indices;
-  bb.w = w;
-  return run_stage_b(bb, max_len, batch, st);
+  SelArgs s{};
+  s.w = w;
+  s.lens = lens;
+  s.max_len = max_len;
+  s.mode = kGiven;
+  s.K = top_k;
+  s.out = indices;
+  return run_select(s, 1, batch, st);
 }
 
 hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
                                     int32_t *pool_out, int pool_blocks, int32_t *indices, void *ws,
                                     hipStream_t st) {
-  int64_t cap = S.max_len;
-  if ((int64_t)pool_blocks * 8 > cap) cap = (int64_t)pool_blocks * 8;
-  TopkWs w = carve(ws, S.batch, cap > 0 ? cap : 1);
-  const int64_t units = ((int64_t)S.max_len + 7) / 8;
-  hipError_t e;
-  if (pool_out == nullptr) {
-    StageA a{};
-    a.L = L; a.S = S; a.q_idx = q_idx; a.units_per_wg = kPosUnitsPerWg; a.need = (uint32_t)top_k; a.w = w;
-    if ((e = run_stage_a<kPos>(a, units, S.batch, st)) != hipSuccess) return e;
-    StageB bb{};
-    bb.S = S; bb.mode = kPos; bb.items_per_wg = kItemsPerWgB; bb.need = (uint32_t)top_k; bb.out = indices; bb.w = w;
-    return run_stage_b(bb, S.max_len, S.batch, st);
+  if (S.batch <= 0) return hipSuccess;
+  const bool hier = pool_out != nullptr;
+  const WsShape sh = ws_shape(S.max_len, hier ? pool_blocks : 0);
+  SelWs w = carve(ws, S.batch, sh);
+  ScanArgs a{L, S, q_idx, top_k, pool_blocks, w};
+  const int gx = (int)(sh.cap_keys / kScanPos);
+  timer_before(kKernIndexScan, st);
+  if (L.idx_f32) {
+    if (hier) scan_kernel<true, true><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
+    else scan_kernel<true, false><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
+  } else {
+    if (hier) scan_kernel<false, true><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
+    else scan_kernel<false, false><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
   }
-  // hierarchical: block maxima -> pool blocks -> this layer's top-K inside the pool
-  StageA a{};
-  a.L = L; a.S = S; a.q_idx = q_idx; a.units_per_wg = kPosUnitsPerWg; a.need = (uint32_t)pool_blocks; a.w = w;
-  if ((e = run_stage_a<kBlockMax>(a, units, S.batch, st)) != hipSuccess) return e;
-  StageB bb{};
-  bb.S = S; bb.mode = kBlockMax; bb.items_per_wg = kItemsPerWgB; bb.need = (uint32_t)pool_blocks; bb.out = pool_out;
-  bb.w = w;
-  if ((e = run_stage_b(bb, units, S.batch, st)) != hipSuccess) return e;
-  return launch_index_select_reindex(L, S, q_idx, top_k, pool_out, pool_blocks, indices, ws, st);
+  timer_after(kKernIndexScan, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SelArgs s{};
+  s.w = w;
+  s.S = S;
+  s.mode = hier ? kFullHier : kFullPos;
+  s.K = top_k;
+  s.P = pool_blocks;
+  s.pool_out = pool_out;
+  s.out = indices;
+  return run_select(s, hier ? 2 : 1, S.batch, st);
 }
 
 hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
                                        const int32_t *pool_in, int pool_blocks, int32_t *indices, void *ws,
                                        hipStream_t st) {
-  int64_t cap = S.max_len;
-  if ((int64_t)pool_blocks * 8 > cap) cap = (int64_t)pool_blocks * 8;
-  TopkWs w = carve(ws, S.batch, cap > 0 ? cap : 1);
-  StageA a{};
-  a.L = L; a.S = S; a.q_idx = q_idx; a.pool = pool_in; a.pool_blocks = pool_blocks;
-  a.units_per_wg = kPoolUnitsPerWg; a.need = (uint32_t)top_k; a.w = w;
-  hipError_t e = run_stage_a<kPool>(a, pool_blocks, S.batch, st);
+  if (S.batch <= 0) return hipSuccess;
+  const WsShape sh = ws_shape(S.max_len, pool_blocks);
+  SelWs w = carve(ws, S.batch, sh);
+  PoolArgs p{L, S, q_idx, pool_in, pool_blocks, top_k, w};
+  const int gx = (pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
+  timer_before(kKernPoolScore, st);
+  if (L.idx_f32) pool_kernel<true><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
+  else pool_kernel<false><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
+  timer_after(kKernPoolScore, st);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  StageB bb{};
-  bb.S = S; bb.mode = kPool; bb.pool = pool_in; bb.pool_blocks = pool_blocks; bb.items_per_wg = kItemsPerWgB;
-  bb.need = (uint32_t)top_k; bb.out = indices; bb.w = w;
-  return run_stage_b(bb, (int64_t)pool_blocks * 8, S.batch, st);
+  SelArgs s{};
+  s.w = w;
+  s.S = S;
+  s.mode = kReindex;
+  s.K = top_k;
+  s.P = pool_blocks;
+  s.out = indices;
+  return run_select(s, 1, S.batch, st);
 }
 
 }  // namespace csa2

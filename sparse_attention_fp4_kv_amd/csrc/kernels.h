@@ -8,6 +8,24 @@
 
 namespace csa2 {
 
+// Kernels that csa2_time_next_launch can time (names in api.hip).
+enum KernelId {
+  kKernIndexScan = 0,   // full scan of the indexer keys (per-position or block-max keys)
+  kKernPoolScore,       // scoring of the pool positions (Reindex, and the Full layer's own top-K)
+  kKernTopkGiven,       // key conversion of caller-given scores
+  kKernTopkCompact,     // threshold compaction + exact refine
+  kKernSparseAttn,
+  kKernAttnCombine,
+  kKernCedProject,
+  kKernFp4Pack,
+  kKernKvAppend,
+  kKernIndexScores,
+  kKernCount
+};
+// Records the armed event pair around the next launch of `id` (no-op otherwise).
+void timer_before(KernelId id, hipStream_t st);
+void timer_after(KernelId id, hipStream_t st);
+
 // Device view of one KV layer's paged pool (validated copy of csa2_kv_layer).
 struct KvLayerDev {
   uint8_t *codes;

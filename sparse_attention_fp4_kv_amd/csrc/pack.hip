@@ -65,6 +65,7 @@ __global__ void __launch_bounds__(64) kv_append_kernel(KvLayerDev L, SeqsDev S, 
   if (blk < 0 || blk >= L.num_blocks) return;
   const int64_t slot = (int64_t)blk * kPage + p % kPage;
   if (t < kLatent / kGroup) {
+    if (latent == nullptr) return;
     const float *src = latent + (int64_t)b * kLatent + t * kGroup;
     float v[16];
 #pragma unroll
@@ -75,7 +76,7 @@ __global__ void __launch_bounds__(64) kv_append_kernel(KvLayerDev L, SeqsDev S, 
     L.scales[slot * (kLatent / kGroup) + t] = (uint8_t)sc;
   } else {
     const int u = t - kLatent / kGroup;  // 0..31
-    if (rope != nullptr && L.rope != nullptr) {
+    if (rope != nullptr && L.rope_dim != 0) {
       for (int r = u; r < L.rope_dim; r += 32) L.rope[slot * L.rope_dim + r] = rope[(int64_t)b * L.rope_dim + r];
     }
     if (idx_key != nullptr && L.idx_keys != nullptr) {
@@ -102,7 +103,9 @@ hipError_t launch_fp4_pack(const float *x, int64_t rows, int channels, uint8_t *
   const int64_t n = rows * (channels / kGroup);
   if (n == 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256;
+  timer_before(kKernFp4Pack, st);
   fp4_pack_kernel<<<dim3((unsigned)blocks), dim3(256), 0, st>>>(x, n, codes, scales);
+  timer_after(kKernFp4Pack, st);
   return hipGetLastError();
 }
 
@@ -118,7 +121,9 @@ hipError_t launch_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_
 hipError_t launch_kv_append(const KvLayerDev &L, const SeqsDev &S, const float *latent, const uint16_t *rope,
                             const void *idx_key, hipStream_t st) {
   if (S.batch == 0) return hipSuccess;
+  timer_before(kKernKvAppend, st);
   kv_append_kernel<<<dim3(S.batch), dim3(64), 0, st>>>(L, S, latent, rope, idx_key);
+  timer_after(kKernKvAppend, st);
   return hipGetLastError();
 }
 

@@ -103,7 +103,7 @@ def test_hierarchical_pool_and_reindex():
         bs = oracle.indexer.block_scores_fast(s0)
         nb = len(bs)
         check_topk(pool[b], dict(enumerate(bs)), P, where=f"pool b={b}")
-        check_topk(idx[b], dict(enumerate(s0)), K, where=f"full-in-pool b={b}")
+        check_topk(idx[b], dict(enumerate(s0)), K, where=f"full b={b}")
         o_pools.append(oracle.indexer.pool_blocks(s0, P))
         assert np.sum(pool[b] >= 0) == min(P, nb)
     o_pool_t = to_dev(np.stack(o_pools).astype(np.int32))
@@ -124,5 +124,65 @@ def test_select_rejects_bad_args():
     q = to_dev(wl.q_idx(st, 0, 1))
     with pytest.raises(csa2.Csa2Error):
         csa2.csa2_index_select(layer, batch, q, 0, csa2.FULL)
-    with pytest.raises(csa2.Csa2Error):  # pool smaller than K
-        csa2.csa2_index_select(layer, batch, q, 64, csa2.FULL, pool_blocks=4, want_pool=True)
+    with pytest.raises(csa2.Csa2Error):  # pool larger than 2048 blocks
+        csa2.csa2_index_select(layer, batch, q, 64, csa2.FULL, pool_blocks=4096, want_pool=True)
+
+
+def test_topk_clustered_scores_take_the_exact_fallback():
+    """Monotone scores put the whole top-K in the last segments, which overflows the
+    per-segment candidate budget; the select must fall back and stay exact."""
+    lens = np.array([200000, 100000, 5000], dtype=np.int32)
+    M = int(lens.max())
+    sc = np.tile(np.arange(M, dtype=np.float32), (3, 1))
+    sc[1] = -sc[1]  # top-K at the front
+    sc[2, :] = np.float32(1.0)
+    sc[2, 1000:3000] = 2.0
+    for K in (64, 2048, 4096):
+        idx = csa2.csa2_topk(to_dev(sc), to_dev(lens), K)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        for b, n in enumerate(lens):
+            ref = oracle.indexer.topk(sc[b, :n].astype(np.float64), K)
+            assert idx[b].tolist() == sorted(ref.tolist(), key=lambda v: (v < 0, v)), (K, b)
+
+
+def _clustered_keys_layer(n, q, lo, hi, seed):
+    """bf16 keys whose scores against q are large exactly on positions [lo, hi)."""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n, 64)).astype(np.float32)
+    k[lo:hi] += 8.0 * q[None, :] / np.linalg.norm(q)
+    keys = wl.to_bf16_bits(k)
+    tables = np.arange(-(-n // 64), dtype=np.int32)[None]
+    layer = csa2.PagedLayer(tables.shape[1], idx_dtype="bf16", device="cuda")
+    fill_layer(layer, tables, [n], keys=[keys])
+    return keys, tables, layer
+
+
+@pytest.mark.parametrize("hier", [False, True])
+def test_full_select_clustered_scores(hier):
+    n = 300000
+    q = np.random.default_rng(5).standard_normal(64).astype(np.float32)
+    keys, tables, layer = _clustered_keys_layer(n, q, 123456, 123456 + 9000, 6)
+    batch = make_batch(tables, [n], n)
+    K, P = 2048, 2048
+    idx, pool = csa2.csa2_index_select(layer, batch, to_dev(q[None]), K, csa2.FULL, pool_blocks=P, want_pool=hier)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()[0]
+    s = oracle.indexer.index_scores(q, oracle.indexer.keys_to_f64(keys, "bf16"))
+    check_topk(idx, dict(enumerate(s)), K, where="clustered full")
+    assert np.all(np.diff(idx[idx >= 0]) > 0), "indices are written in increasing order"
+    if hier:
+        pool = pool.cpu().numpy()[0]
+        check_topk(pool, dict(enumerate(oracle.indexer.block_scores_fast(s))), P, where="clustered pool")
+        assert np.all(np.diff(pool[pool >= 0]) > 0)
+
+
+def test_select_is_deterministic():
+    seq_lens = [70000, 9000]
+    st, tables, keys, layer = _keys_layer(seq_lens, "bf16", True, 44)
+    q = to_dev(wl.q_idx(st, 0, 2))
+    batch = make_batch(tables, seq_lens, 70000)
+    a, pa = csa2.csa2_index_select(layer, batch, q, 2048, csa2.FULL, pool_blocks=2048, want_pool=True)
+    b, pb = csa2.csa2_index_select(layer, batch, q, 2048, csa2.FULL, pool_blocks=2048, want_pool=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(pa, pb)
