@@ -129,4 +129,51 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
+// ---------------------------------------------------------------- wave primitives
+// Lane moves through DPP (data-parallel primitives of the VALU: no LDS round
+// trip).  Controls: quad_perm [1,0,3,2] = 0xB1 and [2,3,0,1] = 0x4E,
+// row_shr:n = 0x110 + n, row_mirror = 0x140, row_half_mirror = 0x141,
+// row_bcast:15 = 0x142, row_bcast:31 = 0x143.  Lanes with no source read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+// Sum over the aligned group of 8 lanes; every lane of the group gets it.
+__device__ __forceinline__ float group8_sum(float s) {
+  s += dpp_f32<0xB1>(s);
+  s += dpp_f32<0x4E>(s);
+  s += dpp_f32<0x141>(s);
+  return s;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+  v += dpp_u32<0x111>(v);
+  v += dpp_u32<0x112>(v);
+  v += dpp_u32<0x114>(v);
+  v += dpp_u32<0x118>(v);
+  v += dpp_u32<0x142, 0xA>(v);
+  v += dpp_u32<0x143, 0xC>(v);
+  return v;
+}
+
+// Inclusive prefix maximum (unsigned) over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_max(uint32_t v) {
+  v = max(v, dpp_u32<0x111>(v));
+  v = max(v, dpp_u32<0x112>(v));
+  v = max(v, dpp_u32<0x114>(v));
+  v = max(v, dpp_u32<0x118>(v));
+  v = max(v, dpp_u32<0x142, 0xA>(v));
+  v = max(v, dpp_u32<0x143, 0xC>(v));
+  return v;
+}
+
+// Value of lane 63 (e.g. the total after an inclusive sum), uniform.
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, 63); }
+
 }  // namespace csa2

@@ -52,9 +52,9 @@ constexpr int kScanPos = 2048;                 // positions per producer workgro
 constexpr int kScanPages = kScanPos / kPage;   // 32
 constexpr int kBlk = 8;                        // positions per pool block
 constexpr int kScanBlocks = kScanPos / kBlk;   // 256
-constexpr int kCandCap = 12288;                // candidates one select workgroup holds in LDS
+constexpr int kCandCap = 6144;                 // candidates one select workgroup holds in LDS
 constexpr int kSelThreads = 512;
-constexpr int kSelIPT = kCandCap / kSelThreads;  // 24
+constexpr int kSelIPT = kCandCap / kSelThreads;  // 12
 constexpr int kPoolBlocksPerWg = 16;           // pool producer: 16 blocks = 128 items
 constexpr int kPoolItemsPerWg = kPoolBlocksPerWg * kBlk;
 constexpr int kMaxPoolItems = 2048 * kBlk;     // 16,384
@@ -153,8 +153,8 @@ struct KeyLoad {
 };
 
 // Lane l works on position l/8 of an aligned run of 8 and on dims 8*(l%8) ..
-// +7 of its key; the 8 partial sums of a position are combined with three xor
-// shuffles, so every lane ends with its position's score.
+// +7 of its key; the 8 partial sums of a position are combined with three DPP
+// lane moves, so every lane ends with its position's score.
 template <bool F32>
 __device__ __forceinline__ KeyLoad load_unit(const void *keys, int64_t slot0, int lane) {
   KeyLoad r;
@@ -194,10 +194,7 @@ __device__ __forceinline__ float unit_score(const KeyLoad &k, const float (&q)[8
     s = fmaf(q[6], __uint_as_float(k.a[3] << 16), s);
     s = fmaf(q[7], __uint_as_float(k.a[3] & 0xFFFF0000u), s);
   }
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  return s;
+  return group8_sum(s);
 }
 
 __device__ __forceinline__ int row_len(const SeqsDev &S, int b) {
@@ -219,20 +216,15 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch, uint32_t *total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const uint32_t incl = wave_inclusive_sum(v);
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
   uint32_t wave_base = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const uint32_t s = scratch[w];
-    if (w < wave) wave_base += s;
-    tot += s;
+    const uint32_t x = scratch[w];
+    wave_base += w < wave ? x : 0u;
+    tot += x;
   }
   __syncthreads();
   *total = tot;
@@ -255,27 +247,18 @@ __device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t ne
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < per / 4; ++j) mine += v[j][0] + v[j][1] + v[j][2] + v[j][3];
-    uint32_t incl = mine;  // sum over lanes t..63
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_down(incl, off);
-      if (t + off < 64) incl += o;
-    }
-    const uint32_t above_me = incl - mine;  // sum over lanes above t
-    const uint64_t hit = __ballot(above_me < need && incl >= need);
+    const uint32_t pre = wave_inclusive_sum(mine);  // lanes 0..t
+    const uint32_t total = wave_last(pre);
+    const uint32_t above_me = total - pre;  // lanes above t
+    const uint64_t hit = __ballot(above_me < need && above_me + mine >= need);
     if (hit) {
       // the boundary bin is one of lane src's: lanes 0..31 take its bins from
       // the top down and a prefix sum over lanes gives each bin's count above
       const int src = __ffsll((unsigned long long)hit) - 1;
-      const uint32_t base = __shfl(above_me, src);
+      const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)above_me, src);
       const int bin = per * src + (per - 1) - (t & (per - 1));
       const uint32_t h = t < per ? hist[bin] : 0u;
-      uint32_t cum = h;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(cum, off);
-        if (t >= off) cum += o;
-      }
+      const uint32_t cum = wave_inclusive_sum(h);
       const uint64_t q = __ballot(t < per && base + cum - h < need && base + cum >= need);
       if (t == __ffsll((unsigned long long)q) - 1) {
         res[0] = (uint32_t)bin;
@@ -284,7 +267,7 @@ __device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t ne
       }
     } else if (t == 0) {
       res[0] = 0u;
-      res[1] = incl - hist[0];
+      res[1] = total - hist[0];
       res[2] = 0u;
     }
   }
@@ -294,9 +277,9 @@ __device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t ne
 // Ordered compaction over a workgroup of NT threads.  Wave w owns items
 // [64 IPT w, 64 IPT (w + 1)); its lane l holds items 64 IPT w + 64 j + l
 // (j < IPT), so item order is (wave, j, lane) order.  Bit j of flags keeps
-// item j of this lane; emit(j, slot) is called for every kept item with its
-// slot base + (kept items before it).  Returns the number kept.  red: NT/64
-// words of LDS.
+// item j of this lane; emit(j, slot, keep) is called for every item, and for
+// a kept one slot = base + (kept items before it).  Returns the number kept.
+// red: NT/64 words of LDS.
 template <int NT, int IPT, class Emit>
 __device__ __forceinline__ uint32_t ordered_emit(uint32_t flags, uint32_t *red, uint32_t base, Emit emit) {
   constexpr int NW = NT / 64;
@@ -322,7 +305,7 @@ __device__ __forceinline__ uint32_t ordered_emit(uint32_t flags, uint32_t *red, 
   uint32_t run = base + wbase;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    if ((flags >> j) & 1u) emit(j, run + (uint32_t)__popcll(bal[j] & below));
+    emit(j, run + (uint32_t)__popcll(bal[j] & below), ((flags >> j) & 1u) != 0u);
     run += (uint32_t)__popcll(bal[j]);
   }
   return tot;
@@ -374,8 +357,8 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
         key != 0u && (!cut || (key >> 21) > d1 || ((key >> 21) == d1 && ((key >> 10) & 0x7FFu) > d2));
     flags |= em ? (1u << j) : 0u;
   }
-  const uint32_t total = ordered_emit<NT, IPT>(flags, red, 0u, [&](int j, uint32_t slot) {
-    cand_seg[slot] = make_uint2(k[j], pos_of(i0 + 64 * j));
+  const uint32_t total = ordered_emit<NT, IPT>(flags, red, 0u, [&](int j, uint32_t slot, bool keep) {
+    if (keep) cand_seg[slot] = make_uint2(k[j], pos_of(i0 + 64 * j));
   });
   if (t == 0) *info = SegInfo{total, edge};
 }
@@ -410,40 +393,41 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     for (int e = 0; e < 8; ++e) q[e] = qp[e];
   }
   __syncthreads();
-  // wave w streams pages 8w .. 8w+7, two pages (16 loads of 1 KB) at a time
-#pragma unroll 1
-  for (int pp = 0; pp < 8; pp += 2) {
-    KeyLoad kl[16];
-    int pid[2];
+  // wave w streams pages 8w .. 8w+7, one page (8 loads of 1 KB) at a time
+  // with the next page's loads in flight
+  KeyLoad kl[2][8];
+  auto issue = [&](int pp, KeyLoad(&dst)[8]) {
+    const int pid = pg[8 * wave + pp];
+    const int id = pid < 0 ? 0 : pid;  // unmapped: read slot 0, masked below
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pid[h] = pg[8 * wave + pp + h];
-    if (can_load) {
+    for (int u = 0; u < 8; ++u) dst[u] = load_unit<F32>(a.L.idx_keys, (int64_t)id * kPage + 8 * u, lane);
+  };
+  if (can_load) {
+    issue(0, kl[0]);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int id = pid[u >> 3] < 0 ? 0 : pid[u >> 3];  // unmapped: read slot 0, masked below
-        kl[u] = load_unit<F32>(a.L.idx_keys, (int64_t)id * kPage + 8 * (u & 7), lane);
-      }
-    } else {
+    for (int pp = 0; pp < 8; ++pp) {
+      if (pp + 1 < 8) issue(pp + 1, kl[(pp + 1) & 1]);
+      const int page = 8 * wave + pp;
+      const bool mapped = pg[page] >= 0;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) kl[u] = KeyLoad{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int page = 8 * wave + pp + (u >> 3);
-      const int lp = page * kPage + 8 * (u & 7) + (lane >> 3);  // local position
-      const bool ok = pid[u >> 3] >= 0 && base + lp < n;
-      const float s = unit_score<F32>(kl[u], q);
-      if ((lane & 7) == 0) pkey[lp] = ok ? score_key(s) : 0u;
-      if constexpr (HIER) {
-        float m = ok ? s : -INFINITY;
-        m = fmaxf(m, __shfl_xor(m, 8));
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        if (lane == 0) bkey[lp >> 3] = (pid[u >> 3] >= 0 && base + (lp & ~7) < n) ? score_key(m) : 0u;
+      for (int u = 0; u < 8; ++u) {
+        const int lp = page * kPage + 8 * u + (lane >> 3);  // local position
+        const float sc = unit_score<F32>(kl[pp & 1][u], q);
+        if ((lane & 7) == 0) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
       }
     }
+  } else {
+    for (int i = tid; i < kScanPos; i += 256) pkey[i] = 0u;
   }
   __syncthreads();
+  if constexpr (HIER) {
+    // block key = largest key of its 8 positions (unmapped or past-the-end positions hold key 0)
+    const u32x4 *p4 = reinterpret_cast<const u32x4 *>(pkey + kBlk * tid);
+    const u32x4 x = p4[0], y = p4[1];
+    uint32_t m = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(y[0], y[1]), max(y[2], y[3])));
+    bkey[tid] = m;
+    __syncthreads();
+  }
   // store every key (the select re-reads segments that overflow their budget)
   {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(pkey);
@@ -616,9 +600,16 @@ struct Thresh {
   bool tie;
 };
 
+// The same test as one 64-bit compare of (key, ~position) against a bound.
+__device__ __forceinline__ uint64_t thresh_bound(const Thresh &th) {
+  const uint32_t kf = (th.kt >> th.ksh) << th.ksh;
+  return ((uint64_t)kf << 32) | (th.tie ? th.pinv : 0u);
+}
+__device__ __forceinline__ bool selected64(uint32_t k, uint32_t p, uint64_t bound) {
+  return ((((uint64_t)k) << 32) | (uint32_t)~p) >= bound;
+}
 __device__ __forceinline__ bool selected(uint32_t k, uint32_t p, const Thresh &th) {
-  const uint32_t a = k >> th.ksh, b = th.kt >> th.ksh;
-  return a > b || (a == b && (!th.tie || (~p) >= th.pinv));
+  return selected64(k, p, thresh_bound(th));
 }
 
 // Smallest key any selected item can have.
@@ -701,11 +692,215 @@ __device__ __forceinline__ uint32_t compact(SelSmem &sm, int64_t n, bool all, co
       if (i < n) k = key(i, valid);
       if (valid && (all || selected(k, pos(i), th))) flags |= 1u << j;
     }
-    written += ordered_emit<kSelThreads, IPT>(flags, sm.red, written, [&](int j, uint32_t slot) {
-      if (slot < out_cap) out[slot] = (int32_t)pos(i0 + 64 * j);  // cap: a repeated pool block
+    written += ordered_emit<kSelThreads, IPT>(flags, sm.red, written, [&](int j, uint32_t slot, bool keep) {
+      if (keep && slot < out_cap) out[slot] = (int32_t)pos(i0 + 64 * j);  // cap: a repeated pool block
     });
   }
   return written < out_cap ? written : out_cap;
+}
+
+// The same two steps for the candidates held in LDS (ck/cp, n <= kCandCap),
+// written without branches around the LDS reads: every level reads 8 items
+// per thread and pass, indexes clamped inside the arrays and masked.
+__device__ __forceinline__ Thresh find_thresh_lds(SelSmem &sm, int n, uint32_t need) {
+  const int t = threadIdx.x;
+  constexpr int kU = 8;
+  Thresh th{0u, 0u, 0, false};
+  uint32_t rem = need, pre = 0, ppre = 0;
+#pragma unroll 1
+  for (int lv = 0; lv < 6; ++lv) {
+    const bool posl = lv >= 3;
+    const int l = posl ? lv - 3 : lv;
+    const int sh = l == 0 ? 21 : (l == 1 ? 10 : 0);
+    const uint32_t hm = l == 0 ? 0u : (l == 1 ? 0xFFE00000u : 0xFFFFFC00u);  // bits fixed by earlier levels
+    const uint32_t dm = l == 2 ? 0x3FFu : 0x7FFu;
+    const uint32_t want = (posl ? ppre : pre) & hm;
+    for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    if (!posl) {
+      for (int c0 = 0; c0 < n; c0 += kU * kSelThreads) {
+        uint32_t k[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) k[u] = sm.ck[min(c0 + u * kSelThreads + t, kCandCap - 1)];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const bool ok = (c0 + u * kSelThreads + t < n) & (k[u] != 0u) & ((k[u] & hm) == want);
+          if (ok) atomicAdd(&sm.hist[(k[u] >> sh) & dm], 1u);
+        }
+      }
+    } else {
+      for (int c0 = 0; c0 < n; c0 += kU * kSelThreads) {
+        uint32_t k[kU], p[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int i = min(c0 + u * kSelThreads + t, kCandCap - 1);
+          k[u] = sm.ck[i];
+          p[u] = ~sm.cp[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const bool ok = (c0 + u * kSelThreads + t < n) & (k[u] != 0u) & (k[u] == pre) & ((p[u] & hm) == want);
+          if (ok) atomicAdd(&sm.hist[(p[u] >> sh) & dm], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    find_threshold(sm.hist, rem, sm.red + 16);
+    const uint32_t d = sm.red[16];
+    rem -= sm.red[17];
+    const bool done = sm.hist[d] == rem;
+    __syncthreads();
+    if (!posl) {
+      pre |= d << sh;
+      th.kt = pre;
+      th.ksh = sh;
+      if (done) return th;
+      if (l == 2) th.tie = true;  // every key bit fixed: ties resolved by position
+    } else {
+      ppre |= d << sh;
+      th.pinv = ppre & ~((1u << sh) - 1u);
+      if (done) return th;
+    }
+  }
+  return th;
+}
+
+// Exact threshold for the top `need` of the n LDS candidates, usually in one
+// histogram pass: digits are taken relative to the candidates' own key range
+// (kmin .. kmax split into at most 2048 bins), so the items spread over the
+// bins.  When the boundary bin holds at most 64 items they are gathered and
+// ranked by one wave with lane reads; otherwise the radix levels run.
+__device__ __forceinline__ Thresh find_thresh_fast(SelSmem &sm, int n, uint32_t need) {
+  constexpr int kU = kSelIPT;  // one pass: n <= kCandCap
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t k[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int i = u * kSelThreads + t;
+    k[u] = i < n ? sm.ck[min(i, kCandCap - 1)] : 0u;
+  }
+  // key range of the valid candidates
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    hi = max(hi, k[u]);
+    lo = min(lo, k[u] ? k[u] : 0xFFFFFFFFu);
+  }
+  hi = wave_inclusive_max(hi);
+  lo = ~wave_inclusive_max(~lo);
+  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
+  if (lane == 63) {
+    sm.red[16 + wave] = hi;
+    sm.red[32 + wave] = lo;
+  }
+  __syncthreads();
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    kmax = max(kmax, sm.red[16 + w]);
+    kmin = min(kmin, sm.red[32 + w]);
+  }
+  const uint32_t span = kmax - kmin;
+  const int shift = span < kBins ? 0 : (32 - __clz((int)(span >> 11)));  // (span >> shift) < 2048
+#pragma unroll
+  for (int u = 0; u < kU; ++u)
+    if (k[u]) atomicAdd(&sm.hist[(k[u] - kmin) >> shift], 1u);
+  __syncthreads();
+  find_threshold(sm.hist, need, sm.red + 16);
+  const uint32_t d = sm.red[16];
+  const uint32_t rem = need - sm.red[17];
+  const uint32_t in_bin = sm.hist[d];
+  Thresh th{0u, 0u, 0, false};
+  if (in_bin == rem) {  // the whole boundary bin is taken
+    th.kt = kmin + (d << shift);
+    __syncthreads();
+    return th;
+  }
+  if (in_bin > 64u) {
+    __syncthreads();
+    return find_thresh_lds(sm, n, need);
+  }
+  // gather the boundary bin (<= 64 items) and rank it in wave 0
+  uint32_t *gk = sm.hist + kBins - 160, *gp = gk + 64, *gn = gk + 128;
+  __syncthreads();
+  if (t == 0) *gn = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    if ((k[u] != 0u) & (((k[u] - kmin) >> shift) == d)) {
+      const uint32_t slot = atomicAdd(gn, 1u);
+      gk[slot] = k[u];
+      gp[slot] = sm.cp[u * kSelThreads + t];
+    }
+  }
+  __syncthreads();
+  if (t < 64) {
+    const uint32_t cnt = *gn;
+    const uint32_t mk = t < (int)cnt ? gk[t] : 0u, mp = t < (int)cnt ? gp[t] : 0xFFFFFFFFu;
+    uint32_t rank = 0;  // items of the bin that come before mine: larger key, or equal key and lower position
+    for (uint32_t j = 0; j < cnt; ++j) {
+      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
+      const uint32_t pj = (uint32_t)__builtin_amdgcn_readlane((int)mp, (int)j);
+      rank += (kj > mk || (kj == mk && pj < mp)) ? 1u : 0u;
+    }
+    // the threshold item: the last one taken (largest rank below rem)
+    const bool cand = t < (int)cnt && rank < rem;
+    const uint32_t r = wave_inclusive_max(cand ? rank + 1u : 0u);
+    const uint32_t best = wave_last(r);
+    const uint64_t who = __ballot(cand && rank + 1u == best);
+    if (t == __ffsll((unsigned long long)who) - 1) {
+      sm.red[16] = mk;
+      sm.red[17] = ~mp;
+    }
+  }
+  __syncthreads();
+  th.kt = sm.red[16];
+  th.pinv = sm.red[17];
+  th.tie = true;
+  __syncthreads();
+  return th;
+}
+
+// Ordered compaction of the selected LDS candidates (all valid ones when
+// `all`) to out[0 .. need), padded with -1.  The kept positions are staged in
+// ck (free once every thread holds its items) and written out with 16-byte
+// stores.  Returns the number of kept items written (at most need).
+__device__ __forceinline__ uint32_t compact_lds(SelSmem &sm, int n, bool all, const Thresh &th, int32_t *out,
+                                                uint32_t need) {
+  constexpr int kU = kSelIPT;  // one pass: n <= kCandCap
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint64_t bound = all ? 0ull : thresh_bound(th);
+  const int i0 = 64 * kU * wave + lane;  // this lane's items: i0 + 64 j
+  uint32_t k[kU], p[kU];
+#pragma unroll
+  for (int j = 0; j < kU; ++j) {
+    const int i = min(i0 + 64 * j, kCandCap - 1);
+    k[j] = sm.ck[i];
+    p[j] = sm.cp[i];
+  }
+  uint32_t flags = 0;
+#pragma unroll
+  for (int j = 0; j < kU; ++j) {
+    const bool keep = (i0 + 64 * j < n) & (k[j] != 0u) & selected64(k[j], p[j], bound);
+    flags |= keep ? (1u << j) : 0u;
+  }
+  // ordered_emit's barriers also order every read of ck above before the writes below
+  uint32_t written = ordered_emit<kSelThreads, kU>(flags, sm.red, 0u, [&](int j, uint32_t slot, bool keep) {
+    if (keep & (slot < need)) sm.ck[slot] = p[j];  // cap: a repeated pool block
+  });
+  written = written < need ? written : need;
+  __syncthreads();
+  for (int i = 4 * t; i < (int)need; i += 4 * kSelThreads) {
+    if (i + 4 <= (int)need && ((need | (uint32_t)(uintptr_t)out) & 3u) == 0u && ((uintptr_t)out & 15u) == 0u) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (uint32_t)(i + e) < written ? sm.ck[i + e] : 0xFFFFFFFFu;
+      *reinterpret_cast<u32x4 *>(out + i) = v;
+    } else {
+      for (int e = 0; e < 4 && i + e < (int)need; ++e) out[i + e] = (uint32_t)(i + e) < written ? (int32_t)sm.ck[i + e] : -1;
+    }
+  }
+  return written;
 }
 
 // A row's candidate stream: nseg segments of ips items; segment s emitted
@@ -728,14 +923,8 @@ __device__ __forceinline__ uint2 stored_item(const Stream &s, int64_t i) {
 
 // Exclusive prefix of v across one wave; *total gets the wave's sum.
 __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t *total) {
-  const int lane = threadIdx.x & 63;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  *total = __shfl(incl, 63);
+  const uint32_t incl = wave_inclusive_sum(v);
+  *total = wave_last(incl);
   return incl - v;
 }
 
@@ -898,13 +1087,8 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
   }
   // largest edge over the row
   {
-    uint32_t e = emax;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t x = __shfl_xor(e, o);
-      e = e > x ? e : x;
-    }
-    if (lane == 0) sm.red[16 + wave] = e;
+    const uint32_t e = wave_inclusive_max(emax);
+    if (lane == 63) sm.red[16 + wave] = e;
   }
   __syncthreads();
   uint32_t max_edge = 0;
@@ -912,12 +1096,6 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
   copy_candidates(sm, st, nseg, nullptr);
   __syncthreads();
 
-  auto lkey = [&](int64_t i, bool &valid) {
-    const uint32_t k = sm.ck[i];
-    valid = k != 0u;
-    return k;
-  };
-  auto lpos = [&](int64_t i) { return sm.cp[i]; };
   // Pass 0 selects among the emitted candidates.  Items a segment left out
   // are below its edge, so when no edge is above the selection's key floor
   // that selection is exact.  Otherwise the segments with such an edge are
@@ -927,10 +1105,10 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
   for (int pass = 0;; ++pass) {
     Thresh th{0u, 0u, 0, false};
     const bool all = n_c <= (uint32_t)need;
-    if (!all) th = find_thresh(sm, (int64_t)n_c, (uint32_t)need, lkey, lpos);
+    if (!all) th = find_thresh_fast(sm, (int)n_c, (uint32_t)need);
     const uint32_t floor_key = all ? 0u : thresh_key_floor(th);
     if (pass == 1 || (all ? max_edge == 0u : max_edge <= floor_key)) {
-      written = compact<8>(sm, n_c, all, th, lkey, lpos, out, (uint32_t)need);
+      written = compact_lds(sm, (int)n_c, all, th, out, (uint32_t)need);
       break;
     }
     // --- overflowing segments: a bitmap in hist (kMaxSeg bits)
@@ -970,6 +1148,7 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
     uint32_t off2 = block_exclusive_scan<kSelThreads>(cnt2, sm.red, &C2);
     if (C2 > (uint32_t)kCandCap) {
       written = select_all_stored(sm, st, need, out);
+      for (int i = (int)written + t; i < need; i += kSelThreads) out[i] = -1;  // slots it did not write
       break;
     }
 #pragma unroll
@@ -987,8 +1166,7 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
     __syncthreads();
     n_c = C2;
   }
-  __syncthreads();
-  for (int i = (int)written + t; i < need; i += kSelThreads) out[i] = -1;
+  (void)written;
 }
 
 // grid (1 or 2, B): x == 0 selects positions (indices), x == 1 the pool blocks.
