@@ -28,6 +28,7 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 csa2_status check_layer(const csa2_kv_layer *l, bool need_kv, bool need_keys, KvLayerDev *out) {
   if (l == nullptr) return CSA2_ERR_INVALID_ARG;
   if (l->block_tokens != 64 || l->latent_dim != 512 || l->num_blocks < 0) return CSA2_ERR_INVALID_ARG;
+  if (l->num_blocks > (1 << 25)) return CSA2_ERR_INVALID_ARG;  // rows are addressed with 32-bit indices
   if (l->rope_dim != 0 && l->rope_dim != 64) return CSA2_ERR_INVALID_ARG;
   if (need_kv) {
     if (l->codes == nullptr || l->scales == nullptr) return CSA2_ERR_INVALID_ARG;

@@ -37,6 +37,8 @@ constexpr int kVLd = kT + 8;           // transposed tile row (f16): 32 entries 
 constexpr int kPLd = kT + 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 32;         // split-K workgroups per (sequence, head group)
+constexpr int kSlotCap = 2048;         // entries one workgroup resolves up front
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
 
 struct AttnArgs {
   KvLayerDev L;
@@ -62,7 +64,7 @@ struct Smem {
   f16 p_hi[16 * MT][kPLd];
   f16 p_lo[16 * MT][kPLd];
   float m_run[16 * MT], l_run[16 * MT], alpha[16 * MT];
-  int64_t slot[kT];
+  uint32_t slot[kSlotCap];       // physical rows of this workgroup's entries (kNoSlot: skipped)
 };
 
 __device__ __forceinline__ f16x8 lds_f16x8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
@@ -78,16 +80,49 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16x8(uint4 v) {
   return r;
 }
 
-template <int MT>
+// Reductions over aligned groups of G = 4, 8 or 16 lanes (DPP, every lane gets the result).
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_f32<0x141>(v));
+  if constexpr (G >= 16) v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  if constexpr (G >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (G >= 16) v += dpp_f32<0x140>(v);
+  return v;
+}
+
+// Raw FP4 row fragment of one entry: 64 channels of codes, their 4 scales and
+// (with rope) 8 rope values.
+struct Raw {
+  uint4 c0, c1, rp;
+  uint32_t sc4;
+  bool valid;
+};
+
+template <int MT, bool ROPE>
 __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   constexpr int HG = 16 * MT;                  // heads in this workgroup
+  constexpr int QW = kLatent + (ROPE ? 64 : 0);  // q row width
+  constexpr int KS = QW / 32;                  // 16 or 18 k-steps of 32 channels
   __shared__ Smem<MT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int h0 = hg * HG;
-  const int qw = kLatent + a.L.rope_dim;       // q row width
   const int n = min(max(a.S.seq_lens[b], 0), a.S.max_len);
-  const int ks_total = qw / 32;                // 16 or 18 k-steps of 32 channels
+
+  const int n_tiles_all = (a.top_k + kT - 1) / kT;
+  const int tile_begin = split * a.tiles_per_split;
+  const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles_all);
+  const int e_begin = tile_begin * kT;
+  const int e_count = max(0, min(tile_end * kT, a.top_k) - e_begin);  // <= kSlotCap (host-chosen splits)
+  const int32_t *idx_row = a.idx + (size_t)b * a.top_k;
 
   // ---- QK^T work of this wave: one M-tile (16 heads) and 1 or 2 N-tiles of 16 entries
   int qk_mt, qk_nt0, qk_ntn;
@@ -95,19 +130,43 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   else if constexpr (MT == 2) { qk_mt = wave >> 1; qk_nt0 = wave & 1; qk_ntn = 1; }
   else { qk_mt = 0; qk_nt0 = wave & 1; qk_ntn = wave < 2 ? 1 : 0; }
 
-  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*ks + 8*(lane/16) .. +7.
-  // All loads are issued before any conversion (no branch between them).
-  f16x8 qf[18];
+  // ---- entry indices of this workgroup, then their physical rows (two dependent
+  // reads for all entries at once; the q loads below overlap them)
+  int pos[kSlotCap / 256];
+#pragma unroll
+  for (int j = 0; j < kSlotCap / 256; ++j) {
+    const int i = 256 * j + tid;
+    const int p = idx_row[min(e_begin + i, a.top_k - 1)];  // clamped read, masked below
+    pos[j] = i < e_count ? p : -1;
+  }
+
+  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*ks + 8*(lane/16) .. +7
+  f16x8 qf[KS];
   {
-    const uint16_t *qrow = a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * qw + 8 * (lane >> 4);
-    uint4 raw[18];
+    const uint16_t *qrow = a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 8 * (lane >> 4);
+    uint4 raw[KS];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
-    const int rk = ks_total > 16 ? 1 : 0;  // rope k-steps re-read the last latent step when absent
+    for (int ks = 0; ks < KS; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
 #pragma unroll
-    for (int ks = 16; ks < 18; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * (rk ? ks : 15));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
+  }
+
+  {
+    int blk[kSlotCap / 256];
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
+    for (int j = 0; j < kSlotCap / 256; ++j) {
+      const int p = pos[j];
+      const bool ok = p >= 0 && p < n && p / kPage < a.S.max_blocks;
+      // clamped read, masked below (a table without columns maps nothing)
+      blk[j] = a.S.max_blocks > 0 ? a.S.block_table[(size_t)b * a.S.max_blocks + (ok ? p / kPage : 0)] : -1;
+      pos[j] = ok ? p : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kSlotCap / 256; ++j) {
+      const int i = 256 * j + tid;
+      const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < a.L.num_blocks;
+      sm.slot[i] = ok ? (uint32_t)blk[j] * kPage + (uint32_t)(pos[j] % kPage) : kNoSlot;
+    }
   }
 
   // ---- PV accumulators: wave owns channels [128*wave, 128*wave+128) for all HG heads
@@ -121,61 +180,42 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     sm.m_run[tid] = -INFINITY;
     sm.l_run[tid] = 0.0f;
   }
+  __syncthreads();
 
-  const int tile_begin = split * a.tiles_per_split;
-  const int n_tiles_all = (a.top_k + kT - 1) / kT;
-  const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles_all);
-  const int32_t *idx_row = a.idx + (size_t)b * a.top_k;
+  // gather of one tile: thread -> entry tid/8, channels 64*(tid%8) .. +63.
+  // Every load is issued unconditionally (a skipped entry reads row 0 and is
+  // zeroed when dequantized; an empty pool never launches a tile).
+  auto load_raw = [&](int tile, Raw &r) {
+    const int e = tid >> 3, cb = tid & 7;
+    const int li = tile * kT + e - e_begin;
+    const uint32_t slot = li < e_count ? sm.slot[li] : kNoSlot;
+    const size_t rs = slot == kNoSlot ? 0 : slot;
+    const uint4 *cp = reinterpret_cast<const uint4 *>(a.L.codes + rs * (kLatent / 2) + 32 * cb);
+    r.c0 = cp[0];
+    r.c1 = cp[1];
+    r.sc4 = *reinterpret_cast<const uint32_t *>(a.L.scales + rs * (kLatent / kGroup) + 4 * cb);
+    if constexpr (ROPE) r.rp = *reinterpret_cast<const uint4 *>(a.L.rope + rs * 64 + 8 * cb);
+    r.valid = slot != kNoSlot;
+  };
 
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int e0 = tile * kT;
-    // 1. resolve the physical slots of this tile's entries
-    if (tid < kT) {
-      const int i = e0 + tid;
-      int64_t slot = -1;
-      if (i < a.top_k) {
-        const int p = idx_row[i];
-        if (p >= 0 && p < n) {
-          const int page = p / kPage;
-          if (page < a.S.max_blocks) {
-            const int blk = a.S.block_table[(size_t)b * a.S.max_blocks + page];
-            if (blk >= 0 && blk < a.L.num_blocks) slot = (int64_t)blk * kPage + p % kPage;
-          }
-        }
-      }
-      sm.slot[tid] = slot;
-    }
-    __syncthreads();
-    // 2. gather + dequantize: thread -> entry tid/8, channels 64*(tid%8) .. +63
+  auto process = [&](const Raw &r, int tile) {
+    // 1. dequantize into the row-major tile
     {
       const int e = tid >> 3, cb = tid & 7;
-      const int64_t slot = sm.slot[e];
-      const int64_t rs = slot < 0 ? 0 : slot;  // invalid entries read slot 0 and are zeroed below
-      uint4 c0 = make_uint4(0, 0, 0, 0), c1 = c0, rp = c0;
-      uint32_t sc4 = 0;
-      if (a.L.num_blocks > 0) {  // uniform; an empty pool has no slot 0
-        const uint4 *cp = reinterpret_cast<const uint4 *>(a.L.codes + rs * (kLatent / 2) + 32 * cb);
-        c0 = cp[0];
-        c1 = cp[1];
-        sc4 = *reinterpret_cast<const uint32_t *>(a.L.scales + rs * (kLatent / kGroup) + 4 * cb);
-        if (a.L.rope_dim) rp = *reinterpret_cast<const uint4 *>(a.L.rope + rs * 64 + 8 * cb);
-      }
-      if (slot < 0) {
-        c0 = c1 = make_uint4(0, 0, 0, 0);
-        sc4 = 0;
-        rp = make_uint4(0, 0, 0, 0);
-      }
-      const uint32_t words[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const uint32_t words[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+      const uint32_t sc4 = r.valid ? r.sc4 : 0u;  // scale 0: the entry's channels are all zero
 #pragma unroll
       for (int wi = 0; wi < 8; ++wi) {
-        const f16 s = (f16)e4m3_decode((sc4 >> (8 * (wi >> 1))) & 0xFFu);
-        const f16x8 v = deq8(words[wi], s);
-        *reinterpret_cast<f16x8 *>(&sm.cq[e][64 * cb + 8 * wi]) = v;
+        const f16 sc = (f16)e4m3_decode((sc4 >> (8 * (wi >> 1))) & 0xFFu);
+        *reinterpret_cast<f16x8 *>(&sm.cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc);
       }
-      if (a.L.rope_dim) *reinterpret_cast<f16x8 *>(&sm.cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
+      if constexpr (ROPE) {
+        const uint4 rp = r.valid ? r.rp : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<f16x8 *>(&sm.cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
+      }
     }
     __syncthreads();
-    // 3. transposed copy for PV: thread -> channels 2*tid, 2*tid+1 over the 32 entries
+    // 2. transposed copy for PV: thread -> channels 2*tid, 2*tid+1 over the 32 entries
     {
       const int c = 2 * tid;
       uint32_t colw[kT];
@@ -194,37 +234,32 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         *reinterpret_cast<uint4 *>(&sm.cv[c + 1][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
     }
-    // 4. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
+    // 3. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
     for (int j = 0; j < qk_ntn; ++j) {
       const int nt = qk_nt0 + j;
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
       const f16 *brow = &sm.cq[16 * nt + (lane & 15)][8 * (lane >> 4)];
-      // B fragments read 4 k-steps ahead of the MFMA that consumes them
-      f16x8 bq[16];
+      f16x8 bq[KS];  // B fragments read 4 k-steps ahead of the MFMA that consumes them
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) bq[ks] = lds_f16x8(brow + 32 * ks);
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        if (ks + 4 < 16) bq[ks + 4] = lds_f16x8(brow + 32 * (ks + 4));
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], bq[ks], s, 0, 0, 0);
-      }
-      if (ks_total > 16) {
-#pragma unroll
-        for (int ks = 16; ks < 18; ++ks)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], lds_f16x8(brow + 32 * ks), s, 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 4 < KS) bq[ks + 4] = lds_f16x8(brow + 32 * (ks + 4));
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], bq[ks], sacc, 0, 0, 0);
       }
       // lane holds S[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
       const int ent = 16 * nt + (lane & 15);
-      const bool valid = sm.slot[ent] >= 0;
+      const int li = tile * kT + ent - e_begin;
+      const bool valid = li < e_count && sm.slot[li] != kNoSlot;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        sm.s[16 * qk_mt + 4 * (lane >> 4) + r][ent] = valid ? s[r] * a.scale_log2 : -INFINITY;
+      for (int rr = 0; rr < 4; ++rr)
+        sm.s[16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
-    // 5. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
+    // 4. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
     {
-      constexpr int TPH = 256 / HG;   // threads per head (16, 8 or 4)
-      constexpr int EPT = kT / TPH;   // entries per thread (2, 4 or 8)
+      constexpr int TPH = 256 / HG;   // threads per head (4, 8 or 16)
+      constexpr int EPT = kT / TPH;   // entries per thread (8, 4 or 2)
       const int h = tid / TPH, part = tid % TPH;
       float v[EPT];
       float mx = -INFINITY;
@@ -233,8 +268,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         v[i] = sm.s[h][part * EPT + i];
         mx = fmaxf(mx, v[i]);
       }
-#pragma unroll
-      for (int off = 1; off < TPH; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      mx = group_max<TPH>(mx);
       const float m_old = sm.m_run[h];
       const float m_new = fmaxf(m_old, mx);
       float sum = 0.f;
@@ -247,8 +281,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         sm.p_hi[h][part * EPT + i] = ph;
         sm.p_lo[h][part * EPT + i] = pl;
       }
-#pragma unroll
-      for (int off = 1; off < TPH; off <<= 1) sum += __shfl_xor(sum, off);
+      sum = group_sum<TPH>(sum);
       __syncthreads();  // every thread has read m_run before it changes
       if (part == 0) {
         const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_old - m_new);
@@ -258,15 +291,15 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // 6. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
+    // 5. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
     {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float al = sm.alpha[16 * mt + 4 * (lane >> 4) + r];
+        for (int rr = 0; rr < 4; ++rr) {
+          const float al = sm.alpha[16 * mt + 4 * (lane >> 4) + rr];
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) acc[mt][nt][r] *= al;
+          for (int nt = 0; nt < 8; ++nt) acc[mt][nt][rr] *= al;
         }
       }
       f16x8 ph[MT], pl[MT];
@@ -286,50 +319,72 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
+  };
+
+  // ---- tiles, each with the next tile's rows already in flight (two register sets)
+  if (tile_begin < tile_end && a.L.num_blocks > 0) {
+    Raw ra, rb;
+    load_raw(tile_begin, ra);
+    for (int tile = tile_begin; tile < tile_end; tile += 2) {
+      load_raw(min(tile + 1, tile_end - 1), rb);
+      process(ra, tile);
+      if (tile + 1 < tile_end) {
+        load_raw(min(tile + 2, tile_end - 1), ra);
+        process(rb, tile + 1);
+      }
+    }
   }
 
-  // ---- write the result (final when unsplit, else a partial for the combine)
-  if (a.splits == 1) {
+  // ---- write the result (final when unsplit, else a partial for the combine),
+  // 16 heads at a time staged through LDS so every store is a coalesced float4
+  float *stage = reinterpret_cast<float *>(&sm.cq[0][0]);  // 16 x 512 floats fit in cq + cv
+  static_assert(sizeof(sm.cq) + sizeof(sm.cv) >= 16 * kLatent * sizeof(float), "staging area");
+  const bool final_out = a.splits == 1;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
+    __syncthreads();  // the previous round's reads (or the last tile) are done
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 16 * mt + 4 * (lane >> 4) + r;
-        const float l = sm.l_run[h];
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
-        float *orow = a.out + ((size_t)b * a.heads + h0 + h) * kLatent + 128 * wave + (lane & 15);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = acc[mt][nt][r] * inv;
+    for (int r = 0; r < 4; ++r) {
+      const int hl = 4 * (lane >> 4) + r;
+      float sc = 1.0f;
+      if (final_out) {
+        const float l = sm.l_run[16 * mt + hl];
+        sc = l > 0.f ? 1.0f / l : 0.f;
       }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) stage[hl * kLatent + 128 * wave + 16 * nt + (lane & 15)] = acc[mt][nt][r] * sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 16 * kLatent / 4 / 256; ++k) {
+      const int f = 256 * k + tid;           // float4 index within the 16 x 512 block
+      const int hl = f / (kLatent / 4), c4 = f % (kLatent / 4);
+      const float4 v = reinterpret_cast<const float4 *>(stage)[f];
+      const size_t h = (size_t)b * a.heads + h0 + 16 * mt + hl;
+      float *dst = final_out ? a.out + h * kLatent : a.part_o + (h * a.splits + split) * kLatent;
+      reinterpret_cast<float4 *>(dst)[c4] = v;
+    }
+  }
+  if (final_out) {
     if (a.lse != nullptr && tid < HG) {
       const float l = sm.l_run[tid];
       a.lse[(size_t)b * a.heads + h0 + tid] = l > 0.f ? (sm.m_run[tid] + log2f(l)) / kLog2e : -INFINITY;
     }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h = 16 * mt + 4 * (lane >> 4) + r;
-        float *orow = a.part_o + (((size_t)b * a.heads + h0 + h) * a.splits + split) * kLatent + 128 * wave +
-                      (lane & 15);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) orow[16 * nt] = acc[mt][nt][r];
-      }
-    if (tid < HG) {
-      float *ml = a.part_ml + (((size_t)b * a.heads + h0 + tid) * a.splits + split) * 2;
-      ml[0] = sm.m_run[tid];
-      ml[1] = sm.l_run[tid];
-    }
+  } else if (tid < HG) {
+    float *ml = a.part_ml + (((size_t)b * a.heads + h0 + tid) * a.splits + split) * 2;
+    ml[0] = sm.m_run[tid];
+    ml[1] = sm.l_run[tid];
   }
 }
 
-// One workgroup of 128 threads per (b, h): merges the splits' partials.
-__global__ void __launch_bounds__(128) attn_combine_kernel(const float *__restrict__ part_o,
-                                                           const float *__restrict__ part_ml, int splits,
-                                                           float *__restrict__ out, float *__restrict__ lse) {
-  const int bh = blockIdx.x;
+// Merges the splits' partials: workgroup (b*H + h, quarter) of 32 threads
+// covers 128 channels of one head, one float4 per thread.
+__global__ void __launch_bounds__(32) attn_combine_kernel(const float *__restrict__ part_o,
+                                                          const float *__restrict__ part_ml, int splits,
+                                                          float *__restrict__ out, float *__restrict__ lse) {
+  const int bh = blockIdx.x, quarter = blockIdx.y;
   const int tid = threadIdx.x;
+  const int c4 = 32 * quarter + tid;  // float4 index within the 512 channels
   // all loads are unconditional (kMaxSplits-bounded unrolled loop): empty
   // splits (m = -inf, l = 0, O = 0) get weight 0
   const float2 *ml = reinterpret_cast<const float2 *>(part_ml + (size_t)bh * splits * 2);
@@ -339,7 +394,7 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(const float *__restri
   for (int s = 0; s < kMaxSplits; ++s) {
     const int sc = s < splits ? s : 0;
     mls[s] = ml[sc];
-    po[s] = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + sc) * kLatent)[tid];
+    po[s] = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + sc) * kLatent)[c4];
   }
   float m = -INFINITY;
 #pragma unroll
@@ -357,18 +412,27 @@ __global__ void __launch_bounds__(128) attn_combine_kernel(const float *__restri
     o.w += w * po[s].w;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[tid] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-  if (lse != nullptr && tid == 0) lse[bh] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
+  reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[c4] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  if (lse != nullptr && quarter == 0 && tid == 0) lse[bh] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
 }
 
-int heads_per_group(int heads) { return heads % 64 == 0 ? 64 : (heads % 32 == 0 ? 32 : 16); }
+// Heads per workgroup.  64 shares each dequantized tile among the most heads;
+// when that leaves the chip short of workgroups (small batches) 16 heads per
+// workgroup give 4x the workgroups, each with a quarter of the MFMA work per
+// tile (the tile is then dequantized once per head group, from L2).
+int heads_per_group(int batch, int heads) {
+  if (heads % 64 == 0 && (int64_t)batch * (heads / 64) >= 32) return 64;
+  return 16;
+}
 
 int choose_splits(int batch, int heads, int top_k) {
-  const int groups = batch * (heads / heads_per_group(heads));
+  const int groups = batch * (heads / heads_per_group(batch, heads));
   const int tiles = (top_k + kT - 1) / kT;
   int splits = (256 + groups - 1) / groups;  // about one workgroup per CU
   if (splits > tiles) splits = tiles;
   if (splits > kMaxSplits) splits = kMaxSplits;
+  const int min_splits = (tiles * kT + kSlotCap - 1) / kSlotCap;  // a workgroup resolves at most kSlotCap entries
+  if (splits < min_splits) splits = min_splits;
   if (splits < 1) splits = 1;
   return splits;
 }
@@ -387,7 +451,7 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
                               const int32_t *indices, int top_k, float scale, float *out, float *lse, void *ws,
                               hipStream_t st) {
   if (S.batch == 0) return hipSuccess;
-  const int hgsz = heads_per_group(heads);
+  const int hgsz = heads_per_group(S.batch, heads);
   const int splits = choose_splits(S.batch, heads, top_k);
   const int tiles = (top_k + kT - 1) / kT;
   AttnArgs a;
@@ -407,14 +471,19 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o_bytes + 255) & ~(size_t)255));
   const dim3 grid(splits, heads / hgsz, S.batch);
   timer_before(kKernSparseAttn, st);
-  if (hgsz == 64) sparse_attn_kernel<4><<<grid, dim3(256), 0, st>>>(a);
-  else if (hgsz == 32) sparse_attn_kernel<2><<<grid, dim3(256), 0, st>>>(a);
-  else sparse_attn_kernel<1><<<grid, dim3(256), 0, st>>>(a);
+  const bool rope = L.rope_dim != 0;
+  if (hgsz == 64) {
+    if (rope) sparse_attn_kernel<4, true><<<grid, dim3(256), 0, st>>>(a);
+    else sparse_attn_kernel<4, false><<<grid, dim3(256), 0, st>>>(a);
+  } else {
+    if (rope) sparse_attn_kernel<1, true><<<grid, dim3(256), 0, st>>>(a);
+    else sparse_attn_kernel<1, false><<<grid, dim3(256), 0, st>>>(a);
+  }
   timer_after(kKernSparseAttn, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   timer_before(kKernAttnCombine, st);
-  attn_combine_kernel<<<dim3(S.batch * heads), dim3(128), 0, st>>>(a.part_o, a.part_ml, splits, out, lse);
+  attn_combine_kernel<<<dim3(S.batch * heads, 4), dim3(32), 0, st>>>(a.part_o, a.part_ml, splits, out, lse);
   timer_after(kKernAttnCombine, st);
   return hipGetLastError();
 }
