@@ -47,6 +47,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = {"index_scan": "indexer.hip", "pool_score": "indexer.hip", "sparse_attn": "attention.hip",
+                  "ced_project": "ced.hip"}
+
+
+def kernel_source_sha(kernel):
+    import hashlib
+
+    path = os.path.join(ROOT, "sparse_attention_fp4_kv_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
 def usable_cores():
     n = len(os.sched_getaffinity(0))
     try:
@@ -487,11 +499,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a known-size reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU design is described "
-              "in DESIGN.md and is not built.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); sharding across GPUs (whole "
+              "sequences per GPU, or one sequence's context split with one all-gather of the local top-K) is "
+              "not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -502,6 +518,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     csa2.lib()
+    if args.calibrate_copy_mib:
+        src = torch.ones(args.calibrate_copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     replicas = args.replicas or {"decode_1m_hierarchical": 4, "decode_b8_64k_rope": 6, "mixed_serving_32_reuse4": 3,
                                  "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1}[args.workload]
     want_cpu = not args.no_cpu_baseline
@@ -576,10 +599,10 @@ def main():
     roof["kernel"] = wk.dominant
     roof["kernel_ms"] = kern_ms
     roof["traffic"] = None
-    try:
+    try:  # counter-derived bytes, only while the kernel source is the one they were taken on
         with open(args.traffic_file) as f:
             t = json.load(f).get(f"{args.workload}:{wk.dominant}")
-        if t and t.get("valid", False):
+        if t and t.get("source_sha256") == kernel_source_sha(wk.dominant):
             roof["traffic"] = t["bytes_per_launch"]
     except Exception:
         pass

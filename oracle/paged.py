@@ -15,7 +15,7 @@ Readings (the pages give no cache layout):
     visible to the same step's selection and attention.
   * A packed 512-channel latent takes 256 + 32 = 288 bytes.  How the pages'
     890 B splits across entries is not given; 890 = 2.5 x 356 is one reading
-    (parity unpinned, see the design notes) and is not used by any kernel.
+    (parity unpinned: nothing on the pages fixes it) and no kernel uses it.
 """
 
 import numpy as np
