@@ -57,12 +57,12 @@ struct AttnArgs {
 };
 
 template <int MT>
-struct Smem {
-  f16 cq[kT][kQkLd];             // row-major dequantized tile (+ rope)
-  f16 cv[kLatent][kVLd];         // transposed dequantized tile
-  float s[16 * MT][kT];          // logits of the tile
-  f16 p_hi[16 * MT][kPLd];
-  f16 p_lo[16 * MT][kPLd];
+struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile access is a 128-bit LDS op
+  __attribute__((aligned(16))) f16 cq[kT][kQkLd];      // row-major dequantized tile (+ rope)
+  __attribute__((aligned(16))) f16 cv[kLatent][kVLd];  // transposed tile: row r holds channel 2r (r < 256) or 2(r-256)+1
+  float s[2][16 * MT][kT + 1];   // logits of the tile (two k-halves when 16 heads; padded rows)
+  __attribute__((aligned(16))) f16 p_hi[16 * MT][kPLd];
+  __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
   float m_run[16 * MT], l_run[16 * MT], alpha[16 * MT];
   uint32_t slot[kSlotCap];       // physical rows of this workgroup's entries (kNoSlot: skipped)
 };
@@ -125,10 +125,14 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   const int32_t *idx_row = a.idx + (size_t)b * a.top_k;
 
   // ---- QK^T work of this wave: one M-tile (16 heads) and 1 or 2 N-tiles of 16 entries
-  int qk_mt, qk_nt0, qk_ntn;
-  if constexpr (MT == 4) { qk_mt = wave; qk_nt0 = 0; qk_ntn = 2; }
-  else if constexpr (MT == 2) { qk_mt = wave >> 1; qk_nt0 = wave & 1; qk_ntn = 1; }
-  else { qk_mt = 0; qk_nt0 = wave & 1; qk_ntn = wave < 2 ? 1 : 0; }
+  // (16 heads: every wave takes one N-tile and half of the k-steps; the two
+  // halves of a logit are added when the softmax reads them)
+  constexpr int QKS = MT == 1 ? KS / 2 : KS;  // k-steps per wave
+  int qk_mt, qk_nt0, qk_ntn, qk_half;
+  if constexpr (MT == 4) { qk_mt = wave; qk_nt0 = 0; qk_ntn = 2; qk_half = 0; }
+  else if constexpr (MT == 2) { qk_mt = wave >> 1; qk_nt0 = wave & 1; qk_ntn = 1; qk_half = 0; }
+  else { qk_mt = 0; qk_nt0 = wave & 1; qk_ntn = 1; qk_half = wave >> 1; }
+  const int qk_k0 = qk_half * QKS;
 
   // ---- entry indices of this workgroup, then their physical rows (two dependent
   // reads for all entries at once; the q loads below overlap them)
@@ -140,15 +144,16 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     pos[j] = i < e_count ? p : -1;
   }
 
-  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*ks + 8*(lane/16) .. +7
-  f16x8 qf[KS];
+  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*(qk_k0 + ks) + 8*(lane/16) .. +7
+  f16x8 qf[QKS];
   {
-    const uint16_t *qrow = a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 8 * (lane >> 4);
-    uint4 raw[KS];
+    const uint16_t *qrow =
+        a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 32 * qk_k0 + 8 * (lane >> 4);
+    uint4 raw[QKS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
+    for (int ks = 0; ks < QKS; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
+    for (int ks = 0; ks < QKS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
   }
 
   {
@@ -215,7 +220,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // 2. transposed copy for PV: thread -> channels 2*tid, 2*tid+1 over the 32 entries
+    // 2. transposed copy for PV: thread -> channels 2*tid (row tid) and 2*tid+1
+    // (row 256+tid) over the 32 entries; neighbouring lanes write neighbouring rows
     {
       const int c = 2 * tid;
       uint32_t colw[kT];
@@ -230,30 +236,30 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
           lo[j] = (x & 0xFFFFu) | (y << 16);
           hi[j] = (x >> 16) | (y & 0xFFFF0000u);
         }
-        *reinterpret_cast<uint4 *>(&sm.cv[c][8 * g]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<uint4 *>(&sm.cv[c + 1][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4 *>(&sm.cv[tid][8 * g]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4 *>(&sm.cv[256 + tid][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
     }
     // 3. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
     for (int j = 0; j < qk_ntn; ++j) {
       const int nt = qk_nt0 + j;
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const f16 *brow = &sm.cq[16 * nt + (lane & 15)][8 * (lane >> 4)];
-      f16x8 bq[KS];  // B fragments read 4 k-steps ahead of the MFMA that consumes them
+      const f16 *brow = &sm.cq[16 * nt + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
+      f16x8 bq[QKS];  // B fragments read 4 k-steps ahead of the MFMA that consumes them
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) bq[ks] = lds_f16x8(brow + 32 * ks);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 4 < KS) bq[ks + 4] = lds_f16x8(brow + 32 * (ks + 4));
+      for (int ks = 0; ks < QKS; ++ks) {
+        if (ks + 4 < QKS) bq[ks + 4] = lds_f16x8(brow + 32 * (ks + 4));
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], bq[ks], sacc, 0, 0, 0);
       }
-      // lane holds S[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
+      // lane holds S[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16] (this wave's k-half)
       const int ent = 16 * nt + (lane & 15);
       const int li = tile * kT + ent - e_begin;
-      const bool valid = li < e_count && sm.slot[li] != kNoSlot;
+      const bool valid = qk_half == 1 || (li < e_count && sm.slot[li] != kNoSlot);  // masked once
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        sm.s[16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * a.scale_log2 : -INFINITY;
+        sm.s[qk_half][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
     // 4. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
@@ -265,7 +271,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        v[i] = sm.s[h][part * EPT + i];
+        v[i] = sm.s[0][h][part * EPT + i];
+        if constexpr (MT == 1) v[i] += sm.s[1][h][part * EPT + i];
         mx = fmaxf(mx, v[i]);
       }
       mx = group_max<TPH>(mx);
@@ -291,7 +298,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // 5. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
+    // 5. O = alpha * O + P V  (wave: transposed-tile rows 128*wave .. +127, all heads)
     {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -321,16 +328,24 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  // ---- tiles, each with the next tile's rows already in flight (two register sets)
+  // ---- tiles, each with the next two tiles' rows already in flight (three
+  // register sets; loads past the last tile re-read the last tile)
   if (tile_begin < tile_end && a.L.num_blocks > 0) {
-    Raw ra, rb;
+    const int last = tile_end - 1;
+    Raw ra, rb, rc;
     load_raw(tile_begin, ra);
-    for (int tile = tile_begin; tile < tile_end; tile += 2) {
-      load_raw(min(tile + 1, tile_end - 1), rb);
+    load_raw(min(tile_begin + 1, last), rb);
+    load_raw(min(tile_begin + 2, last), rc);
+    for (int tile = tile_begin; tile < tile_end; tile += 3) {
       process(ra, tile);
+      load_raw(min(tile + 3, last), ra);
       if (tile + 1 < tile_end) {
-        load_raw(min(tile + 2, tile_end - 1), ra);
         process(rb, tile + 1);
+        load_raw(min(tile + 4, last), rb);
+      }
+      if (tile + 2 < tile_end) {
+        process(rc, tile + 2);
+        load_raw(min(tile + 5, last), rc);
       }
     }
   }
@@ -352,7 +367,11 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         sc = l > 0.f ? 1.0f / l : 0.f;
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) stage[hl * kLatent + 128 * wave + 16 * nt + (lane & 15)] = acc[mt][nt][r] * sc;
+      for (int nt = 0; nt < 8; ++nt) {
+        const int row = 128 * wave + 16 * nt + (lane & 15);  // PV column = transposed-tile row
+        const int ch = row < 256 ? 2 * row : 2 * (row - 256) + 1;
+        stage[hl * kLatent + ch] = acc[mt][nt][r] * sc;
+      }
     }
     __syncthreads();
 #pragma unroll

@@ -231,7 +231,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
   return wave_base + incl - v;
 }
 
-// Threshold digit of a 2048-bin histogram in LDS, computed by wave 0 alone:
+// Threshold digit of a 2048-bin histogram in LDS, computed by wave 0:
 // the bin d with sum(hist[d+1..]) < need <= sum(hist[d..]).  Result in
 // res[0] = d, res[1] = sum(hist[d+1..]), res[2] = found (0 when all bins hold
 // fewer than `need`; then d = 0 and res[1] = total - hist[0]).  Every thread
@@ -315,7 +315,8 @@ __device__ __forceinline__ uint32_t ordered_emit(uint32_t flags, uint32_t *red, 
 // Emits the best items of a producer workgroup (keys in LDS, key 0 = no item)
 // as an ordered candidate segment of at most `cap` items: whole 11-bit key
 // bins from the top, then the best 11-bit sub-bins of the boundary bin.
-// Thread t owns items [IPT*t, IPT*t + IPT); pos_of(i) is item i's position.
+// Lane l of wave w owns items 64 IPT w + 64 j + l; pos_of(i) is item i's
+// position.
 template <int NT, int IPT, class PosOf>
 __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
                                              uint32_t *hist, uint32_t *red, PosOf pos_of) {

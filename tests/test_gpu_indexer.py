@@ -186,3 +186,50 @@ def test_select_is_deterministic():
     b, pb = csa2.csa2_index_select(layer, batch, q, 2048, csa2.FULL, pool_blocks=2048, want_pool=True)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(pa, pb)
+
+
+def test_full_select_1m_hierarchical_and_reindex():
+    """The 1M-token shape: 512 scan segments with small candidate budgets (top-12 extraction per segment)."""
+    seq_lens = [1 << 20, 700001]
+    P, K = 2048, 2048
+    st, tables, keys, layer = _keys_layer(seq_lens, "bf16", False, 45)
+    q0 = wl.q_idx(st, 0, len(seq_lens))
+    q1 = wl.q_idx(st, 1, len(seq_lens))
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    idx, pool = csa2.csa2_index_select(layer, batch, to_dev(q0), K, csa2.FULL, pool_blocks=P, want_pool=True)
+    idx1, _ = csa2.csa2_index_select(layer, batch, to_dev(q1), K, csa2.REINDEX, pool_in=pool, pool_blocks=P)
+    torch.cuda.synchronize()
+    idx, pool, idx1 = idx.cpu().numpy(), pool.cpu().numpy(), idx1.cpu().numpy()
+    for b, n in enumerate(seq_lens):
+        kf = oracle.indexer.keys_to_f64(keys[b], "bf16")
+        s0 = oracle.indexer.index_scores(q0[b], kf)
+        check_topk(idx[b], dict(enumerate(s0)), K, where=f"1M full b={b}")
+        assert np.all(np.diff(idx[b][idx[b] >= 0]) > 0)
+        check_topk(pool[b], dict(enumerate(oracle.indexer.block_scores_fast(s0))), P, where=f"1M pool b={b}")
+        # Reindex over the GPU's pool: every pool block is a valid block, so score its positions
+        pos = oracle.indexer.pool_positions(pool[b][pool[b] >= 0], n)
+        s1 = oracle.indexer.index_scores(q1[b], kf[pos])
+        check_topk(idx1[b], dict(zip(pos.tolist(), s1)), K, where=f"1M reindex b={b}")
+
+
+def test_full_select_1m_heavy_ties():
+    """Integer-valued keys and query: scores tie in large groups at the K-th value, so segment
+    cuts fall inside ties and the select must re-read segments (or run over every stored key)."""
+    n = 1 << 20
+    rng = np.random.default_rng(46)
+    k = rng.integers(-2, 3, size=(n, 64)).astype(np.float32)
+    keys = wl.to_bf16_bits(k)
+    q = np.zeros((1, 64), dtype=np.float32)
+    q[0, :4] = 1.0
+    tables = np.arange(n // 64, dtype=np.int32)[None]
+    layer = csa2.PagedLayer(tables.shape[1], idx_dtype="bf16", device="cuda")
+    fill_layer(layer, tables, [n], keys=[keys])
+    batch = make_batch(tables, [n], n)
+    idx, pool = csa2.csa2_index_select(layer, batch, to_dev(q), 2048, csa2.FULL, pool_blocks=2048, want_pool=True)
+    torch.cuda.synchronize()
+    idx, pool = idx.cpu().numpy()[0], pool.cpu().numpy()[0]
+    s = oracle.indexer.index_scores(q[0], oracle.indexer.keys_to_f64(keys, "bf16"))
+    ref = oracle.indexer.topk(s, 2048)
+    assert set(idx.tolist()) == set(ref.tolist()), "exact ties: lower positions win"
+    bs = oracle.indexer.block_scores_fast(s)
+    assert set(pool.tolist()) == set(oracle.indexer.topk(bs, 2048).tolist())
