@@ -361,6 +361,7 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
   const uint32_t total = ordered_emit<NT, IPT>(flags, red, 0u, [&](int j, uint32_t slot, bool keep) {
     if (keep) cand_seg[slot] = make_uint2(k[j], pos_of(i0 + 64 * j));
   });
+  for (int i = (int)total + t; i < cap; i += NT) cand_seg[i] = make_uint2(0u, 0u);  // unused slots: no item
   if (t == 0) *info = SegInfo{total, edge};
 }
 
@@ -394,26 +395,29 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     for (int e = 0; e < 8; ++e) q[e] = qp[e];
   }
   __syncthreads();
-  // wave w streams pages 8w .. 8w+7, one page (8 loads of 1 KB) at a time
-  // with the next page's loads in flight
-  KeyLoad kl[2][8];
+  // wave w streams pages w, w+4, .., w+28 (the workgroup's four waves read
+  // four neighbouring pages at a time), one page (8 loads of 1 KB) at a time
+  // with the next pages' loads in flight
+  constexpr int kDepth = 2;  // pages whose loads are in flight (deeper measured slower)
+  KeyLoad kl[kDepth][8];
   auto issue = [&](int pp, KeyLoad(&dst)[8]) {
-    const int pid = pg[8 * wave + pp];
+    const int pid = pg[4 * pp + wave];
     const int id = pid < 0 ? 0 : pid;  // unmapped: read slot 0, masked below
 #pragma unroll
     for (int u = 0; u < 8; ++u) dst[u] = load_unit<F32>(a.L.idx_keys, (int64_t)id * kPage + 8 * u, lane);
   };
   if (can_load) {
-    issue(0, kl[0]);
+#pragma unroll
+    for (int pp = 0; pp < kDepth - 1; ++pp) issue(pp, kl[pp]);
 #pragma unroll
     for (int pp = 0; pp < 8; ++pp) {
-      if (pp + 1 < 8) issue(pp + 1, kl[(pp + 1) & 1]);
-      const int page = 8 * wave + pp;
+      if (pp + kDepth - 1 < 8) issue(pp + kDepth - 1, kl[(pp + kDepth - 1) % kDepth]);
+      const int page = 4 * pp + wave;
       const bool mapped = pg[page] >= 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int lp = page * kPage + 8 * u + (lane >> 3);  // local position
-        const float sc = unit_score<F32>(kl[pp & 1][u], q);
+        const float sc = unit_score<F32>(kl[pp % kDepth][u], q);
         if ((lane & 7) == 0) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
       }
     }
@@ -1057,12 +1061,27 @@ __device__ __forceinline__ uint32_t select_all_stored(SelSmem &sm, const Stream 
 __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int need, int32_t *out) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nseg = st.nseg < kMaxSeg ? st.nseg : kMaxSeg;
-  // --- segment infos: thread t owns segments kSegPerThread * t .. + kSegPerThread - 1 (loads first)
+  const int slots = nseg * st.cap;  // <= kCandCap
+  // --- every candidate slot (segment s owns slots [s cap, s cap + cap), unused
+  // ones hold key 0, so slot order is position order) and the segment infos
+  // (thread t: segments kSegPerThread t ..), all loads issued before any use
+  uint2 v[kSelIPT];
+#pragma unroll
+  for (int u = 0; u < kSelIPT; ++u) {
+    const int j = t + kSelThreads * u;
+    v[u] = st.cand[j < slots ? j : 0];
+  }
   SegInfo si[kSegPerThread];
 #pragma unroll
   for (int j = 0; j < kSegPerThread; ++j) {
     const int s = kSegPerThread * t + j;
     si[j] = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)];
+  }
+#pragma unroll
+  for (int u = 0; u < kSelIPT; ++u) {
+    const int j = t + kSelThreads * u;  // < kCandCap
+    sm.ck[j] = j < slots ? v[u].x : 0u;
+    sm.cp[j] = v[u].y;
   }
   uint32_t cnt = 0, emax = 0;
 #pragma unroll
@@ -1073,28 +1092,15 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
       emax = emax > si[j].edge ? emax : si[j].edge;
     }
   }
-  uint32_t C;
-  {
-    uint32_t off = block_exclusive_scan<kSelThreads>(cnt, sm.red, &C);
-#pragma unroll
-    for (int j = 0; j < kSegPerThread; ++j) {
-      const int s = kSegPerThread * t + j;
-      if (s < nseg) {
-        sm.seg_cnt[s] = si[j].count;
-        sm.seg_off[s] = off;
-        off += si[j].count;
-      }
-    }
-  }
-  // largest edge over the row
+  // largest edge over the row (per wave; combined after the scan's barriers)
   {
     const uint32_t e = wave_inclusive_max(emax);
     if (lane == 63) sm.red[16 + wave] = e;
   }
-  __syncthreads();
+  uint32_t C;  // candidates in the slots
+  block_exclusive_scan<kSelThreads>(cnt, sm.red, &C);
   uint32_t max_edge = 0;
   for (int w = 0; w < kSelThreads / 64; ++w) max_edge = max_edge > sm.red[16 + w] ? max_edge : sm.red[16 + w];
-  copy_candidates(sm, st, nseg, nullptr);
   __syncthreads();
 
   // Pass 0 selects among the emitted candidates.  Items a segment left out
@@ -1102,10 +1108,10 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
   // that selection is exact.  Otherwise the segments with such an edge are
   // re-read in full (items at or above the floor only) and pass 1 selects
   // among the larger set, which is then exact: its threshold can only rise.
-  uint32_t n_c = C, written = 0;
+  uint32_t n_c = (uint32_t)slots, n_valid = C, written = 0;  // extent of ck/cp, items in it
   for (int pass = 0;; ++pass) {
     Thresh th{0u, 0u, 0, false};
-    const bool all = n_c <= (uint32_t)need;
+    const bool all = n_valid <= (uint32_t)need;
     if (!all) th = find_thresh_fast(sm, (int)n_c, (uint32_t)need);
     const uint32_t floor_key = all ? 0u : thresh_key_floor(th);
     if (pass == 1 || (all ? max_edge == 0u : max_edge <= floor_key)) {
@@ -1132,6 +1138,12 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
       if (t % tpw == 0) ovf_l[t / tpw] = word;
     }
     __syncthreads();
+    // emitted counts of every segment (the overflowing ones are recounted below)
+#pragma unroll
+    for (int j = 0; j < kSegPerThread; ++j) {
+      const int s = kSegPerThread * t + j;
+      if (s < nseg) sm.seg_cnt[s] = si[j].count;
+    }
     // --- count, one wave per overflowing segment (wave w: segments w, w+16, ...)
     for (int s = wave; s < nseg; s += kSelThreads / 64)
       if (is_ovf(s)) {
@@ -1166,6 +1178,7 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
       if (is_ovf(s)) wave_segment<true>(sm, st, s, floor_key, sm.seg_off[s]);
     __syncthreads();
     n_c = C2;
+    n_valid = C2;
   }
   (void)written;
 }
