@@ -9,9 +9,9 @@
 //   out[t][n] = sum_k H[t][k] * W[n][k],  n = l * 576 + c  (c < 512: C_l, else Z_l)
 // with H [tokens][hidden] and the weights in out x in orientation, so both
 // operands are read along k (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
-// A workgroup computes a 128 x 128 output tile with 4 waves (64 x 64 each,
-// 2 x 2 MFMA tiles of 32 x 32), k-steps of 64 staged through LDS with a
-// register prefetch of the next step.  The epilogue parks the fp32 tile in
+// A workgroup computes a 256 x 128 output tile with 4 waves (128 x 64 each,
+// 4 x 2 MFMA tiles of 32 x 32), k-steps of 32 staged through LDS with a
+// register prefetch of the next step; two workgroups share a CU.  The epilogue parks the fp32 tile in
 // LDS and packs each 16-channel group of C straight to E2M1 + E4M3 (the same
 // rounding rules as the standalone pack) and rounds Z to bf16, so C never
 // reaches HBM in fp32 (unless the optional debug copy is asked for).
@@ -22,12 +22,11 @@ namespace csa2 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 256, BN = 128, BK = 32;
 constexpr int kLdA = BK + 8;   // bf16 per LDS row (pad breaks bank conflicts)
-constexpr int kLdC = BN + 4;   // fp32 per epilogue row
+constexpr int kWM = 128, kWN = 64;  // wave tile: 4 x 2 MFMA tiles of 32 x 32
+constexpr int kLdC = BN + 4;   // fp32 per epilogue row (128 rows at a time)
 constexpr int kNPerLayer = kLatent + kIdxDim;  // 576
-
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 struct CedArgs {
   const uint16_t *h;
@@ -55,48 +54,55 @@ union SmemCed {
     uint16_t a[2][BM][kLdA];
     uint16_t b[2][BN][kLdA];
   } ab;
-  float c[BM][kLdC];
+  float c[kWM][kLdC];  // half of the output tile at a time in the epilogue
 };
 
+// 256 x 128 output tile per workgroup, 4 waves of 128 x 64 (8 independent
+// 32 x 32 accumulators per wave: each A fragment feeds 2 MFMAs, each B
+// fragment 4); two workgroups fit one CU.
 __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
   __shared__ __attribute__((aligned(16))) SmemCed sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
   const int n_total = a.n_layers * kNPerLayer;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
 
-  // global -> register staging: thread loads rows (tid / 8) + 32 * i, 16-byte column chunk tid % 8
-  const int ld_row = tid >> 3, ld_col = 8 * (tid & 7);
+  // global -> register staging: a thread loads rows (tid / 4) + 64 i of A (i < 4) and of
+  // B (i < 2), 16-byte column chunk tid % 4
+  const int ld_row = tid >> 2, ld_col = 8 * (tid & 3);
   const uint16_t *a_src[4];
-  const uint16_t *b_src[4];
+  const uint16_t *b_src[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + ld_row + 32 * i;
+    const int64_t m = m0 + ld_row + 64 * i;
     a_src[i] = m < a.tokens ? a.h + m * a.hidden + ld_col : nullptr;
-    const int n = n0 + ld_row + 32 * i;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = n0 + ld_row + 64 * i;
     b_src[i] = n < n_total ? weight_row(a, n) : nullptr;
     if (b_src[i]) b_src[i] += ld_col;
   }
-  uint4 ra[4], rb[4];
+  uint4 ra[4], rb[2];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
       ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
       rb[i] = b_src[i] ? *reinterpret_cast<const uint4 *>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
-    }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4 *>(&sm.ab.a[buf][ld_row + 32 * i][ld_col]) = ra[i];
-      *reinterpret_cast<uint4 *>(&sm.ab.b[buf][ld_row + 32 * i][ld_col]) = rb[i];
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(&sm.ab.a[buf][ld_row + 64 * i][ld_col]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(&sm.ab.b[buf][ld_row + 64 * i][ld_col]) = rb[i];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -111,14 +117,15 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
     if (ks + 1 < k_steps) fetch((ks + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[4], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 4; ++i)
         fa[i] = *reinterpret_cast<const bf16x8 *>(&sm.ab.a[buf][wm + 32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
-        fb[i] = *reinterpret_cast<const bf16x8 *>(&sm.ab.b[buf][wn + 32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
-      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8 *>(&sm.ab.b[buf][wn + 32 * j + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
@@ -126,52 +133,58 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
     __syncthreads();
   }
 
-  // ---- epilogue: fp32 tile -> LDS -> pack / round / store
+  // ---- epilogue: 128 rows at a time -> LDS -> pack / round / store
   // lane holds out[wm + 32i + 8*(e/4) + 4*(lane/32) + e%4][wn + 32j + lane%32]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int half = 0; half < 2; ++half) {
+    if ((wave >> 1) == half) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        sm.c[wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][wn + 32 * j + (lane & 31)] = acc[i][j][e];
-  __syncthreads();
-  // 128 rows x 8 groups of 16 columns = 1024 groups, 4 per thread
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int g = tid + 256 * it;
-    const int r = g >> 3, cg = g & 7;
-    const int64_t t = m0 + r;
-    const int n = n0 + 16 * cg;
-    if (t >= a.tokens || n >= n_total) continue;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = sm.c[r][16 * cg + i];
-    const int l = n / kNPerLayer, c = n % kNPerLayer;
-    const size_t row = (size_t)l * a.tokens + t;
-    if (c < kLatent) {
-      uint32_t w0, w1;
-      const uint32_t sc = pack_group16(v, &w0, &w1);
-      reinterpret_cast<uint2 *>(a.codes + row * (kLatent / 2))[c / kGroup] = make_uint2(w0, w1);
-      a.scales[row * (kLatent / kGroup) + c / kGroup] = (uint8_t)sc;
-      if (a.c_f32 != nullptr) {
-        float4 *dst = reinterpret_cast<float4 *>(a.c_f32 + row * kLatent + c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-      }
-    } else if (a.z != nullptr && a.w_z != nullptr) {
-      uint32_t packed[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
-        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-        packed[i] = lo | (hi << 16);
-      }
-      uint4 *dst = reinterpret_cast<uint4 *>(a.z + row * kIdxDim + (c - kLatent));
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+          for (int e = 0; e < 16; ++e)
+            sm.c[32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][wn + 32 * j + (lane & 31)] = acc[i][j][e];
     }
+    __syncthreads();
+    // 128 rows x 8 groups of 16 columns = 1024 groups, 4 per thread
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int g = tid + 256 * it;
+      const int r = g >> 3, cg = g & 7;
+      const int64_t t = m0 + kWM * half + r;
+      const int n = n0 + 16 * cg;
+      if (t >= a.tokens || n >= n_total) continue;
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = sm.c[r][16 * cg + i];
+      const int l = n / kNPerLayer, c = n % kNPerLayer;
+      const size_t row = (size_t)l * a.tokens + t;
+      if (c < kLatent) {
+        uint32_t w0, w1;
+        const uint32_t sc = pack_group16(v, &w0, &w1);
+        reinterpret_cast<uint2 *>(a.codes + row * (kLatent / 2))[c / kGroup] = make_uint2(w0, w1);
+        a.scales[row * (kLatent / kGroup) + c / kGroup] = (uint8_t)sc;
+        if (a.c_f32 != nullptr) {
+          float4 *dst = reinterpret_cast<float4 *>(a.c_f32 + row * kLatent + c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
+      } else if (a.z != nullptr && a.w_z != nullptr) {
+        uint32_t packed[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t lo = __float_as_uint(v[2 * i]), hi = __float_as_uint(v[2 * i + 1]);
+          lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+          hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+          packed[i] = lo | (hi << 16);
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(a.z + row * kIdxDim + (c - kLatent));
+        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      }
+    }
+    __syncthreads();
   }
 }
 
