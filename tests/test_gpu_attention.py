@@ -105,3 +105,15 @@ def test_identity_vs_permuted_table_bitwise():
         torch.cuda.synchronize()
         outs.append((out.cpu().numpy(), lse.cpu().numpy()))
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_batch8_64k_rope_launch_shape():
+    """8 sequences x 65,536 tokens, 64 heads + rope, K 2048: the 16-head split launch of batched decode."""
+    _run_and_check([65536] * 8, 64, 2048, rope_dim=64, seed=51)
+
+
+def test_batch32_launch_shape():
+    """32 sequences, 64 heads, K 2048: the 64-heads-per-workgroup launch used for large batches."""
+    rng = np.random.default_rng(52)
+    lens = [int(v) for v in np.exp(rng.uniform(np.log(1500), np.log(40000), size=32))]
+    _run_and_check(lens, 64, 2048, seed=52)
