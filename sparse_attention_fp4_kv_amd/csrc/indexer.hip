@@ -593,7 +593,7 @@ struct SelSmem {
   uint32_t hist[kBins];
   uint32_t seg_cnt[kMaxSeg];  // candidates a segment contributes
   uint32_t seg_off[kMaxSeg];  // where they start in ck/cp
-  uint32_t red[kSelThreads / 64 + 24];
+  uint32_t red[80];  // scans (0..7), threshold search (16..18), per-wave values (16..23, 32..39, 48..55, 64..71)
 };
 
 // Threshold of a selection: an item (key k, position p) is selected when
@@ -770,46 +770,68 @@ __device__ __forceinline__ Thresh find_thresh_lds(SelSmem &sm, int n, uint32_t n
   return th;
 }
 
-// Exact threshold for the top `need` of the n LDS candidates, usually in one
-// histogram pass: digits are taken relative to the candidates' own key range
-// (kmin .. kmax split into at most 2048 bins), so the items spread over the
-// bins.  When the boundary bin holds at most 64 items they are gathered and
-// ranked by one wave with lane reads; otherwise the radix levels run.
-__device__ __forceinline__ Thresh find_thresh_fast(SelSmem &sm, int n, uint32_t need) {
-  constexpr int kU = kSelIPT;  // one pass: n <= kCandCap
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  uint32_t k[kU];
+// The candidates a select thread holds in registers: items
+// i = 64 kSelIPT wave + 64 j + lane (j < kSelIPT) of the candidate array, so
+// item order is (wave, j, lane) order; key 0 marks an empty item.
+struct Items {
+  uint32_t k[kSelIPT], p[kSelIPT];
+};
+
+__device__ __forceinline__ int item_index(int j) {
+  return 64 * kSelIPT * (int)(threadIdx.x >> 6) + 64 * j + (int)(threadIdx.x & 63);
+}
+
+__device__ __forceinline__ void load_items_lds(const SelSmem &sm, int n, Items &it) {
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int i = u * kSelThreads + t;
-    k[u] = i < n ? sm.ck[min(i, kCandCap - 1)] : 0u;
+  for (int j = 0; j < kSelIPT; ++j) {
+    const int i = item_index(j);  // < kCandCap
+    it.k[j] = i < n ? sm.ck[i] : 0u;
+    it.p[j] = sm.cp[i];
   }
-  // key range of the valid candidates
+}
+
+// Key range [kmin, kmax] of the valid items of the workgroup (one barrier).
+__device__ __forceinline__ void items_key_range(SelSmem &sm, const Items &it, uint32_t *kmin, uint32_t *kmax) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    hi = max(hi, k[u]);
-    lo = min(lo, k[u] ? k[u] : 0xFFFFFFFFu);
+  for (int j = 0; j < kSelIPT; ++j) {
+    hi = max(hi, it.k[j]);
+    lo = min(lo, it.k[j] ? it.k[j] : 0xFFFFFFFFu);
   }
   hi = wave_inclusive_max(hi);
   lo = ~wave_inclusive_max(~lo);
-  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
   if (lane == 63) {
-    sm.red[16 + wave] = hi;
-    sm.red[32 + wave] = lo;
+    sm.red[32 + wave] = hi;
+    sm.red[48 + wave] = lo;
   }
   __syncthreads();
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
   for (int w = 0; w < kSelThreads / 64; ++w) {
-    kmax = max(kmax, sm.red[16 + w]);
-    kmin = min(kmin, sm.red[32 + w]);
+    mx = max(mx, sm.red[32 + w]);
+    mn = min(mn, sm.red[48 + w]);
   }
+  *kmin = mn;
+  *kmax = mx;
+}
+
+// Exact threshold for the top `need` of the items (at least `need` valid ones;
+// n = extent of the candidate array), usually in one histogram pass: digits
+// are taken relative to the items' own key range [kmin, kmax] split into at
+// most 2048 bins, so the items spread over the bins.  When the boundary bin
+// holds at most 64 items they are gathered and ranked by one wave; otherwise
+// the items go to LDS and the radix levels run.
+__device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it, int n, uint32_t need,
+                                                    uint32_t kmin, uint32_t kmax) {
+  const int t = threadIdx.x;
+  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
   const uint32_t span = kmax - kmin;
   const int shift = span < kBins ? 0 : (32 - __clz((int)(span >> 11)));  // (span >> shift) < 2048
+  __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kU; ++u)
-    if (k[u]) atomicAdd(&sm.hist[(k[u] - kmin) >> shift], 1u);
+  for (int j = 0; j < kSelIPT; ++j)
+    if (it.k[j]) atomicAdd(&sm.hist[(it.k[j] - kmin) >> shift], 1u);
   __syncthreads();
   find_threshold(sm.hist, need, sm.red + 16);
   const uint32_t d = sm.red[16];
@@ -821,7 +843,13 @@ __device__ __forceinline__ Thresh find_thresh_fast(SelSmem &sm, int n, uint32_t 
     __syncthreads();
     return th;
   }
-  if (in_bin > 64u) {
+  if (in_bin > 64u) {  // heavy ties or clustering: radix levels over the items in LDS
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSelIPT; ++j) {
+      sm.ck[item_index(j)] = it.k[j];
+      sm.cp[item_index(j)] = it.p[j];
+    }
     __syncthreads();
     return find_thresh_lds(sm, n, need);
   }
@@ -831,11 +859,11 @@ __device__ __forceinline__ Thresh find_thresh_fast(SelSmem &sm, int n, uint32_t 
   if (t == 0) *gn = 0u;
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    if ((k[u] != 0u) & (((k[u] - kmin) >> shift) == d)) {
+  for (int j = 0; j < kSelIPT; ++j) {
+    if ((it.k[j] != 0u) & (((it.k[j] - kmin) >> shift) == d)) {
       const uint32_t slot = atomicAdd(gn, 1u);
-      gk[slot] = k[u];
-      gp[slot] = sm.cp[u * kSelThreads + t];
+      gk[slot] = it.k[j];
+      gp[slot] = it.p[j];
     }
   }
   __syncthreads();
@@ -843,10 +871,13 @@ __device__ __forceinline__ Thresh find_thresh_fast(SelSmem &sm, int n, uint32_t 
     const uint32_t cnt = *gn;
     const uint32_t mk = t < (int)cnt ? gk[t] : 0u, mp = t < (int)cnt ? gp[t] : 0xFFFFFFFFu;
     uint32_t rank = 0;  // items of the bin that come before mine: larger key, or equal key and lower position
-    for (uint32_t j = 0; j < cnt; ++j) {
-      const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)j);
-      const uint32_t pj = (uint32_t)__builtin_amdgcn_readlane((int)mp, (int)j);
-      rank += (kj > mk || (kj == mk && pj < mp)) ? 1u : 0u;
+    for (uint32_t j0 = 0; j0 < cnt; j0 += 8) {
+#pragma unroll
+      for (uint32_t dj = 0; dj < 8; ++dj) {
+        const uint32_t j = j0 + dj;
+        const uint32_t kj = gk[j & 63], pj = gp[j & 63];  // broadcast reads
+        rank += (j < cnt && (kj > mk || (kj == mk && pj < mp))) ? 1u : 0u;
+      }
     }
     // the threshold item: the last one taken (largest rank below rem)
     const bool cand = t < (int)cnt && rank < rem;
@@ -866,32 +897,23 @@ __device__ __forceinline__ Thresh find_thresh_fast(SelSmem &sm, int n, uint32_t 
   return th;
 }
 
-// Ordered compaction of the selected LDS candidates (all valid ones when
-// `all`) to out[0 .. need), padded with -1.  The kept positions are staged in
-// ck (free once every thread holds its items) and written out with 16-byte
-// stores.  Returns the number of kept items written (at most need).
-__device__ __forceinline__ uint32_t compact_lds(SelSmem &sm, int n, bool all, const Thresh &th, int32_t *out,
-                                                uint32_t need) {
-  constexpr int kU = kSelIPT;  // one pass: n <= kCandCap
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+// Ordered compaction of the selected items (all valid ones when `all`) to
+// out[0 .. need), padded with -1.  The kept positions are staged in ck and
+// written out with 16-byte stores.  Returns the number of kept items written
+// (at most need).
+__device__ __forceinline__ uint32_t compact_items(SelSmem &sm, const Items &it, bool all, const Thresh &th,
+                                                  int32_t *out, uint32_t need) {
+  const int t = threadIdx.x;
   const uint64_t bound = all ? 0ull : thresh_bound(th);
-  const int i0 = 64 * kU * wave + lane;  // this lane's items: i0 + 64 j
-  uint32_t k[kU], p[kU];
-#pragma unroll
-  for (int j = 0; j < kU; ++j) {
-    const int i = min(i0 + 64 * j, kCandCap - 1);
-    k[j] = sm.ck[i];
-    p[j] = sm.cp[i];
-  }
   uint32_t flags = 0;
 #pragma unroll
-  for (int j = 0; j < kU; ++j) {
-    const bool keep = (i0 + 64 * j < n) & (k[j] != 0u) & selected64(k[j], p[j], bound);
+  for (int j = 0; j < kSelIPT; ++j) {
+    const bool keep = (it.k[j] != 0u) & selected64(it.k[j], it.p[j], bound);
     flags |= keep ? (1u << j) : 0u;
   }
-  // ordered_emit's barriers also order every read of ck above before the writes below
-  uint32_t written = ordered_emit<kSelThreads, kU>(flags, sm.red, 0u, [&](int j, uint32_t slot, bool keep) {
-    if (keep & (slot < need)) sm.ck[slot] = p[j];  // cap: a repeated pool block
+  // ordered_emit's barriers also order every earlier read of ck before the staging writes
+  uint32_t written = ordered_emit<kSelThreads, kSelIPT>(flags, sm.red, 0u, [&](int j, uint32_t slot, bool keep) {
+    if (keep & (slot < need)) sm.ck[slot] = it.p[j];  // cap: a repeated pool block
   });
   written = written < need ? written : need;
   __syncthreads();
@@ -1063,44 +1085,63 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
   const int nseg = st.nseg < kMaxSeg ? st.nseg : kMaxSeg;
   const int slots = nseg * st.cap;  // <= kCandCap
   // --- every candidate slot (segment s owns slots [s cap, s cap + cap), unused
-  // ones hold key 0, so slot order is position order) and the segment infos
-  // (thread t: segments kSegPerThread t ..), all loads issued before any use
-  uint2 v[kSelIPT];
+  // ones hold key 0, so slot order is position order) straight into registers,
+  // and the segment infos (thread t: segments kSegPerThread t ..); all loads
+  // are issued before any use
+  Items it;
+  {
+    uint2 v[kSelIPT];
 #pragma unroll
-  for (int u = 0; u < kSelIPT; ++u) {
-    const int j = t + kSelThreads * u;
-    v[u] = st.cand[j < slots ? j : 0];
-  }
-  SegInfo si[kSegPerThread];
+    for (int j = 0; j < kSelIPT; ++j) {
+      const int i = item_index(j);
+      v[j] = st.cand[i < slots ? i : 0];
+    }
+    SegInfo si[kSegPerThread];
 #pragma unroll
-  for (int j = 0; j < kSegPerThread; ++j) {
-    const int s = kSegPerThread * t + j;
-    si[j] = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)];
-  }
+    for (int j = 0; j < kSegPerThread; ++j) {
+      const int s = kSegPerThread * t + j;
+      si[j] = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)];
+    }
 #pragma unroll
-  for (int u = 0; u < kSelIPT; ++u) {
-    const int j = t + kSelThreads * u;  // < kCandCap
-    sm.ck[j] = j < slots ? v[u].x : 0u;
-    sm.cp[j] = v[u].y;
-  }
-  uint32_t cnt = 0, emax = 0;
+    for (int j = 0; j < kSelIPT; ++j) {
+      it.k[j] = item_index(j) < slots ? v[j].x : 0u;
+      it.p[j] = v[j].y;
+    }
+    uint32_t cnt = 0, emax = 0, lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-  for (int j = 0; j < kSegPerThread; ++j) {
-    const int s = kSegPerThread * t + j;
-    if (s < nseg) {
-      cnt += si[j].count;
-      emax = emax > si[j].edge ? emax : si[j].edge;
+    for (int j = 0; j < kSegPerThread; ++j) {
+      const int s = kSegPerThread * t + j;
+      if (s < nseg) {
+        cnt += si[j].count;
+        emax = max(emax, si[j].edge);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSelIPT; ++j) {
+      hi = max(hi, it.k[j]);
+      lo = min(lo, it.k[j] ? it.k[j] : 0xFFFFFFFFu);
+    }
+    // one exchange for the candidate count, the largest edge and the key range
+    cnt = wave_last(wave_inclusive_sum(cnt));
+    emax = wave_inclusive_max(emax);
+    hi = wave_inclusive_max(hi);
+    lo = ~wave_inclusive_max(~lo);
+    if (lane == 63) {
+      sm.red[16 + wave] = emax;
+      sm.red[32 + wave] = hi;
+      sm.red[48 + wave] = lo;
+      sm.red[64 + wave] = cnt;
     }
   }
-  // largest edge over the row (per wave; combined after the scan's barriers)
-  {
-    const uint32_t e = wave_inclusive_max(emax);
-    if (lane == 63) sm.red[16 + wave] = e;
+  __syncthreads();
+  uint32_t max_edge = 0, kmax = 0, kmin = 0xFFFFFFFFu, C = 0;  // C: candidates in the slots
+#pragma unroll
+  for (int w = 0; w < kSelThreads / 64; ++w) {
+    max_edge = max(max_edge, sm.red[16 + w]);
+    kmax = max(kmax, sm.red[32 + w]);
+    kmin = min(kmin, sm.red[48 + w]);
+    C += sm.red[64 + w];
   }
-  uint32_t C;  // candidates in the slots
-  block_exclusive_scan<kSelThreads>(cnt, sm.red, &C);
-  uint32_t max_edge = 0;
-  for (int w = 0; w < kSelThreads / 64; ++w) max_edge = max_edge > sm.red[16 + w] ? max_edge : sm.red[16 + w];
   __syncthreads();
 
   // Pass 0 selects among the emitted candidates.  Items a segment left out
@@ -1108,14 +1149,14 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
   // that selection is exact.  Otherwise the segments with such an edge are
   // re-read in full (items at or above the floor only) and pass 1 selects
   // among the larger set, which is then exact: its threshold can only rise.
-  uint32_t n_c = (uint32_t)slots, n_valid = C, written = 0;  // extent of ck/cp, items in it
+  uint32_t n_c = (uint32_t)slots, n_valid = C, written = 0;  // extent of the candidates, items in it
   for (int pass = 0;; ++pass) {
     Thresh th{0u, 0u, 0, false};
     const bool all = n_valid <= (uint32_t)need;
-    if (!all) th = find_thresh_fast(sm, (int)n_c, (uint32_t)need);
+    if (!all) th = find_thresh_items(sm, it, (int)n_c, (uint32_t)need, kmin, kmax);
     const uint32_t floor_key = all ? 0u : thresh_key_floor(th);
     if (pass == 1 || (all ? max_edge == 0u : max_edge <= floor_key)) {
-      written = compact_lds(sm, (int)n_c, all, th, out, (uint32_t)need);
+      written = compact_items(sm, it, all, th, out, (uint32_t)need);
       break;
     }
     // --- overflowing segments: a bitmap in hist (kMaxSeg bits)
@@ -1142,7 +1183,7 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
 #pragma unroll
     for (int j = 0; j < kSegPerThread; ++j) {
       const int s = kSegPerThread * t + j;
-      if (s < nseg) sm.seg_cnt[s] = si[j].count;
+      if (s < nseg) sm.seg_cnt[s] = st.info[s].count;
     }
     // --- count, one wave per overflowing segment (wave w: segments w, w+16, ...)
     for (int s = wave; s < nseg; s += kSelThreads / 64)
@@ -1179,6 +1220,8 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
     __syncthreads();
     n_c = C2;
     n_valid = C2;
+    load_items_lds(sm, (int)n_c, it);
+    items_key_range(sm, it, &kmin, &kmax);
   }
   (void)written;
 }
