@@ -397,38 +397,49 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 }
 
 // Merges the splits' partials: workgroup (b*H + h, quarter) of 32 threads
-// covers 128 channels of one head, one float4 per thread.
+// covers 128 channels of one head, one float4 per thread.  Splits are read 32
+// at a time (all loads of a chunk issued together) and merged online.
 __global__ void __launch_bounds__(32) attn_combine_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
                                                           float *__restrict__ out, float *__restrict__ lse) {
+  constexpr int kChunk = 32;
   const int bh = blockIdx.x, quarter = blockIdx.y;
   const int tid = threadIdx.x;
   const int c4 = 32 * quarter + tid;  // float4 index within the 512 channels
-  // all loads are unconditional (kMaxSplits-bounded unrolled loop): empty
-  // splits (m = -inf, l = 0, O = 0) get weight 0
   const float2 *ml = reinterpret_cast<const float2 *>(part_ml + (size_t)bh * splits * 2);
-  float2 mls[kMaxSplits];
-  float4 po[kMaxSplits];
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    const int sc = s < splits ? s : 0;
-    mls[s] = ml[sc];
-    po[s] = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + sc) * kLatent)[c4];
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
-    if (s < splits) m = fmaxf(m, mls[s].x);
+  float m = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  float l = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += kChunk) {
+    // unconditional loads (clamped split index); splits past the end and empty
+    // splits (m = -inf, l = 0, O = 0) get weight 0
+    float2 mls[kChunk];
+    float4 po[kChunk];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    const float w = (s < splits && mls[s].x != -INFINITY) ? exp2f(mls[s].x - m) : 0.f;
-    l += w * mls[s].y;
-    o.x += w * po[s].x;
-    o.y += w * po[s].y;
-    o.z += w * po[s].z;
-    o.w += w * po[s].w;
+    for (int s = 0; s < kChunk; ++s) {
+      const int sc = s0 + s < splits ? s0 + s : s0;
+      mls[s] = ml[sc];
+      po[s] = reinterpret_cast<const float4 *>(part_o + ((size_t)bh * splits + sc) * kLatent)[c4];
+    }
+    float mc = m;
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s)
+      if (s0 + s < splits) mc = fmaxf(mc, mls[s].x);
+    const float r = (m == -INFINITY) ? 0.f : exp2f(m - mc);  // rescale what is merged so far
+    l *= r;
+    o.x *= r;
+    o.y *= r;
+    o.z *= r;
+    o.w *= r;
+#pragma unroll
+    for (int s = 0; s < kChunk; ++s) {
+      const float w = (s0 + s < splits && mls[s].x != -INFINITY) ? exp2f(mls[s].x - mc) : 0.f;
+      l += w * mls[s].y;
+      o.x += w * po[s].x;
+      o.y += w * po[s].y;
+      o.z += w * po[s].z;
+      o.w += w * po[s].w;
+    }
+    m = mc;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[c4] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
