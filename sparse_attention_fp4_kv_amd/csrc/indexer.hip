@@ -231,14 +231,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
   return wave_base + incl - v;
 }
 
-// Threshold digit of a 2048-bin histogram in LDS, computed by wave 0:
+// Threshold digit of a 2048-bin histogram in LDS, computed by one wave:
 // the bin d with sum(hist[d+1..]) < need <= sum(hist[d..]).  Result in
 // res[0] = d, res[1] = sum(hist[d+1..]), res[2] = found (0 when all bins hold
-// fewer than `need`; then d = 0 and res[1] = total - hist[0]).  Every thread
-// must call it (it ends with a barrier).
-__device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t need, uint32_t *res) {
-  const int t = threadIdx.x;
-  if (t < 64) {
+// fewer than `need`; then d = 0 and res[1] = total - hist[0]).  All 64 lanes
+// of the calling wave take part; the caller synchronizes before reading res.
+__device__ __forceinline__ void find_threshold_wave(const uint32_t *hist, uint32_t need, uint32_t *res) {
+  const int t = threadIdx.x & 63;
+  {
     constexpr int per = kBins / 64;  // lane l owns bins [32l, 32l+32)
     const u32x4 *h4 = reinterpret_cast<const u32x4 *>(&hist[per * t]);
     u32x4 v[per / 4];
@@ -271,6 +271,11 @@ __device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t ne
       res[2] = 0u;
     }
   }
+}
+
+// The same search run by wave 0, followed by a barrier (every thread calls it).
+__device__ __forceinline__ void find_threshold(const uint32_t *hist, uint32_t need, uint32_t *res) {
+  if (threadIdx.x < 64) find_threshold_wave(hist, need, res);
   __syncthreads();
 }
 
@@ -365,6 +370,109 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
   if (t == 0) *info = SegInfo{total, edge};
 }
 
+// Both segments of a hierarchical scan workgroup at once (positions: 2048
+// keys, 8 per thread; blocks: 256 keys, 1 per thread), with the same cut rule
+// as emit_segment: the two histograms share each barrier and their threshold
+// searches run side by side in waves 0 and 1.
+template <class PosP, class PosB>
+__device__ __forceinline__ void emit_segment_pair(const uint32_t *pkeys, int cap_p, uint2 *cand_p, SegInfo *info_p,
+                                                  PosP pos_p, const uint32_t *bkeys, int cap_b, uint2 *cand_b,
+                                                  SegInfo *info_b, PosB pos_b, uint32_t *hist_p, uint32_t *hist_b,
+                                                  uint32_t *red) {
+  constexpr int NT = 256;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int ip0 = 64 * 8 * wave + lane, ib = 64 * wave + lane;
+  uint32_t kp[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kp[j] = pkeys[ip0 + 64 * j];
+  const uint32_t kb = bkeys[ib];
+  for (int i = t; i < kBins; i += NT) {
+    hist_p[i] = 0u;
+    hist_b[i] = 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (kp[j]) atomicAdd(&hist_p[kp[j] >> 21], 1u);
+  if (kb) atomicAdd(&hist_b[kb >> 21], 1u);
+  __syncthreads();
+  if (wave == 0) find_threshold_wave(hist_p, (uint32_t)cap_p + 1u, red + 16);
+  if (wave == 1) find_threshold_wave(hist_b, (uint32_t)cap_b + 1u, red + 20);
+  __syncthreads();
+  const uint32_t d1p = red[16], above_p = red[17], d1b = red[20], above_b = red[21];
+  const bool cut_p = red[18] != 0u, cut_b = red[22] != 0u;
+  uint32_t d2p = 0, d2b = 0, edge_p = 0, edge_b = 0;
+  if (cut_p || cut_b) {
+    // level 2 inside each boundary bin d1: room for cap - above of its items
+    // (every read of the histograms ended at the barrier above)
+    for (int i = t; i < kBins; i += NT) {
+      hist_p[i] = 0u;
+      hist_b[i] = 0u;
+    }
+    __syncthreads();
+    if (cut_p) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (kp[j] && (kp[j] >> 21) == d1p) atomicAdd(&hist_p[(kp[j] >> 10) & 0x7FFu], 1u);
+    }
+    if (cut_b && kb && (kb >> 21) == d1b) atomicAdd(&hist_b[(kb >> 10) & 0x7FFu], 1u);
+    __syncthreads();
+    if (wave == 0 && cut_p) find_threshold_wave(hist_p, (uint32_t)cap_p - above_p + 1u, red + 16);
+    if (wave == 1 && cut_b) find_threshold_wave(hist_b, (uint32_t)cap_b - above_b + 1u, red + 20);
+    __syncthreads();
+    if (cut_p) {
+      d2p = red[16];
+      const uint64_t e = ((uint64_t)d1p << 21) + ((uint64_t)(d2p + 1u) << 10);
+      edge_p = e > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)e;
+    }
+    if (cut_b) {
+      d2b = red[20];
+      const uint64_t e = ((uint64_t)d1b << 21) + ((uint64_t)(d2b + 1u) << 10);
+      edge_b = e > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)e;
+    }
+  }
+  auto emit = [](uint32_t key, bool cut, uint32_t d1, uint32_t d2) {
+    return key != 0u && (!cut || (key >> 21) > d1 || ((key >> 21) == d1 && ((key >> 10) & 0x7FFu) > d2));
+  };
+  // ordered compaction of both segments with one exchange of wave totals
+  const uint64_t below = __lanemask_lt();
+  uint64_t bal[8];
+  uint32_t wtot_p = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bal[j] = __ballot(emit(kp[j], cut_p, d1p, d2p));
+    wtot_p += (uint32_t)__popcll(bal[j]);
+  }
+  const bool keep_b = emit(kb, cut_b, d1b, d2b);
+  const uint64_t bal_b = __ballot(keep_b);
+  if (lane == 0) {
+    red[wave] = wtot_p;
+    red[4 + wave] = (uint32_t)__popcll(bal_b);
+  }
+  __syncthreads();
+  uint32_t run = 0, total_p = 0, slot_b = 0, total_b = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t xp = red[w], xb = red[4 + w];
+    run += w < wave ? xp : 0u;
+    slot_b += w < wave ? xb : 0u;
+    total_p += xp;
+    total_b += xb;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if ((bal[j] >> lane) & 1u) cand_p[run + (uint32_t)__popcll(bal[j] & below)] = make_uint2(kp[j], pos_p(ip0 + 64 * j));
+    run += (uint32_t)__popcll(bal[j]);
+  }
+  if (keep_b) cand_b[slot_b + (uint32_t)__popcll(bal_b & below)] = make_uint2(kb, pos_b(ib));
+  for (int i = (int)total_p + t; i < cap_p; i += NT) cand_p[i] = make_uint2(0u, 0u);  // unused slots: no item
+  for (int i = (int)total_b + t; i < cap_b; i += NT) cand_b[i] = make_uint2(0u, 0u);
+  if (t == 0) {
+    *info_p = SegInfo{total_p, edge_p};
+    *info_b = SegInfo{total_b, edge_b};
+  }
+}
+
 // ------------------------------------------------------------------ producer: full scan
 struct ScanArgs {
   KvLayerDev L;
@@ -380,6 +488,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
   __shared__ __attribute__((aligned(16))) uint32_t bkey[kScanBlocks];
   __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist2[HIER ? kBins : 4];  // block-key histogram
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -442,18 +551,18 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     if constexpr (HIER) a.w.bkeys[(size_t)b * a.w.cap_blocks + base / kBlk + tid] = bkey[tid];
   }
   const int nseg = (n + kScanPos - 1) / kScanPos;
-  {
-    const int cap = seg_budget(a.K, nseg, kScanPos);
+  const int cap = seg_budget(a.K, nseg, kScanPos);
+  if constexpr (HIER) {
+    const int cap_b = seg_budget(a.P, nseg, kScanBlocks);
+    emit_segment_pair(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                      a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
+                      bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
+                      a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
+                      hist, hist2, red);
+  } else {
     emit_segment<256, 8>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                          a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
                          [&](int i) { return (uint32_t)(base + i); });
-  }
-  if constexpr (HIER) {
-    __syncthreads();
-    const int cap = seg_budget(a.P, nseg, kScanBlocks);
-    emit_segment<256, 1>(bkey, cap, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap,
-                         a.w.seg_blk + (size_t)b * a.w.max_seg + wg, hist, red,
-                         [&](int i) { return (uint32_t)(base / kBlk + i); });
   }
 }
 
