@@ -699,10 +699,10 @@ struct SelArgs {
 struct SelSmem {
   uint32_t ck[kCandCap];      // candidate keys
   uint32_t cp[kCandCap];      // candidate positions
-  uint32_t hist[kBins];
+  __attribute__((aligned(16))) uint32_t hist[kBins];
   uint32_t seg_cnt[kMaxSeg];  // candidates a segment contributes
   uint32_t seg_off[kMaxSeg];  // where they start in ck/cp
-  uint32_t red[80];  // scans (0..7), threshold search (16..18), per-wave values (16..23, 32..39, 48..55, 64..71)
+  uint32_t red[80];  // scans (0..7), threshold search (16..18), per-wave values (16..23, 32..39, 48..55, 64..71), gather count (76)
 };
 
 // Threshold of a selection: an item (key k, position p) is selected when
@@ -925,19 +925,26 @@ __device__ __forceinline__ void items_key_range(SelSmem &sm, const Items &it, ui
   *kmax = mx;
 }
 
+// Zeroes the histogram and the gather counter for find_thresh_items.
+__device__ __forceinline__ void clear_for_search(SelSmem &sm) {
+  u32x4 *h4 = reinterpret_cast<u32x4 *>(sm.hist);
+  for (int i = threadIdx.x; i < kBins / 4; i += kSelThreads) h4[i] = u32x4{0u, 0u, 0u, 0u};
+  if (threadIdx.x == 0) sm.red[76] = 0u;
+}
+
 // Exact threshold for the top `need` of the items (at least `need` valid ones;
 // n = extent of the candidate array), usually in one histogram pass: digits
 // are taken relative to the items' own key range [kmin, kmax] split into at
 // most 2048 bins, so the items spread over the bins.  When the boundary bin
-// holds at most 64 items they are gathered and ranked by one wave; otherwise
-// the items go to LDS and the radix levels run.
+// holds at most 64 items they are gathered (into seg_cnt) and ranked by one
+// wave; otherwise the items go to LDS and the radix levels run.
+// On entry hist and the gather counter red[76] are zero and a barrier
+// separates the call from earlier reads of red[16..17] and seg_cnt.
 __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it, int n, uint32_t need,
                                                     uint32_t kmin, uint32_t kmax) {
   const int t = threadIdx.x;
-  for (int i = t; i < kBins; i += kSelThreads) sm.hist[i] = 0u;
   const uint32_t span = kmax - kmin;
   const int shift = span < kBins ? 0 : (32 - __clz((int)(span >> 11)));  // (span >> shift) < 2048
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kSelIPT; ++j)
     if (it.k[j]) atomicAdd(&sm.hist[(it.k[j] - kmin) >> shift], 1u);
@@ -949,7 +956,6 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
   Thresh th{0u, 0u, 0, false};
   if (in_bin == rem) {  // the whole boundary bin is taken
     th.kt = kmin + (d << shift);
-    __syncthreads();
     return th;
   }
   if (in_bin > 64u) {  // heavy ties or clustering: radix levels over the items in LDS
@@ -963,10 +969,7 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
     return find_thresh_lds(sm, n, need);
   }
   // gather the boundary bin (<= 64 items) and rank it in wave 0
-  uint32_t *gk = sm.hist + kBins - 160, *gp = gk + 64, *gn = gk + 128;
-  __syncthreads();
-  if (t == 0) *gn = 0u;
-  __syncthreads();
+  uint32_t *gk = sm.seg_cnt, *gp = sm.seg_cnt + 64, *gn = sm.red + 76;
 #pragma unroll
   for (int j = 0; j < kSelIPT; ++j) {
     if ((it.k[j] != 0u) & (((it.k[j] - kmin) >> shift) == d)) {
@@ -980,13 +983,20 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
     const uint32_t cnt = *gn;
     const uint32_t mk = t < (int)cnt ? gk[t] : 0u, mp = t < (int)cnt ? gp[t] : 0xFFFFFFFFu;
     uint32_t rank = 0;  // items of the bin that come before mine: larger key, or equal key and lower position
-    for (uint32_t j0 = 0; j0 < cnt; j0 += 8) {
+    for (uint32_t j0 = 0; j0 < cnt; j0 += 16) {
+      u32x4 kq[4], pq[4];  // 16 items per round, broadcast 16-byte reads issued together
 #pragma unroll
-      for (uint32_t dj = 0; dj < 8; ++dj) {
-        const uint32_t j = j0 + dj;
-        const uint32_t kj = gk[j & 63], pj = gp[j & 63];  // broadcast reads
-        rank += (j < cnt && (kj > mk || (kj == mk && pj < mp))) ? 1u : 0u;
+      for (int q = 0; q < 4; ++q) {
+        kq[q] = *reinterpret_cast<const u32x4 *>(gk + j0 + 4 * q);
+        pq[q] = *reinterpret_cast<const u32x4 *>(gp + j0 + 4 * q);
       }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t j = j0 + 4 * q + e, kj = kq[q][e], pj = pq[q][e];
+          rank += ((j < cnt) & ((kj > mk) | ((kj == mk) & (pj < mp)))) ? 1u : 0u;
+        }
     }
     // the threshold item: the last one taken (largest rank below rem)
     const bool cand = t < (int)cnt && rank < rem;
@@ -1002,28 +1012,43 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
   th.kt = sm.red[16];
   th.pinv = sm.red[17];
   th.tie = true;
-  __syncthreads();
   return th;
 }
 
 // Ordered compaction of the selected items (all valid ones when `all`) to
 // out[0 .. need), padded with -1.  The kept positions are staged in ck and
 // written out with 16-byte stores.  Returns the number of kept items written
-// (at most need).
+// (at most need).  A barrier separates the call from earlier reads of ck and
+// of red[0..7].
 __device__ __forceinline__ uint32_t compact_items(SelSmem &sm, const Items &it, bool all, const Thresh &th,
                                                   int32_t *out, uint32_t need) {
-  const int t = threadIdx.x;
+  constexpr int NW = kSelThreads / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint64_t bound = all ? 0ull : thresh_bound(th);
-  uint32_t flags = 0;
+  const uint64_t below = __lanemask_lt();
+  uint64_t bal[kSelIPT];
+  uint32_t wtot = 0;
 #pragma unroll
   for (int j = 0; j < kSelIPT; ++j) {
-    const bool keep = (it.k[j] != 0u) & selected64(it.k[j], it.p[j], bound);
-    flags |= keep ? (1u << j) : 0u;
+    bal[j] = __ballot((it.k[j] != 0u) & selected64(it.k[j], it.p[j], bound));
+    wtot += (uint32_t)__popcll(bal[j]);
   }
-  // ordered_emit's barriers also order every earlier read of ck before the staging writes
-  uint32_t written = ordered_emit<kSelThreads, kSelIPT>(flags, sm.red, 0u, [&](int j, uint32_t slot, bool keep) {
-    if (keep & (slot < need)) sm.ck[slot] = it.p[j];  // cap: a repeated pool block
-  });
+  if (lane == 0) sm.red[wave] = wtot;
+  __syncthreads();
+  uint32_t run = 0, written = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t x = sm.red[w];
+    run += w < wave ? x : 0u;
+    written += x;
+  }
+  // items in (wave, j, lane) order: stream order
+#pragma unroll
+  for (int j = 0; j < kSelIPT; ++j) {
+    const uint32_t slot = run + (uint32_t)__popcll(bal[j] & below);
+    if (((bal[j] >> lane) & 1u) & (slot < need)) sm.ck[slot] = it.p[j];  // cap: a repeated pool block
+    run += (uint32_t)__popcll(bal[j]);
+  }
   written = written < need ? written : need;
   __syncthreads();
   for (int i = 4 * t; i < (int)need; i += 4 * kSelThreads) {
@@ -1187,6 +1212,77 @@ __device__ __forceinline__ uint32_t select_all_stored(SelSmem &sm, const Stream 
   return compact<2>(sm, st.items, all, th, gkey, gpos, out, (uint32_t)need);
 }
 
+// Overflow path of a selection: re-reads every segment whose edge is above
+// floor_key (items at or above the floor only) next to the other segments'
+// emitted candidates, into ck/cp in stream order.  Returns false when the
+// selection was finished here instead (more than kCandCap items: out written
+// from the stored items directly); else *n_c is the number of items in ck/cp.
+__device__ __forceinline__ bool reload_overflowing(SelSmem &sm, const Stream &st, int nseg, uint32_t floor_key,
+                                                   int need, int32_t *out, int *n_c) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // --- overflowing segments: a bitmap in hist (kMaxSeg bits)
+  uint32_t *ovf_l = sm.hist;
+  auto is_ovf = [&](int s) { return (ovf_l[s >> 5] >> (s & 31)) & 1u; };
+  __syncthreads();
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kSegPerThread; ++j) {
+    const int s = kSegPerThread * t + j;
+    const uint32_t edge = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)].edge;
+    if (s < nseg && edge > floor_key) mine |= 1u << j;
+  }
+  // thread t's bits land at bit kSegPerThread * (t % tpw) of word t / tpw
+  {
+    constexpr int tpw = 32 / kSegPerThread;
+    uint32_t word = mine << (kSegPerThread * (t % tpw));
+#pragma unroll
+    for (int o = 1; o < tpw; o <<= 1) word |= __shfl_xor(word, o);
+    if (t % tpw == 0) ovf_l[t / tpw] = word;
+  }
+  __syncthreads();
+  // emitted counts of every segment (the overflowing ones are recounted below)
+#pragma unroll
+  for (int j = 0; j < kSegPerThread; ++j) {
+    const int s = kSegPerThread * t + j;
+    if (s < nseg) sm.seg_cnt[s] = st.info[s].count;
+  }
+  // --- count, one wave per overflowing segment (wave w: segments w, w+8, ...)
+  for (int s = wave; s < nseg; s += kSelThreads / 64)
+    if (is_ovf(s)) {
+      const uint32_t c = wave_segment<false>(sm, st, s, floor_key, 0u);
+      if (lane == 0) sm.seg_cnt[s] = c;
+    }
+  __syncthreads();
+  uint32_t cnt2 = 0;
+#pragma unroll
+  for (int j = 0; j < kSegPerThread; ++j) {
+    const int s = kSegPerThread * t + j;
+    if (s < nseg) cnt2 += sm.seg_cnt[s];
+  }
+  uint32_t C2;
+  uint32_t off2 = block_exclusive_scan<kSelThreads>(cnt2, sm.red, &C2);
+  if (C2 > (uint32_t)kCandCap) {
+    const uint32_t written = select_all_stored(sm, st, need, out);
+    for (int i = (int)written + t; i < need; i += kSelThreads) out[i] = -1;  // slots it did not write
+    return false;
+  }
+#pragma unroll
+  for (int j = 0; j < kSegPerThread; ++j) {
+    const int s = kSegPerThread * t + j;
+    if (s < nseg) {
+      sm.seg_off[s] = off2;
+      off2 += sm.seg_cnt[s];
+    }
+  }
+  __syncthreads();
+  copy_candidates(sm, st, nseg, ovf_l);
+  for (int s = wave; s < nseg; s += kSelThreads / 64)
+    if (is_ovf(s)) wave_segment<true>(sm, st, s, floor_key, sm.seg_off[s]);
+  __syncthreads();
+  *n_c = (int)C2;
+  return true;
+}
+
 // Top `need` of a row from its stream, in increasing position order (stream
 // order for a pool), -1 padded.
 __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int need, int32_t *out) {
@@ -1242,6 +1338,7 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
       sm.red[64 + wave] = cnt;
     }
   }
+  clear_for_search(sm);
   __syncthreads();
   uint32_t max_edge = 0, kmax = 0, kmin = 0xFFFFFFFFu, C = 0;  // C: candidates in the slots
 #pragma unroll
@@ -1251,88 +1348,36 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
     kmin = min(kmin, sm.red[48 + w]);
     C += sm.red[64 + w];
   }
-  __syncthreads();
+  // (red[16..71] is next written after the histogram barrier)
 
   // Pass 0 selects among the emitted candidates.  Items a segment left out
   // are below its edge, so when no edge is above the selection's key floor
   // that selection is exact.  Otherwise the segments with such an edge are
   // re-read in full (items at or above the floor only) and pass 1 selects
   // among the larger set, which is then exact: its threshold can only rise.
-  uint32_t n_c = (uint32_t)slots, n_valid = C, written = 0;  // extent of the candidates, items in it
-  for (int pass = 0;; ++pass) {
+  // (Straight-line passes: the overflow path's set-up stays off the common one.)
+  int n_c = 0;
+  {
     Thresh th{0u, 0u, 0, false};
-    const bool all = n_valid <= (uint32_t)need;
-    if (!all) th = find_thresh_items(sm, it, (int)n_c, (uint32_t)need, kmin, kmax);
+    const bool all = C <= (uint32_t)need;
+    if (!all) th = find_thresh_items(sm, it, slots, (uint32_t)need, kmin, kmax);
     const uint32_t floor_key = all ? 0u : thresh_key_floor(th);
-    if (pass == 1 || (all ? max_edge == 0u : max_edge <= floor_key)) {
-      written = compact_items(sm, it, all, th, out, (uint32_t)need);
-      break;
+    if (all ? max_edge == 0u : max_edge <= floor_key) {
+      compact_items(sm, it, all, th, out, (uint32_t)need);
+      return;
     }
-    // --- overflowing segments: a bitmap in hist (kMaxSeg bits)
-    uint32_t *ovf_l = sm.hist;
-    auto is_ovf = [&](int s) { return (ovf_l[s >> 5] >> (s & 31)) & 1u; };
-    __syncthreads();
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < kSegPerThread; ++j) {  // edges re-read: keeps registers free on the common path
-      const int s = kSegPerThread * t + j;
-      const uint32_t edge = st.info[s < nseg ? s : (nseg > 0 ? nseg - 1 : 0)].edge;
-      if (s < nseg && edge > floor_key) mine |= 1u << j;
-    }
-    // thread t's bits land at bit kSegPerThread * (t % tpw) of word t / tpw
-    {
-      constexpr int tpw = 32 / kSegPerThread;
-      uint32_t word = mine << (kSegPerThread * (t % tpw));
-#pragma unroll
-      for (int o = 1; o < tpw; o <<= 1) word |= __shfl_xor(word, o);
-      if (t % tpw == 0) ovf_l[t / tpw] = word;
-    }
-    __syncthreads();
-    // emitted counts of every segment (the overflowing ones are recounted below)
-#pragma unroll
-    for (int j = 0; j < kSegPerThread; ++j) {
-      const int s = kSegPerThread * t + j;
-      if (s < nseg) sm.seg_cnt[s] = st.info[s].count;
-    }
-    // --- count, one wave per overflowing segment (wave w: segments w, w+16, ...)
-    for (int s = wave; s < nseg; s += kSelThreads / 64)
-      if (is_ovf(s)) {
-        const uint32_t c = wave_segment<false>(sm, st, s, floor_key, 0u);
-        if (lane == 0) sm.seg_cnt[s] = c;
-      }
-    __syncthreads();
-    uint32_t cnt2 = 0;
-#pragma unroll
-    for (int j = 0; j < kSegPerThread; ++j) {
-      const int s = kSegPerThread * t + j;
-      if (s < nseg) cnt2 += sm.seg_cnt[s];
-    }
-    uint32_t C2;
-    uint32_t off2 = block_exclusive_scan<kSelThreads>(cnt2, sm.red, &C2);
-    if (C2 > (uint32_t)kCandCap) {
-      written = select_all_stored(sm, st, need, out);
-      for (int i = (int)written + t; i < need; i += kSelThreads) out[i] = -1;  // slots it did not write
-      break;
-    }
-#pragma unroll
-    for (int j = 0; j < kSegPerThread; ++j) {
-      const int s = kSegPerThread * t + j;
-      if (s < nseg) {
-        sm.seg_off[s] = off2;
-        off2 += sm.seg_cnt[s];
-      }
-    }
-    __syncthreads();
-    copy_candidates(sm, st, nseg, ovf_l);
-    for (int s = wave; s < nseg; s += kSelThreads / 64)
-      if (is_ovf(s)) wave_segment<true>(sm, st, s, floor_key, sm.seg_off[s]);
-    __syncthreads();
-    n_c = C2;
-    n_valid = C2;
-    load_items_lds(sm, (int)n_c, it);
+    if (!reload_overflowing(sm, st, nseg, floor_key, need, out, &n_c)) return;
+    load_items_lds(sm, n_c, it);
+    clear_for_search(sm);  // the bitmap in hist was last read before reload's final barrier
     items_key_range(sm, it, &kmin, &kmax);
   }
-  (void)written;
+  {
+    // pass 1 over the n_c items now in LDS (all valid)
+    Thresh th{0u, 0u, 0, false};
+    const bool all = n_c <= need;
+    if (!all) th = find_thresh_items(sm, it, n_c, (uint32_t)need, kmin, kmax);
+    compact_items(sm, it, all, th, out, (uint32_t)need);
+  }
 }
 
 // grid (1 or 2, B): x == 0 selects positions (indices), x == 1 the pool blocks.
