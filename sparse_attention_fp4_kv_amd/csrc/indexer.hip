@@ -927,19 +927,25 @@ __device__ __forceinline__ void items_key_range(SelSmem &sm, const Items &it, ui
 
 // Zeroes the histogram and the gather counter for find_thresh_items.
 __device__ __forceinline__ void clear_for_search(SelSmem &sm) {
-  u32x4 *h4 = reinterpret_cast<u32x4 *>(sm.hist);
-  for (int i = threadIdx.x; i < kBins / 4; i += kSelThreads) h4[i] = u32x4{0u, 0u, 0u, 0u};
+  u32x4 *h4 = reinterpret_cast<u32x4 *>(sm.hist), *s4 = reinterpret_cast<u32x4 *>(sm.seg_cnt);
+  for (int i = threadIdx.x; i < kBins / 4; i += kSelThreads) {
+    h4[i] = u32x4{0u, 0u, 0u, 0u};
+    s4[i] = u32x4{0u, 0u, 0u, 0u};  // second-level histogram
+  }
   if (threadIdx.x == 0) sm.red[76] = 0u;
 }
 
 // Exact threshold for the top `need` of the items (at least `need` valid ones;
-// n = extent of the candidate array), usually in one histogram pass: digits
-// are taken relative to the items' own key range [kmin, kmax] split into at
-// most 2048 bins, so the items spread over the bins.  When the boundary bin
-// holds at most 64 items they are gathered (into seg_cnt) and ranked by one
-// wave; otherwise the items go to LDS and the radix levels run.
-// On entry hist and the gather counter red[76] are zero and a barrier
-// separates the call from earlier reads of red[16..17] and seg_cnt.
+// n = extent of the candidate array), usually in one or two histogram passes:
+// digits are taken relative to the items' own key range [kmin, kmax] split
+// into at most 2048 bins, so the items spread over the bins, and a boundary
+// bin of at most 64 items is split the same way once more (second-level
+// histogram in seg_cnt).  Equal keys left in a boundary bin are ranked by
+// one wave (gathered into seg_off); a larger boundary bin sends the items to
+// LDS for the radix levels.
+// On entry hist, seg_cnt[0 .. 2048) and the gather counter red[76] are zero
+// and a barrier separates the call from earlier reads of red[16..17] and
+// seg_off.
 __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it, int n, uint32_t need,
                                                     uint32_t kmin, uint32_t kmax) {
   const int t = threadIdx.x;
@@ -951,7 +957,7 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
   __syncthreads();
   find_threshold(sm.hist, need, sm.red + 16);
   const uint32_t d = sm.red[16];
-  const uint32_t rem = need - sm.red[17];
+  uint32_t rem = need - sm.red[17];
   const uint32_t in_bin = sm.hist[d];
   Thresh th{0u, 0u, 0, false};
   if (in_bin == rem) {  // the whole boundary bin is taken
@@ -968,11 +974,31 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
     __syncthreads();
     return find_thresh_lds(sm, n, need);
   }
-  // gather the boundary bin (<= 64 items) and rank it in wave 0
-  uint32_t *gk = sm.seg_cnt, *gp = sm.seg_cnt + 64, *gn = sm.red + 76;
+  // second level over the boundary bin's keys [base, base + 2^shift)
+  uint32_t lo_key = kmin + (d << shift);  // the items that remain are in [lo_key, lo_key + 2^sub)
+  int sub = shift;
+  if (shift > 0) {
+    const int shift2 = shift > 11 ? shift - 11 : 0;
+    uint32_t *h2 = sm.seg_cnt;
+#pragma unroll
+    for (int j = 0; j < kSelIPT; ++j)
+      if ((it.k[j] != 0u) & (((it.k[j] - kmin) >> shift) == d)) atomicAdd(&h2[(it.k[j] - lo_key) >> shift2], 1u);
+    __syncthreads();
+    find_threshold(h2, rem, sm.red + 20);
+    const uint32_t d2 = sm.red[20];
+    rem -= sm.red[21];
+    lo_key += d2 << shift2;
+    if (h2[d2] == rem) {  // the whole second-level bin is taken
+      th.kt = lo_key;
+      return th;
+    }
+    sub = shift2;
+  }
+  // gather the remaining bin (<= 64 items) and rank it in wave 0
+  uint32_t *gk = sm.seg_off, *gp = sm.seg_off + 64, *gn = sm.red + 76;
 #pragma unroll
   for (int j = 0; j < kSelIPT; ++j) {
-    if ((it.k[j] != 0u) & (((it.k[j] - kmin) >> shift) == d)) {
+    if ((it.k[j] >= lo_key) & (((it.k[j] - lo_key) >> sub) == 0u)) {
       const uint32_t slot = atomicAdd(gn, 1u);
       gk[slot] = it.k[j];
       gp[slot] = it.p[j];
@@ -1042,25 +1068,16 @@ __device__ __forceinline__ uint32_t compact_items(SelSmem &sm, const Items &it, 
     run += w < wave ? x : 0u;
     written += x;
   }
-  // items in (wave, j, lane) order: stream order
+  // items in (wave, j, lane) order: stream order; the kept items of one
+  // (wave, j) land in consecutive slots, so each store covers one run
 #pragma unroll
   for (int j = 0; j < kSelIPT; ++j) {
     const uint32_t slot = run + (uint32_t)__popcll(bal[j] & below);
-    if (((bal[j] >> lane) & 1u) & (slot < need)) sm.ck[slot] = it.p[j];  // cap: a repeated pool block
+    if (((bal[j] >> lane) & 1u) & (slot < need)) out[slot] = (int32_t)it.p[j];  // cap: a repeated pool block
     run += (uint32_t)__popcll(bal[j]);
   }
   written = written < need ? written : need;
-  __syncthreads();
-  for (int i = 4 * t; i < (int)need; i += 4 * kSelThreads) {
-    if (i + 4 <= (int)need && ((need | (uint32_t)(uintptr_t)out) & 3u) == 0u && ((uintptr_t)out & 15u) == 0u) {
-      u32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = (uint32_t)(i + e) < written ? sm.ck[i + e] : 0xFFFFFFFFu;
-      *reinterpret_cast<u32x4 *>(out + i) = v;
-    } else {
-      for (int e = 0; e < 4 && i + e < (int)need; ++e) out[i + e] = (uint32_t)(i + e) < written ? (int32_t)sm.ck[i + e] : -1;
-    }
-  }
+  for (int i = (int)written + t; i < (int)need; i += kSelThreads) out[i] = -1;
   return written;
 }
 
@@ -1316,18 +1333,15 @@ __device__ __forceinline__ void select_stream(SelSmem &sm, const Stream &st, int
 #pragma unroll
     for (int j = 0; j < kSegPerThread; ++j) {
       const int s = kSegPerThread * t + j;
-      if (s < nseg) {
-        cnt += si[j].count;
-        emax = max(emax, si[j].edge);
-      }
+      if (s < nseg) emax = max(emax, si[j].edge);
     }
 #pragma unroll
     for (int j = 0; j < kSelIPT; ++j) {
       hi = max(hi, it.k[j]);
       lo = min(lo, it.k[j] ? it.k[j] : 0xFFFFFFFFu);
+      cnt += (uint32_t)__popcll(__ballot(it.k[j] != 0u));  // candidates: the slots with a key
     }
     // one exchange for the candidate count, the largest edge and the key range
-    cnt = wave_last(wave_inclusive_sum(cnt));
     emax = wave_inclusive_max(emax);
     hi = wave_inclusive_max(hi);
     lo = ~wave_inclusive_max(~lo);

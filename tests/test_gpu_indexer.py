@@ -56,6 +56,24 @@ def test_topk_exact_on_given_scores_with_ties():
             assert np.sum(idx[b] < 0) == max(0, K - n)
 
 
+def test_topk_narrow_key_range():
+    """Scores within a few thousand ulps of each other: the histogram bins are single keys, so
+    a partly taken bin is a group of equal scores ranked by position."""
+    rng = np.random.default_rng(9)
+    lens = np.array([37, 64, 65, 2, 5000], dtype=np.int32)
+    M = int(lens.max())
+    ulps = rng.integers(0, 40, size=(len(lens), M)).astype(np.int64)
+    sc = (np.float32(1.5).view(np.int32) + ulps).astype(np.int32).view(np.float32)
+    sc[0, :] = np.float32(-3.25)  # one value
+    for K in (1, 7, 33, 2048):
+        idx = csa2.csa2_topk(to_dev(sc), to_dev(lens), K)
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        for b, n in enumerate(lens):
+            ref = oracle.indexer.topk(sc[b, :n].astype(np.float64), K)
+            assert set(idx[b].tolist()) == set(ref.tolist()), (K, b)
+
+
 def test_topk_random_scores_repeatable_workspace():
     rng = np.random.default_rng(8)
     lens = np.array([65536, 30000, 4096], dtype=np.int32)
