@@ -59,7 +59,7 @@ struct AttnArgs {
 template <int MT>
 struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile access is a 128-bit LDS op
   __attribute__((aligned(16))) f16 cq[kT][kQkLd];      // row-major dequantized tile (+ rope)
-  __attribute__((aligned(16))) f16 cv[kLatent][kVLd];  // transposed tile: row r holds channel 2r (r < 256) or 2(r-256)+1
+  __attribute__((aligned(16))) f16 cv[kLatent][kVLd];  // transposed tile: row r holds channel r
   float s[2][16 * MT][kT + 1];   // logits of the tile (two k-halves when 16 heads; padded rows)
   __attribute__((aligned(16))) f16 p_hi[16 * MT][kPLd];
   __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
@@ -220,8 +220,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // 2. transposed copy for PV: thread -> channels 2*tid (row tid) and 2*tid+1
-    // (row 256+tid) over the 32 entries; neighbouring lanes write neighbouring rows
+    // 2. transposed copy for PV: thread -> channels 2*tid and 2*tid+1 (rows
+    // 2*tid and 2*tid+1) over the 32 entries
     {
       const int c = 2 * tid;
       uint32_t colw[kT];
@@ -236,8 +236,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
           lo[j] = (x & 0xFFFFu) | (y << 16);
           hi[j] = (x >> 16) | (y & 0xFFFF0000u);
         }
-        *reinterpret_cast<uint4 *>(&sm.cv[tid][8 * g]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<uint4 *>(&sm.cv[256 + tid][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4 *>(&sm.cv[c][8 * g]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4 *>(&sm.cv[c + 1][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
     }
     // 3. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
@@ -350,40 +350,27 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- write the result (final when unsplit, else a partial for the combine),
-  // 16 heads at a time staged through LDS so every store is a coalesced float4
-  float *stage = reinterpret_cast<float *>(&sm.cq[0][0]);  // 16 x 512 floats fit in cq + cv
-  static_assert(sizeof(sm.cq) + sizeof(sm.cv) >= 16 * kLatent * sizeof(float), "staging area");
+  // ---- write the result straight from the accumulators (PV column = channel):
+  // final rows when unsplit, else a partial for the combine; the 16 lanes of a
+  // row group write 64 contiguous bytes.
   const bool final_out = a.splits == 1;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    __syncthreads();  // the previous round's reads (or the last tile) are done
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int hl = 4 * (lane >> 4) + r;
+      const int hl = 16 * mt + 4 * (lane >> 4) + r;
+      const size_t h = (size_t)b * a.heads + h0 + hl;
       float sc = 1.0f;
+      float *dst = a.part_o + (h * a.splits + split) * kLatent;
       if (final_out) {
-        const float l = sm.l_run[16 * mt + hl];
+        const float l = sm.l_run[hl];
         sc = l > 0.f ? 1.0f / l : 0.f;
+        dst = a.out + h * kLatent;
       }
+      dst += 128 * wave + (lane & 15);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int row = 128 * wave + 16 * nt + (lane & 15);  // PV column = transposed-tile row
-        const int ch = row < 256 ? 2 * row : 2 * (row - 256) + 1;
-        stage[hl * kLatent + ch] = acc[mt][nt][r] * sc;
-      }
+      for (int nt = 0; nt < 8; ++nt) dst[16 * nt] = acc[mt][nt][r] * sc;
     }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16 * kLatent / 4 / 256; ++k) {
-      const int f = 256 * k + tid;           // float4 index within the 16 x 512 block
-      const int hl = f / (kLatent / 4), c4 = f % (kLatent / 4);
-      const float4 v = reinterpret_cast<const float4 *>(stage)[f];
-      const size_t h = (size_t)b * a.heads + h0 + 16 * mt + hl;
-      float *dst = final_out ? a.out + h * kLatent : a.part_o + (h * a.splits + split) * kLatent;
-      reinterpret_cast<float4 *>(dst)[c4] = v;
-    }
-  }
   if (final_out) {
     if (a.lse != nullptr && tid < HG) {
       const float l = sm.l_run[tid];
