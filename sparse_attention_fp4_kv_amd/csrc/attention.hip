@@ -16,8 +16,10 @@
 //   * Entries are processed in tiles of 32.  A tile's FP4 codes are gathered
 //     straight into registers (8 lanes per 256-byte row), dequantized with the
 //     hardware E2M1 -> fp16 convert plus one packed multiply by the E4M3 scale
-//     (exact), and written to LDS twice: row-major (QK^T operand, channels
-//     contiguous) and transposed (PV operand, entries contiguous).
+//     (exact), and written once to LDS, row-major.  QK^T reads its operand
+//     (channels contiguous) with 16-byte loads; PV reads its operand (entries
+//     contiguous) with gfx950's transposing LDS loads, so no transposed copy
+//     of the tile is made.
 //   * Online softmax in fp32 (exp2 domain).  P enters the PV contraction as
 //     fp16 hi + lo parts (two MFMAs), which keeps the output within ~1e-5
 //     relative of an fp32 P; a single fp16 P is not accurate enough for
@@ -33,7 +35,6 @@ namespace {
 
 constexpr int kT = 32;                 // entries per tile
 constexpr int kQkLd = kLatent + 64 + 8;  // row-major tile row (f16): 512 latent + 64 rope + pad
-constexpr int kVLd = kT + 8;           // transposed tile row (f16): 32 entries + pad
 constexpr int kPLd = kT + 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 32;         // split-K workgroups per (sequence, head group)
@@ -59,7 +60,6 @@ struct AttnArgs {
 template <int MT>
 struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile access is a 128-bit LDS op
   __attribute__((aligned(16))) f16 cq[kT][kQkLd];      // row-major dequantized tile (+ rope)
-  __attribute__((aligned(16))) f16 cv[kLatent][kVLd];  // transposed tile: row r holds channel r
   float s[2][16 * MT][kT + 1];   // logits of the tile (two k-halves when 16 heads; padded rows)
   __attribute__((aligned(16))) f16 p_hi[16 * MT][kPLd];
   __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
@@ -68,6 +68,24 @@ struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile 
 };
 
 __device__ __forceinline__ f16x8 lds_f16x8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// PV operand (B of v_mfma_f32_16x16x32_f16, k = entries, n = channels) read
+// straight from the row-major tile with two transposing LDS loads.  Within a
+// group of 16 lanes, ds_read_b64_tr_b16 hands lane i element i % 4 of the
+// 8-byte chunks read by lanes 4 e + i / 4 (e = 0..3).  Lane L of k-group
+// g = L / 16 therefore points at row 8 g + (L / 4) % 4 (+ 4 for the second
+// load), channels n0 + 4 (L % 4) .. + 3, and receives rows 8 g .. 8 g + 7 of
+// channel n0 + L % 16.  p: that lane's first-load address.
+__device__ __forceinline__ f16x8 pv_operand(const f16 *p) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * kQkLd));
+  const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(f16x8, ab);
+}
 
 __device__ __forceinline__ f16x8 bf16x8_to_f16x8(uint4 v) {
   f16x8 r;
@@ -220,27 +238,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // 2. transposed copy for PV: thread -> channels 2*tid and 2*tid+1 (rows
-    // 2*tid and 2*tid+1) over the 32 entries
-    {
-      const int c = 2 * tid;
-      uint32_t colw[kT];
-#pragma unroll
-      for (int e = 0; e < kT; ++e) colw[e] = *reinterpret_cast<const uint32_t *>(&sm.cq[e][c]);
-#pragma unroll
-      for (int g = 0; g < kT / 8; ++g) {
-        uint32_t lo[4], hi[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t x = colw[8 * g + 2 * j], y = colw[8 * g + 2 * j + 1];
-          lo[j] = (x & 0xFFFFu) | (y << 16);
-          hi[j] = (x >> 16) | (y & 0xFFFF0000u);
-        }
-        *reinterpret_cast<uint4 *>(&sm.cv[c][8 * g]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<uint4 *>(&sm.cv[c + 1][8 * g]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      }
-    }
-    // 3. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
+    // 2. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
     for (int j = 0; j < qk_ntn; ++j) {
       const int nt = qk_nt0 + j;
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
@@ -262,7 +260,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         sm.s[qk_half][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
-    // 4. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
+    // 3. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
     {
       constexpr int TPH = 256 / HG;   // threads per head (4, 8 or 16)
       constexpr int EPT = kT / TPH;   // entries per thread (8, 4 or 2)
@@ -298,7 +296,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
     __syncthreads();
-    // 5. O = alpha * O + P V  (wave: transposed-tile rows 128*wave .. +127, all heads)
+    // 4. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
     {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -317,7 +315,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const f16x8 bv = lds_f16x8(&sm.cv[128 * wave + 16 * nt + (lane & 15)][8 * (lane >> 4)]);
+        const f16x8 bv = pv_operand(&sm.cq[8 * (lane >> 4) + ((lane >> 2) & 3)][128 * wave + 16 * nt + 4 * (lane & 3)]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv, acc[mt][nt], 0, 0, 0);
