@@ -59,7 +59,7 @@ struct AttnArgs {
 
 template <int MT>
 struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile access is a 128-bit LDS op
-  __attribute__((aligned(16))) f16 cq[kT][kQkLd];      // row-major dequantized tile (+ rope)
+  __attribute__((aligned(16))) f16 cq[3][kT][kQkLd];   // row-major dequantized tiles (+ rope), used in turn
   float s[2][16 * MT][kT + 1];   // logits of the tile (two k-halves when 16 heads; padded rows)
   __attribute__((aligned(16))) f16 p_hi[16 * MT][kPLd];
   __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
@@ -199,11 +199,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (tid < HG) {
-    sm.m_run[tid] = -INFINITY;
-    sm.l_run[tid] = 0.0f;
-  }
-  __syncthreads();
+  __syncthreads();  // slot[] is complete
 
   // gather of one tile: thread -> entry tid/8, channels 64*(tid%8) .. +63.
   // Every load is issued unconditionally (a skipped entry reads row 0 and is
@@ -221,28 +217,39 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     r.valid = slot != kNoSlot;
   };
 
-  auto process = [&](const Raw &r, int tile) {
-    // 1. dequantize into the row-major tile
-    {
-      const int e = tid >> 3, cb = tid & 7;
-      const uint32_t words[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-      const uint32_t sc4 = r.valid ? r.sc4 : 0u;  // scale 0: the entry's channels are all zero
+  // dequantize one tile's row fragments into a row-major tile buffer
+  auto dequant = [&](const Raw &r, f16 (*cq)[kQkLd]) {
+    const int e = tid >> 3, cb = tid & 7;
+    const uint32_t words[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    const uint32_t sc4 = r.valid ? r.sc4 : 0u;  // scale 0: the entry's channels are all zero
 #pragma unroll
-      for (int wi = 0; wi < 8; ++wi) {
-        const f16 sc = (f16)e4m3_decode((sc4 >> (8 * (wi >> 1))) & 0xFFu);
-        *reinterpret_cast<f16x8 *>(&sm.cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc);
-      }
-      if constexpr (ROPE) {
-        const uint4 rp = r.valid ? r.rp : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<f16x8 *>(&sm.cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
-      }
+    for (int wi = 0; wi < 8; ++wi) {
+      const f16 sc = (f16)e4m3_decode((sc4 >> (8 * (wi >> 1))) & 0xFFu);
+      *reinterpret_cast<f16x8 *>(&cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc);
     }
-    __syncthreads();
-    // 2. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
+    if constexpr (ROPE) {
+      const uint4 rp = r.valid ? r.rp : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<f16x8 *>(&cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
+    }
+  };
+
+  // online-softmax state: thread -> head tid / TPH, entries (tid % TPH) * EPT ..
+  // + EPT - 1 of a tile; the TPH threads of a head keep the same running max
+  // and sum in registers
+  constexpr int TPH = 256 / HG;   // threads per head (4, 8 or 16)
+  constexpr int EPT = kT / TPH;   // entries per thread (8, 4 or 2)
+  const int sm_h = tid / TPH, sm_part = tid % TPH;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // One tile from buffer cq, with the next tile's dequantization into cq_next
+  // (three buffers in turn) in the same phase.  Two barriers per tile: the
+  // buffer a phase writes was last read two barriers earlier.
+  auto step = [&](int tile, f16 (*cq)[kQkLd], const Raw *next, f16 (*cq_next)[kQkLd]) {
+    // 1. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
     for (int j = 0; j < qk_ntn; ++j) {
       const int nt = qk_nt0 + j;
       f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const f16 *brow = &sm.cq[16 * nt + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
+      const f16 *brow = &cq[16 * nt + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
       f16x8 bq[QKS];  // B fragments read 4 k-steps ahead of the MFMA that consumes them
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) bq[ks] = lds_f16x8(brow + 32 * ks);
@@ -259,44 +266,38 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       for (int rr = 0; rr < 4; ++rr)
         sm.s[qk_half][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * a.scale_log2 : -INFINITY;
     }
+    if (next != nullptr) dequant(*next, cq_next);
     __syncthreads();
-    // 3. online softmax: thread -> head tid / TPH, entries (tid % TPH) * EPT .. +EPT-1
+    // 2. online softmax
     {
-      constexpr int TPH = 256 / HG;   // threads per head (4, 8 or 16)
-      constexpr int EPT = kT / TPH;   // entries per thread (8, 4 or 2)
-      const int h = tid / TPH, part = tid % TPH;
       float v[EPT];
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        v[i] = sm.s[0][h][part * EPT + i];
-        if constexpr (MT == 1) v[i] += sm.s[1][h][part * EPT + i];
+        v[i] = sm.s[0][sm_h][sm_part * EPT + i];
+        if constexpr (MT == 1) v[i] += sm.s[1][sm_h][sm_part * EPT + i];
         mx = fmaxf(mx, v[i]);
       }
       mx = group_max<TPH>(mx);
-      const float m_old = sm.m_run[h];
-      const float m_new = fmaxf(m_old, mx);
+      const float m_new = fmaxf(m_run, mx);
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(v[i] - m_new);
-        sum += p;
-        const f16 ph = (f16)p;
-        const f16 pl = (f16)(p - (float)ph);
-        sm.p_hi[h][part * EPT + i] = ph;
-        sm.p_lo[h][part * EPT + i] = pl;
+        const float pv = (m_new == -INFINITY) ? 0.f : exp2f(v[i] - m_new);
+        sum += pv;
+        const f16 ph = (f16)pv;
+        const f16 pl = (f16)(pv - (float)ph);
+        sm.p_hi[sm_h][sm_part * EPT + i] = ph;
+        sm.p_lo[sm_h][sm_part * EPT + i] = pl;
       }
       sum = group_sum<TPH>(sum);
-      __syncthreads();  // every thread has read m_run before it changes
-      if (part == 0) {
-        const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_old - m_new);
-        sm.alpha[h] = al;
-        sm.m_run[h] = m_new;
-        sm.l_run[h] = sm.l_run[h] * al + sum;
-      }
+      const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      l_run = l_run * al + sum;
+      m_run = m_new;
+      if (sm_part == 0) sm.alpha[sm_h] = al;
     }
     __syncthreads();
-    // 4. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
+    // 3. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
     {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -315,7 +316,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const f16x8 bv = pv_operand(&sm.cq[8 * (lane >> 4) + ((lane >> 2) & 3)][128 * wave + 16 * nt + 4 * (lane & 3)]);
+        const f16x8 bv = pv_operand(&cq[8 * (lane >> 4) + ((lane >> 2) & 3)][128 * wave + 16 * nt + 4 * (lane & 3)]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv, acc[mt][nt], 0, 0, 0);
@@ -323,30 +324,38 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         }
       }
     }
-    __syncthreads();
   };
 
-  // ---- tiles, each with the next two tiles' rows already in flight (three
-  // register sets; loads past the last tile re-read the last tile)
+  // ---- tiles: three register sets of raw rows (each tile's loads are issued
+  // three tiles ahead; loads past the last tile re-read the last tile) and
+  // three tile buffers, so the unrolled loop keeps both in step
   if (tile_begin < tile_end && a.L.num_blocks > 0) {
     const int last = tile_end - 1;
     Raw ra, rb, rc;
     load_raw(tile_begin, ra);
     load_raw(min(tile_begin + 1, last), rb);
     load_raw(min(tile_begin + 2, last), rc);
+    dequant(ra, sm.cq[0]);
+    load_raw(min(tile_begin + 3, last), ra);
+    __syncthreads();
     for (int tile = tile_begin; tile < tile_end; tile += 3) {
-      process(ra, tile);
-      load_raw(min(tile + 3, last), ra);
+      step(tile, sm.cq[0], tile + 1 < tile_end ? &rb : nullptr, sm.cq[1]);
+      load_raw(min(tile + 4, last), rb);
       if (tile + 1 < tile_end) {
-        process(rb, tile + 1);
-        load_raw(min(tile + 4, last), rb);
+        step(tile + 1, sm.cq[1], tile + 2 < tile_end ? &rc : nullptr, sm.cq[2]);
+        load_raw(min(tile + 5, last), rc);
       }
       if (tile + 2 < tile_end) {
-        process(rc, tile + 2);
-        load_raw(min(tile + 5, last), rc);
+        step(tile + 2, sm.cq[2], tile + 3 < tile_end ? &ra : nullptr, sm.cq[0]);
+        load_raw(min(tile + 6, last), ra);
       }
     }
   }
+  if (sm_part == 0) {
+    sm.m_run[sm_h] = m_run;
+    sm.l_run[sm_h] = l_run;
+  }
+  __syncthreads();
 
   // ---- write the result straight from the accumulators (PV column = channel):
   // final rows when unsplit, else a partial for the combine; the 16 lanes of a
