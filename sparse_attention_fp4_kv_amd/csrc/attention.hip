@@ -201,11 +201,16 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 
   __syncthreads();  // slot[] is complete
 
-  // gather of one tile: thread -> entry tid/8, channels 64*(tid%8) .. +63.
-  // Every load is issued unconditionally (a skipped entry reads row 0 and is
-  // zeroed when dequantized; an empty pool never launches a tile).
+  // gather of one tile: thread -> entry tile_entry, channel block tile_block
+  // (channels 64 tile_block .. + 63).  A wave covers 8 entries; its
+  // lanes 16 i .. 16 i + 15 take the 8 entries at blocks 2 i and 2 i + 1, so
+  // each 16-byte LDS store of the dequantized tile (row stride 73 x 16 bytes)
+  // lands the 16 lanes on 16 different bank groups.  Every load is issued
+  // unconditionally (a skipped entry reads row 0 and is zeroed when
+  // dequantized; an empty pool never launches a tile).
+  const int tile_entry = (tid & 7) + 8 * wave, tile_block = (lane >> 3) & 7;
   auto load_raw = [&](int tile, Raw &r) {
-    const int e = tid >> 3, cb = tid & 7;
+    const int e = tile_entry, cb = tile_block;
     const int li = tile * kT + e - e_begin;
     const uint32_t slot = li < e_count ? sm.slot[li] : kNoSlot;
     const size_t rs = slot == kNoSlot ? 0 : slot;
@@ -218,17 +223,22 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   };
 
   // dequantize one tile's row fragments into a row-major tile buffer
+  // (branch-free: a skipped entry is masked to scale 0 and rope 0, so its
+  // channels are all zero; the four E4M3 scales go through the hardware fp8
+  // convert, exact in fp16)
   auto dequant = [&](const Raw &r, f16 (*cq)[kQkLd]) {
-    const int e = tid >> 3, cb = tid & 7;
+    const int e = tile_entry, cb = tile_block;
+    const uint32_t vmask = 0u - (uint32_t)r.valid;
     const uint32_t words[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-    const uint32_t sc4 = r.valid ? r.sc4 : 0u;  // scale 0: the entry's channels are all zero
+    const uint32_t sc4 = r.sc4 & vmask;
+    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, false);  // scale bytes 0, 1
+    const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, true);   // scale bytes 2, 3
+    const f16 sc[4] = {s01[0], s01[1], s23[0], s23[1]};
 #pragma unroll
-    for (int wi = 0; wi < 8; ++wi) {
-      const f16 sc = (f16)e4m3_decode((sc4 >> (8 * (wi >> 1))) & 0xFFu);
-      *reinterpret_cast<f16x8 *>(&cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc);
-    }
+    for (int wi = 0; wi < 8; ++wi)
+      *reinterpret_cast<f16x8 *>(&cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc[wi >> 1]);
     if constexpr (ROPE) {
-      const uint4 rp = r.valid ? r.rp : make_uint4(0, 0, 0, 0);
+      const uint4 rp = make_uint4(r.rp.x & vmask, r.rp.y & vmask, r.rp.z & vmask, r.rp.w & vmask);
       *reinterpret_cast<f16x8 *>(&cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
     }
   };
