@@ -938,11 +938,10 @@ __device__ __forceinline__ void clear_for_search(SelSmem &sm) {
 // Exact threshold for the top `need` of the items (at least `need` valid ones;
 // n = extent of the candidate array), usually in one or two histogram passes:
 // digits are taken relative to the items' own key range [kmin, kmax] split
-// into at most 2048 bins, so the items spread over the bins, and a boundary
-// bin of at most 64 items is split the same way once more (second-level
-// histogram in seg_cnt).  Equal keys left in a boundary bin are ranked by
-// one wave (gathered into seg_off); a larger boundary bin sends the items to
-// LDS for the radix levels.
+// into at most 2048 bins, so the items spread over the bins, and the
+// boundary bin is split the same way once more (second-level histogram in
+// seg_cnt).  At most 64 items left in the final bin are ranked by one wave
+// (gathered into seg_off); more send the items to LDS for the radix levels.
 // On entry hist, seg_cnt[0 .. 2048) and the gather counter red[76] are zero
 // and a barrier separates the call from earlier reads of red[16..17] and
 // seg_off.
@@ -964,19 +963,10 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
     th.kt = kmin + (d << shift);
     return th;
   }
-  if (in_bin > 64u) {  // heavy ties or clustering: radix levels over the items in LDS
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kSelIPT; ++j) {
-      sm.ck[item_index(j)] = it.k[j];
-      sm.cp[item_index(j)] = it.p[j];
-    }
-    __syncthreads();
-    return find_thresh_lds(sm, n, need);
-  }
   // second level over the boundary bin's keys [base, base + 2^shift)
   uint32_t lo_key = kmin + (d << shift);  // the items that remain are in [lo_key, lo_key + 2^sub)
   int sub = shift;
+  uint32_t remaining = in_bin;
   if (shift > 0) {
     const int shift2 = shift > 11 ? shift - 11 : 0;
     uint32_t *h2 = sm.seg_cnt;
@@ -988,11 +978,22 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
     const uint32_t d2 = sm.red[20];
     rem -= sm.red[21];
     lo_key += d2 << shift2;
-    if (h2[d2] == rem) {  // the whole second-level bin is taken
+    remaining = h2[d2];
+    if (remaining == rem) {  // the whole second-level bin is taken
       th.kt = lo_key;
       return th;
     }
     sub = shift2;
+  }
+  if (remaining > 64u) {  // heavy ties or clustering: radix levels over the items in LDS
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSelIPT; ++j) {
+      sm.ck[item_index(j)] = it.k[j];
+      sm.cp[item_index(j)] = it.p[j];
+    }
+    __syncthreads();
+    return find_thresh_lds(sm, n, need);
   }
   // gather the remaining bin (<= 64 items) and rank it in wave 0
   uint32_t *gk = sm.seg_off, *gp = sm.seg_off + 64, *gn = sm.red + 76;
