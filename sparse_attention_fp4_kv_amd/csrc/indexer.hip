@@ -374,23 +374,21 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
 // keys, 8 per thread; blocks: 256 keys, 1 per thread), with the same cut rule
 // as emit_segment: the two histograms share each barrier and their threshold
 // searches run side by side in waves 0 and 1.
+// hist[0..3]: level-1 and level-2 histograms of positions and blocks, zeroed
+// by the caller before a barrier that precedes the call.
 template <class PosP, class PosB>
 __device__ __forceinline__ void emit_segment_pair(const uint32_t *pkeys, int cap_p, uint2 *cand_p, SegInfo *info_p,
                                                   PosP pos_p, const uint32_t *bkeys, int cap_b, uint2 *cand_b,
-                                                  SegInfo *info_b, PosB pos_b, uint32_t *hist_p, uint32_t *hist_b,
+                                                  SegInfo *info_b, PosB pos_b, uint32_t (*hist)[kBins],
                                                   uint32_t *red) {
   constexpr int NT = 256;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ip0 = 64 * 8 * wave + lane, ib = 64 * wave + lane;
+  uint32_t *hist_p = hist[0], *hist_b = hist[1];
   uint32_t kp[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) kp[j] = pkeys[ip0 + 64 * j];
   const uint32_t kb = bkeys[ib];
-  for (int i = t; i < kBins; i += NT) {
-    hist_p[i] = 0u;
-    hist_b[i] = 0u;
-  }
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < 8; ++j)
     if (kp[j]) atomicAdd(&hist_p[kp[j] >> 21], 1u);
@@ -404,12 +402,8 @@ __device__ __forceinline__ void emit_segment_pair(const uint32_t *pkeys, int cap
   uint32_t d2p = 0, d2b = 0, edge_p = 0, edge_b = 0;
   if (cut_p || cut_b) {
     // level 2 inside each boundary bin d1: room for cap - above of its items
-    // (every read of the histograms ended at the barrier above)
-    for (int i = t; i < kBins; i += NT) {
-      hist_p[i] = 0u;
-      hist_b[i] = 0u;
-    }
-    __syncthreads();
+    hist_p = hist[2];
+    hist_b = hist[3];
     if (cut_p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
@@ -487,14 +481,20 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   __shared__ int32_t pg[kScanPages];
   __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
   __shared__ __attribute__((aligned(16))) uint32_t bkey[kScanBlocks];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
-  __shared__ __attribute__((aligned(16))) uint32_t hist2[HIER ? kBins : 4];  // block-key histogram
+  // histograms of the emission: positions (level 1, 2) and, hierarchical,
+  // blocks (level 1, 2); zeroed while the first loads are in flight
+  __shared__ __attribute__((aligned(16))) uint32_t hist[HIER ? 4 : 1][kBins];
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = row_len(a.S, b);
   const int64_t base = (int64_t)wg * kScanPos;
   if (base >= n) return;  // segments past the row are never read
+  if constexpr (HIER) {
+    u32x4 *h4 = reinterpret_cast<u32x4 *>(&hist[0][0]);
+#pragma unroll
+    for (int i = 0; i < 4 * kBins / 4 / 256; ++i) h4[256 * i + tid] = u32x4{0u, 0u, 0u, 0u};
+  }
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
   if (tid < kScanPages) pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
   float q[8];
@@ -558,10 +558,10 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
                       bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
                       a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
-                      hist, hist2, red);
+                      hist, red);
   } else {
     emit_segment<256, 8>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
-                         a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
+                         a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist[0], red,
                          [&](int i) { return (uint32_t)(base + i); });
   }
 }
