@@ -322,35 +322,40 @@ __device__ __forceinline__ uint32_t ordered_emit(uint32_t flags, uint32_t *red, 
 // bins from the top, then the best 11-bit sub-bins of the boundary bin.
 // Lane l of wave w owns items 64 IPT w + 64 j + l; pos_of(i) is item i's
 // position.
+// Zeroes NH histograms of kBins words with a 256-thread workgroup.
+template <int NH>
+__device__ __forceinline__ void zero_hists(uint32_t (*hist)[kBins]) {
+  u32x4 *h4 = reinterpret_cast<u32x4 *>(&hist[0][0]);
+#pragma unroll
+  for (int i = 0; i < NH * kBins / 4 / 256; ++i) h4[256 * i + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// hist[0], hist[1]: level-1 and level-2 histograms, zeroed by the caller
+// before a barrier that precedes the call (zero_hists).
 template <int NT, int IPT, class PosOf>
 __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
-                                             uint32_t *hist, uint32_t *red, PosOf pos_of) {
+                                             uint32_t (*hist)[kBins], uint32_t *red, PosOf pos_of) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i0 = 64 * IPT * wave + lane;  // this lane's items: i0 + 64 j
   uint32_t k[IPT];
 #pragma unroll
   for (int j = 0; j < IPT; ++j) k[j] = keys_l[i0 + 64 * j];
-  for (int i = t; i < kBins; i += NT) hist[i] = 0u;
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < IPT; ++j)
-    if (k[j]) atomicAdd(&hist[k[j] >> 21], 1u);
+    if (k[j]) atomicAdd(&hist[0][k[j] >> 21], 1u);
   __syncthreads();
-  find_threshold(hist, (uint32_t)cap + 1u, red + 16);
+  find_threshold(hist[0], (uint32_t)cap + 1u, red + 16);
   const uint32_t d1 = red[16], above = red[17];
   const bool cut = red[18] != 0u;
   uint32_t d2 = 0, edge = 0;
   if (cut) {
     // level 2 inside the boundary bin d1: room for cap - above of its items
     const uint32_t room = (uint32_t)cap - above;
-    __syncthreads();
-    for (int i = t; i < kBins; i += NT) hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int j = 0; j < IPT; ++j)
-      if (k[j] && (k[j] >> 21) == d1) atomicAdd(&hist[(k[j] >> 10) & 0x7FFu], 1u);
+      if (k[j] && (k[j] >> 21) == d1) atomicAdd(&hist[1][(k[j] >> 10) & 0x7FFu], 1u);
     __syncthreads();
-    find_threshold(hist, room + 1u, red + 16);
+    find_threshold(hist[1], room + 1u, red + 16);
     d2 = red[16];  // found: bin d1 holds more than `room` items
     const uint64_t e = ((uint64_t)d1 << 21) + ((uint64_t)(d2 + 1u) << 10);
     edge = e > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)e;
@@ -483,18 +488,14 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t bkey[kScanBlocks];
   // histograms of the emission: positions (level 1, 2) and, hierarchical,
   // blocks (level 1, 2); zeroed while the first loads are in flight
-  __shared__ __attribute__((aligned(16))) uint32_t hist[HIER ? 4 : 1][kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[HIER ? 4 : 2][kBins];
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = row_len(a.S, b);
   const int64_t base = (int64_t)wg * kScanPos;
   if (base >= n) return;  // segments past the row are never read
-  if constexpr (HIER) {
-    u32x4 *h4 = reinterpret_cast<u32x4 *>(&hist[0][0]);
-#pragma unroll
-    for (int i = 0; i < 4 * kBins / 4 / 256; ++i) h4[256 * i + tid] = u32x4{0u, 0u, 0u, 0u};
-  }
+  zero_hists<HIER ? 4 : 2>(hist);
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
   if (tid < kScanPages) pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
   float q[8];
@@ -561,7 +562,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
                       hist, red);
   } else {
     emit_segment<256, 8>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
-                         a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist[0], red,
+                         a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
                          [&](int i) { return (uint32_t)(base + i); });
   }
 }
@@ -578,12 +579,13 @@ struct GivenArgs {
 
 __global__ void __launch_bounds__(256) given_kernel(GivenArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins];
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x, tid = threadIdx.x;
   const int n = min(max(a.lens[b], 0), a.max_len);
   const int64_t base = (int64_t)wg * kScanPos;
   if (base >= n) return;
+  zero_hists<2>(hist);
   float v[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {  // loads first, clamped inside the row
@@ -621,7 +623,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   __shared__ int64_t slot0[kPoolBlocksPerWg];
   __shared__ int32_t tok0[kPoolBlocksPerWg];
   __shared__ uint32_t key_l[256];
-  __shared__ __attribute__((aligned(16))) uint32_t hist[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins];
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -644,6 +646,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
     tok0[tid] = t0;
   }
   key_l[tid] = 0u;  // items 128..255 stay empty
+  zero_hists<2>(hist);
   float q[8];
   {
     const float *qp = a.q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
