@@ -20,7 +20,9 @@
 //     (channels contiguous) with 16-byte loads; PV reads its operand (entries
 //     contiguous) with gfx950's transposing LDS loads, so no transposed copy
 //     of the tile is made.
-//   * Online softmax in fp32 (exp2 domain).  P enters the PV contraction as
+//   * Online softmax in fp32 (exp2 domain) against a reference max that
+//     moves only when a logit exceeds it by more than 8 (so most tiles skip
+//     rescaling the accumulators).  P enters the PV contraction as
 //     fp16 hi + lo parts (two MFMAs), which keeps the output within ~1e-5
 //     relative of an fp32 P; a single fp16 P is not accurate enough for
 //     latents with x20 outlier channels.
@@ -289,7 +291,10 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         mx = fmaxf(mx, v[i]);
       }
       mx = group_max<TPH>(mx);
-      const float m_new = fmaxf(m_run, mx);
+      // The reference m_run moves only when a logit exceeds it by more than
+      // 2^8 (in the exp2 domain): weights stay below 2^8, O and l are left
+      // unscaled on most tiles, and O / l is the same ratio.
+      const float m_new = mx > m_run + 8.f ? mx : m_run;
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
@@ -301,7 +306,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         sm.p_lo[sm_h][sm_part * EPT + i] = pl;
       }
       sum = group_sum<TPH>(sum);
-      const float al = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      // (from an empty state O and l are zero: no rescaling either)
+      const float al = (m_new == m_run || m_run == -INFINITY) ? 1.f : exp2f(m_run - m_new);
       l_run = l_run * al + sum;
       m_run = m_new;
       if (sm_part == 0) sm.alpha[sm_h] = al;
@@ -309,14 +315,22 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     __syncthreads();
     // 3. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
     {
+      float al[MT][4];
+      bool rescale = false;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float al = sm.alpha[16 * mt + 4 * (lane >> 4) + rr];
-#pragma unroll
-          for (int nt = 0; nt < 8; ++nt) acc[mt][nt][rr] *= al;
+          al[mt][rr] = sm.alpha[16 * mt + 4 * (lane >> 4) + rr];
+          rescale |= al[mt][rr] != 1.f;
         }
+      if (__ballot(rescale)) {  // the accumulators live in AGPRs: scale only when a reference moved
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) acc[mt][nt][rr] *= al[mt][rr];
       }
       f16x8 ph[MT], pl[MT];
 #pragma unroll
