@@ -414,16 +414,17 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   }
 }
 
-// Merges the splits' partials: workgroup (b*H + h, quarter) of 32 threads
-// covers 128 channels of one head, one float4 per thread.  Splits are read 32
+// Merges the splits' partials: workgroup (b*H + h, half) of one full wave
+// covers 256 channels of one head, one float4 per thread.  Splits are read 32
 // at a time (all loads of a chunk issued together) and merged online.
-__global__ void __launch_bounds__(32) attn_combine_kernel(const float *__restrict__ part_o,
+constexpr int kCombineThreads = 64;
+__global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
                                                           float *__restrict__ out, float *__restrict__ lse) {
   constexpr int kChunk = 32;
-  const int bh = blockIdx.x, quarter = blockIdx.y;
+  const int bh = blockIdx.x, quarter = blockIdx.y;  // quarter: which kCombineThreads float4s
   const int tid = threadIdx.x;
-  const int c4 = 32 * quarter + tid;  // float4 index within the 512 channels
+  const int c4 = kCombineThreads * quarter + tid;  // float4 index within the 512 channels
   const float2 *ml = reinterpret_cast<const float2 *>(part_ml + (size_t)bh * splits * 2);
   float m = -INFINITY, l = 0.f;
   float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -531,7 +532,8 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   timer_before(kKernAttnCombine, st);
-  attn_combine_kernel<<<dim3(S.batch * heads, 4), dim3(32), 0, st>>>(a.part_o, a.part_ml, splits, out, lse);
+  attn_combine_kernel<<<dim3(S.batch * heads, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
+      a.part_o, a.part_ml, splits, out, lse);
   timer_after(kKernAttnCombine, st);
   return hipGetLastError();
 }
