@@ -14,10 +14,18 @@ Sources:
        layers score and select only inside that pool.
 
 Readings taken where the pages are silent (listed in the design notes):
-  * Score: a single-query dot product score[t] = q_idx . k_idx[t] (64 dims),
-    evaluated in float64 from the stored key values (fp32 or bf16) and an fp32
-    query.  The pages give head counts for the real indexer (32 query heads,
-    dim 128) but no combining rule.
+  * Score (64-dim fp32 / bf16 keys): a single-query dot product
+    score[t] = q_idx . k_idx[t], evaluated in float64 from the stored key
+    values and an fp32 query.
+  * Score at the pages' indexer shape ([P1] section "CSA2": 32 indexer query
+    heads of dimension 128; FP4 storage as in section "FP4 KV cache"): keys
+    stored in the same FP4 format as the latent (E2M1 + one E4M3 scale per 16
+    dims, 72 B per 128-dim key), queries given per head in fp16 with one fp32
+    weight per head, and heads combined as
+        score[t] = sum_h w[h] * max(0, q[h] . k[t]),
+    the weighted-ReLU rule of DeepSeek's earlier lightning indexer; the pages
+    give the head count and dimension but no combining rule.  Evaluated in
+    float64 from the exact dequantized keys and the fp16 query values.
   * Top-K: the K largest scores; equal scores go to the lower position; when
     fewer than K positions are visible the result is padded with -1.  The
     selection is a set (order is not part of the result).
@@ -41,10 +49,26 @@ def keys_to_f64(keys, dtype):
     raise ValueError(dtype)
 
 
-def index_scores(q_idx, keys_f64):
-    """score[t] = sum_d q_idx[d] * k[t, d] in float64.  q_idx: fp32 [D]; keys: [n][D]."""
-    q = np.asarray(q_idx, dtype=np.float32).astype(np.float64)
-    return keys_f64 @ q
+def fp4_keys_to_f64(codes, scales):
+    """FP4 indexer keys (codes [n][D/2], scales [n][D/16], the latent's format) -> float64 [n][D]."""
+    from .fp4 import fp4_unpack
+
+    return fp4_unpack(codes, scales)
+
+
+def index_scores(q_idx, keys_f64, w=None):
+    """Index scores in float64; keys: [n][D].
+
+    w is None: score[t] = sum_d q_idx[d] * k[t, d], q_idx fp32 [D].
+    w given:   score[t] = sum_h w[h] * max(0, sum_d q_idx[h, d] * k[t, d]),
+               q_idx fp16 [H][D] (the query heads), w fp32 [H].
+    """
+    if w is None:
+        q = np.asarray(q_idx, dtype=np.float32).astype(np.float64)
+        return keys_f64 @ q
+    q = np.asarray(q_idx, dtype=np.float16).astype(np.float64)
+    ww = np.asarray(w, dtype=np.float32).astype(np.float64)
+    return np.maximum(keys_f64 @ q.T, 0.0) @ ww
 
 
 def topk(scores, k, positions=None):
@@ -101,19 +125,19 @@ def pool_positions(block_ids, n, block_tokens=8):
     return np.sort(pos[pos < n])
 
 
-def full_select(q_idx, keys_f64, k, pool_blocks_max=None, block_tokens=8):
+def full_select(q_idx, keys_f64, k, pool_blocks_max=None, block_tokens=8, w=None):
     """Full mode: scores over all visible positions -> (indices, pool block ids or None)."""
-    s = index_scores(q_idx, keys_f64)
+    s = index_scores(q_idx, keys_f64, w)
     idx = topk(s, k)
     pool = pool_blocks(s, pool_blocks_max, block_tokens) if pool_blocks_max else None
     return idx, pool
 
 
-def reindex_select(q_idx, keys_f64, k, pool_block_ids, block_tokens=8):
+def reindex_select(q_idx, keys_f64, k, pool_block_ids, block_tokens=8, w=None):
     """Reindex mode: this layer's own query scores only the pool positions."""
     n = keys_f64.shape[0]
     pos = pool_positions(pool_block_ids, n, block_tokens)
-    s = index_scores(q_idx, keys_f64[pos])
+    s = index_scores(q_idx, keys_f64[pos], w)
     return topk(s, k, positions=pos)
 
 

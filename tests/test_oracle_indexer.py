@@ -10,7 +10,13 @@
   position and Reindex is plain top-K; with P >= K the Full layer's top-K lies
   in the pool except at exact ties of the K-th score;
 - the scores against an fp32-exact case (small integers) and a direct sum;
-- the page fact 2048 blocks x 8 positions = 16,384 candidates.
+- the page fact 2048 blocks x 8 positions = 16,384 candidates;
+- the multi-head FP4 indexer score (32 heads x 128 dims at the pages' shape):
+  exact rational brute force on small integer heads, FP4 keys and dyadic
+  weights; per-head ReLU clipping on a hand-computed case; one non-negative
+  head reduces to the dot product; invariance under head permutation and
+  linearity in the weights; the 72-byte key; Full selection and pool with it
+  against rank counting.
 """
 
 import numpy as np
@@ -136,3 +142,82 @@ def test_reuse_is_identity():
 def test_pool_size_fact(golden):
     g = golden("kv_facts.json")
     assert g["pool_blocks"]["value"] * g["pool_block_tokens"]["value"] == g["pool_positions"]["value"]
+
+
+# ---------------------------------------------------------------- multi-head FP4 indexer
+def _mh_direct(q, w, k):
+    """Brute force with exact rationals: sum_h w[h] * max(0, sum_d q[h, d] k[t, d])."""
+    from fractions import Fraction
+
+    out = []
+    for t in range(k.shape[0]):
+        tot = Fraction(0)
+        for h in range(q.shape[0]):
+            dot = sum(Fraction(float(q[h, d])) * Fraction(float(k[t, d])) for d in range(q.shape[1]))
+            tot += Fraction(float(w[h])) * max(dot, Fraction(0))
+        out.append(tot)
+    return out
+
+
+def test_mh_scores_exact_on_small_values():
+    """Small integer-valued heads, FP4 keys and dyadic weights: the float64 score is exact."""
+    from oracle import fp4
+
+    rng = np.random.default_rng(11)
+    H, D, n = 5, 32, 12
+    q = rng.integers(-3, 4, size=(H, D)).astype(np.float16)
+    w = np.array([0.5, -1.25, 2.0, 0.0, 3.0], dtype=np.float32)
+    codes, scales = fp4.fp4_pack(rng.integers(-6, 7, size=(n, D)).astype(np.float32))
+    k = indexer.fp4_keys_to_f64(codes, scales)
+    got = indexer.index_scores(q, k, w)
+    want = _mh_direct(q, w, k)
+    assert [float(x) for x in want] == got.tolist()
+
+
+def test_mh_scores_relu_clips_each_head():
+    """A head whose dot is negative adds nothing; the others add w * dot."""
+    q = np.array([[1.0, 0.0], [-1.0, 0.0], [0.0, 2.0]], dtype=np.float16)
+    w = np.array([1.0, 10.0, 0.5], dtype=np.float32)
+    k = np.array([[3.0, 1.0], [-2.0, -1.0]])
+    # t = 0: heads give 3, -3 (clipped), 2 -> 3 + 0 + 1 = 4; t = 1: -2 (clipped), 2, -2 (clipped) -> 20
+    assert indexer.index_scores(q, k, w).tolist() == [4.0, 20.0]
+
+
+def test_mh_scores_single_head_is_the_dot_where_nonnegative():
+    rng = np.random.default_rng(12)
+    D = 128
+    q = rng.integers(0, 3, size=(1, D)).astype(np.float16)
+    k = rng.integers(0, 5, size=(40, D)).astype(np.float64)
+    assert np.array_equal(indexer.index_scores(q, k, np.ones(1, np.float32)), indexer.index_scores(q[0], k))
+
+
+def test_mh_scores_head_order_and_weight_scale():
+    rng = np.random.default_rng(13)
+    H, D = 32, 128
+    q = (rng.standard_normal((H, D)) * 4).astype(np.float16)
+    w = rng.standard_normal(H).astype(np.float32)
+    k = rng.integers(-6, 7, size=(50, D)).astype(np.float64) * 0.5
+    perm = rng.permutation(H)
+    a = indexer.index_scores(q, k, w)
+    np.testing.assert_allclose(indexer.index_scores(q[perm], k, w[perm]), a, rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(indexer.index_scores(q, k, 2 * w), 2 * a, rtol=0, atol=0)
+
+
+def test_fp4_indexer_key_bytes():
+    """A 128-dim key in the latent's FP4 format: 64 bytes of nibbles + 8 E4M3 scales."""
+    from oracle import fp4
+
+    assert fp4.packed_row_bytes(128) == 72
+
+
+def test_mh_full_select_brute_force():
+    rng = np.random.default_rng(14)
+    H, D, n, K = 4, 16, 60, 7
+    q = rng.integers(-2, 3, size=(H, D)).astype(np.float16)
+    w = np.array([1.0, 0.5, 2.0, 0.25], dtype=np.float32)
+    k = rng.integers(-2, 3, size=(n, D)).astype(np.float64)
+    idx, pool = indexer.full_select(q, k, K, pool_blocks_max=3, w=w)
+    s = [float(x) for x in _mh_direct(q, w, k)]
+    assert set(int(i) for i in idx) == _rank_select(s, K)
+    bs = indexer.block_scores(s)
+    assert set(int(j) for j in pool if j >= 0) == _rank_select(list(bs), 3)
