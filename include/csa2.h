@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 
 typedef enum {
   CSA2_OK = 0,
@@ -47,7 +47,9 @@ typedef enum {
   CSA2_ERR_HIP = 4           /* a HIP launch or runtime call failed               */
 } csa2_status;
 
-typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1 } csa2_dtype;
+/* Indexer key storage.  CSA2_FP4: the latent's FP4 format applied to the
+ * keys ([P1] "FP4 KV cache"), for the multi-head indexer of [P1] "CSA2". */
+typedef enum { CSA2_F32 = 0, CSA2_BF16 = 1, CSA2_FP4 = 2 } csa2_dtype;
 
 /* CSA2 layer modes that run the indexer ([P1] "CSA2", mode table).  Reuse
  * mode runs no indexer: pass an earlier call's indices to the attention of
@@ -63,8 +65,13 @@ typedef void *csa2_stream; /* hipStream_t */
  *   scales  [num_blocks * block_tokens][latent_dim / 16] E4M3FN, one per 16 channels
  *   rope    [num_blocks * block_tokens][rope_dim] bf16, or NULL when rope_dim == 0
  *   idx_keys[num_blocks * block_tokens][idx_dim] of idx_dtype, or NULL for a
- *           layer that never selects
- * block_tokens must be 64; latent_dim must be 512; rope_dim 0 or 64; idx_dim 64. */
+ *           layer that never selects; with CSA2_FP4 the E2M1 nibbles
+ *           [..][idx_dim / 2] (byte j = dims 2j | 2j+1 << 4) and
+ *   idx_scales[num_blocks * block_tokens][idx_dim / 16] E4M3FN, one per 16 dims
+ * block_tokens must be 64; latent_dim must be 512; rope_dim 0 or 64.  Indexer:
+ * CSA2_F32 / CSA2_BF16 keys have idx_dim 64 and idx_heads 1 (one query);
+ * CSA2_FP4 keys have idx_dim 128 and idx_heads in [1, 32] query heads
+ * ([P1] "CSA2": 32 indexer query heads of dimension 128). */
 typedef struct {
   uint8_t *codes;
   uint8_t *scales;
@@ -75,7 +82,9 @@ typedef struct {
   int32_t latent_dim;
   int32_t rope_dim;
   int32_t idx_dim;
-  int32_t idx_dtype; /* csa2_dtype */
+  int32_t idx_dtype;   /* csa2_dtype */
+  uint8_t *idx_scales; /* CSA2_FP4 keys only, else NULL */
+  int32_t idx_heads;
 } csa2_kv_layer;
 
 /* Batch view.  Position p of sequence b lives in slot
@@ -123,7 +132,8 @@ csa2_status csa2_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t
  * this library's).  For every sequence b, packs latent[b] (device fp32
  * [batch][latent_dim]) into the slot of position seq_lens[b] and copies
  * rope[b] (device bf16 [batch][rope_dim]) and idx_key[b] (device
- * [batch][idx_dim] of idx_dtype) beside it.  Any of the three may be NULL
+ * [batch][idx_dim] of idx_dtype; fp32 for CSA2_FP4 keys, which are packed
+ * like the latent) beside it.  Any of the three may be NULL
  * (not all): a key-only pool appends just idx_key; a layer with a rope
  * side-band needs rope whenever latent is given.  The caller increments
  * seq_lens afterwards.  A position whose page is not mapped (page index beyond
@@ -145,13 +155,18 @@ csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidde
                                 const uint16_t *w_kv, const uint16_t *w_z, uint8_t *codes,
                                 uint8_t *scales, uint16_t *z, float *c_f32, csa2_stream stream);
 
-/* ---- Indexer scores alone (the scoring step of [P1] "CSA2"):
- * scores[b][t] = sum_d q_idx[b][d] * k_idx[b, t][d] for t < seq_lens[b]
- * (fp32 accumulation); entries t >= seq_lens[b] up to max_seq_len are written
- * as -inf.  q_idx: device fp32 [batch][idx_dim]; scores: device fp32
- * [batch][max_seq_len]. */
-csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx,
-                              float *scores, csa2_stream stream);
+/* ---- Indexer scores alone (the scoring step of [P1] "CSA2").  For
+ * t < seq_lens[b], with k = the stored key of position t:
+ *   CSA2_F32 / CSA2_BF16 keys: scores[b][t] = sum_d q_idx[b][d] * k[d],
+ *     q_idx device fp32 [batch][idx_dim], w_idx NULL;
+ *   CSA2_FP4 keys: scores[b][t] = sum_h w_idx[b][h] * max(0, sum_d q_idx[b][h][d] * k[d]),
+ *     q_idx device fp16 [batch][idx_heads][idx_dim], w_idx device fp32
+ *     [batch][idx_heads] (the combining rule across heads is this library's
+ *     reading; the pages give only the head count and dimension).
+ * fp32 accumulation; entries t >= seq_lens[b] up to max_seq_len are written
+ * as -inf.  scores: device fp32 [batch][max_seq_len]. */
+csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const void *q_idx,
+                              const float *w_idx, float *scores, csa2_stream stream);
 
 /* ---- Top-K of given scores: for each row b the top_k largest of
  * scores[b][0 .. lens[b]) (ties: lower position wins), written to
@@ -178,15 +193,16 @@ csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *le
  *   the blocks (increasing when pool_in comes from FULL).  Ids that are
  *   negative or past the sequence are skipped; a repeated id is scored
  *   twice, so its positions may repeat.
- * keys: the layer whose idx_keys are scored; q_idx: device fp32
- * [batch][idx_dim]; indices: device int32 [batch][top_k].
+ * keys: the layer whose idx_keys are scored; q_idx, w_idx: the query as
+ * for csa2_index_scores (scores as defined there); indices: device int32
+ * [batch][top_k].
  * top_k in [1, 4096]; pool_block_tokens must be 8 and pool_blocks in
  * [1, 2048]; max_seq_len at most 8,388,608.  Results are deterministic. */
 csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len, int32_t top_k,
                                              int32_t pool_blocks, int32_t pool_block_tokens,
                                              size_t *bytes);
-csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx,
-                              int32_t top_k, int32_t mode, const int32_t *pool_in, int32_t *pool_out,
+csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, const void *q_idx,
+                              const float *w_idx, int32_t top_k, int32_t mode, const int32_t *pool_in, int32_t *pool_out,
                               int32_t pool_blocks, int32_t pool_block_tokens, int32_t *indices,
                               void *ws, size_t ws_bytes, csa2_stream stream);
 

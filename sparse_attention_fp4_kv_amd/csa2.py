@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-F32, BF16 = 0, 1
+F32, BF16, FP4 = 0, 1, 2
 FULL, REINDEX = 0, 1
 PAGE = 64
 
@@ -40,6 +40,8 @@ class KvLayer(ctypes.Structure):
         ("rope_dim", ctypes.c_int32),
         ("idx_dim", ctypes.c_int32),
         ("idx_dtype", ctypes.c_int32),
+        ("idx_scales", ctypes.c_void_p),
+        ("idx_heads", ctypes.c_int32),
     ]
 
 
@@ -70,11 +72,11 @@ SIGNATURES = {
     "csa2_fp4_unpack": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P]),
     "csa2_kv_append": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P, _P]),
     "csa2_ced_kv_project": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
-    "csa2_index_scores": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P]),
+    "csa2_index_scores": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P, _P]),
     "csa2_topk_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_topk": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "csa2_index_select_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
-    "csa2_index_select": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
+    "csa2_index_select": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "csa2_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_sparse_fp4_decode_attn": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "csa2_block_pool_create": (_P, [_I32]),
@@ -138,10 +140,12 @@ class PagedLayer:
 
     codes [num_blocks*64][256] u8, scales [num_blocks*64][32] u8,
     rope [num_blocks*64][rope_dim] bf16 bits (int16) or None,
-    idx_keys [num_blocks*64][64] fp32 / bf16 bits (int16) or None.
+    idx_keys [num_blocks*64][64] fp32 / bf16 bits (int16), or for idx_dtype
+    "fp4" [num_blocks*64][64] u8 nibbles of 128-dim keys with idx_scales
+    [num_blocks*64][8] u8 (scored with idx_heads query heads), or None.
     """
 
-    def __init__(self, num_blocks, rope_dim=0, idx_dtype=None, device="cuda"):
+    def __init__(self, num_blocks, rope_dim=0, idx_dtype=None, device="cuda", idx_heads=32):
         rows = num_blocks * PAGE
         self.num_blocks = num_blocks
         self.codes = torch.zeros((rows, 256), dtype=torch.uint8, device=device)
@@ -153,8 +157,12 @@ class PagedLayer:
             self.idx_keys = torch.zeros((rows, 64), dtype=torch.float32, device=device)
         elif idx_dtype == "bf16":
             self.idx_keys = torch.zeros((rows, 64), dtype=torch.int16, device=device)
+        elif idx_dtype == "fp4":
+            self.idx_keys = torch.zeros((rows, 64), dtype=torch.uint8, device=device)
         else:
             self.idx_keys = None
+        self.idx_scales = torch.zeros((rows, 8), dtype=torch.uint8, device=device) if idx_dtype == "fp4" else None
+        self.idx_heads = idx_heads if idx_dtype == "fp4" else 1
 
     def struct(self):
         return KvLayer(
@@ -162,7 +170,10 @@ class PagedLayer:
             rope=self.rope.data_ptr() if self.rope is not None else None,
             idx_keys=self.idx_keys.data_ptr() if self.idx_keys is not None else None,
             num_blocks=self.num_blocks, block_tokens=PAGE, latent_dim=512, rope_dim=self.rope_dim,
-            idx_dim=64, idx_dtype=F32 if self.idx_dtype == "f32" else BF16)
+            idx_dim=128 if self.idx_dtype == "fp4" else 64,
+            idx_dtype={"f32": F32, "fp4": FP4}.get(self.idx_dtype, BF16),
+            idx_scales=self.idx_scales.data_ptr() if self.idx_scales is not None else None,
+            idx_heads=self.idx_heads)
 
 
 class Batch:
@@ -250,11 +261,12 @@ def csa2_ced_kv_project(h, w_kv, w_z=None, c_f32=False):
     return codes, scales, z, c
 
 
-def csa2_index_scores(layer, batch, q_idx, max_len):
+def csa2_index_scores(layer, batch, q_idx, max_len, w_idx=None):
+    """q_idx fp32 [B, 64] (fp32 / bf16 keys) or fp16 [B, heads, 128] with w_idx fp32 [B, heads] (FP4 keys)."""
     scores = torch.empty((batch.batch, max_len), dtype=torch.float32, device=q_idx.device)
     kv, sq = layer.struct(), batch.struct()
-    _check(lib().csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), _ptr(q_idx), _ptr(scores), _stream()),
-           "csa2_index_scores")
+    _check(lib().csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), _ptr(q_idx), _ptr(w_idx), _ptr(scores),
+                                   _stream()), "csa2_index_scores")
     return scores
 
 
@@ -283,7 +295,7 @@ def index_select_workspace_bytes(batch, max_len, top_k, pool_blocks=0):
 
 
 def csa2_index_select(layer, batch, q_idx, top_k, mode=FULL, pool_in=None, pool_blocks=0, want_pool=False,
-                      ws=None, indices=None, pool_out=None):
+                      ws=None, indices=None, pool_out=None, w_idx=None):
     """Full (optionally hierarchical: want_pool) or Reindex selection -> (indices, pool_out or None)."""
     B = batch.batch
     dev = q_idx.device
@@ -296,7 +308,8 @@ def csa2_index_select(layer, batch, q_idx, top_k, mode=FULL, pool_in=None, pool_
     if want_pool and pool_out is None:
         pool_out = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
     kv, sq = layer.struct(), batch.struct()
-    _check(lib().csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), _ptr(q_idx), top_k, mode, _ptr(pool_in),
+    _check(lib().csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), _ptr(q_idx), _ptr(w_idx), top_k, mode,
+                                   _ptr(pool_in),
                                    _ptr(pool_out) if want_pool else None, pool_blocks, 8 if pooled else 0,
                                    _ptr(indices), _ptr(ws), ws.numel(), _stream()), "csa2_index_select")
     return indices, (pool_out if want_pool else None)

@@ -23,6 +23,16 @@ csa2_status from_hip(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Indexer keys of a layer: 64-dim fp32 / bf16 with one query head, or 128-dim
+// FP4 (nibbles + E4M3 scales) with 1 .. 32 query heads.
+bool keys_ok(const csa2_kv_layer *l) {
+  if (l->idx_keys == nullptr || !aligned(l->idx_keys, 16)) return false;
+  if (l->idx_dtype == CSA2_F32 || l->idx_dtype == CSA2_BF16) return l->idx_dim == 64 && l->idx_heads == 1;
+  if (l->idx_dtype != CSA2_FP4) return false;
+  return l->idx_dim == 128 && l->idx_heads >= 1 && l->idx_heads <= 32 && l->idx_scales != nullptr &&
+         aligned(l->idx_scales, 8);
+}
+
 // Checks a layer and produces its device view.  need_kv: codes/scales are read;
 // need_keys: idx_keys are read.
 csa2_status check_layer(const csa2_kv_layer *l, bool need_kv, bool need_keys, KvLayerDev *out) {
@@ -35,18 +45,26 @@ csa2_status check_layer(const csa2_kv_layer *l, bool need_kv, bool need_keys, Kv
     if (!aligned(l->codes, 16) || !aligned(l->scales, 16)) return CSA2_ERR_INVALID_ARG;
     if (l->rope_dim != 0 && (l->rope == nullptr || !aligned(l->rope, 16))) return CSA2_ERR_INVALID_ARG;
   }
-  if (need_keys) {
-    if (l->idx_keys == nullptr || l->idx_dim != 64 || !aligned(l->idx_keys, 16)) return CSA2_ERR_INVALID_ARG;
-    if (l->idx_dtype != CSA2_F32 && l->idx_dtype != CSA2_BF16) return CSA2_ERR_INVALID_ARG;
-  }
+  if (need_keys && !keys_ok(l)) return CSA2_ERR_INVALID_ARG;
   out->codes = l->codes;
   out->scales = l->scales;
   out->rope = l->rope_dim ? l->rope : nullptr;
   out->idx_keys = l->idx_keys;
+  out->idx_scales = l->idx_dtype == CSA2_FP4 ? l->idx_scales : nullptr;
   out->num_blocks = l->num_blocks;
   out->rope_dim = l->rope_dim;
   out->idx_f32 = l->idx_dtype == CSA2_F32 ? 1 : 0;
+  out->idx_fp4 = l->idx_dtype == CSA2_FP4 ? 1 : 0;
+  out->idx_heads = l->idx_dtype == CSA2_FP4 ? l->idx_heads : 1;
   return CSA2_OK;
+}
+
+// The query of an indexer call matches the keys' kind: fp32 [B][64] and no
+// weights for fp32 / bf16 keys, fp16 heads and fp32 weights for FP4 keys.
+bool query_ok(const csa2_kv_layer *l, const void *q_idx, const float *w_idx) {
+  if (q_idx == nullptr) return false;
+  if (l->idx_dtype == CSA2_FP4) return w_idx != nullptr && aligned(q_idx, 16) && aligned(w_idx, 4);
+  return w_idx == nullptr && aligned(q_idx, 4);
 }
 
 csa2_status check_seqs(const csa2_seqs *s, SeqsDev *out) {
@@ -162,9 +180,7 @@ csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, co
   if (latent == nullptr && rope == nullptr && idx_key == nullptr) return CSA2_ERR_INVALID_ARG;
   if (rope != nullptr && (L.rope_dim == 0 || layer->rope == nullptr)) return CSA2_ERR_INVALID_ARG;
   if (latent != nullptr && L.rope_dim != 0 && rope == nullptr) return CSA2_ERR_INVALID_ARG;
-  if (idx_key != nullptr && (layer->idx_keys == nullptr || layer->idx_dim != 64 ||
-                             (layer->idx_dtype != CSA2_F32 && layer->idx_dtype != CSA2_BF16)))
-    return CSA2_ERR_INVALID_ARG;
+  if (idx_key != nullptr && !keys_ok(layer)) return CSA2_ERR_INVALID_ARG;
   return from_hip(launch_kv_append(L, S, latent, rope, idx_key, as_stream(stream)));
 }
 
@@ -183,16 +199,16 @@ csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidde
                                      as_stream(stream)));
 }
 
-csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx, float *scores,
-                              csa2_stream stream) {
+csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const void *q_idx,
+                              const float *w_idx, float *scores, csa2_stream stream) {
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(keys, false, true, &L);
   if (st != CSA2_OK) return st;
   if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
   if (S.batch == 0 || S.max_len == 0) return CSA2_OK;
-  if (q_idx == nullptr || scores == nullptr) return CSA2_ERR_INVALID_ARG;
-  return from_hip(launch_index_scores(L, S, q_idx, scores, as_stream(stream)));
+  if (!query_ok(keys, q_idx, w_idx) || scores == nullptr) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_index_scores(L, S, IdxQuery{q_idx, w_idx}, scores, as_stream(stream)));
 }
 
 csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top_k, size_t *bytes) {
@@ -224,8 +240,9 @@ csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len,
   return CSA2_OK;
 }
 
-csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, const float *q_idx, int32_t top_k,
-                              int32_t mode, const int32_t *pool_in, int32_t *pool_out, int32_t pool_blocks,
+csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, const void *q_idx,
+                              const float *w_idx, int32_t top_k, int32_t mode, const int32_t *pool_in,
+                              int32_t *pool_out, int32_t pool_blocks,
                               int32_t pool_block_tokens, int32_t *indices, void *ws, size_t ws_bytes,
                               csa2_stream stream) {
   KvLayerDev L;
@@ -242,15 +259,16 @@ csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
   if (mode == CSA2_REINDEX && (pool_in == nullptr || pool_out != nullptr)) return CSA2_ERR_INVALID_ARG;
   if (mode == CSA2_FULL && pool_in != nullptr) return CSA2_ERR_INVALID_ARG;
   if (S.batch == 0) return CSA2_OK;
-  if (q_idx == nullptr || indices == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (!query_ok(keys, q_idx, w_idx) || indices == nullptr) return CSA2_ERR_INVALID_ARG;
   const size_t need = index_select_workspace_bytes(S.batch, S.max_len, top_k, pooled ? pool_blocks : 0);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
   hipError_t e;
+  const IdxQuery q{q_idx, w_idx};
   if (mode == CSA2_FULL)
-    e = launch_index_select_full(L, S, q_idx, top_k, pool_out, pool_out ? pool_blocks : 0, indices, ws,
+    e = launch_index_select_full(L, S, q, top_k, pool_out, pool_out ? pool_blocks : 0, indices, ws,
                                  as_stream(stream));
   else
-    e = launch_index_select_reindex(L, S, q_idx, top_k, pool_in, pool_blocks, indices, ws, as_stream(stream));
+    e = launch_index_select_reindex(L, S, q, top_k, pool_in, pool_blocks, indices, ws, as_stream(stream));
   return from_hip(e);
 }
 

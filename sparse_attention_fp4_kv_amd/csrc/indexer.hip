@@ -197,6 +197,72 @@ __device__ __forceinline__ float unit_score(const KeyLoad &k, const float (&q)[8
   return group8_sum(s);
 }
 
+// ---- multi-head FP4 keys: 32 query heads x 128 dims on v_mfma_f32_32x32x16_f16
+// One tile = 32 positions x 32 heads.  Lane l works on position l % 32 of the
+// tile and half h = l / 32 of the key: dims 64 h .. 64 h + 63 (32 nibble bytes
+// and 4 E4M3 scales).  The contraction's 16-wide k-step ks pairs dims
+// 64 h + 8 ks .. + 7 of both halves, for the query (A, row = head) and the key
+// (B, column = position) alike, so every lane dequantizes only its own bytes.
+// D lane l holds heads 8 (e / 4) + 4 h + e % 4 (e < 16) of position l % 32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kFp4IdxDim = 128;
+constexpr int kFp4IdxMaxHeads = 32;
+
+enum KeyFmt { kKeyBf16 = 0, kKeyF32 = 1, kKeyFp4 = 2 };
+
+struct Fp4Half {
+  u32x4 c0, c1;  // 64 nibbles
+  uint32_t sc;   // 4 scales
+};
+
+__device__ __forceinline__ Fp4Half load_fp4_half(const KvLayerDev &L, int64_t slot, int lane) {
+  const int h = lane >> 5;
+  const u32x4 *cp =
+      reinterpret_cast<const u32x4 *>(static_cast<const uint8_t *>(L.idx_keys) + slot * (kFp4IdxDim / 2) + 32 * h);
+  Fp4Half r;
+  r.c0 = __builtin_nontemporal_load(cp);
+  r.c1 = __builtin_nontemporal_load(cp + 1);
+  r.sc = __builtin_nontemporal_load(
+      reinterpret_cast<const uint32_t *>(L.idx_scales + slot * (kFp4IdxDim / kGroup) + 4 * h));
+  return r;
+}
+
+struct Fp4Query {
+  f16x8 qa[8];   // this lane's head row (lane % 32), dims 64 h + 8 ks .. + 7
+  float wr[16];  // weights of the 16 heads this lane's results hold (0 past the heads)
+};
+
+__device__ __forceinline__ void load_fp4_query(IdxQuery q, int b, int heads, int lane, Fp4Query &Q) {
+  const int r = lane & 31, h = lane >> 5;
+  const f16 *qrow = static_cast<const f16 *>(q.q) + ((size_t)b * heads + (r < heads ? r : 0)) * kFp4IdxDim + 64 * h;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const f16x8 v = *reinterpret_cast<const f16x8 *>(qrow + 8 * ks);
+    Q.qa[ks] = r < heads ? v : f16x8{};
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = 8 * (e >> 2) + 4 * h + (e & 3);
+    Q.wr[e] = row < heads ? q.w[(size_t)b * heads + row] : 0.0f;
+  }
+}
+
+// Score of this lane's position: sum over heads of w * max(0, q . k) (both
+// lanes of a position return it).
+__device__ __forceinline__ float fp4_tile_score(const Fp4Half &k, const Fp4Query &Q) {
+  const uint32_t words[8] = {k.c0[0], k.c0[1], k.c0[2], k.c0[3], k.c1[0], k.c1[1], k.c1[2], k.c1[3]};
+  const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.sc, 1.0f, false);
+  const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(k.sc, 1.0f, true);
+  const f16 sc[4] = {s01[0], s01[1], s23[0], s23[1]};
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.qa[ks], deq8(words[ks], sc[ks >> 1]), acc, 0, 0, 0);
+  float part = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) part = fmaf(Q.wr[e], fmaxf(acc[e], 0.0f), part);
+  return part + __shfl_xor(part, 32);
+}
+
 __device__ __forceinline__ int row_len(const SeqsDev &S, int b) {
   const int n = S.seq_lens[b];
   return n < 0 ? 0 : (n > S.max_len ? S.max_len : n);
@@ -476,13 +542,14 @@ __device__ __forceinline__ void emit_segment_pair(const uint32_t *pkeys, int cap
 struct ScanArgs {
   KvLayerDev L;
   SeqsDev S;
-  const float *q_idx;
+  IdxQuery q;
   int K, P;  // top-K, pool blocks (hierarchical)
   SelWs w;
 };
 
-template <bool F32, bool HIER>
+template <int KF, bool HIER>
 __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
+  constexpr bool F32 = KF == kKeyF32;
   __shared__ int32_t pg[kScanPages];
   __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
   __shared__ __attribute__((aligned(16))) uint32_t bkey[kScanBlocks];
@@ -499,16 +566,46 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
   if (tid < kScanPages) pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
   float q[8];
-  {
-    const float *qp = a.q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
+  Fp4Query Q;
+  if constexpr (KF == kKeyFp4) {
+    load_fp4_query(a.q, b, a.L.idx_heads, lane, Q);
+  } else {
+    const float *qp = static_cast<const float *>(a.q.q) + (size_t)b * kIdxDim + 8 * (lane & 7);
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = qp[e];
   }
   __syncthreads();
   // wave w streams pages w, w+4, .., w+28 (the workgroup's four waves read
-  // four neighbouring pages at a time), one page (8 loads of 1 KB) at a time
-  // with the next pages' loads in flight
+  // four neighbouring pages at a time), one page at a time (8 loads of 1 KB,
+  // or for FP4 keys two tiles of 32 positions) with the next page's loads in
+  // flight
   constexpr int kDepth = 2;  // pages whose loads are in flight (deeper measured slower)
+  if constexpr (KF == kKeyFp4) {
+    if (can_load) {
+      Fp4Half kt[kDepth][2];
+      auto issue4 = [&](int pp, Fp4Half(&dst)[2]) {
+        const int pid = pg[4 * pp + wave];
+        const int64_t s0 = (int64_t)(pid < 0 ? 0 : pid) * kPage;  // unmapped: read slot 0, masked below
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dst[j] = load_fp4_half(a.L, s0 + 32 * j + (lane & 31), lane);
+      };
+      issue4(0, kt[0]);
+#pragma unroll
+      for (int pp = 0; pp < 8; ++pp) {
+        if (pp + 1 < 8) issue4(pp + 1, kt[(pp + 1) % kDepth]);
+        const int page = 4 * pp + wave;
+        const bool mapped = pg[page] >= 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int lp = page * kPage + 32 * j + (lane & 31);  // local position
+          const float sc = fp4_tile_score(kt[pp % kDepth][j], Q);
+          if (lane < 32) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
+        }
+      }
+    } else {
+      for (int i = tid; i < kScanPos; i += 256) pkey[i] = 0u;
+    }
+  } else {
   KeyLoad kl[kDepth][8];
   auto issue = [&](int pp, KeyLoad(&dst)[8]) {
     const int pid = pg[4 * pp + wave];
@@ -533,6 +630,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     }
   } else {
     for (int i = tid; i < kScanPos; i += 256) pkey[i] = 0u;
+  }
   }
   __syncthreads();
   if constexpr (HIER) {
@@ -609,7 +707,7 @@ __global__ void __launch_bounds__(256) given_kernel(GivenArgs a) {
 struct PoolArgs {
   KvLayerDev L;
   SeqsDev S;
-  const float *q_idx;
+  IdxQuery q;
   const int32_t *pool;  // [B][pool_blocks]
   int pool_blocks;
   int K;
@@ -618,8 +716,9 @@ struct PoolArgs {
 
 // Workgroup w scores pool blocks [16w, 16w+16) of its row (wave v: blocks
 // 4v .. 4v+3), stores every (key, position) and emits a budgeted segment.
-template <bool F32>
+template <int KF>
 __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
+  constexpr bool F32 = KF == kKeyF32;
   __shared__ int64_t slot0[kPoolBlocksPerWg];
   __shared__ int32_t tok0[kPoolBlocksPerWg];
   __shared__ uint32_t key_l[256];
@@ -647,9 +746,23 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   }
   key_l[tid] = 0u;  // items 128..255 stay empty
   zero_hists<2>(hist);
+  if constexpr (KF == kKeyFp4) {
+    // wave v: its 4 blocks are one tile of 32 positions (lane % 32 -> block 4 v + p / 8, position p % 8)
+    Fp4Query Q;
+    load_fp4_query(a.q, b, a.L.idx_heads, lane, Q);
+    __syncthreads();
+    const int p = lane & 31, blk = 4 * wave + (p >> 3);
+    const int64_t s0 = slot0[blk];
+    Fp4Half kh = Fp4Half{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, 0u};
+    if (a.L.num_blocks > 0) kh = load_fp4_half(a.L, (s0 < 0 ? 0 : s0) + (p & 7), lane);  // unmapped: slot 0, masked below
+    const float s = fp4_tile_score(kh, Q);
+    const int t0 = tok0[blk];
+    const bool ok = t0 >= 0 && t0 + (p & 7) < n;
+    if (lane < 32) key_l[blk * kBlk + (p & 7)] = ok ? score_key(s) : 0u;
+  } else {
   float q[8];
   {
-    const float *qp = a.q_idx + (size_t)b * kIdxDim + 8 * (lane & 7);
+    const float *qp = static_cast<const float *>(a.q.q) + (size_t)b * kIdxDim + 8 * (lane & 7);
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = qp[e];
   }
@@ -672,6 +785,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
     const float s = unit_score<F32>(kl[u], q);
     const bool ok = t0 >= 0 && t0 + (lane >> 3) < n;
     if ((lane & 7) == 0) key_l[blk * kBlk + (lane >> 3)] = ok ? score_key(s) : 0u;
+  }
   }
   __syncthreads();
   auto pos_of = [&](int i) { return (uint32_t)(tok0[i >> 3] + (i & 7)); };
@@ -1435,10 +1549,34 @@ __global__ void __launch_bounds__(256) scores_kernel(KvLayerDev L, SeqsDev S, co
   for (int64_t u = u_begin + wave; u < u_end; u += 4) {
     const int64_t t0 = u * 8;
     const int blk = (t0 < n && L.num_blocks > 0) ? page_block(S, L.num_blocks, b, t0 / kPage) : -1;
-    const KeyLoad kl = load_unit<F32>(L.idx_keys, blk < 0 ? 0 : (int64_t)blk * kPage + t0 % kPage, lane);
+    KeyLoad kl = KeyLoad{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}};
+    if (L.num_blocks > 0)  // unmapped: slot 0, masked below (an empty pool has no slot 0)
+      kl = load_unit<F32>(L.idx_keys, blk < 0 ? 0 : (int64_t)blk * kPage + t0 % kPage, lane);
     const float s = unit_score<F32>(kl, q);
     const int64_t t = t0 + (lane >> 3);
     if ((lane & 7) == 0 && t < S.max_len) scores[(size_t)b * S.max_len + t] = (blk >= 0 && t < n) ? s : -INFINITY;
+  }
+}
+
+// FP4 keys, multi-head score: tiles of 32 positions, a wave per tile.
+__global__ void __launch_bounds__(256) scores_fp4_kernel(KvLayerDev L, SeqsDev S, IdxQuery qi, float *scores,
+                                                         int tiles_per_wg) {
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = row_len(S, b);
+  const int64_t total_tiles = ((int64_t)S.max_len + 31) / 32;
+  const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_wg;
+  const int64_t t_end = min(t_begin + tiles_per_wg, total_tiles);
+  Fp4Query Q;
+  load_fp4_query(qi, b, L.idx_heads, lane, Q);
+  for (int64_t tile = t_begin + wave; tile < t_end; tile += 4) {  // wave-uniform trip count
+    const int64_t t = tile * 32 + (lane & 31);
+    const int blk = (t < n && L.num_blocks > 0) ? page_block(S, L.num_blocks, b, t / kPage) : -1;
+    Fp4Half kh = Fp4Half{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, 0u};
+    if (L.num_blocks > 0)  // unmapped: slot 0, masked below (an empty pool has no slot 0)
+      kh = load_fp4_half(L, blk < 0 ? 0 : (int64_t)blk * kPage + t % kPage, lane);
+    const float s = fp4_tile_score(kh, Q);
+    if (lane < 32 && t < S.max_len) scores[(size_t)b * S.max_len + t] = (blk >= 0 && t < n) ? s : -INFINITY;
   }
 }
 
@@ -1461,13 +1599,22 @@ size_t index_select_workspace_bytes(int batch, int max_len, int top_k, int pool_
   return ws_bytes_for(batch, ws_shape(max_len, pool_blocks));
 }
 
-hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, float *scores,
-                               hipStream_t st) {
+hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, IdxQuery q, float *scores, hipStream_t st) {
+  if (S.batch <= 0 || S.max_len <= 0) return hipSuccess;
+  if (L.idx_fp4) {
+    const int64_t tiles = ((int64_t)S.max_len + 31) / 32;
+    const int per = 16;
+    const dim3 grid((unsigned)((tiles + per - 1) / per), (unsigned)S.batch);
+    timer_before(kKernIndexScores, st);
+    scores_fp4_kernel<<<grid, dim3(256), 0, st>>>(L, S, q, scores, per);
+    timer_after(kKernIndexScores, st);
+    return hipGetLastError();
+  }
   const int64_t units = ((int64_t)S.max_len + 7) / 8;
   const int per = 64;
   const int64_t gx = (units + per - 1) / per;
-  if (gx <= 0 || S.batch <= 0) return hipSuccess;
   const dim3 grid((unsigned)gx, (unsigned)S.batch);
+  const float *q_idx = static_cast<const float *>(q.q);
   timer_before(kKernIndexScores, st);
   if (L.idx_f32) scores_kernel<true><<<grid, dim3(256), 0, st>>>(L, S, q_idx, scores, per);
   else scores_kernel<false><<<grid, dim3(256), 0, st>>>(L, S, q_idx, scores, per);
@@ -1497,7 +1644,7 @@ hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t
   return run_select(s, 1, batch, st);
 }
 
-hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
+hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                     int32_t *pool_out, int pool_blocks, int32_t *indices, void *ws,
                                     hipStream_t st) {
   if (S.batch <= 0) return hipSuccess;
@@ -1507,12 +1654,16 @@ hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, const
   ScanArgs a{L, S, q_idx, top_k, pool_blocks, w};
   const int gx = (int)(sh.cap_keys / kScanPos);
   timer_before(kKernIndexScan, st);
-  if (L.idx_f32) {
-    if (hier) scan_kernel<true, true><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
-    else scan_kernel<true, false><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
+  const dim3 grid(gx, S.batch);
+  if (L.idx_fp4) {
+    if (hier) scan_kernel<kKeyFp4, true><<<grid, dim3(256), 0, st>>>(a);
+    else scan_kernel<kKeyFp4, false><<<grid, dim3(256), 0, st>>>(a);
+  } else if (L.idx_f32) {
+    if (hier) scan_kernel<kKeyF32, true><<<grid, dim3(256), 0, st>>>(a);
+    else scan_kernel<kKeyF32, false><<<grid, dim3(256), 0, st>>>(a);
   } else {
-    if (hier) scan_kernel<false, true><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
-    else scan_kernel<false, false><<<dim3(gx, S.batch), dim3(256), 0, st>>>(a);
+    if (hier) scan_kernel<kKeyBf16, true><<<grid, dim3(256), 0, st>>>(a);
+    else scan_kernel<kKeyBf16, false><<<grid, dim3(256), 0, st>>>(a);
   }
   timer_after(kKernIndexScan, st);
   hipError_t e = hipGetLastError();
@@ -1528,7 +1679,7 @@ hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, const
   return run_select(s, hier ? 2 : 1, S.batch, st);
 }
 
-hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
+hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                        const int32_t *pool_in, int pool_blocks, int32_t *indices, void *ws,
                                        hipStream_t st) {
   if (S.batch <= 0) return hipSuccess;
@@ -1537,8 +1688,9 @@ hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, co
   PoolArgs p{L, S, q_idx, pool_in, pool_blocks, top_k, w};
   const int gx = (pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
   timer_before(kKernPoolScore, st);
-  if (L.idx_f32) pool_kernel<true><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
-  else pool_kernel<false><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
+  if (L.idx_fp4) pool_kernel<kKeyFp4><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
+  else if (L.idx_f32) pool_kernel<kKeyF32><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
+  else pool_kernel<kKeyBf16><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
   timer_after(kKernPoolScore, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

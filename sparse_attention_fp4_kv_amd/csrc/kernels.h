@@ -32,9 +32,19 @@ struct KvLayerDev {
   uint8_t *scales;
   uint16_t *rope;
   void *idx_keys;
+  uint8_t *idx_scales;  // FP4 keys
   int num_blocks;
-  int rope_dim;  // 0 or 64
-  int idx_f32;   // 1: fp32 keys, 0: bf16 keys
+  int rope_dim;   // 0 or 64
+  int idx_f32;    // 1: fp32 keys (64 dims)
+  int idx_fp4;    // 1: FP4 keys (128 dims, multi-head score); else bf16 (64 dims)
+  int idx_heads;  // query heads of the FP4 score (1 .. 32)
+};
+
+// The indexer query of one call: fp32 [B][64] for fp32 / bf16 keys (w null),
+// fp16 [B][idx_heads][128] plus fp32 weights [B][idx_heads] for FP4 keys.
+struct IdxQuery {
+  const void *q;
+  const float *w;
 };
 
 // Device view of a batch (validated copy of csa2_seqs).
@@ -56,15 +66,14 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
 
 // ---- indexer / top-K (indexer.hip)
 size_t topk_workspace_bytes(int batch, int max_items, int top_k);
-hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, float *scores,
-                               hipStream_t st);
+hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, IdxQuery q, float *scores, hipStream_t st);
 hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t *lens, int batch, int max_len,
                               int top_k, int32_t *indices, void *ws, hipStream_t st);
 size_t index_select_workspace_bytes(int batch, int max_len, int top_k, int pool_blocks);
-hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
+hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                     int32_t *pool_out, int pool_blocks, int32_t *indices, void *ws,
                                     hipStream_t st);
-hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, const float *q_idx, int top_k,
+hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                        const int32_t *pool_in, int pool_blocks, int32_t *indices, void *ws,
                                        hipStream_t st);
 

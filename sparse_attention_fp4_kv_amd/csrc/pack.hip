@@ -80,7 +80,19 @@ __global__ void __launch_bounds__(64) kv_append_kernel(KvLayerDev L, SeqsDev S, 
       for (int r = u; r < L.rope_dim; r += 32) L.rope[slot * L.rope_dim + r] = rope[(int64_t)b * L.rope_dim + r];
     }
     if (idx_key != nullptr && L.idx_keys != nullptr) {
-      if (L.idx_f32) {
+      if (L.idx_fp4) {  // 128 fp32 dims packed like the latent: lane u < 8 packs dims 16u .. 16u+15
+        constexpr int kDim = 128;
+        if (u < kDim / kGroup) {
+          const float *src = static_cast<const float *>(idx_key) + (int64_t)b * kDim + u * kGroup;
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) v[i] = src[i];
+          uint32_t w0, w1;
+          const uint32_t sc = pack_group16(v, &w0, &w1);
+          reinterpret_cast<uint2 *>(static_cast<uint8_t *>(L.idx_keys) + slot * (kDim / 2))[u] = make_uint2(w0, w1);
+          L.idx_scales[slot * (kDim / kGroup) + u] = (uint8_t)sc;
+        }
+      } else if (L.idx_f32) {
         const float *src = static_cast<const float *>(idx_key) + (int64_t)b * kIdxDim;
         float *dst = static_cast<float *>(L.idx_keys) + slot * kIdxDim;
         for (int r = u; r < kIdxDim; r += 32) dst[r] = src[r];

@@ -23,6 +23,8 @@ import numpy as np
 
 LATENT = 512
 IDX_DIM = 64
+IDX4_DIM = 128   # multi-head indexer: key / query-head width
+IDX4_HEADS = 32  # multi-head indexer: query heads
 PAGE = 64
 
 
@@ -79,7 +81,7 @@ def workload(wid):
 
 # Stream names, in spawn order.  Appending new names at the end keeps old streams stable.
 _NAMES = ("lens", "latent", "outliers", "idx_keys", "q_idx", "q", "rope", "tables", "append", "ced_h",
-          "ced_wkv", "ced_wz", "misc")
+          "ced_wkv", "ced_wz", "misc", "idx_keys4", "q_idx4", "w_idx")
 
 
 class Streams:
@@ -120,6 +122,21 @@ def idx_keys(st, seq, n, dtype, dim=IDX_DIM):
     """Indexer keys of one sequence: fp32 array, or bf16 bits (uint16)."""
     x = st.gen("idx_keys", seq).standard_normal((n, dim), dtype=np.float32)
     return x if dtype == "f32" else to_bf16_bits(x)
+
+
+def idx4_keys(st, seq, n, dim=IDX4_DIM):
+    """fp32 [n][128] multi-head indexer keys before they are stored as FP4: N(0, 1)."""
+    return st.gen("idx_keys4", seq).standard_normal((n, dim), dtype=np.float32)
+
+
+def q_idx_heads(st, layer, batch, heads=IDX4_HEADS, dim=IDX4_DIM):
+    """fp16 [batch][heads][128] indexer query heads: N(0, 1) rounded to fp16."""
+    return st.gen("q_idx4", layer).standard_normal((batch, heads, dim), dtype=np.float32).astype(np.float16)
+
+
+def w_idx(st, layer, batch, heads=IDX4_HEADS):
+    """fp32 [batch][heads] per-head indexer weights: N(0, 1 / heads)."""
+    return st.gen("w_idx", layer).standard_normal((batch, heads), dtype=np.float32) / np.float32(math.sqrt(heads))
 
 
 def rope_rows(st, layer, seq, n, dim):

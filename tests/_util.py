@@ -40,7 +40,8 @@ def fill_layer(layer, tables, seq_lens, latents=None, keys=None, ropes=None):
     """Write per-sequence arrays into the paged pool at the table's physical rows.
 
     latents[b]: fp32 [n_b][512] (packed on the GPU); keys[b]: fp32 or bf16 bits
-    [n_b][64]; ropes[b]: bf16 bits [n_b][64].
+    [n_b][64], or for an FP4 layer fp32 [n_b][128] (packed on the GPU);
+    ropes[b]: bf16 bits [n_b][64].
     """
     for b, n in enumerate(seq_lens):
         if n == 0:
@@ -51,7 +52,11 @@ def fill_layer(layer, tables, seq_lens, latents=None, keys=None, ropes=None):
             codes, scales = csa2.csa2_fp4_pack(to_dev(latents[b]))
             layer.codes[rows_t] = codes
             layer.scales[rows_t] = scales
-        if keys is not None:
+        if keys is not None and layer.idx_dtype == "fp4":
+            codes, scales = csa2.csa2_fp4_pack(to_dev(keys[b]))
+            layer.idx_keys[rows_t] = codes
+            layer.idx_scales[rows_t] = scales
+        elif keys is not None:
             layer.idx_keys[rows_t] = to_dev(keys[b])
         if ropes is not None:
             layer.rope[rows_t] = to_dev(ropes[b])

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(csa2.LIB_PATH)
     for name in header_functions():
         assert hasattr(raw, name), name
-    assert csa2.lib().csa2_abi_version() == 1
+    assert csa2.lib().csa2_abi_version() == 2
     assert csa2.lib().csa2_status_string(3) == b"workspace missing or too small"
 
 
@@ -55,19 +55,31 @@ def test_validation_rejects_before_launch():
     assert L.csa2_attn_workspace_size(1, 64, 2048, 512, ctypes.byref(n)) == csa2.OK
     # a layer with the wrong page size is rejected
     kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=16, num_blocks=1, block_tokens=32, latent_dim=512,
-                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16)
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
     sq = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=1, max_seq_len=64)
-    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, 16, s) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, None, 16, s) == csa2.ERR_INVALID_ARG
     kv.block_tokens = 64
     sq.max_seq_len = 65  # beyond max_blocks_per_seq * 64
-    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, 16, s) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, None, 16, s) == csa2.ERR_INVALID_ARG
     sq.max_seq_len = 64
     # too-small workspace
-    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, 8, csa2.FULL, None, None, 0, 0, 16, 256, 1,
+    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, None, 8, csa2.FULL, None, None, 0, 0, 16, 256, 1,
                                s) == csa2.ERR_WORKSPACE
     # Reindex without a pool
-    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, 8, csa2.REINDEX, None, None, 16, 8, 16, 256,
+    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, None, 8, csa2.REINDEX, None, None, 16, 8, 16, 256,
                                1 << 30, s) == csa2.ERR_INVALID_ARG
+    # weights are for FP4 keys only
+    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, 16, 16, s) == csa2.ERR_INVALID_ARG
+    # FP4 keys: 128 dims, 1..32 heads, scales present, weights required
+    kv.idx_dtype, kv.idx_dim, kv.idx_heads, kv.idx_scales = csa2.FP4, 128, 32, 16
+    assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, None, 16, s) == csa2.ERR_INVALID_ARG
+    for field, bad in (("idx_dim", 64), ("idx_heads", 33), ("idx_heads", 0), ("idx_scales", None)):
+        good = getattr(kv, field)
+        setattr(kv, field, bad)
+        assert L.csa2_index_scores(ctypes.byref(kv), ctypes.byref(sq), 16, 16, 16, s) == csa2.ERR_INVALID_ARG
+        setattr(kv, field, good)
+    assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, 16, 8, csa2.FULL, None, None, 0, 0, 16, 256, 1,
+                               s) == csa2.ERR_WORKSPACE
 
 
 @needs_lib

@@ -251,3 +251,114 @@ def test_full_select_1m_heavy_ties():
     assert set(idx.tolist()) == set(ref.tolist()), "exact ties: lower positions win"
     bs = oracle.indexer.block_scores_fast(s)
     assert set(pool.tolist()) == set(oracle.indexer.topk(bs, 2048).tolist())
+
+
+# ---------------------------------------------------------------- multi-head FP4 indexer keys
+def _fp4_layer(seq_lens, heads, permuted, seed):
+    st = wl.Streams(seed)
+    tables, nb = build_tables(st, seq_lens, permuted)
+    keys = [wl.idx4_keys(st, b, n) for b, n in enumerate(seq_lens)]
+    layer = csa2.PagedLayer(nb, idx_dtype="fp4", idx_heads=heads, device="cuda")
+    fill_layer(layer, tables, seq_lens, keys=keys)
+    return st, tables, keys, layer
+
+
+def _fp4_oracle_keys(layer, tables, keys, b, n, check_stored=True):
+    """Oracle float64 keys of sequence b (packed by the oracle), and the stored bytes compared bit-exact."""
+    codes, scales = oracle.fp4.fp4_pack(keys[b])
+    if check_stored and n:
+        rows = torch.from_numpy(oracle.paged.physical_rows(tables[b], np.arange(n))).cuda()
+        assert np.array_equal(layer.idx_keys[rows].cpu().numpy(), codes), f"stored codes b={b}"
+        assert np.array_equal(layer.idx_scales[rows].cpu().numpy(), scales), f"stored scales b={b}"
+    return oracle.indexer.fp4_keys_to_f64(codes, scales)
+
+
+@pytest.mark.parametrize("heads", [32, 7, 1])
+def test_fp4_scores_match_oracle(heads):
+    seq_lens = [1000, 64, 1, 4096 + 13, 0]
+    st, tables, keys, layer = _fp4_layer(seq_lens, heads, True, 50)
+    q = wl.q_idx_heads(st, 0, len(seq_lens), heads)
+    w = wl.w_idx(st, 0, len(seq_lens), heads)
+    max_len = max(seq_lens) + 5
+    batch = make_batch(tables, seq_lens, max_len)
+    s = csa2.csa2_index_scores(layer, batch, to_dev(q), max_len, w_idx=to_dev(w))
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    for b, n in enumerate(seq_lens):
+        kf = _fp4_oracle_keys(layer, tables, keys, b, n)
+        ref = oracle.indexer.index_scores(q[b], kf, w[b])
+        # fp32 accumulation: error bounded by a few ulps of the sum of absolute terms
+        mag = np.maximum(np.abs(kf) @ np.abs(q[b].astype(np.float64)).T, 0.0) @ np.abs(w[b].astype(np.float64))
+        err = np.abs(s[b, :n] - ref)
+        assert np.all(err <= 1e-6 * mag + 1e-30), (b, float(np.max(err / (mag + 1e-30))))
+        assert np.all(np.isneginf(s[b, n:]))
+
+
+@pytest.mark.parametrize("permuted", [False, True])
+def test_fp4_full_select(permuted):
+    seq_lens = [4096, 65536 + 17, 100, 3000]
+    st, tables, keys, layer = _fp4_layer(seq_lens, 32, permuted, 51)
+    q, w = wl.q_idx_heads(st, 0, len(seq_lens)), wl.w_idx(st, 0, len(seq_lens))
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    for K in (256, 2048):
+        idx, _ = csa2.csa2_index_select(layer, batch, to_dev(q), K, csa2.FULL, w_idx=to_dev(w))
+        torch.cuda.synchronize()
+        idx = idx.cpu().numpy()
+        for b, n in enumerate(seq_lens):
+            s = oracle.indexer.index_scores(q[b], _fp4_oracle_keys(layer, tables, keys, b, n, K == 256), w[b])
+            check_topk(idx[b], dict(enumerate(s)), K, where=f"K={K} b={b}")
+
+
+def test_fp4_hierarchical_pool_and_reindex():
+    seq_lens = [200000, 16384, 50, 70001]
+    P, K = 2048, 2048
+    st, tables, keys, layer = _fp4_layer(seq_lens, 32, True, 52)
+    q0, w0 = wl.q_idx_heads(st, 0, len(seq_lens)), wl.w_idx(st, 0, len(seq_lens))
+    q1, w1 = wl.q_idx_heads(st, 1, len(seq_lens)), wl.w_idx(st, 1, len(seq_lens))
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    idx, pool = csa2.csa2_index_select(layer, batch, to_dev(q0), K, csa2.FULL, pool_blocks=P, want_pool=True,
+                                       w_idx=to_dev(w0))
+    torch.cuda.synchronize()
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    o_pools, kfs = [], []
+    for b, n in enumerate(seq_lens):
+        kf = _fp4_oracle_keys(layer, tables, keys, b, n)
+        kfs.append(kf)
+        s0 = oracle.indexer.index_scores(q0[b], kf, w0[b])
+        check_topk(pool[b], dict(enumerate(oracle.indexer.block_scores_fast(s0))), P, where=f"pool b={b}")
+        check_topk(idx[b], dict(enumerate(s0)), K, where=f"full b={b}")
+        o_pools.append(oracle.indexer.pool_blocks(s0, P))
+    # Reindex fed with the oracle's pool, so a difference is the Reindex kernel's
+    o_pool_t = to_dev(np.stack(o_pools).astype(np.int32))
+    idx1, _ = csa2.csa2_index_select(layer, batch, to_dev(q1), K, csa2.REINDEX, pool_in=o_pool_t, pool_blocks=P,
+                                     w_idx=to_dev(w1))
+    torch.cuda.synchronize()
+    idx1 = idx1.cpu().numpy()
+    for b, n in enumerate(seq_lens):
+        pos = oracle.indexer.pool_positions(o_pools[b], n)
+        s1 = oracle.indexer.index_scores(q1[b], kfs[b][pos], w1[b])
+        check_topk(idx1[b], dict(zip(pos.tolist(), s1)), K, where=f"reindex b={b}")
+
+
+def test_fp4_append_packs_keys():
+    """kv_append stores a 128-dim fp32 key as FP4 codes + E4M3 scales, bit-exact with the oracle's pack,
+    at the physical slot of position seq_lens[b] and nowhere else."""
+    st = wl.Streams(53)
+    seq_lens = [63, 64, 0, 130]
+    tables, nb = build_tables(st, seq_lens, True, extra_blocks=1)
+    layer = csa2.PagedLayer(nb, idx_dtype="fp4", device="cuda")
+    batch = make_batch(tables, seq_lens)
+    new_keys = wl.idx4_keys(st, 99, len(seq_lens))
+    new_keys[1, :16] = 0.0     # an all-zero group
+    new_keys[2, 16:32] *= 1e4  # a group whose scale saturates
+    csa2.csa2_kv_append(layer, batch, None, None, to_dev(new_keys))
+    torch.cuda.synchronize()
+    codes, scales = oracle.fp4.fp4_pack(new_keys)
+    gc, gs = layer.idx_keys.cpu().numpy(), layer.idx_scales.cpu().numpy()
+    written = []
+    for b, n in enumerate(seq_lens):
+        row = int(oracle.paged.physical_rows(tables[b], np.array([n]))[0])
+        written.append(row)
+        assert np.array_equal(gc[row], codes[b]) and np.array_equal(gs[row], scales[b]), b
+    others = np.setdiff1d(np.arange(gc.shape[0]), written)
+    assert not gc[others].any() and not gs[others].any()
