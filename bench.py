@@ -11,7 +11,8 @@ Other workloads (--workload): decode_b8_64k_rope (8 x 65,536 tokens, rope
 side-band, permuted page tables, one Full layer), mixed_serving_32_reuse4 (32
 requests with log-uniform lengths, append to 4 KV layers, one Full selection
 reused by 4 attentions), ced_prefill_16k_x20 (CED projection GEMM with the
-fused pack), tiny_b1_4k.
+fused pack), tiny_b1_4k, decode_1m_fp4_indexer (the 1M case with FP4 indexer
+keys of 128 dims scored by 32 weighted query heads).
 
 Timing: inputs are resident in HBM; R replicas of the cache rotate so every
 step reads data evicted from the 256 MB last-level cache; each replica's step
@@ -40,7 +41,7 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "sparse FP4-KV decode attn queries/s + achieved HBM GB/s vs MI355X peak"
 WORKLOADS = ("decode_1m_hierarchical", "decode_b8_64k_rope", "mixed_serving_32_reuse4", "ced_prefill_16k_x20",
-             "tiny_b1_4k")
+             "tiny_b1_4k", "decode_1m_fp4_indexer")
 
 
 def log(*a):
@@ -95,7 +96,11 @@ class Decode:
                 c, sc = csa2.csa2_fp4_pack(torch.from_numpy(latent[s:e]).to(self.dev))
                 layer.codes[rows] = c
                 layer.scales[rows] = sc
-            if keys is not None:
+            if keys is not None and layer.idx_dtype == "fp4":
+                c, sc = csa2.csa2_fp4_pack(torch.from_numpy(keys[s:e]).to(self.dev))
+                layer.idx_keys[rows] = c
+                layer.idx_scales[rows] = sc
+            elif keys is not None:
                 k = keys[s:e] if keys.dtype == np.float32 else keys[s:e].view(np.int16)
                 layer.idx_keys[rows] = torch.from_numpy(np.ascontiguousarray(k)).to(self.dev)
             if rope is not None:
@@ -104,37 +109,50 @@ class Decode:
     def clone_layer(self, layer):
         c = self.csa2.PagedLayer.__new__(self.csa2.PagedLayer)
         c.__dict__.update(layer.__dict__)
-        for k in ("codes", "scales", "rope", "idx_keys"):
+        for k in ("codes", "scales", "rope", "idx_keys", "idx_scales"):
             t = getattr(layer, k)
             setattr(c, k, t.clone() if t is not None else None)
         return c
 
 
 class Decode1M(Decode):
-    """1M-token hierarchical decode: Full + 3 Reindex layers over one shared KV and key pool."""
+    """1M-token hierarchical decode: Full + 3 Reindex layers over one shared KV and key pool.
+
+    Indexer keys are bf16[64] with one fp32 query, or (idx_dtype "fp4") FP4[128]
+    scored by 32 fp16 query heads with fp32 weights."""
 
     def __init__(self, w, replicas, dev, cpu_needed):
         super().__init__(w, replicas, dev)
         torch, csa2, wl = self.torch, self.csa2, self.wl
         n = w.seq_lens[0]
         self.n, self.H, self.K, self.P, self.L = n, w.heads, w.top_k, w.pool_blocks, w.layers
+        self.fp4 = w.idx_dtype == "fp4"
+        self.IH = w.extra.get("idx_heads", 1)
         t0 = time.time()
         self.latent = wl.latent_rows(self.st, 0, 0, n)
-        self.keys = wl.idx_keys(self.st, 0, n, "bf16")
-        self.q_idx = [wl.q_idx(self.st, l, 1) for l in range(self.L)]
+        if self.fp4:
+            self.keys = wl.idx4_keys(self.st, 0, n)
+            self.q_idx = [wl.q_idx_heads(self.st, l, 1, self.IH) for l in range(self.L)]
+            self.w_idx = [wl.w_idx(self.st, l, 1, self.IH) for l in range(self.L)]
+        else:
+            self.keys = wl.idx_keys(self.st, 0, n, "bf16")
+            self.q_idx = [wl.q_idx(self.st, l, 1) for l in range(self.L)]
+            self.w_idx = [None] * self.L
         self.q = [wl.q_heads(self.st, l, 1, self.H, 512) for l in range(self.L)]
         log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
         nb = n // 64
         table = np.arange(nb, dtype=np.int32)
-        base = csa2.PagedLayer(nb, idx_dtype="bf16", device=dev)
+        base = csa2.PagedLayer(nb, idx_dtype=w.idx_dtype, idx_heads=self.IH, device=dev)
         self._fill(base, table, n, latent=self.latent, keys=self.keys)
         self.layers = [base] + [self.clone_layer(base) for _ in range(replicas - 1)]
         bt = torch.from_numpy(table[None].copy()).to(dev)
         self.batch = csa2.Batch(bt, torch.tensor([n], dtype=torch.int32, device=dev), n)
         self.batch_prev = csa2.Batch(bt, torch.tensor([n - 1], dtype=torch.int32, device=dev), n)
         self.new_latent = torch.from_numpy(self.latent[n - 1 : n].copy()).to(dev)
-        self.new_key = torch.from_numpy(self.keys[n - 1 : n].view(np.int16).copy()).to(dev)
+        nk = self.keys[n - 1 : n]
+        self.new_key = torch.from_numpy((nk if self.fp4 else nk.view(np.int16)).copy()).to(dev)
         self.q_idx_d = [torch.from_numpy(q).to(dev) for q in self.q_idx]
+        self.w_idx_d = [torch.from_numpy(x).to(dev) if x is not None else None for x in self.w_idx]
         self.q_d = [torch.from_numpy(q.view(np.int16)).to(dev) for q in self.q]
         self.sel_ws = csa2.workspace(csa2.index_select_workspace_bytes(1, n, self.K, self.P), dev)
         self.attn_ws = csa2.workspace(csa2.attn_workspace_bytes(1, self.H, self.K), dev)
@@ -145,7 +163,10 @@ class Decode1M(Decode):
         self.kf64 = None
         if cpu_needed:
             import oracle
-            self.kf64 = oracle.indexer.keys_to_f64(self.keys, "bf16")
+            if self.fp4:
+                self.kf64 = oracle.indexer.fp4_keys_to_f64(*oracle.fp4.fp4_pack(self.keys))
+            else:
+                self.kf64 = oracle.indexer.keys_to_f64(self.keys, "bf16")
         torch.cuda.synchronize()
 
     queries_per_step = property(lambda self: self.L)
@@ -157,30 +178,39 @@ class Decode1M(Decode):
         for l in range(self.L):
             if l == 0:
                 csa2.csa2_index_select(layer, self.batch, self.q_idx_d[0], self.K, csa2.FULL, pool_blocks=self.P,
-                                       want_pool=True, ws=self.sel_ws, indices=self.idx[0], pool_out=self.pool)
+                                       want_pool=True, ws=self.sel_ws, indices=self.idx[0], pool_out=self.pool,
+                                       w_idx=self.w_idx_d[0])
             else:
                 csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l], self.K, csa2.REINDEX, pool_in=self.pool,
-                                       pool_blocks=self.P, ws=self.sel_ws, indices=self.idx[l])
+                                       pool_blocks=self.P, ws=self.sel_ws, indices=self.idx[l], w_idx=self.w_idx_d[l])
             csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.idx[l], self.w.sigma,
                                              ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
 
+    # indexer key bytes per token (FP4: 64 B of codes + 8 scales) and query bytes per selection
+    key_bytes = property(lambda self: 72 if self.fp4 else 128)
+    qsel_bytes = property(lambda self: self.IH * 128 * 2 + self.IH * 4 if self.fp4 else 64 * 4)
+
     def algorithmic_bytes(self):
         n, K, P, H, L = self.n, self.K, self.P, self.H, self.L
-        scan = n * 128 + 64 * 4
-        reindex = (L - 1) * (P * 8 * 128 + 64 * 4)
+        scan = n * self.key_bytes + self.qsel_bytes
+        reindex = (L - 1) * (P * 8 * self.key_bytes + self.qsel_bytes)
         kv = L * K * 288
         qio = L * (H * 512 * 2 + H * 512 * 4 + H * 4)
-        append = 512 * 4 + 128 + 288 + 128
+        append = 512 * 4 + 288 + (128 * 4 + 72 if self.fp4 else 128 + 128)
         return scan + reindex + kv + qio + append
 
     def dominant_bytes(self):
-        return self.n * 128 + 64 * 4  # every key once + the query
+        return self.n * self.key_bytes + self.qsel_bytes  # every key once + the query
+
+    def dominant_flops(self):
+        return 2 * self.n * self.IH * 128 if self.fp4 else 0  # fp16 MFMA: every key against every head
 
     def oracle_step(self):
         import oracle
 
-        idx, pool = oracle.indexer.full_select(self.q_idx[0][0], self.kf64, self.K, pool_blocks_max=self.P)
-        sel = [idx] + [oracle.indexer.reindex_select(self.q_idx[l][0], self.kf64, self.K, pool)
+        w = [x[0] if x is not None else None for x in self.w_idx]
+        idx, pool = oracle.indexer.full_select(self.q_idx[0][0], self.kf64, self.K, pool_blocks_max=self.P, w=w[0])
+        sel = [idx] + [oracle.indexer.reindex_select(self.q_idx[l][0], self.kf64, self.K, pool, w=w[l])
                        for l in range(1, self.L)]
         outs = []
         for l in range(self.L):
@@ -192,7 +222,8 @@ class Decode1M(Decode):
     def config(self):
         return {"workload": self.w.name, "batch": 1, "seq_len": self.n, "heads": self.H, "top_k": self.K,
                 "pool": f"{self.P}x8", "layers": "1 Full + 3 Reindex", "kv_bytes_per_token": 288,
-                "idx_key": "bf16[64]", "append_per_step": 1, "replicas": self.replicas}
+                "idx_key": f"fp4[128] (64 B codes + 8 E4M3 scales), {self.IH} fp16 query heads" if self.fp4
+                else "bf16[64]", "append_per_step": 1, "replicas": self.replicas}
 
 
 class DecodeBatch(Decode):
@@ -420,9 +451,9 @@ def make(name, replicas, dev, cpu_needed):
     from sparse_attention_fp4_kv_amd import workloads as wl
 
     wid = {"tiny_b1_4k": 1, "decode_b8_64k_rope": 2, "ced_prefill_16k_x20": 3, "decode_1m_hierarchical": 4,
-           "mixed_serving_32_reuse4": 5}[name]
+           "mixed_serving_32_reuse4": 5, "decode_1m_fp4_indexer": 6}[name]
     w = wl.workload(wid)
-    if wid == 4:
+    if wid in (4, 6):
         return Decode1M(w, replicas, dev, cpu_needed)
     if wid == 5:
         return MixedServing(w, replicas, dev, cpu_needed)
@@ -526,7 +557,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     replicas = args.replicas or {"decode_1m_hierarchical": 4, "decode_b8_64k_rope": 6, "mixed_serving_32_reuse4": 3,
-                                 "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1}[args.workload]
+                                 "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1, "decode_1m_fp4_indexer": 4}[args.workload]
     want_cpu = not args.no_cpu_baseline
     wk = make(args.workload, replicas, dev, want_cpu)
     R = wk.replicas
@@ -596,6 +627,9 @@ def main():
         roof = {"bound": "hbm", "achieved": wk.dominant_bytes() / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if getattr(wk, "dominant_flops", lambda: 0)():
+        tf = wk.dominant_flops() / (kern_ms * 1e-3) / 1e12
+        roof["mfma_tflops"], roof["mfma_frac"] = tf, tf / BF16_PEAK_TFLOPS  # fp16 dense peak = bf16's
     roof["kernel"] = wk.dominant
     roof["kernel_ms"] = kern_ms
     roof["traffic"] = None

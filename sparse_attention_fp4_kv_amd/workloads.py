@@ -57,7 +57,8 @@ def _loguniform_lens(n, lo, hi, seed_seq):
 
 
 def workload(wid):
-    """The five workloads (tiny plumbing, 8 x 64K decode, CED prefill, 1M hierarchical, mixed serving)."""
+    """The workloads (tiny plumbing, 8 x 64K decode, CED prefill, 1M hierarchical, mixed serving, and the 1M
+    hierarchical case with the multi-head FP4 indexer)."""
     if wid == 1:
         return Workload(1, "tiny_b1_4k", batch=1, heads=16, top_k=256, sigma=1 / math.sqrt(512),
                         seq_lens=(4096,), idx_dtype="f32")
@@ -76,6 +77,11 @@ def workload(wid):
         return Workload(5, "mixed_serving_32_reuse4", batch=32, heads=64, top_k=2048, sigma=1 / math.sqrt(512),
                         seq_lens=lens, idx_dtype="bf16", permuted_tables=True, layers=4, reuse_layers=3,
                         kv_pools=4, append=True)
+    if wid == 6:
+        # the 1M-token case with the multi-head indexer: FP4 keys of 128 dims, 32 query heads
+        return Workload(6, "decode_1m_fp4_indexer", batch=1, heads=64, top_k=2048, sigma=1 / math.sqrt(512),
+                        seq_lens=(1 << 20,), idx_dtype="fp4", hierarchical=True, layers=4, reindex_layers=3,
+                        extra=dict(idx_heads=IDX4_HEADS))
     raise ValueError(wid)
 
 
