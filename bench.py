@@ -11,8 +11,10 @@ Other workloads (--workload): decode_b8_64k_rope (8 x 65,536 tokens, rope
 side-band, permuted page tables, one Full layer), mixed_serving_32_reuse4 (32
 requests with log-uniform lengths, append to 4 KV layers, one Full selection
 reused by 4 attentions), ced_prefill_16k_x20 (CED projection GEMM with the
-fused pack), tiny_b1_4k, decode_1m_fp4_indexer (the 1M case with FP4 indexer
-keys of 128 dims scored by 32 weighted query heads).
+fused pack; ced_prefill_16k_x20_h5120 at hidden 5120), tiny_b1_4k,
+decode_1m_fp4_indexer (the 1M case with FP4 indexer keys of 128 dims scored by
+32 weighted query heads), decode_1m_decoder_x20 (the decoder's 20-layer
+Full / Reindex / Reuse schedule at top-K 512 over one KV source).
 
 Timing: inputs are resident in HBM; R replicas of the cache rotate so every
 step reads data evicted from the 256 MB last-level cache; each replica's step
@@ -41,7 +43,7 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 METRIC = "sparse FP4-KV decode attn queries/s + achieved HBM GB/s vs MI355X peak"
 WORKLOADS = ("decode_1m_hierarchical", "decode_b8_64k_rope", "mixed_serving_32_reuse4", "ced_prefill_16k_x20",
-             "tiny_b1_4k", "decode_1m_fp4_indexer")
+             "tiny_b1_4k", "decode_1m_fp4_indexer", "decode_1m_decoder_x20", "ced_prefill_16k_x20_h5120")
 
 
 def log(*a):
@@ -226,6 +228,65 @@ class Decode1M(Decode):
                 else "bf16[64]", "append_per_step": 1, "replicas": self.replicas}
 
 
+class DecoderX20(Decode1M):
+    """The decoder's schedule at its own shapes: 20 layers over one KV source in 5 groups of 4; the first
+    group's lead layer is Full (and builds the 2048 x 8 pool), the other groups' lead layers Reindex the
+    pool, and the 3 other layers of each group Reuse their lead's indices.  Top-K 512, FP4 indexer keys
+    scored by 32 query heads, 64 attention heads per layer."""
+
+    def __init__(self, w, replicas, dev, cpu_needed):
+        super().__init__(w, replicas, dev, cpu_needed)
+        self.G = w.extra["group_size"]
+        self.leads = list(range(0, self.L, self.G))
+        self.gidx = self.torch.empty((len(self.leads), 1, self.K), dtype=self.torch.int32, device=dev)
+
+    def step(self, r):
+        csa2, layer = self.csa2, self.layers[r]
+        csa2.csa2_kv_append(layer, self.batch_prev, self.new_latent, idx_key=self.new_key)
+        for g, l0 in enumerate(self.leads):
+            if g == 0:
+                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l0], self.K, csa2.FULL, pool_blocks=self.P,
+                                       want_pool=True, ws=self.sel_ws, indices=self.gidx[g], pool_out=self.pool,
+                                       w_idx=self.w_idx_d[l0])
+            else:
+                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l0], self.K, csa2.REINDEX, pool_in=self.pool,
+                                       pool_blocks=self.P, ws=self.sel_ws, indices=self.gidx[g],
+                                       w_idx=self.w_idx_d[l0])
+            for l in range(l0, l0 + self.G):  # the lead and its Reuse layers
+                csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
+                                                 ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
+
+    def algorithmic_bytes(self):
+        n, K, P, H, L = self.n, self.K, self.P, self.H, self.L
+        scan = n * self.key_bytes + self.qsel_bytes
+        reindex = (len(self.leads) - 1) * (P * 8 * self.key_bytes + self.qsel_bytes)
+        kv = L * K * 288
+        qio = L * (H * 512 * 2 + H * 512 * 4 + H * 4)
+        append = 512 * 4 + 288 + 128 * 4 + 72
+        return scan + reindex + kv + qio + append
+
+    def oracle_step(self):
+        import oracle
+
+        w = [x[0] for x in self.w_idx]
+        idx, pool = oracle.indexer.full_select(self.q_idx[0][0], self.kf64, self.K, pool_blocks_max=self.P, w=w[0])
+        sel = {0: idx}
+        for l0 in self.leads[1:]:
+            sel[l0] = oracle.indexer.reindex_select(self.q_idx[l0][0], self.kf64, self.K, pool, w=w[l0])
+        outs = []
+        for l0 in self.leads:
+            v = oracle.attention.valid_slots(oracle.indexer.reuse_select(sel[l0]), self.n)
+            c = oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(self.latent[v]))
+            for l in range(l0, l0 + self.G):
+                outs.append(oracle.attention.sparse_attention(self.q[l][0], c, self.w.sigma))
+        return outs
+
+    def config(self):
+        c = super().config()
+        c["layers"] = "20 in 5 groups of 4: Full + 3 Reuse, then 4 x (Reindex + 3 Reuse), one KV source"
+        return c
+
+
 class DecodeBatch(Decode):
     """Batched decode with one Full selection per step and attention (config 2 style; tiny case too)."""
 
@@ -396,7 +457,7 @@ class MixedServing(Decode):
 
 
 class CedPrefill:
-    """CED projection of 16,384 tokens x 4096 hidden into 20 layers (512 FP4 + 64 bf16 channels each)."""
+    """CED projection of 16,384 tokens x hidden (4096 or 5120) into 20 layers (512 FP4 + 64 bf16 channels each)."""
 
     def __init__(self, w, replicas, dev, cpu_needed):
         import torch
@@ -451,13 +512,16 @@ def make(name, replicas, dev, cpu_needed):
     from sparse_attention_fp4_kv_amd import workloads as wl
 
     wid = {"tiny_b1_4k": 1, "decode_b8_64k_rope": 2, "ced_prefill_16k_x20": 3, "decode_1m_hierarchical": 4,
-           "mixed_serving_32_reuse4": 5, "decode_1m_fp4_indexer": 6}[name]
+           "mixed_serving_32_reuse4": 5, "decode_1m_fp4_indexer": 6, "decode_1m_decoder_x20": 7,
+           "ced_prefill_16k_x20_h5120": 8}[name]
     w = wl.workload(wid)
+    if wid == 7:
+        return DecoderX20(w, replicas, dev, cpu_needed)
     if wid in (4, 6):
         return Decode1M(w, replicas, dev, cpu_needed)
     if wid == 5:
         return MixedServing(w, replicas, dev, cpu_needed)
-    if wid == 3:
+    if wid in (3, 8):
         return CedPrefill(w, replicas, dev, cpu_needed)
     return DecodeBatch(w, replicas, dev, cpu_needed)
 
@@ -499,7 +563,9 @@ def cpu_baseline(wk, budget_s):
                 wk.oracle_step()
                 calls += 1
                 queries += wk.L
-            sample = f"{calls} full 4-layer steps (1M-token scan, pool, 3 Reindex, 4 attentions)"
+            sample = (f"{calls} full 20-layer steps (1M-token scan, pool, 4 Reindex, 20 attentions)"
+                      if isinstance(wk, DecoderX20) else
+                      f"{calls} full 4-layer steps (1M-token scan, pool, 3 Reindex, 4 attentions)")
         else:
             b = 0
             while calls < 1 or time.time() - t0 < budget_s:
@@ -557,7 +623,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     replicas = args.replicas or {"decode_1m_hierarchical": 4, "decode_b8_64k_rope": 6, "mixed_serving_32_reuse4": 3,
-                                 "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1, "decode_1m_fp4_indexer": 4}[args.workload]
+                                 "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1, "decode_1m_fp4_indexer": 4,
+                                 "decode_1m_decoder_x20": 4, "ced_prefill_16k_x20_h5120": 1}[args.workload]
     want_cpu = not args.no_cpu_baseline
     wk = make(args.workload, replicas, dev, want_cpu)
     R = wk.replicas

@@ -57,8 +57,9 @@ def _loguniform_lens(n, lo, hi, seed_seq):
 
 
 def workload(wid):
-    """The workloads (tiny plumbing, 8 x 64K decode, CED prefill, 1M hierarchical, mixed serving, and the 1M
-    hierarchical case with the multi-head FP4 indexer)."""
+    """The workloads (tiny plumbing, 8 x 64K decode, CED prefill, 1M hierarchical, mixed serving, the 1M
+    hierarchical case with the multi-head FP4 indexer, the 20-layer decoder schedule at top-K 512, CED at
+    hidden 5120)."""
     if wid == 1:
         return Workload(1, "tiny_b1_4k", batch=1, heads=16, top_k=256, sigma=1 / math.sqrt(512),
                         seq_lens=(4096,), idx_dtype="f32")
@@ -82,6 +83,16 @@ def workload(wid):
         return Workload(6, "decode_1m_fp4_indexer", batch=1, heads=64, top_k=2048, sigma=1 / math.sqrt(512),
                         seq_lens=(1 << 20,), idx_dtype="fp4", hierarchical=True, layers=4, reindex_layers=3,
                         extra=dict(idx_heads=IDX4_HEADS))
+    if wid == 7:
+        # the decoder's own shapes: top-K 512, 20 layers over one KV source in 5 groups of 4 (the first group
+        # Full + 3 Reuse, the others Reindex + 3 Reuse), multi-head FP4 indexer
+        return Workload(7, "decode_1m_decoder_x20", batch=1, heads=64, top_k=512, sigma=1 / math.sqrt(512),
+                        seq_lens=(1 << 20,), idx_dtype="fp4", hierarchical=True, layers=20, reindex_layers=4,
+                        reuse_layers=15, extra=dict(idx_heads=IDX4_HEADS, group_size=4))
+    if wid == 8:
+        # CED projection at the model's hidden size 5120
+        return Workload(8, "ced_prefill_16k_x20_h5120", batch=0, heads=0, top_k=0, sigma=0.0,
+                        extra=dict(tokens=16384, hidden=5120, layers=20, kv=512, z=64))
     raise ValueError(wid)
 
 

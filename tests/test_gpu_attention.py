@@ -69,6 +69,11 @@ def test_ragged_topk(K):
     _run_and_check([6000], 64, K)
 
 
+def test_decoder_topk512():
+    """The decoder's top-K of 512 entries, 64 heads, long sequences."""
+    _run_and_check([65536, 100000], 64, 512, seed=53)
+
+
 def test_invalid_and_empty_selections():
     seq_lens = [500, 10, 300]
     K = 64

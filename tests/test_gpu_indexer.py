@@ -94,7 +94,7 @@ def test_full_select(dtype, permuted):
     st, tables, keys, layer = _keys_layer(seq_lens, dtype, permuted, 41)
     q = wl.q_idx(st, 0, len(seq_lens))
     batch = make_batch(tables, seq_lens, max(seq_lens))
-    for K in (256, 2048):
+    for K in (256, 512, 2048):
         idx, _ = csa2.csa2_index_select(layer, batch, to_dev(q), K, csa2.FULL)
         torch.cuda.synchronize()
         idx = idx.cpu().numpy()
@@ -103,9 +103,10 @@ def test_full_select(dtype, permuted):
             check_topk(idx[b], dict(enumerate(s)), K, where=f"K={K} b={b}")
 
 
-def test_hierarchical_pool_and_reindex():
+@pytest.mark.parametrize("K", [512, 2048])
+def test_hierarchical_pool_and_reindex(K):
     seq_lens = [200000, 16384, 50, 70001]
-    P, K = 2048, 2048
+    P = 2048
     st, tables, keys, layer = _keys_layer(seq_lens, "bf16", True, 42)
     q0 = wl.q_idx(st, 0, len(seq_lens))
     q1 = wl.q_idx(st, 1, len(seq_lens))
@@ -300,7 +301,7 @@ def test_fp4_full_select(permuted):
     st, tables, keys, layer = _fp4_layer(seq_lens, 32, permuted, 51)
     q, w = wl.q_idx_heads(st, 0, len(seq_lens)), wl.w_idx(st, 0, len(seq_lens))
     batch = make_batch(tables, seq_lens, max(seq_lens))
-    for K in (256, 2048):
+    for K in (256, 512, 2048):
         idx, _ = csa2.csa2_index_select(layer, batch, to_dev(q), K, csa2.FULL, w_idx=to_dev(w))
         torch.cuda.synchronize()
         idx = idx.cpu().numpy()
@@ -309,9 +310,10 @@ def test_fp4_full_select(permuted):
             check_topk(idx[b], dict(enumerate(s)), K, where=f"K={K} b={b}")
 
 
-def test_fp4_hierarchical_pool_and_reindex():
+@pytest.mark.parametrize("K", [512, 2048])
+def test_fp4_hierarchical_pool_and_reindex(K):
     seq_lens = [200000, 16384, 50, 70001]
-    P, K = 2048, 2048
+    P = 2048
     st, tables, keys, layer = _fp4_layer(seq_lens, 32, True, 52)
     q0, w0 = wl.q_idx_heads(st, 0, len(seq_lens)), wl.w_idx(st, 0, len(seq_lens))
     q1, w1 = wl.q_idx_heads(st, 1, len(seq_lens)), wl.w_idx(st, 1, len(seq_lens))
