@@ -28,9 +28,11 @@ Modules:
   indexer    indexer scores, top-K, the hierarchical block pool, Reindex, Reuse.
   attention  sparse decode attention over dequantized FP4 entries.
   paged      paged-cache addressing and the bytes-per-token arithmetic.
+  latent     RMSNorm + RoPE of a KV latent before the pack, and the indexer key
+             projected from the cached entry.
 
 Parity status of every function is stated in its docstring; the pins live in
 ``tests/test_oracle_*.py`` and ``tests/golden/``.
 """
 
-from . import fp4, ced, indexer, attention, paged  # noqa: F401
+from . import fp4, ced, indexer, attention, paged, latent  # noqa: F401
