@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 2
+#define CSA2_ABI_VERSION 3
 
 typedef enum {
   CSA2_OK = 0,
@@ -154,6 +154,56 @@ csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, co
 csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,
                                 const uint16_t *w_kv, const uint16_t *w_z, uint8_t *codes,
                                 uint8_t *scales, uint16_t *z, float *c_f32, csa2_stream stream);
+
+/* ---- Finishing a KV latent before it is cached, and the indexer key taken
+ * from the cached entry.  [P1] "FP4 KV cache": the 512-channel latent is
+ * RMS-normalised (learned weight) and rotated by RoPE before the FP4 pack;
+ * [P1] "CSA2": a Full layer's indexer K is a projection of the main KV (32
+ * indexer heads of dimension 128) and V4 keeps indexer keys in FP4.  This
+ * library's reading of what the pages leave open, for a raw latent x at token
+ * position p:
+ *   y_j = x_j / sqrt(mean_j x_j^2 + eps) * gamma_j            (j < 512)
+ *   channels 448 + 2i, 449 + 2i (i < 32) turned by the fp32 angle
+ *   fl32(p * fl32(theta^(-2i/64))): (a, b) -> (a cos - b sin, a sin + b cos)
+ *   entry = FP4 pack of y (csa2_fp4_pack rules)
+ *   key   = FP4 pack of W_idx * dequant(entry)  (128 dims; 64 code bytes +
+ *           8 scales, the CSA2_FP4 indexer-key layout)
+ * fp32 arithmetic; p is taken exactly below 2^24. */
+typedef struct {
+  const float *gamma;     /* device fp32 [n_layers][512] RMSNorm weights */
+  float eps;              /* RMSNorm epsilon, > 0 */
+  float rope_theta;       /* RoPE base, > 0, or 0 for no rotation */
+  const uint16_t *w_idx;  /* device bf16 [n_layers][128][512] (out x in), or NULL: no key */
+} csa2_kv_finish;
+
+/* Finishes rows c[l][t] (device fp32 [n_layers][tokens][512], position
+ * pos0 + t, layer l's gamma and W_idx) into codes [n_layers][tokens][256] and
+ * scales [..][32], and, with fin->w_idx, idx_codes [..][64] and idx_scales
+ * [..][8].  x_f32 [..][512] (finished latent before packing) and k_f32
+ * [..][128] (key before packing) are optional fp32 copies (NULL: skipped).
+ * tokens, n_layers >= 0; pos0 >= 0 and pos0 + tokens <= 2^24. */
+csa2_status csa2_kv_finish_rows(const float *c, int64_t tokens, int32_t n_layers, int64_t pos0,
+                                const csa2_kv_finish *fin, uint8_t *codes, uint8_t *scales,
+                                uint8_t *idx_codes, uint8_t *idx_scales, float *x_f32, float *k_f32,
+                                csa2_stream stream);
+
+/* csa2_ced_kv_project with the finish: C_l = H W_l^KV (fp32 accumulators,
+ * written to c_f32 [n_layers][tokens][512], required: it is the hand-over
+ * buffer) and then csa2_kv_finish_rows on C (token t at position pos0 + t).
+ * No Z: the indexer key comes from the main KV. */
+csa2_status csa2_ced_kv_project_finished(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,
+                                         const uint16_t *w_kv, const csa2_kv_finish *fin, int64_t pos0,
+                                         float *c_f32, uint8_t *codes, uint8_t *scales, uint8_t *idx_codes,
+                                         uint8_t *idx_scales, csa2_stream stream);
+
+/* csa2_kv_append with the finish: for every sequence b the raw latent[b]
+ * (device fp32 [batch][512]) at position p = seq_lens[b] is finished and
+ * stored in p's slot; with fin->w_idx (gamma [512], w_idx [128][512] of this
+ * layer) its FP4 indexer key is stored beside it.  The layer has no rope
+ * side-band (the rotation lives inside the latent); it has CSA2_FP4 indexer
+ * keys exactly when fin->w_idx is given.  Unmapped pages are skipped. */
+csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
+                                    const csa2_kv_finish *fin, csa2_stream stream);
 
 /* ---- Indexer scores alone (the scoring step of [P1] "CSA2").  For
  * t < seq_lens[b], with k = the stored key of position t:

@@ -55,6 +55,17 @@ class Seqs(ctypes.Structure):
     ]
 
 
+class KvFinish(ctypes.Structure):
+    """csa2_kv_finish: RMSNorm weights, epsilon, RoPE base and the indexer-key projection."""
+
+    _fields_ = [
+        ("gamma", ctypes.c_void_p),
+        ("eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_float),
+        ("w_idx", ctypes.c_void_p),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -72,6 +83,11 @@ SIGNATURES = {
     "csa2_fp4_unpack": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P]),
     "csa2_kv_append": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P, _P]),
     "csa2_ced_kv_project": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "csa2_kv_finish_rows": (ctypes.c_int, [_P, _I64, _I32, _I64, ctypes.POINTER(KvFinish), _P, _P, _P, _P, _P, _P,
+                                           _P]),
+    "csa2_ced_kv_project_finished": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, ctypes.POINTER(KvFinish), _I64, _P,
+                                                    _P, _P, _P, _P, _P]),
+    "csa2_kv_append_finished": (ctypes.c_int, [_PKV, _PSQ, _P, ctypes.POINTER(KvFinish), _P]),
     "csa2_index_scores": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P, _P]),
     "csa2_topk_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_topk": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
@@ -259,6 +275,57 @@ def csa2_ced_kv_project(h, w_kv, w_z=None, c_f32=False):
     _check(lib().csa2_ced_kv_project(_ptr(h), T, hidden, L, _ptr(w_kv), _ptr(w_z), _ptr(codes), _ptr(scales), _ptr(z),
                                      _ptr(c), _stream()), "csa2_ced_kv_project")
     return codes, scales, z, c
+
+
+def _finish(gamma, eps, theta, w_idx):
+    _require(gamma, torch.float32, "gamma")
+    return KvFinish(gamma=gamma.data_ptr(), eps=eps, rope_theta=theta,
+                    w_idx=w_idx.data_ptr() if w_idx is not None else None)
+
+
+def csa2_kv_finish_rows(c, gamma, eps, theta, w_idx=None, pos0=0, debug=False):
+    """c fp32 [L, T, 512] raw latents; gamma fp32 [L, 512]; w_idx bf16 bits [L, 128, 512] (int16) or None.
+
+    Returns (codes [L,T,256], scales [L,T,32], idx_codes [L,T,64] | None, idx_scales [L,T,8] | None,
+    x_f32 [L,T,512] | None, k_f32 [L,T,128] | None); the fp32 copies only with debug."""
+    _require(c, torch.float32, "c")
+    L, T, _ = c.shape
+    dev = c.device
+    codes = torch.empty((L, T, 256), dtype=torch.uint8, device=dev)
+    scales = torch.empty((L, T, 32), dtype=torch.uint8, device=dev)
+    kc = torch.empty((L, T, 64), dtype=torch.uint8, device=dev) if w_idx is not None else None
+    ks = torch.empty((L, T, 8), dtype=torch.uint8, device=dev) if w_idx is not None else None
+    x = torch.empty((L, T, 512), dtype=torch.float32, device=dev) if debug else None
+    k = torch.empty((L, T, 128), dtype=torch.float32, device=dev) if debug and w_idx is not None else None
+    fin = _finish(gamma, eps, theta, w_idx)
+    _check(lib().csa2_kv_finish_rows(_ptr(c), T, L, pos0, ctypes.byref(fin), _ptr(codes), _ptr(scales), _ptr(kc),
+                                     _ptr(ks), _ptr(x), _ptr(k), _stream()), "csa2_kv_finish_rows")
+    return codes, scales, kc, ks, x, k
+
+
+def csa2_ced_kv_project_finished(h, w_kv, gamma, eps, theta, w_idx=None, pos0=0):
+    """CED projection followed by the finish; returns (codes, scales, idx_codes | None, idx_scales | None, c_f32)."""
+    T, hidden = h.shape
+    L = w_kv.shape[0]
+    dev = h.device
+    c = torch.empty((L, T, 512), dtype=torch.float32, device=dev)
+    codes = torch.empty((L, T, 256), dtype=torch.uint8, device=dev)
+    scales = torch.empty((L, T, 32), dtype=torch.uint8, device=dev)
+    kc = torch.empty((L, T, 64), dtype=torch.uint8, device=dev) if w_idx is not None else None
+    ks = torch.empty((L, T, 8), dtype=torch.uint8, device=dev) if w_idx is not None else None
+    fin = _finish(gamma, eps, theta, w_idx)
+    _check(lib().csa2_ced_kv_project_finished(_ptr(h), T, hidden, L, _ptr(w_kv), ctypes.byref(fin), pos0, _ptr(c),
+                                              _ptr(codes), _ptr(scales), _ptr(kc), _ptr(ks), _stream()),
+           "csa2_ced_kv_project_finished")
+    return codes, scales, kc, ks, c
+
+
+def csa2_kv_append_finished(layer, batch, latent, gamma, eps, theta, w_idx=None):
+    """Raw latent fp32 [B, 512] finished into the slot of position seq_lens[b]; gamma [512], w_idx [128, 512]."""
+    kv, sq = layer.struct(), batch.struct()
+    fin = _finish(gamma, eps, theta, w_idx)
+    _check(lib().csa2_kv_append_finished(ctypes.byref(kv), ctypes.byref(sq), _ptr(latent), ctypes.byref(fin),
+                                         _stream()), "csa2_kv_append_finished")
 
 
 def csa2_index_scores(layer, batch, q_idx, max_len, w_idx=None):

@@ -91,7 +91,7 @@ ArmedTimer g_timer;
 
 const char *const kKernelNames[kKernCount] = {"index_scan",  "pool_score",   "topk_given", "topk_compact",
                                               "sparse_attn", "attn_combine", "ced_project", "fp4_pack",
-                                              "kv_append",   "index_scores"};
+                                              "kv_append",   "index_scores", "kv_finish"};
 
 }  // namespace
 
@@ -182,6 +182,85 @@ csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, co
   if (latent != nullptr && L.rope_dim != 0 && rope == nullptr) return CSA2_ERR_INVALID_ARG;
   if (idx_key != nullptr && !keys_ok(layer)) return CSA2_ERR_INVALID_ARG;
   return from_hip(launch_kv_append(L, S, latent, rope, idx_key, as_stream(stream)));
+}
+
+namespace {
+csa2_status check_finish(const csa2_kv_finish *fin, csa2::KvFinish *out) {
+  if (fin == nullptr || fin->gamma == nullptr || !aligned(fin->gamma, 16)) return CSA2_ERR_INVALID_ARG;
+  if (!(fin->eps > 0.0f) || !(fin->eps < 3.0e38f)) return CSA2_ERR_INVALID_ARG;
+  if (!(fin->rope_theta >= 0.0f) || !(fin->rope_theta < 3.0e38f)) return CSA2_ERR_INVALID_ARG;
+  if (fin->w_idx != nullptr && !aligned(fin->w_idx, 16)) return CSA2_ERR_INVALID_ARG;
+  *out = csa2::KvFinish{fin->gamma, fin->eps, fin->rope_theta, fin->w_idx};
+  return CSA2_OK;
+}
+
+csa2_status check_finish_rows(int64_t tokens, int32_t n_layers, int64_t pos0, const csa2_kv_finish *fin,
+                              uint8_t *codes, uint8_t *scales, uint8_t *idx_codes, uint8_t *idx_scales,
+                              const float *x_f32, const float *k_f32, csa2::KvFinish *f) {
+  if (tokens < 0 || n_layers < 0 || n_layers > 4096 || pos0 < 0) return CSA2_ERR_INVALID_ARG;
+  if (pos0 + tokens > ((int64_t)1 << 24)) return CSA2_ERR_INVALID_ARG;
+  csa2_status st = check_finish(fin, f);
+  if (st != CSA2_OK) return st;
+  if (codes == nullptr || scales == nullptr || !aligned(codes, 4)) return CSA2_ERR_INVALID_ARG;
+  if (fin->w_idx != nullptr) {
+    if (idx_codes == nullptr || idx_scales == nullptr || !aligned(idx_codes, 8)) return CSA2_ERR_INVALID_ARG;
+  } else if (idx_codes != nullptr || idx_scales != nullptr || k_f32 != nullptr) {
+    return CSA2_ERR_INVALID_ARG;
+  }
+  if ((x_f32 && !aligned(x_f32, 16)) || (k_f32 && !aligned(k_f32, 16))) return CSA2_ERR_INVALID_ARG;
+  return CSA2_OK;
+}
+}  // namespace
+
+csa2_status csa2_kv_finish_rows(const float *c, int64_t tokens, int32_t n_layers, int64_t pos0,
+                                const csa2_kv_finish *fin, uint8_t *codes, uint8_t *scales, uint8_t *idx_codes,
+                                uint8_t *idx_scales, float *x_f32, float *k_f32, csa2_stream stream) {
+  KvFinish f;
+  csa2_status st = check_finish_rows(tokens, n_layers, pos0, fin, codes, scales, idx_codes, idx_scales, x_f32,
+                                     k_f32, &f);
+  if (st != CSA2_OK) return st;
+  if (tokens == 0 || n_layers == 0) return CSA2_OK;
+  if (c == nullptr || !aligned(c, 16)) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_kv_finish_rows(c, tokens, n_layers, pos0, f, codes, scales, idx_codes, idx_scales, x_f32,
+                                        k_f32, as_stream(stream)));
+}
+
+csa2_status csa2_ced_kv_project_finished(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,
+                                         const uint16_t *w_kv, const csa2_kv_finish *fin, int64_t pos0,
+                                         float *c_f32, uint8_t *codes, uint8_t *scales, uint8_t *idx_codes,
+                                         uint8_t *idx_scales, csa2_stream stream) {
+  if (hidden <= 0 || hidden % 64 != 0 || tokens > (int64_t)1 << 31) return CSA2_ERR_INVALID_ARG;
+  KvFinish f;
+  csa2_status st = check_finish_rows(tokens, n_layers, pos0, fin, codes, scales, idx_codes, idx_scales, nullptr,
+                                     nullptr, &f);
+  if (st != CSA2_OK) return st;
+  if (tokens == 0 || n_layers == 0) return CSA2_OK;
+  if (h == nullptr || w_kv == nullptr || c_f32 == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (!aligned(h, 16) || !aligned(w_kv, 16) || !aligned(c_f32, 16)) return CSA2_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_ced_project(h, tokens, hidden, n_layers, w_kv, nullptr, nullptr, nullptr, nullptr, c_f32, s);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(launch_kv_finish_rows(c_f32, tokens, n_layers, pos0, f, codes, scales, idx_codes, idx_scales,
+                                        nullptr, nullptr, s));
+}
+
+csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
+                                    const csa2_kv_finish *fin, csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  KvFinish f;
+  csa2_status st = check_layer(layer, true, false, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if ((st = check_finish(fin, &f)) != CSA2_OK) return st;
+  if (L.rope_dim != 0 || !aligned(layer->codes, 4)) return CSA2_ERR_INVALID_ARG;
+  const bool fp4_keys = layer->idx_keys != nullptr && layer->idx_dtype == CSA2_FP4;
+  if (fp4_keys != (fin->w_idx != nullptr)) return CSA2_ERR_INVALID_ARG;
+  if (fp4_keys && !keys_ok(layer)) return CSA2_ERR_INVALID_ARG;
+  if (!fp4_keys && layer->idx_keys != nullptr) return CSA2_ERR_INVALID_ARG;
+  if (S.batch == 0) return CSA2_OK;
+  if (latent == nullptr || !aligned(latent, 16)) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_kv_append_finish(L, S, latent, f, as_stream(stream)));
 }
 
 csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,

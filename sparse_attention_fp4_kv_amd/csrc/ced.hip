@@ -161,10 +161,12 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
       const int l = n / kNPerLayer, c = n % kNPerLayer;
       const size_t row = (size_t)l * a.tokens + t;
       if (c < kLatent) {
-        uint32_t w0, w1;
-        const uint32_t sc = pack_group16(v, &w0, &w1);
-        reinterpret_cast<uint2 *>(a.codes + row * (kLatent / 2))[c / kGroup] = make_uint2(w0, w1);
-        a.scales[row * (kLatent / kGroup) + c / kGroup] = (uint8_t)sc;
+        if (a.codes != nullptr) {  // null: the caller finishes C (norm, rotation) before packing
+          uint32_t w0, w1;
+          const uint32_t sc = pack_group16(v, &w0, &w1);
+          reinterpret_cast<uint2 *>(a.codes + row * (kLatent / 2))[c / kGroup] = make_uint2(w0, w1);
+          a.scales[row * (kLatent / kGroup) + c / kGroup] = (uint8_t)sc;
+        }
         if (a.c_f32 != nullptr) {
           float4 *dst = reinterpret_cast<float4 *>(a.c_f32 + row * kLatent + c);
 #pragma unroll

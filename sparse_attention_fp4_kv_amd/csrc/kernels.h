@@ -20,6 +20,7 @@ enum KernelId {
   kKernFp4Pack,
   kKernKvAppend,
   kKernIndexScores,
+  kKernKvFinish,
   kKernCount
 };
 // Records the armed event pair around the next launch of `id` (no-op otherwise).
@@ -84,6 +85,20 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
                               hipStream_t st);
 
 // ---- CED projection (ced.hip)
+// Latent finish (RMSNorm, RoPE, FP4 pack) and the FP4 indexer key projected
+// from the cached entry.
+struct KvFinish {
+  const float *gamma;      // [layers][512]
+  float eps;               // > 0
+  float theta;             // RoPE base, 0: no rotation
+  const uint16_t *w_idx;   // [layers][128][512] bf16, or null
+};
+hipError_t launch_kv_finish_rows(const float *c, int64_t tokens, int n_layers, int64_t pos0, const KvFinish &fin,
+                                 uint8_t *codes, uint8_t *scales, uint8_t *k_codes, uint8_t *k_scales, float *x_f32,
+                                 float *k_f32, hipStream_t st);
+hipError_t launch_kv_append_finish(const KvLayerDev &L, const SeqsDev &S, const float *latent, const KvFinish &fin,
+                                   hipStream_t st);
+
 hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int n_layers, const uint16_t *w_kv,
                               const uint16_t *w_z, uint8_t *codes, uint8_t *scales, uint16_t *z, float *c_f32,
                               hipStream_t st);

@@ -98,7 +98,7 @@ def workload(wid):
 
 # Stream names, in spawn order.  Appending new names at the end keeps old streams stable.
 _NAMES = ("lens", "latent", "outliers", "idx_keys", "q_idx", "q", "rope", "tables", "append", "ced_h",
-          "ced_wkv", "ced_wz", "misc", "idx_keys4", "q_idx4", "w_idx")
+          "ced_wkv", "ced_wz", "misc", "idx_keys4", "q_idx4", "w_idx", "gamma", "w_idx_kv")
 
 
 class Streams:
@@ -154,6 +154,14 @@ def q_idx_heads(st, layer, batch, heads=IDX4_HEADS, dim=IDX4_DIM):
 def w_idx(st, layer, batch, heads=IDX4_HEADS):
     """fp32 [batch][heads] per-head indexer weights: N(0, 1 / heads)."""
     return st.gen("w_idx", layer).standard_normal((batch, heads), dtype=np.float32) / np.float32(math.sqrt(heads))
+
+
+def kv_finish_inputs(st, layers, key_dim=IDX4_DIM):
+    """RMSNorm weights fp32 [layers][512] ~ U(0.25, 1) and the indexer-key projection from the main KV,
+    bf16 bits [layers][128][512] ~ N(0, 1/512) (out x in)."""
+    gamma = st.gen("gamma").uniform(0.25, 1.0, size=(layers, LATENT)).astype(np.float32)
+    w = st.gen("w_idx_kv").standard_normal((layers, key_dim, LATENT), dtype=np.float32) / np.float32(math.sqrt(LATENT))
+    return gamma, to_bf16_bits(w)
 
 
 def rope_rows(st, layer, seq, n, dim):

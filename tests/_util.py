@@ -100,3 +100,40 @@ def oracle_attention_rows(latent, ropes, q_bits, sel, n, sigma):
     c = oracle.fp4.fp4_unpack(codes, scales)
     rope = oracle.ced.bf16_bits_to_f64(ropes[valid]) if ropes is not None else None
     return oracle.attention.sparse_attention(q_bits, c, sigma, rope_sel=rope)
+
+
+def pack_close(codes_g, scales_g, x_ref, rel=1e-5, abs_=1e-6):
+    """FP4 bytes from the GPU (codes [n][C/2], scales [n][C/16]) against the oracle's pack of x_ref
+    (float64 [n][C], computed by the oracle in exact arithmetic): a group may differ only where x_ref
+    sits within `rel` of a decision point (the scale's rounding boundary or an element threshold), or
+    a differing sign belongs to a value within `abs_` of zero.  Returns the number of differing groups."""
+    fp4 = oracle.fp4
+    x = np.asarray(x_ref, dtype=np.float64)
+    n, C = x.shape
+    oc, os_ = fp4.fp4_pack(x.astype(np.float32))
+    codes_g, scales_g = np.asarray(codes_g), np.asarray(scales_g)
+
+    def nibbles(c):
+        return np.stack([c & 0xF, c >> 4], axis=-1).reshape(n, C).astype(np.int64)
+
+    ng, no = nibbles(codes_g), nibbles(oc)
+    gd = (scales_g != os_) | np.any((ng != no).reshape(n, C // 16, 16), axis=-1)
+    for r, g in zip(*np.nonzero(gd)):
+        xs = x[r, 16 * g:16 * g + 16]
+        amax = float(np.max(np.abs(xs)))
+        sg = int(scales_g[r, g])
+        if sg != int(os_[r, g]):
+            cand = {int(fp4.e4m3_encode(np.float64(amax * (1 - rel) / 6))), int(fp4.e4m3_encode(np.float64(amax * (1 + rel) / 6)))}
+            assert sg in cand, f"row {r} group {g}: scale {sg:#x}, oracle {int(os_[r, g]):#x}, amax {amax}"
+        s = float(fp4.e4m3_decode(np.uint8(sg)))
+        for i in np.nonzero(ng[r, 16 * g:16 * g + 16] != (no[r, 16 * g:16 * g + 16] if sg == int(os_[r, g]) else -1))[0]:
+            v = xs[i]
+            got = int(ng[r, 16 * g + i])
+            if s == 0:
+                assert got == 0, f"row {r} group {g}: nibble {got:#x} under a zero scale"
+                continue
+            lo = int(fp4.e2m1_quantize_magnitude(abs(v) * (1 - rel) - abs_, s))
+            hi = int(fp4.e2m1_quantize_magnitude(abs(v) * (1 + rel) + abs_, s))
+            assert lo <= (got & 7) <= hi, f"row {r} group {g} elem {i}: nibble {got:#x}, value {v}, scale {s}"
+            assert (got >> 3) == int(np.signbit(v)) or abs(v) <= abs_, f"row {r} group {g} elem {i}: sign"
+    return int(np.sum(gd))

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(csa2.LIB_PATH)
     for name in header_functions():
         assert hasattr(raw, name), name
-    assert csa2.lib().csa2_abi_version() == 2
+    assert csa2.lib().csa2_abi_version() == 3
     assert csa2.lib().csa2_status_string(3) == b"workspace missing or too small"
 
 
@@ -80,6 +80,41 @@ def test_validation_rejects_before_launch():
         setattr(kv, field, good)
     assert L.csa2_index_select(ctypes.byref(kv), ctypes.byref(sq), 16, 16, 8, csa2.FULL, None, None, 0, 0, 16, 256, 1,
                                s) == csa2.ERR_WORKSPACE
+
+
+@needs_lib
+def test_finish_validation_rejects_before_launch():
+    L = csa2.lib()
+    s = None
+    fin = csa2.KvFinish(gamma=16, eps=1e-6, rope_theta=10000.0, w_idx=16)
+    P = ctypes.byref
+    # tokens == 0 is a no-op once the arguments are valid
+    assert L.csa2_kv_finish_rows(None, 0, 1, 0, P(fin), 16, 16, 16, 16, None, None, s) == csa2.OK
+    # positions beyond 2^24
+    assert L.csa2_kv_finish_rows(16, 10, 1, (1 << 24) - 5, P(fin), 16, 16, 16, 16, None, None,
+                                 s) == csa2.ERR_INVALID_ARG
+    # the key outputs are required with W_idx and refused without it
+    assert L.csa2_kv_finish_rows(16, 10, 1, 0, P(fin), 16, 16, None, 16, None, None, s) == csa2.ERR_INVALID_ARG
+    fin.w_idx = None
+    assert L.csa2_kv_finish_rows(16, 10, 1, 0, P(fin), 16, 16, 16, 16, None, None, s) == csa2.ERR_INVALID_ARG
+    for field, bad in (("eps", 0.0), ("eps", -1.0), ("rope_theta", -1.0), ("gamma", None), ("gamma", 8)):
+        good = getattr(fin, field)
+        setattr(fin, field, bad)
+        assert L.csa2_kv_finish_rows(16, 10, 1, 0, P(fin), 16, 16, None, None, None, None,
+                                     s) == csa2.ERR_INVALID_ARG, field
+        setattr(fin, field, good)
+    assert L.csa2_kv_finish_rows(16, 10, 1, 0, None, 16, 16, None, None, None, None, s) == csa2.ERR_INVALID_ARG
+    # CED with the finish needs the hand-over buffer
+    assert L.csa2_ced_kv_project_finished(16, 10, 64, 1, 16, P(fin), 0, None, 16, 16, None, None,
+                                          s) == csa2.ERR_INVALID_ARG
+    # the finishing append: a layer with bf16 keys cannot take a key projected from the main KV
+    kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=16, num_blocks=1, block_tokens=64, latent_dim=512,
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
+    sq = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=1, max_seq_len=64)
+    assert L.csa2_kv_append_finished(P(kv), P(sq), 16, P(fin), s) == csa2.ERR_INVALID_ARG
+    # FP4 keys need W_idx
+    kv.idx_dtype, kv.idx_dim, kv.idx_heads, kv.idx_scales = csa2.FP4, 128, 32, 16
+    assert L.csa2_kv_append_finished(P(kv), P(sq), 16, P(fin), s) == csa2.ERR_INVALID_ARG
 
 
 @needs_lib
