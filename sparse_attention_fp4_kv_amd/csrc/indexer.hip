@@ -1375,12 +1375,14 @@ __device__ __forceinline__ bool reload_overflowing(SelSmem &sm, const Stream &st
     if (t % tpw == 0) ovf_l[t / tpw] = word;
   }
   __syncthreads();
-  // emitted counts of every segment (the overflowing ones are recounted below)
+  // emitted counts of every segment (the overflowing ones are recounted below,
+  // by other waves: the barrier orders the two writes of such a count)
 #pragma unroll
   for (int j = 0; j < kSegPerThread; ++j) {
     const int s = kSegPerThread * t + j;
     if (s < nseg) sm.seg_cnt[s] = st.info[s].count;
   }
+  __syncthreads();
   // --- count, one wave per overflowing segment (wave w: segments w, w+8, ...)
   for (int s = wave; s < nseg; s += kSelThreads / 64)
     if (is_ovf(s)) {
