@@ -11,7 +11,9 @@ Other workloads (--workload): decode_b8_64k_rope (8 x 65,536 tokens, rope
 side-band, permuted page tables, one Full layer), mixed_serving_32_reuse4 (32
 requests with log-uniform lengths, append to 4 KV layers, one Full selection
 reused by 4 attentions), ced_prefill_16k_x20 (CED projection GEMM with the
-fused pack; ced_prefill_16k_x20_h5120 at hidden 5120), tiny_b1_4k,
+fused pack; ced_prefill_16k_x20_h5120 at hidden 5120;
+ced_prefill_16k_x20_finished with RMSNorm, RoPE and the FP4 indexer key from
+the cached entry), tiny_b1_4k,
 decode_1m_fp4_indexer (the 1M case with FP4 indexer keys of 128 dims scored by
 32 weighted query heads), decode_1m_decoder_x20 (the decoder's 20-layer
 Full / Reindex / Reuse schedule at top-K 512 over one KV source).
@@ -41,9 +43,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+FINISH_EPS, FINISH_THETA = 1e-6, 10000.0  # RMSNorm epsilon and RoPE base of the finishing workloads
 METRIC = "sparse FP4-KV decode attn queries/s + achieved HBM GB/s vs MI355X peak"
 WORKLOADS = ("decode_1m_hierarchical", "decode_b8_64k_rope", "mixed_serving_32_reuse4", "ced_prefill_16k_x20",
-             "tiny_b1_4k", "decode_1m_fp4_indexer", "decode_1m_decoder_x20", "ced_prefill_16k_x20_h5120")
+             "tiny_b1_4k", "decode_1m_fp4_indexer", "decode_1m_decoder_x20", "ced_prefill_16k_x20_h5120",
+             "ced_prefill_16k_x20_finished")
 
 
 def log(*a):
@@ -130,8 +134,13 @@ class Decode1M(Decode):
         self.n, self.H, self.K, self.P, self.L = n, w.heads, w.top_k, w.pool_blocks, w.layers
         self.fp4 = w.idx_dtype == "fp4"
         self.IH = w.extra.get("idx_heads", 1)
+        self.finish = w.extra.get("finish", False)  # raw latents finished (norm, RoPE, pack, key) on the way in
         t0 = time.time()
         self.latent = wl.latent_rows(self.st, 0, 0, n)
+        if self.finish:
+            self.gamma, self.w_kv_idx = wl.kv_finish_inputs(self.st, 1)
+            self.gamma_d = torch.from_numpy(self.gamma[0].copy()).to(dev)
+            self.w_kv_idx_d = torch.from_numpy(self.w_kv_idx[0].view(np.int16).copy()).to(dev)
         if self.fp4:
             self.keys = wl.idx4_keys(self.st, 0, n)
             self.q_idx = [wl.q_idx_heads(self.st, l, 1, self.IH) for l in range(self.L)]
@@ -145,7 +154,10 @@ class Decode1M(Decode):
         nb = n // 64
         table = np.arange(nb, dtype=np.int32)
         base = csa2.PagedLayer(nb, idx_dtype=w.idx_dtype, idx_heads=self.IH, device=dev)
-        self._fill(base, table, n, latent=self.latent, keys=self.keys)
+        if self.finish:
+            self._fill_finished(base, n)
+        else:
+            self._fill(base, table, n, latent=self.latent, keys=self.keys)
         self.layers = [base] + [self.clone_layer(base) for _ in range(replicas - 1)]
         bt = torch.from_numpy(table[None].copy()).to(dev)
         self.batch = csa2.Batch(bt, torch.tensor([n], dtype=torch.int32, device=dev), n)
@@ -163,7 +175,17 @@ class Decode1M(Decode):
         self.out = torch.empty((self.L, 1, self.H, 512), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.L, 1, self.H), dtype=torch.float32, device=dev)
         self.kf64 = None
-        if cpu_needed:
+        self.o_entries = None
+        if cpu_needed and self.finish:
+            import oracle
+            parts = [oracle.latent.kv_entry(self.latent[s:s + (1 << 17)], np.arange(s, min(n, s + (1 << 17))),
+                                            self.gamma[0], FINISH_EPS, FINISH_THETA, self.w_kv_idx[0])
+                     for s in range(0, n, 1 << 17)]
+            self.o_entries = (np.concatenate([p[1] for p in parts]), np.concatenate([p[2] for p in parts]))
+            self.kf64 = oracle.indexer.fp4_keys_to_f64(np.concatenate([p[4] for p in parts]),
+                                                       np.concatenate([p[5] for p in parts]))
+            del parts
+        elif cpu_needed:
             import oracle
             if self.fp4:
                 self.kf64 = oracle.indexer.fp4_keys_to_f64(*oracle.fp4.fp4_pack(self.keys))
@@ -174,9 +196,35 @@ class Decode1M(Decode):
     queries_per_step = property(lambda self: self.L)
     dominant = "index_scan"
 
+    def _fill_finished(self, layer, n, chunk=1 << 17):
+        """Identity page table: finish raw latents of positions [s, e) straight into rows [s, e)."""
+        torch, csa2 = self.torch, self.csa2
+        for s in range(0, n, chunk):
+            e = min(n, s + chunk)
+            c = torch.from_numpy(self.latent[s:e][None].copy()).to(self.dev)
+            codes, scales, kc, ks, _, _ = csa2.csa2_kv_finish_rows(c, self.gamma_d[None], FINISH_EPS, FINISH_THETA,
+                                                                   self.w_kv_idx_d[None], pos0=s)
+            layer.codes[s:e], layer.scales[s:e] = codes[0], scales[0]
+            layer.idx_keys[s:e], layer.idx_scales[s:e] = kc[0], ks[0]
+
+    def _append(self, layer):
+        if self.finish:
+            self.csa2.csa2_kv_append_finished(layer, self.batch_prev, self.new_latent, self.gamma_d, FINISH_EPS,
+                                              FINISH_THETA, self.w_kv_idx_d)
+        else:
+            self.csa2.csa2_kv_append(layer, self.batch_prev, self.new_latent, idx_key=self.new_key)
+
+    def _oracle_kv(self, v):
+        """Oracle float64 cache entries of positions v."""
+        import oracle
+
+        if self.o_entries is not None:
+            return oracle.fp4.fp4_unpack(self.o_entries[0][v], self.o_entries[1][v])
+        return oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(self.latent[v]))
+
     def step(self, r):
         csa2, layer = self.csa2, self.layers[r]
-        csa2.csa2_kv_append(layer, self.batch_prev, self.new_latent, idx_key=self.new_key)
+        self._append(layer)
         for l in range(self.L):
             if l == 0:
                 csa2.csa2_index_select(layer, self.batch, self.q_idx_d[0], self.K, csa2.FULL, pool_blocks=self.P,
@@ -217,8 +265,7 @@ class Decode1M(Decode):
         outs = []
         for l in range(self.L):
             v = oracle.attention.valid_slots(sel[l], self.n)
-            c = oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(self.latent[v]))
-            outs.append(oracle.attention.sparse_attention(self.q[l][0], c, self.w.sigma))
+            outs.append(oracle.attention.sparse_attention(self.q[l][0], self._oracle_kv(v), self.w.sigma))
         return outs
 
     def config(self):
@@ -242,7 +289,7 @@ class DecoderX20(Decode1M):
 
     def step(self, r):
         csa2, layer = self.csa2, self.layers[r]
-        csa2.csa2_kv_append(layer, self.batch_prev, self.new_latent, idx_key=self.new_key)
+        self._append(layer)
         for g, l0 in enumerate(self.leads):
             if g == 0:
                 csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l0], self.K, csa2.FULL, pool_blocks=self.P,
@@ -262,7 +309,7 @@ class DecoderX20(Decode1M):
         reindex = (len(self.leads) - 1) * (P * 8 * self.key_bytes + self.qsel_bytes)
         kv = L * K * 288
         qio = L * (H * 512 * 2 + H * 512 * 4 + H * 4)
-        append = 512 * 4 + 288 + 128 * 4 + 72
+        append = 512 * 4 + 288 + 72 + (512 * 4 + 128 * 512 * 2 if self.finish else 128 * 4)
         return scan + reindex + kv + qio + append
 
     def oracle_step(self):
@@ -276,7 +323,7 @@ class DecoderX20(Decode1M):
         outs = []
         for l0 in self.leads:
             v = oracle.attention.valid_slots(oracle.indexer.reuse_select(sel[l0]), self.n)
-            c = oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(self.latent[v]))
+            c = self._oracle_kv(v)
             for l in range(l0, l0 + self.G):
                 outs.append(oracle.attention.sparse_attention(self.q[l][0], c, self.w.sigma))
         return outs
@@ -477,6 +524,16 @@ class CedPrefill:
         self.codes = torch.empty((self.L, self.T, 256), dtype=torch.uint8, device=dev)
         self.scales = torch.empty((self.L, self.T, 32), dtype=torch.uint8, device=dev)
         self.z = torch.empty((self.L, self.T, 64), dtype=torch.int16, device=dev)
+        self.finish = e.get("finish", False)  # C finished (RMSNorm, RoPE, pack) + FP4 key from the cached entry
+        if self.finish:
+            self.gamma, self.w_idx = wl.kv_finish_inputs(st, self.L)
+            self.gamma_d = torch.from_numpy(self.gamma).to(dev)
+            self.w_idx_d = torch.from_numpy(self.w_idx.view(np.int16)).to(dev)
+            self.c_ws = torch.empty((self.L, self.T, 512), dtype=torch.float32, device=dev)
+            self.kc = torch.empty((self.L, self.T, 64), dtype=torch.uint8, device=dev)
+            self.ks = torch.empty((self.L, self.T, 8), dtype=torch.uint8, device=dev)
+            self.fin = csa2.KvFinish(gamma=self.gamma_d.data_ptr(), eps=FINISH_EPS, rope_theta=FINISH_THETA,
+                                     w_idx=self.w_idx_d.data_ptr())
         self.replicas = 1
         torch.cuda.synchronize()
 
@@ -485,14 +542,30 @@ class CedPrefill:
 
     def step(self, r):
         c = self.csa2
+        if self.finish:
+            import ctypes
+
+            c._check(c.lib().csa2_ced_kv_project_finished(
+                c._ptr(self.h_d), self.T, self.Hd, self.L, c._ptr(self.wkv_d), ctypes.byref(self.fin), 0,
+                c._ptr(self.c_ws), c._ptr(self.codes), c._ptr(self.scales), c._ptr(self.kc), c._ptr(self.ks),
+                c._stream()), "csa2_ced_kv_project_finished")
+            return
         c._check(c.lib().csa2_ced_kv_project(c._ptr(self.h_d), self.T, self.Hd, self.L, c._ptr(self.wkv_d),
                                              c._ptr(self.wz_d), c._ptr(self.codes), c._ptr(self.scales),
                                              c._ptr(self.z), None, c._stream()), "csa2_ced_kv_project")
 
+    def gemm_flops(self):  # the projection GEMM alone (the dominant kernel)
+        return 2.0 * self.T * self.Hd * self.L * (512 if self.finish else 576)
+
     def flops(self):
+        if self.finish:  # C (512 per layer) and the 128-dim key from the 512-dim entry
+            return 2.0 * self.T * self.L * 512 * (self.Hd + 128)
         return 2.0 * self.T * self.Hd * self.L * 576
 
     def algorithmic_bytes(self):
+        if self.finish:  # + the fp32 hand-over of C (written, read), W_idx and gamma, the FP4 key
+            return (self.T * self.Hd * 2 + self.L * 512 * self.Hd * 2 + self.L * self.T * (288 + 72 + 2 * 2048)
+                    + self.L * (128 * 512 * 2 + 2048))
         return self.T * self.Hd * 2 + self.L * 576 * self.Hd * 2 + self.L * self.T * (288 + 128)
 
     def dominant_bytes(self):
@@ -501,11 +574,16 @@ class CedPrefill:
     def oracle_step(self, rows=64):
         import oracle
 
+        if self.finish:
+            C, _ = oracle.ced.ced_project(self.h[:rows], self.wkv, None)
+            return [oracle.latent.kv_entry(C[l], np.arange(rows), self.gamma[l], FINISH_EPS, FINISH_THETA,
+                                           self.w_idx[l]) for l in range(self.L)]
         return oracle.ced.ced_project_and_pack(self.h[:rows], self.wkv, self.wz)
 
     def config(self):
         return {"workload": self.w.name, "tokens": self.T, "hidden": self.Hd, "layers": self.L,
-                "out_per_layer": "512 FP4 + 64 bf16"}
+                "out_per_layer": "512 FP4 (RMSNorm + RoPE) + FP4 key [128] from the entry" if self.finish
+                else "512 FP4 + 64 bf16"}
 
 
 def make(name, replicas, dev, cpu_needed):
@@ -513,7 +591,7 @@ def make(name, replicas, dev, cpu_needed):
 
     wid = {"tiny_b1_4k": 1, "decode_b8_64k_rope": 2, "ced_prefill_16k_x20": 3, "decode_1m_hierarchical": 4,
            "mixed_serving_32_reuse4": 5, "decode_1m_fp4_indexer": 6, "decode_1m_decoder_x20": 7,
-           "ced_prefill_16k_x20_h5120": 8}[name]
+           "ced_prefill_16k_x20_h5120": 8, "ced_prefill_16k_x20_finished": 9}[name]
     w = wl.workload(wid)
     if wid == 7:
         return DecoderX20(w, replicas, dev, cpu_needed)
@@ -521,7 +599,7 @@ def make(name, replicas, dev, cpu_needed):
         return Decode1M(w, replicas, dev, cpu_needed)
     if wid == 5:
         return MixedServing(w, replicas, dev, cpu_needed)
-    if wid in (3, 8):
+    if wid in (3, 8, 9):
         return CedPrefill(w, replicas, dev, cpu_needed)
     return DecodeBatch(w, replicas, dev, cpu_needed)
 
@@ -550,7 +628,7 @@ def cpu_baseline(wk, budget_s):
                 wk.oracle_step(rows)
                 reps += 1
             dt = time.time() - t0
-            fl = 2.0 * rows * reps * wk.Hd * wk.L * 576
+            fl = wk.flops() * rows * reps / wk.T
             return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
                     "sample": f"{reps} x {rows}-token slices x 20 layers of the CED projection + pack (float64)",
                     "usable_cores": cores_avail}
@@ -624,7 +702,8 @@ def main():
         del src, dst
     replicas = args.replicas or {"decode_1m_hierarchical": 4, "decode_b8_64k_rope": 6, "mixed_serving_32_reuse4": 3,
                                  "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1, "decode_1m_fp4_indexer": 4,
-                                 "decode_1m_decoder_x20": 4, "ced_prefill_16k_x20_h5120": 1}[args.workload]
+                                 "decode_1m_decoder_x20": 4, "ced_prefill_16k_x20_h5120": 1,
+                                 "ced_prefill_16k_x20_finished": 1}[args.workload]
     want_cpu = not args.no_cpu_baseline
     wk = make(args.workload, replicas, dev, want_cpu)
     R = wk.replicas
@@ -684,7 +763,7 @@ def main():
         res.update({"metric": "CED KV projection TFLOP/s (bf16 MFMA, fused FP4 pack) vs MI355X peak",
                     "value": tf, "unit": "TFLOP/s", "dtype": "bf16",
                     "mfma_frac": tf / BF16_PEAK_TFLOPS, "bytes_written_per_step": wk.L * wk.T * (288 + 128)})
-        roof = {"bound": "mfma", "achieved": wk.flops() / (kern_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": wk.gemm_flops() / (kern_ms * 1e-3) / 1e12, "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s"}
     else:
         qps = wk.queries_per_step / (ms * 1e-3)

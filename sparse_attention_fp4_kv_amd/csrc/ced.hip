@@ -6,7 +6,8 @@
 // Z_l = H W_l^Z.  The FP4 format of C is the one in section "FP4 KV cache".
 //
 // Design (ours): all layers form one GEMM
-//   out[t][n] = sum_k H[t][k] * W[n][k],  n = l * 576 + c  (c < 512: C_l, else Z_l)
+//   out[t][n] = sum_k H[t][k] * W[n][k],  n = l * 576 + c  (c < 512: C_l, else Z_l),
+//   or n = l * 512 + c when no W^Z is given
 // with H [tokens][hidden] and the weights in out x in orientation, so both
 // operands are read along k (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 // A workgroup computes a 256 x 128 output tile with 4 waves (128 x 64 each,
@@ -26,7 +27,8 @@ constexpr int BM = 256, BN = 128, BK = 32;
 constexpr int kLdA = BK + 8;   // bf16 per LDS row (pad breaks bank conflicts)
 constexpr int kWM = 128, kWN = 64;  // wave tile: 4 x 2 MFMA tiles of 32 x 32
 constexpr int kLdC = BN + 4;   // fp32 per epilogue row (128 rows at a time)
-constexpr int kNPerLayer = kLatent + kIdxDim;  // 576
+// output columns per layer: 512 of C, then 64 of Z when W^Z is given
+__device__ __forceinline__ int per_layer(const void *w_z) { return w_z != nullptr ? kLatent + kIdxDim : kLatent; }
 
 struct CedArgs {
   const uint16_t *h;
@@ -43,7 +45,8 @@ struct CedArgs {
 
 // Row n of the combined weight matrix, or null for a Z row without weights.
 __device__ __forceinline__ const uint16_t *weight_row(const CedArgs &a, int n) {
-  const int l = n / kNPerLayer, c = n % kNPerLayer;
+  const int npl = per_layer(a.w_z);
+  const int l = n / npl, c = n % npl;
   if (c < kLatent) return a.w_kv + ((size_t)l * kLatent + c) * a.hidden;
   if (a.w_z == nullptr) return nullptr;
   return a.w_z + ((size_t)l * kIdxDim + (c - kLatent)) * a.hidden;
@@ -65,7 +68,7 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
-  const int n_total = a.n_layers * kNPerLayer;
+  const int n_total = a.n_layers * per_layer(a.w_z);
   const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
 
   // global -> register staging: a thread loads rows (tid / 4) + 64 i of A (i < 4) and of
@@ -158,7 +161,7 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
       float v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = sm.c[r][16 * cg + i];
-      const int l = n / kNPerLayer, c = n % kNPerLayer;
+      const int l = n / per_layer(a.w_z), c = n % per_layer(a.w_z);
       const size_t row = (size_t)l * a.tokens + t;
       if (c < kLatent) {
         if (a.codes != nullptr) {  // null: the caller finishes C (norm, rotation) before packing
@@ -197,7 +200,7 @@ hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int
                               hipStream_t st) {
   if (tokens == 0 || n_layers == 0) return hipSuccess;
   CedArgs a{h, w_kv, w_z, tokens, hidden, n_layers, codes, scales, z, c_f32};
-  const int n_total = n_layers * kNPerLayer;
+  const int n_total = n_layers * (w_z != nullptr ? kLatent + kIdxDim : kLatent);
   const dim3 grid((n_total + BN - 1) / BN, (unsigned)((tokens + BM - 1) / BM));
   timer_before(kKernCedProject, st);
   ced_kernel<<<grid, dim3(256), 0, st>>>(a);

@@ -85,14 +85,19 @@ def workload(wid):
                         extra=dict(idx_heads=IDX4_HEADS))
     if wid == 7:
         # the decoder's own shapes: top-K 512, 20 layers over one KV source in 5 groups of 4 (the first group
-        # Full + 3 Reuse, the others Reindex + 3 Reuse), multi-head FP4 indexer
+        # Full + 3 Reuse, the others Reindex + 3 Reuse), multi-head FP4 indexer; raw latents are finished
+        # (RMSNorm, RoPE, pack) with the indexer key projected from the cached entry
         return Workload(7, "decode_1m_decoder_x20", batch=1, heads=64, top_k=512, sigma=1 / math.sqrt(512),
                         seq_lens=(1 << 20,), idx_dtype="fp4", hierarchical=True, layers=20, reindex_layers=4,
-                        reuse_layers=15, extra=dict(idx_heads=IDX4_HEADS, group_size=4))
+                        reuse_layers=15, extra=dict(idx_heads=IDX4_HEADS, group_size=4, finish=True))
     if wid == 8:
         # CED projection at the model's hidden size 5120
         return Workload(8, "ced_prefill_16k_x20_h5120", batch=0, heads=0, top_k=0, sigma=0.0,
                         extra=dict(tokens=16384, hidden=5120, layers=20, kv=512, z=64))
+    if wid == 9:
+        # CED projection followed by the finish (RMSNorm, RoPE, pack) and the FP4 indexer key from the entry
+        return Workload(9, "ced_prefill_16k_x20_finished", batch=0, heads=0, top_k=0, sigma=0.0,
+                        extra=dict(tokens=16384, hidden=4096, layers=20, kv=512, z=0, finish=True))
     raise ValueError(wid)
 
 
