@@ -30,9 +30,11 @@ Modules:
   paged      paged-cache addressing and the bytes-per-token arithmetic.
   latent     RMSNorm + RoPE of a KV latent before the pack, and the indexer key
              projected from the cached entry.
+  swa        the sliding-window branch: FP8 window entries and the merge with the
+             global branch.
 
 Parity status of every function is stated in its docstring; the pins live in
 ``tests/test_oracle_*.py`` and ``tests/golden/``.
 """
 
-from . import fp4, ced, indexer, attention, paged, latent  # noqa: F401
+from . import fp4, ced, indexer, attention, paged, latent, swa  # noqa: F401
