@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 3
+#define CSA2_ABI_VERSION 4
 
 typedef enum {
   CSA2_OK = 0,
@@ -204,6 +204,40 @@ csa2_status csa2_ced_kv_project_finished(const uint16_t *h, int64_t tokens, int3
  * keys exactly when fin->w_idx is given.  Unmapped pages are skipped. */
 csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
                                     const csa2_kv_finish *fin, csa2_stream stream);
+
+/* ---- The sliding-window branch.  [P1] "KV bottleneck": a local
+ * sliding-window attention branch runs beside the global one; [P1] "Causal
+ * Encoder-Decoder": the window n_win is 128; [P1] "FP4 KV cache": the SWA KV
+ * stays in FP8.  This library's reading: a window entry is the layer's
+ * 512-channel local latent (key = value, no rope part), stored as E4M3FN
+ * codes with one fp32 scale per token (s = amax / 448, code =
+ * E4M3_RNE(x / s) with x's sign, saturating); position p lives in ring slot
+ * p mod 128; the window of a sequence of n positions is n-128 .. n-1; the two
+ * branches form one softmax over the union of their entries. */
+typedef struct {
+  uint8_t *codes;  /* device [batch][128][512] E4M3FN, caller-owned */
+  float *scales;   /* device [batch][128] */
+  int32_t batch;   /* sequences the ring arrays hold */
+} csa2_swa_window;
+
+/* Packs latent[b] (device fp32 [batch][512]) into slot positions[b] mod 128
+ * of sequence b's ring (positions: device int32 [batch], the new token's
+ * position; negative: skipped).  batch <= win->batch. */
+csa2_status csa2_swa_append(const csa2_swa_window *win, const int32_t *positions, int32_t batch,
+                            const float *latent, csa2_stream stream);
+
+/* Attention of every head over the window of each sequence (seq_lens: device
+ * int32 [batch], positions held, current token included), merged in place
+ * into the global branch's result: out (device fp32 [batch][heads][512]) and
+ * lse (device fp32 [batch][heads], natural log; -inf for an empty global
+ * selection) become the attention over the union of both branches' entries.
+ * q: device bf16 [batch][heads][q_dim] (q_dim 512, or 576 with a rope part
+ * that the window does not use); softmax_scale as for the global branch;
+ * heads a multiple of 16 in [16, 128].  A sequence with an empty window is
+ * left as it is. */
+csa2_status csa2_swa_attn_merge(const csa2_swa_window *win, const int32_t *seq_lens, int32_t batch,
+                                const uint16_t *q, int32_t heads, int32_t q_dim, float softmax_scale, float *out,
+                                float *lse, csa2_stream stream);
 
 /* ---- Indexer scores alone (the scoring step of [P1] "CSA2").  For
  * t < seq_lens[b], with k = the stored key of position t:

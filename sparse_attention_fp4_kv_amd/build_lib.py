@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
-SOURCES = ["api.hip", "pack.hip", "indexer.hip", "attention.hip", "ced.hip", "latent.hip"]
+SOURCES = ["api.hip", "pack.hip", "indexer.hip", "attention.hip", "ced.hip", "latent.hip", "swa.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

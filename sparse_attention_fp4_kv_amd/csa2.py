@@ -66,6 +66,12 @@ class KvFinish(ctypes.Structure):
     ]
 
 
+class SwaWindow(ctypes.Structure):
+    """csa2_swa_window: the FP8 ring of 128 slots per sequence."""
+
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("batch", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -88,6 +94,9 @@ SIGNATURES = {
     "csa2_ced_kv_project_finished": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, ctypes.POINTER(KvFinish), _I64, _P,
                                                     _P, _P, _P, _P, _P]),
     "csa2_kv_append_finished": (ctypes.c_int, [_PKV, _PSQ, _P, ctypes.POINTER(KvFinish), _P]),
+    "csa2_swa_append": (ctypes.c_int, [ctypes.POINTER(SwaWindow), _P, _I32, _P, _P]),
+    "csa2_swa_attn_merge": (ctypes.c_int, [ctypes.POINTER(SwaWindow), _P, _I32, _P, _I32, _I32, ctypes.c_float, _P,
+                                           _P, _P]),
     "csa2_index_scores": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _P, _P]),
     "csa2_topk_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_topk": (ctypes.c_int, [_P, _I64, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
@@ -326,6 +335,33 @@ def csa2_kv_append_finished(layer, batch, latent, gamma, eps, theta, w_idx=None)
     fin = _finish(gamma, eps, theta, w_idx)
     _check(lib().csa2_kv_append_finished(ctypes.byref(kv), ctypes.byref(sq), _ptr(latent), ctypes.byref(fin),
                                          _stream()), "csa2_kv_append_finished")
+
+
+class SwaRing:
+    """Sliding-window ring of one layer: codes [batch][128][512] u8 (E4M3FN), scales [batch][128] fp32."""
+
+    def __init__(self, batch, device="cuda"):
+        self.codes = torch.zeros((batch, 128, 512), dtype=torch.uint8, device=device)
+        self.scales = torch.zeros((batch, 128), dtype=torch.float32, device=device)
+        self.batch = batch
+
+    def struct(self):
+        return SwaWindow(codes=self.codes.data_ptr(), scales=self.scales.data_ptr(), batch=self.batch)
+
+
+def csa2_swa_append(ring, positions, latent):
+    """positions int32 [B] (device), latent fp32 [B, 512]."""
+    w = ring.struct()
+    _check(lib().csa2_swa_append(ctypes.byref(w), _ptr(positions), latent.shape[0], _ptr(latent), _stream()),
+           "csa2_swa_append")
+
+
+def csa2_swa_attn_merge(ring, seq_lens, q, softmax_scale, out, lse):
+    """Merges the window attention into (out [B, H, 512], lse [B, H]) in place; q bf16 bits [B, H, 512 (+64)]."""
+    B, H, D = q.shape
+    w = ring.struct()
+    _check(lib().csa2_swa_attn_merge(ctypes.byref(w), _ptr(seq_lens), B, _ptr(q), H, D, softmax_scale, _ptr(out),
+                                     _ptr(lse), _stream()), "csa2_swa_attn_merge")
 
 
 def csa2_index_scores(layer, batch, q_idx, max_len, w_idx=None):

@@ -91,7 +91,7 @@ ArmedTimer g_timer;
 
 const char *const kKernelNames[kKernCount] = {"index_scan",  "pool_score",   "topk_given", "topk_compact",
                                               "sparse_attn", "attn_combine", "ced_project", "fp4_pack",
-                                              "kv_append",   "index_scores", "kv_finish"};
+                                              "kv_append",   "index_scores", "kv_finish",    "swa_attn"};
 
 }  // namespace
 
@@ -261,6 +261,31 @@ csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs 
   if (S.batch == 0) return CSA2_OK;
   if (latent == nullptr || !aligned(latent, 16)) return CSA2_ERR_INVALID_ARG;
   return from_hip(launch_kv_append_finish(L, S, latent, f, as_stream(stream)));
+}
+
+csa2_status csa2_swa_append(const csa2_swa_window *win, const int32_t *positions, int32_t batch,
+                            const float *latent, csa2_stream stream) {
+  if (win == nullptr || batch < 0 || batch > win->batch) return CSA2_ERR_INVALID_ARG;
+  if (batch == 0) return CSA2_OK;
+  if (win->codes == nullptr || win->scales == nullptr || positions == nullptr || latent == nullptr)
+    return CSA2_ERR_INVALID_ARG;
+  if (!aligned(win->codes, 8) || !aligned(win->scales, 4) || !aligned(latent, 16)) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_swa_append(win->codes, win->scales, positions, batch, latent, as_stream(stream)));
+}
+
+csa2_status csa2_swa_attn_merge(const csa2_swa_window *win, const int32_t *seq_lens, int32_t batch,
+                                const uint16_t *q, int32_t heads, int32_t q_dim, float softmax_scale, float *out,
+                                float *lse, csa2_stream stream) {
+  if (win == nullptr || batch < 0 || batch > win->batch) return CSA2_ERR_INVALID_ARG;
+  if (heads < 16 || heads > 128 || heads % 16 != 0 || (q_dim != 512 && q_dim != 576)) return CSA2_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 3.0e38f)) return CSA2_ERR_INVALID_ARG;
+  if (batch == 0) return CSA2_OK;
+  if (win->codes == nullptr || win->scales == nullptr || seq_lens == nullptr || q == nullptr || out == nullptr ||
+      lse == nullptr)
+    return CSA2_ERR_INVALID_ARG;
+  if (!aligned(win->codes, 16) || !aligned(q, 16) || !aligned(out, 4) || !aligned(lse, 4)) return CSA2_ERR_INVALID_ARG;
+  return from_hip(launch_swa_attn_merge(win->codes, win->scales, seq_lens, batch, q, heads, q_dim, softmax_scale,
+                                        out, lse, as_stream(stream)));
 }
 
 csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,

@@ -21,6 +21,7 @@ enum KernelId {
   kKernKvAppend,
   kKernIndexScores,
   kKernKvFinish,
+  kKernSwaAttn,
   kKernCount
 };
 // Records the armed event pair around the next launch of `id` (no-op otherwise).
@@ -98,6 +99,13 @@ hipError_t launch_kv_finish_rows(const float *c, int64_t tokens, int n_layers, i
                                  float *k_f32, hipStream_t st);
 hipError_t launch_kv_append_finish(const KvLayerDev &L, const SeqsDev &S, const float *latent, const KvFinish &fin,
                                    hipStream_t st);
+
+// Sliding-window branch: FP8 ring of 128 slots per sequence.
+hipError_t launch_swa_append(uint8_t *codes, float *scales, const int32_t *pos, int batch, const float *latent,
+                             hipStream_t st);
+hipError_t launch_swa_attn_merge(const uint8_t *codes, const float *scales, const int32_t *lens, int batch,
+                                 const uint16_t *q, int heads, int qdim, float softmax_scale, float *out, float *lse,
+                                 hipStream_t st);
 
 hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int n_layers, const uint16_t *w_kv,
                               const uint16_t *w_z, uint8_t *codes, uint8_t *scales, uint16_t *z, float *c_f32,

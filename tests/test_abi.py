@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(csa2.LIB_PATH)
     for name in header_functions():
         assert hasattr(raw, name), name
-    assert csa2.lib().csa2_abi_version() == 3
+    assert csa2.lib().csa2_abi_version() == 4
     assert csa2.lib().csa2_status_string(3) == b"workspace missing or too small"
 
 
@@ -115,6 +115,19 @@ def test_finish_validation_rejects_before_launch():
     # FP4 keys need W_idx
     kv.idx_dtype, kv.idx_dim, kv.idx_heads, kv.idx_scales = csa2.FP4, 128, 32, 16
     assert L.csa2_kv_append_finished(P(kv), P(sq), 16, P(fin), s) == csa2.ERR_INVALID_ARG
+
+
+@needs_lib
+def test_swa_validation_rejects_before_launch():
+    L = csa2.lib()
+    P = ctypes.byref
+    w = csa2.SwaWindow(codes=16, scales=16, batch=2)
+    assert L.csa2_swa_append(P(w), 16, 3, 16, None) == csa2.ERR_INVALID_ARG  # beyond the ring's batch
+    assert L.csa2_swa_append(P(w), 16, 0, None, None) == csa2.OK
+    for heads, qd in ((8, 512), (24, 512), (144, 512), (16, 520)):
+        assert L.csa2_swa_attn_merge(P(w), 16, 1, 16, heads, qd, 0.1, 16, 16, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_swa_attn_merge(P(w), 16, 1, 16, 16, 512, 0.0, 16, 16, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_swa_attn_merge(P(w), 16, 1, 16, 16, 512, 0.1, 16, None, None) == csa2.ERR_INVALID_ARG
 
 
 @needs_lib
