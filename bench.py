@@ -16,7 +16,8 @@ ced_prefill_16k_x20_finished with RMSNorm, RoPE and the FP4 indexer key from
 the cached entry), tiny_b1_4k,
 decode_1m_fp4_indexer (the 1M case with FP4 indexer keys of 128 dims scored by
 32 weighted query heads), decode_1m_decoder_x20 (the decoder's 20-layer
-Full / Reindex / Reuse schedule at top-K 512 over one KV source).
+Full / Reindex / Reuse schedule at top-K 512 over one KV source; _swa adds
+each layer's FP8 sliding-window branch merged with the global one).
 
 Timing: inputs are resident in HBM; R replicas of the cache rotate so every
 step reads data evicted from the 256 MB last-level cache; each replica's step
@@ -47,7 +48,7 @@ FINISH_EPS, FINISH_THETA = 1e-6, 10000.0  # RMSNorm epsilon and RoPE base of the
 METRIC = "sparse FP4-KV decode attn queries/s + achieved HBM GB/s vs MI355X peak"
 WORKLOADS = ("decode_1m_hierarchical", "decode_b8_64k_rope", "mixed_serving_32_reuse4", "ced_prefill_16k_x20",
              "tiny_b1_4k", "decode_1m_fp4_indexer", "decode_1m_decoder_x20", "ced_prefill_16k_x20_h5120",
-             "ced_prefill_16k_x20_finished")
+             "ced_prefill_16k_x20_finished", "decode_1m_decoder_x20_swa")
 
 
 def log(*a):
@@ -286,6 +287,22 @@ class DecoderX20(Decode1M):
         self.G = w.extra["group_size"]
         self.leads = list(range(0, self.L, self.G))
         self.gidx = self.torch.empty((len(self.leads), 1, self.K), dtype=self.torch.int32, device=dev)
+        self.swa = w.extra.get("swa", False)
+        if self.swa:  # every layer's own window of 128 local latents (FP8), one ring per layer and replica
+            csa2, torch = self.csa2, self.torch
+            n = self.n
+            self.win_lat = [self.wl.latent_rows(self.st, 100 + l, 0, 128) for l in range(self.L)]
+            self.rings = [[csa2.SwaRing(1, dev) for _ in range(self.L)] for _ in range(replicas)]
+            for l in range(self.L):
+                lat_d = torch.from_numpy(self.win_lat[l]).to(dev)
+                for j in range(128):
+                    csa2.csa2_swa_append(self.rings[0][l], torch.tensor([n - 128 + j], dtype=torch.int32, device=dev),
+                                         lat_d[j:j + 1])
+                for r in range(1, replicas):
+                    self.rings[r][l].codes.copy_(self.rings[0][l].codes)
+                    self.rings[r][l].scales.copy_(self.rings[0][l].scales)
+            self.win_new = [torch.from_numpy(self.win_lat[l][127:128].copy()).to(dev) for l in range(self.L)]
+            torch.cuda.synchronize()
 
     def step(self, r):
         csa2, layer = self.csa2, self.layers[r]
@@ -300,8 +317,13 @@ class DecoderX20(Decode1M):
                                        pool_blocks=self.P, ws=self.sel_ws, indices=self.gidx[g],
                                        w_idx=self.w_idx_d[l0])
             for l in range(l0, l0 + self.G):  # the lead and its Reuse layers
+                if self.swa:  # the layer's own window entry of the new token
+                    csa2.csa2_swa_append(self.rings[r][l], self.batch_prev.seq_lens, self.win_new[l])
                 csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
                                                  ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
+                if self.swa:
+                    csa2.csa2_swa_attn_merge(self.rings[r][l], self.batch.seq_lens, self.q_d[l], self.w.sigma,
+                                             self.out[l], self.lse[l])
 
     def algorithmic_bytes(self):
         n, K, P, H, L = self.n, self.K, self.P, self.H, self.L
@@ -310,6 +332,9 @@ class DecoderX20(Decode1M):
         kv = L * K * 288
         qio = L * (H * 512 * 2 + H * 512 * 4 + H * 4)
         append = 512 * 4 + 288 + 72 + (512 * 4 + 128 * 512 * 2 if self.finish else 128 * 4)
+        if self.swa:  # per layer: the new window entry, and the window read twice (QK, then PV)
+            append += L * (512 * 4 + 512 + 4)
+            kv += L * 2 * 128 * (512 + 4)
         return scan + reindex + kv + qio + append
 
     def oracle_step(self):
@@ -325,12 +350,18 @@ class DecoderX20(Decode1M):
             v = oracle.attention.valid_slots(oracle.indexer.reuse_select(sel[l0]), self.n)
             c = self._oracle_kv(v)
             for l in range(l0, l0 + self.G):
-                outs.append(oracle.attention.sparse_attention(self.q[l][0], c, self.w.sigma))
+                o = oracle.attention.sparse_attention(self.q[l][0], c, self.w.sigma)
+                if self.swa:
+                    win = oracle.swa.swa_unpack(*oracle.swa.swa_pack(self.win_lat[l]))
+                    o = oracle.swa.merge(*o, *oracle.swa.swa_attention(self.q[l][0], win, self.w.sigma))
+                outs.append(o)
         return outs
 
     def config(self):
         c = super().config()
         c["layers"] = "20 in 5 groups of 4: Full + 3 Reuse, then 4 x (Reindex + 3 Reuse), one KV source"
+        if self.swa:
+            c["swa"] = "per layer: FP8 window of 128 (E4M3 + fp32 per-token scale), merged with the global branch"
         return c
 
 
@@ -591,9 +622,9 @@ def make(name, replicas, dev, cpu_needed):
 
     wid = {"tiny_b1_4k": 1, "decode_b8_64k_rope": 2, "ced_prefill_16k_x20": 3, "decode_1m_hierarchical": 4,
            "mixed_serving_32_reuse4": 5, "decode_1m_fp4_indexer": 6, "decode_1m_decoder_x20": 7,
-           "ced_prefill_16k_x20_h5120": 8, "ced_prefill_16k_x20_finished": 9}[name]
+           "ced_prefill_16k_x20_h5120": 8, "ced_prefill_16k_x20_finished": 9, "decode_1m_decoder_x20_swa": 10}[name]
     w = wl.workload(wid)
-    if wid == 7:
+    if wid in (7, 10):
         return DecoderX20(w, replicas, dev, cpu_needed)
     if wid in (4, 6):
         return Decode1M(w, replicas, dev, cpu_needed)
@@ -703,7 +734,7 @@ def main():
     replicas = args.replicas or {"decode_1m_hierarchical": 4, "decode_b8_64k_rope": 6, "mixed_serving_32_reuse4": 3,
                                  "ced_prefill_16k_x20": 1, "tiny_b1_4k": 1, "decode_1m_fp4_indexer": 4,
                                  "decode_1m_decoder_x20": 4, "ced_prefill_16k_x20_h5120": 1,
-                                 "ced_prefill_16k_x20_finished": 1}[args.workload]
+                                 "ced_prefill_16k_x20_finished": 1, "decode_1m_decoder_x20_swa": 4}[args.workload]
     want_cpu = not args.no_cpu_baseline
     wk = make(args.workload, replicas, dev, want_cpu)
     R = wk.replicas

@@ -129,7 +129,11 @@ __global__ void __launch_bounds__(256) swa_attn_kernel(SwaArgs a) {
     if (tid < kWin) sm.tok_scale[tid] = tid < nwin ? a.scales[(size_t)b * kWin + tid] : 0.0f;
     if (tid < kHg) sm.lse_g[tid] = a.lse[(size_t)b * a.heads + h0 + tid];
   }
-  // B fragments of QK^T straight from the ring: wave w owns entries 32w .. 32w+31
+  // Every global read of the kernel is issued here, so one memory latency
+  // covers them all: the B fragments of QK^T (wave w owns entries
+  // 32w .. 32w+31), this thread's share of the window for the PV staging
+  // (slot tid / 2, channels 128 (tid % 2) .. + 127 of each half) and the
+  // global result this lane merges into.
   uint2 kb[2][16];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -138,6 +142,23 @@ __global__ void __launch_bounds__(256) swa_attn_kernel(SwaArgs a) {
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) kb[nb][kk] = *reinterpret_cast<const uint2 *>(row + 32 * kk);
   }
+  const int se = tid >> 1, sc0 = 128 * (tid & 1);
+  uint4 raw[2][8];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(win + (size_t)(se < nwin ? se : 0) * kLatent + 256 * half + sc0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw[half][i] = src[i];
+  }
+  float og[2][4][4];  // global out of (half, nb, i): head 4 (lane / 16) + i, channel 256 half + 64 wave + 16 nb + lane % 16
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        og[half][nb][i] = a.out[((size_t)b * a.heads + h0 + 4 * (lane >> 4) + i) * kLatent + 256 * half + 64 * wave +
+                                16 * nb + (lane & 15)];
   __syncthreads();
   // ---- logits (log2 domain), masked past the window
   {
@@ -204,18 +225,14 @@ __global__ void __launch_bounds__(256) swa_attn_kernel(SwaArgs a) {
     __syncthreads();  // P and the softmax state written / the previous half's reads of v done
     {
       // stage channels 256 half .. +255 of every slot as fp16 (zeros past the window)
-      const int e = tid >> 1, c0 = 128 * (tid & 1);
-      const uint4 *src = reinterpret_cast<const uint4 *>(win + (size_t)(e < nwin ? e : 0) * kLatent + 256 * half + c0);
-      uint4 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = src[i];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        f16x8 lo = fp8x8_to_f16(make_uint2(raw[i].x, raw[i].y));
-        f16x8 hi = fp8x8_to_f16(make_uint2(raw[i].z, raw[i].w));
-        if (e >= nwin) lo = hi = f16x8{};
-        *reinterpret_cast<f16x8 *>(&sm.v[e][c0 + 16 * i]) = lo;
-        *reinterpret_cast<f16x8 *>(&sm.v[e][c0 + 16 * i + 8]) = hi;
+        const uint4 r = raw[half][i];
+        f16x8 lo = fp8x8_to_f16(make_uint2(r.x, r.y));
+        f16x8 hi = fp8x8_to_f16(make_uint2(r.z, r.w));
+        if (se >= nwin) lo = hi = f16x8{};
+        *reinterpret_cast<f16x8 *>(&sm.v[se][sc0 + 16 * i]) = lo;
+        *reinterpret_cast<f16x8 *>(&sm.v[se][sc0 + 16 * i + 8]) = hi;
       }
     }
     __syncthreads();
@@ -242,14 +259,13 @@ __global__ void __launch_bounds__(256) swa_attn_kernel(SwaArgs a) {
         const int h = 4 * (lane >> 4) + i;
         const float os = o[nb][i] * un * sm.inv_l[h];
         const float lg = sm.lse_g[h], ls = sm.lse_s[h];
-        float *dst = a.out + ((size_t)b * a.heads + h0 + h) * kLatent + c;
-        if (lg == -INFINITY) {
-          *dst = os;
-        } else {
+        float r = os;
+        if (lg != -INFINITY) {
           const float m = fmaxf(lg, ls);
           const float wg = expf(lg - m), ws = expf(ls - m);
-          *dst = (wg * *dst + ws * os) / (wg + ws);
+          r = (wg * og[half][nb][i] + ws * os) / (wg + ws);
         }
+        a.out[((size_t)b * a.heads + h0 + h) * kLatent + c] = r;
       }
     }
   }

@@ -90,6 +90,12 @@ def workload(wid):
         return Workload(7, "decode_1m_decoder_x20", batch=1, heads=64, top_k=512, sigma=1 / math.sqrt(512),
                         seq_lens=(1 << 20,), idx_dtype="fp4", hierarchical=True, layers=20, reindex_layers=4,
                         reuse_layers=15, extra=dict(idx_heads=IDX4_HEADS, group_size=4, finish=True))
+    if wid == 10:
+        # the 20-layer decoder schedule with each layer's sliding-window branch (FP8 window of 128, merged with
+        # the global branch)
+        return Workload(10, "decode_1m_decoder_x20_swa", batch=1, heads=64, top_k=512, sigma=1 / math.sqrt(512),
+                        seq_lens=(1 << 20,), idx_dtype="fp4", hierarchical=True, layers=20, reindex_layers=4,
+                        reuse_layers=15, extra=dict(idx_heads=IDX4_HEADS, group_size=4, finish=True, swa=True))
     if wid == 8:
         # CED projection at the model's hidden size 5120
         return Workload(8, "ced_prefill_16k_x20_h5120", batch=0, heads=0, top_k=0, sigma=0.0,
