@@ -250,22 +250,31 @@ __global__ void __launch_bounds__(256) swa_attn_kernel(SwaArgs a) {
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bv, o[nb], 0, 0, 0);
       }
     }
-    const float un = sm.unnorm;
+    // merge weights of this lane's 4 heads: out = cg * global + cs * (window accumulator)
+    float cg[4], cs[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * (lane >> 4) + i;
+      const float lg = sm.lse_g[h], ls = sm.lse_s[h];
+      const float win = sm.unnorm * sm.inv_l[h];  // accumulator -> window result
+      if (lg == -INFINITY) {
+        cg[i] = 0.0f;
+        cs[i] = win;
+      } else {
+        const float m = fmaxf(lg, ls);
+        const float wg = expf(lg - m), ws = expf(ls - m);
+        const float rn = 1.0f / (wg + ws);
+        cg[i] = wg * rn;
+        cs[i] = ws * rn * win;
+      }
+    }
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int c = 256 * half + 64 * wave + 16 * nb + (lane & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * (lane >> 4) + i;
-        const float os = o[nb][i] * un * sm.inv_l[h];
-        const float lg = sm.lse_g[h], ls = sm.lse_s[h];
-        float r = os;
-        if (lg != -INFINITY) {
-          const float m = fmaxf(lg, ls);
-          const float wg = expf(lg - m), ws = expf(ls - m);
-          r = (wg * og[half][nb][i] + ws * os) / (wg + ws);
-        }
-        a.out[((size_t)b * a.heads + h0 + h) * kLatent + c] = r;
+        a.out[((size_t)b * a.heads + h0 + h) * kLatent + c] = fmaf(cg[i], og[half][nb][i], cs[i] * o[nb][i]);
       }
     }
   }
