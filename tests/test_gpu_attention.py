@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from sparse_attention_fp4_kv_amd import csa2, workloads as wl
 
 from _util import ATTN_TOL, LSE_TOL, build_tables, fill_layer, make_batch, oracle_attention_rows, to_dev
@@ -122,3 +123,29 @@ def test_batch32_launch_shape():
     rng = np.random.default_rng(52)
     lens = [int(v) for v in np.exp(rng.uniform(np.log(1500), np.log(40000), size=32))]
     _run_and_check(lens, 64, 2048, seed=52)
+
+
+def test_attention_1m_decoder_shape():
+    """The decoder's attention at full size: one sequence of 1,048,576 positions behind a permuted page
+    table, 64 heads, top-K 512.  Only the selected rows are filled (with their own latents); any read of
+    another row would see zeros and fail the comparison."""
+    n, H, K = 1 << 20, 64, 512
+    st = wl.Streams(55)
+    tables, nb = build_tables(st, [n], True)
+    rng = np.random.default_rng(55)
+    sel = np.sort(rng.choice(n, size=K, replace=False)).astype(np.int32)
+    lat_sel = wl.latent_rows(st, 0, 0, K)
+    layer = csa2.PagedLayer(nb, device="cuda")
+    rows = torch.from_numpy(oracle.paged.physical_rows(tables[0], sel)).cuda()
+    codes, scales = csa2.csa2_fp4_pack(to_dev(lat_sel))
+    layer.codes[rows] = codes
+    layer.scales[rows] = scales
+    q = wl.q_heads(st, 0, 1, H, 512)
+    sigma = 1 / math.sqrt(512)
+    batch = make_batch(tables, [n], n)
+    out, lse = csa2.csa2_sparse_fp4_decode_attn(layer, batch, to_dev(q), to_dev(sel[None]), sigma)
+    torch.cuda.synchronize()
+    c = oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(lat_sel))
+    o_out, o_lse = oracle.attention.sparse_attention(q[0], c, sigma)
+    assert float(np.max(np.abs(out.cpu().numpy()[0] - o_out))) <= ATTN_TOL
+    assert float(np.max(np.abs(lse.cpu().numpy()[0] - o_lse))) <= LSE_TOL

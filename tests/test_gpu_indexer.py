@@ -266,7 +266,11 @@ def _fp4_layer(seq_lens, heads, permuted, seed):
 
 def _fp4_oracle_keys(layer, tables, keys, b, n, check_stored=True):
     """Oracle float64 keys of sequence b (packed by the oracle), and the stored bytes compared bit-exact."""
-    codes, scales = oracle.fp4.fp4_pack(keys[b])
+    if n > (1 << 18):  # the oracle's pack in slices (memory)
+        parts = [oracle.fp4.fp4_pack(keys[b][s:s + (1 << 18)]) for s in range(0, n, 1 << 18)]
+        codes, scales = np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    else:
+        codes, scales = oracle.fp4.fp4_pack(keys[b])
     if check_stored and n:
         rows = torch.from_numpy(oracle.paged.physical_rows(tables[b], np.arange(n))).cuda()
         assert np.array_equal(layer.idx_keys[rows].cpu().numpy(), codes), f"stored codes b={b}"
@@ -364,3 +368,29 @@ def test_fp4_append_packs_keys():
         assert np.array_equal(gc[row], codes[b]) and np.array_equal(gs[row], scales[b]), b
     others = np.setdiff1d(np.arange(gc.shape[0]), written)
     assert not gc[others].any() and not gs[others].any()
+
+
+@pytest.mark.parametrize("K", [512])
+def test_fp4_full_select_1m_hierarchical_and_reindex(K):
+    """The decoder's indexer at full size: 1,048,576 FP4 keys of 128 dims, 32 weighted heads, top-K 512, the
+    2048 x 8 pool and a Reindex over it (the launch shapes the 1M benchmarks time)."""
+    n = 1 << 20
+    P = 2048
+    st, tables, keys, layer = _fp4_layer([n], 32, False, 54)
+    q0, w0 = wl.q_idx_heads(st, 0, 1), wl.w_idx(st, 0, 1)
+    q1, w1 = wl.q_idx_heads(st, 1, 1), wl.w_idx(st, 1, 1)
+    batch = make_batch(tables, [n], n)
+    idx, pool = csa2.csa2_index_select(layer, batch, to_dev(q0), K, csa2.FULL, pool_blocks=P, want_pool=True,
+                                       w_idx=to_dev(w0))
+    idx1, _ = csa2.csa2_index_select(layer, batch, to_dev(q1), K, csa2.REINDEX, pool_in=pool, pool_blocks=P,
+                                     w_idx=to_dev(w1))
+    torch.cuda.synchronize()
+    idx, pool, idx1 = idx.cpu().numpy()[0], pool.cpu().numpy()[0], idx1.cpu().numpy()[0]
+    kf = _fp4_oracle_keys(layer, tables, keys, 0, n, check_stored=False)
+    s0 = oracle.indexer.index_scores(q0[0], kf, w0[0])
+    check_topk(idx, dict(enumerate(s0)), K, where="1M fp4 full")
+    assert np.all(np.diff(idx[idx >= 0]) > 0)
+    check_topk(pool, dict(enumerate(oracle.indexer.block_scores_fast(s0))), P, where="1M fp4 pool")
+    pos = oracle.indexer.pool_positions(pool[pool >= 0], n)
+    s1 = oracle.indexer.index_scores(q1[0], kf[pos], w1[0])
+    check_topk(idx1, dict(zip(pos.tolist(), s1)), K, where="1M fp4 reindex")
