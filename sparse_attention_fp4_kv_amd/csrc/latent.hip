@@ -82,10 +82,16 @@ __device__ __forceinline__ int64_t row_slot(const FinishArgs &a, int64_t r, int6
   return (int64_t)blk * kPage + p % kPage;
 }
 
+// Sum over the wave through DPP row shifts and broadcasts (VALU only; a
+// __shfl_xor butterfly costs one LDS round trip per step).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f32<0x111>(v);
+  v += dpp_f32<0x112>(v);
+  v += dpp_f32<0x114>(v);
+  v += dpp_f32<0x118>(v);
+  v += __uint_as_float(dpp_u32<0x142, 0xA>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x143, 0xC>(__float_as_uint(v)));
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
 
 __device__ __forceinline__ uint16_t exact_bf16(float v) { return (uint16_t)(__float_as_uint(v) >> 16); }
@@ -149,7 +155,7 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, dpp_f32<0xB1>(amax));  // the group's other lane (quad_perm 1,0,3,2)
     const uint32_t sc = e4m3_encode(__fdiv_rn(amax, 6.0f));
     const float s = e4m3_decode(sc);
     uint32_t word = 0u;
