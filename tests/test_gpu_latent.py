@@ -134,3 +134,14 @@ def test_append_finished_matches_rows_at_the_slot():
         pack_close(gc[row:row + 1], gs[row:row + 1], xr, rel=4e-6, abs_=4e-6)
     others = np.setdiff1d(np.arange(gc.shape[0]), written)
     assert not gc[others].any() and not gs[others].any() and not gk[others].any() and not gks[others].any()
+
+
+def test_finish_rows_without_key_projection():
+    """Without W_idx only the entry is written, and it is the same entry as with the key."""
+    L, T = 2, 70
+    c, gamma, w_idx = _inputs(84, L, T)
+    a = csa2.csa2_kv_finish_rows(to_dev(c), to_dev(gamma), EPS, THETA, None, pos0=5)
+    b = csa2.csa2_kv_finish_rows(to_dev(c), to_dev(gamma), EPS, THETA, to_dev(w_idx), pos0=5)
+    torch.cuda.synchronize()
+    assert a[2] is None and a[3] is None
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
