@@ -11,8 +11,9 @@
 // with H [tokens][hidden] and the weights in out x in orientation, so both
 // operands are read along k (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 // A workgroup computes a 256 x 128 output tile with 4 waves (128 x 64 each,
-// 4 x 2 MFMA tiles of 32 x 32), k-steps of 32 staged through LDS with a
-// register prefetch of the next step; two workgroups share a CU.  The epilogue parks the fp32 tile in
+// 4 x 2 MFMA tiles of 32 x 32), k-steps of 64 staged through one LDS buffer
+// with a register prefetch of the next step (the loads have a whole k-step of
+// 32 MFMAs per wave to arrive); two workgroups share a CU.  The epilogue parks the fp32 tile in
 // LDS and packs each 16-channel group of C straight to E2M1 + E4M3 (the same
 // rounding rules as the standalone pack) and rounds Z to bf16, so C never
 // reaches HBM in fp32 (unless the optional debug copy is asked for).
@@ -23,7 +24,7 @@ namespace csa2 {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 32;
+constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int kLdA = BK + 8;   // bf16 per LDS row (pad breaks bank conflicts)
 constexpr int kWM = 128, kWN = 64;  // wave tile: 4 x 2 MFMA tiles of 32 x 32
 constexpr int kLdC = BN + 4;   // fp32 per epilogue row (128 rows at a time)
@@ -54,8 +55,8 @@ __device__ __forceinline__ const uint16_t *weight_row(const CedArgs &a, int n) {
 
 union SmemCed {
   struct {
-    uint16_t a[2][BM][kLdA];
-    uint16_t b[2][BN][kLdA];
+    uint16_t a[1][BM][kLdA];  // one buffer: the next k-step waits in registers
+    uint16_t b[1][BN][kLdA];
   } ab;
   float c[kWM][kLdC];  // half of the output tile at a time in the epilogue
 };
@@ -71,36 +72,36 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
   const int n_total = a.n_layers * per_layer(a.w_z);
   const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
 
-  // global -> register staging: a thread loads rows (tid / 4) + 64 i of A (i < 4) and of
-  // B (i < 2), 16-byte column chunk tid % 4
-  const int ld_row = tid >> 2, ld_col = 8 * (tid & 3);
-  const uint16_t *a_src[4];
-  const uint16_t *b_src[2];
+  // global -> register staging: a thread loads rows (tid / 8) + 32 i of A (i < 8) and of
+  // B (i < 4), 16-byte column chunk tid % 8
+  const int ld_row = tid >> 3, ld_col = 8 * (tid & 7);
+  const uint16_t *a_src[8];
+  const uint16_t *b_src[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + ld_row + 64 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t m = m0 + ld_row + 32 * i;
     a_src[i] = m < a.tokens ? a.h + m * a.hidden + ld_col : nullptr;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = n0 + ld_row + 64 * i;
+  for (int i = 0; i < 4; ++i) {
+    const int n = n0 + ld_row + 32 * i;
     b_src[i] = n < n_total ? weight_row(a, n) : nullptr;
     if (b_src[i]) b_src[i] += ld_col;
   }
-  uint4 ra[4], rb[2];
+  uint4 ra[8], rb[4];
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
       ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
       rb[i] = b_src[i] ? *reinterpret_cast<const uint4 *>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(&sm.ab.a[buf][ld_row + 64 * i][ld_col]) = ra[i];
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&sm.ab.a[buf][ld_row + 32 * i][ld_col]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4 *>(&sm.ab.b[buf][ld_row + 64 * i][ld_col]) = rb[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(&sm.ab.b[buf][ld_row + 32 * i][ld_col]) = rb[i];
   };
 
   f32x16 acc[4][2];
@@ -116,7 +117,7 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
   stash(0);
   __syncthreads();
   for (int ks = 0; ks < k_steps; ++ks) {
-    const int buf = ks & 1;
+    const int buf = 0;
     if (ks + 1 < k_steps) fetch((ks + 1) * BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
@@ -132,7 +133,8 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < k_steps) stash(buf ^ 1);
+    __syncthreads();  // every wave is done reading the tile
+    if (ks + 1 < k_steps) stash(0);
     __syncthreads();
   }
 
