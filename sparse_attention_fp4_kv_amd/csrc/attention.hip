@@ -27,7 +27,9 @@
 //     relative of an fp32 P; a single fp16 P is not accurate enough for
 //     latents with x20 outlier channels.
 //   * Split-K over entries across workgroups for small batches; partial
-//     (m, l, O) are merged by an lse-weighted combine kernel.
+//     (m, l, O) are merged by an lse-weighted combine kernel (one wave per
+//     256 channels when there are few splits, one workgroup per 64 channels
+//     that loads all splits at once when there are many).
 #include "common.h"
 #include "kernels.h"
 
@@ -465,6 +467,63 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const flo
   if (lse != nullptr && quarter == 0 && tid == 0) lse[bh] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
 }
 
+// The same merge for many splits and few heads (batch-1 decode): workgroup
+// (b*H + h, q) covers 64 channels of one head with 256 threads, 16 float4
+// columns x 16 split groups (splits g and g + 16 each), then one merge of the
+// 16 groups through LDS: one round of loads instead of 32 in sequence.
+constexpr int kWideThreads = 256;
+constexpr int kWideCols = 16;  // float4 columns per workgroup
+__global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const float *__restrict__ part_o,
+                                                          const float *__restrict__ part_ml, int splits,
+                                                          float *__restrict__ out, float *__restrict__ lse) {
+  constexpr int kGroups = kWideThreads / kWideCols;  // 16
+  static_assert(kMaxSplits <= 2 * kGroups, "two splits per thread");
+  __shared__ float4 so[kGroups][kWideCols];
+  __shared__ float gm[kGroups], sl[kGroups];
+  const int bh = blockIdx.x, q = blockIdx.y;
+  const int tid = threadIdx.x, col = tid % kWideCols, g = tid / kWideCols;
+  const int c4 = kWideCols * q + col;
+  const float2 *ml = reinterpret_cast<const float2 *>(part_ml + (size_t)bh * splits * 2);
+  const float4 *po = reinterpret_cast<const float4 *>(part_o + (size_t)bh * splits * kLatent);
+  const int s0 = g, s1 = g + kGroups;
+  const bool v0 = s0 < splits, v1 = s1 < splits;
+  const float2 a0 = ml[v0 ? s0 : 0], a1 = ml[v1 ? s1 : 0];
+  const float4 p0 = po[(size_t)(v0 ? s0 : 0) * (kLatent / 4) + c4];
+  const float4 p1 = po[(size_t)(v1 ? s1 : 0) * (kLatent / 4) + c4];
+  const float m0 = v0 ? a0.x : -INFINITY, m1 = v1 ? a1.x : -INFINITY;
+  const float m = fmaxf(m0, m1);
+  const float w0 = m0 == -INFINITY ? 0.f : exp2f(m0 - m), w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - m);
+  const float l = w0 * (v0 ? a0.y : 0.f) + w1 * (v1 ? a1.y : 0.f);
+  so[g][col] = make_float4(w0 * p0.x + w1 * p1.x, w0 * p0.y + w1 * p1.y, w0 * p0.z + w1 * p1.z,
+                           w0 * p0.w + w1 * p1.w);
+  if (col == 0) {
+    gm[g] = m;
+    sl[g] = l;
+  }
+  __syncthreads();
+  if (tid < kWideCols) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) mx = fmaxf(mx, gm[i]);
+    float lt = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < kGroups; ++i) {
+      const float w = gm[i] == -INFINITY ? 0.f : exp2f(gm[i] - mx);
+      const float4 x = so[i][tid];
+      lt += w * sl[i];
+      o.x += w * x.x;
+      o.y += w * x.y;
+      o.z += w * x.z;
+      o.w += w * x.w;
+    }
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[kWideCols * q + tid] =
+        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (lse != nullptr && q == 0 && tid == 0) lse[bh] = lt > 0.f ? (mx + log2f(lt)) / kLog2e : -INFINITY;
+  }
+}
+
 // Heads per workgroup.  64 shares each dequantized tile among the most heads;
 // when that leaves the chip short of workgroups (small batches) 16 heads per
 // workgroup give 4x the workgroups, each with a quarter of the MFMA work per
@@ -532,8 +591,12 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   timer_before(kKernAttnCombine, st);
-  attn_combine_kernel<<<dim3(S.batch * heads, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
-      a.part_o, a.part_ml, splits, out, lse);
+  if (splits > 16)
+    attn_combine_wide_kernel<<<dim3(S.batch * heads, kLatent / 4 / kWideCols), dim3(kWideThreads), 0, st>>>(
+        a.part_o, a.part_ml, splits, out, lse);
+  else
+    attn_combine_kernel<<<dim3(S.batch * heads, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
+        a.part_o, a.part_ml, splits, out, lse);
   timer_after(kKernAttnCombine, st);
   return hipGetLastError();
 }
