@@ -591,7 +591,7 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   timer_before(kKernAttnCombine, st);
-  if (splits > 16)
+  if (splits > 8)
     attn_combine_wide_kernel<<<dim3(S.batch * heads, kLatent / 4 / kWideCols), dim3(kWideThreads), 0, st>>>(
         a.part_o, a.part_ml, splits, out, lse);
   else

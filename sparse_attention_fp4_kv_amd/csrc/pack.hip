@@ -51,12 +51,46 @@ __global__ void __launch_bounds__(256) fp4_unpack_kernel(const uint8_t *__restri
 
 // One workgroup of 64 threads per sequence: threads 0..31 pack the 32 groups
 // of the 512-channel latent into the slot of position seq_lens[b]; the rest
-// copy the rope side-band and the indexer key.
+// copy the rope side-band and the indexer key (threads 32..39 pack an FP4 key).
+// Every operand is read before the slot is known (none depends on it), so the
+// operand loads are in flight together with the two table reads.
 __global__ void __launch_bounds__(64) kv_append_kernel(KvLayerDev L, SeqsDev S, const float *__restrict__ latent,
                                                        const uint16_t *__restrict__ rope,
                                                        const void *__restrict__ idx_key) {
+  constexpr int kKey4 = 128;  // FP4 indexer key dims
   const int b = blockIdx.x;
   const int t = threadIdx.x;
+  const int u = t - kLatent / kGroup;  // 0..31 in the upper half
+  const bool has_key = idx_key != nullptr && L.idx_keys != nullptr;
+  const float *gsrc = nullptr;  // the 16 values this thread packs, if any
+  if (u < 0) {
+    if (latent != nullptr) gsrc = latent + (int64_t)b * kLatent + t * kGroup;
+  } else if (has_key && L.idx_fp4 && u < kKey4 / kGroup) {
+    gsrc = static_cast<const float *>(idx_key) + (int64_t)b * kKey4 + u * kGroup;
+  }
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = gsrc != nullptr ? gsrc[i] : 0.f;
+  const bool copy_rope = u >= 0 && rope != nullptr && L.rope_dim != 0;  // rope_dim is 64
+  uint16_t r0 = 0, r1 = 0;
+  if (copy_rope) {
+    r0 = rope[(int64_t)b * 64 + u];
+    r1 = rope[(int64_t)b * 64 + u + 32];
+  }
+  const bool copy_key = u >= 0 && has_key && !L.idx_fp4;  // dims u and u + 32 of 64
+  uint32_t k0 = 0, k1 = 0;
+  if (copy_key) {
+    if (L.idx_f32) {
+      const uint32_t *src = static_cast<const uint32_t *>(idx_key) + (int64_t)b * kIdxDim;
+      k0 = src[u];
+      k1 = src[u + 32];
+    } else {
+      const uint16_t *src = static_cast<const uint16_t *>(idx_key) + (int64_t)b * kIdxDim;
+      k0 = src[u];
+      k1 = src[u + 32];
+    }
+  }
+
   const int p = S.seq_lens[b];
   if (p < 0) return;
   const int page = p / kPage;
@@ -64,43 +98,30 @@ __global__ void __launch_bounds__(64) kv_append_kernel(KvLayerDev L, SeqsDev S, 
   const int blk = S.block_table[(int64_t)b * S.max_blocks + page];
   if (blk < 0 || blk >= L.num_blocks) return;
   const int64_t slot = (int64_t)blk * kPage + p % kPage;
-  if (t < kLatent / kGroup) {
-    if (latent == nullptr) return;
-    const float *src = latent + (int64_t)b * kLatent + t * kGroup;
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = src[i];
+  if (gsrc != nullptr) {
     uint32_t w0, w1;
     const uint32_t sc = pack_group16(v, &w0, &w1);
-    reinterpret_cast<uint2 *>(L.codes + slot * (kLatent / 2))[t] = make_uint2(w0, w1);
-    L.scales[slot * (kLatent / kGroup) + t] = (uint8_t)sc;
-  } else {
-    const int u = t - kLatent / kGroup;  // 0..31
-    if (rope != nullptr && L.rope_dim != 0) {
-      for (int r = u; r < L.rope_dim; r += 32) L.rope[slot * L.rope_dim + r] = rope[(int64_t)b * L.rope_dim + r];
+    if (u < 0) {
+      reinterpret_cast<uint2 *>(L.codes + slot * (kLatent / 2))[t] = make_uint2(w0, w1);
+      L.scales[slot * (kLatent / kGroup) + t] = (uint8_t)sc;
+    } else {
+      reinterpret_cast<uint2 *>(static_cast<uint8_t *>(L.idx_keys) + slot * (kKey4 / 2))[u] = make_uint2(w0, w1);
+      L.idx_scales[slot * (kKey4 / kGroup) + u] = (uint8_t)sc;
     }
-    if (idx_key != nullptr && L.idx_keys != nullptr) {
-      if (L.idx_fp4) {  // 128 fp32 dims packed like the latent: lane u < 8 packs dims 16u .. 16u+15
-        constexpr int kDim = 128;
-        if (u < kDim / kGroup) {
-          const float *src = static_cast<const float *>(idx_key) + (int64_t)b * kDim + u * kGroup;
-          float v[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v[i] = src[i];
-          uint32_t w0, w1;
-          const uint32_t sc = pack_group16(v, &w0, &w1);
-          reinterpret_cast<uint2 *>(static_cast<uint8_t *>(L.idx_keys) + slot * (kDim / 2))[u] = make_uint2(w0, w1);
-          L.idx_scales[slot * (kDim / kGroup) + u] = (uint8_t)sc;
-        }
-      } else if (L.idx_f32) {
-        const float *src = static_cast<const float *>(idx_key) + (int64_t)b * kIdxDim;
-        float *dst = static_cast<float *>(L.idx_keys) + slot * kIdxDim;
-        for (int r = u; r < kIdxDim; r += 32) dst[r] = src[r];
-      } else {
-        const uint16_t *src = static_cast<const uint16_t *>(idx_key) + (int64_t)b * kIdxDim;
-        uint16_t *dst = static_cast<uint16_t *>(L.idx_keys) + slot * kIdxDim;
-        for (int r = u; r < kIdxDim; r += 32) dst[r] = src[r];
-      }
+  }
+  if (copy_rope) {
+    L.rope[slot * 64 + u] = r0;
+    L.rope[slot * 64 + u + 32] = r1;
+  }
+  if (copy_key) {
+    if (L.idx_f32) {
+      uint32_t *dst = static_cast<uint32_t *>(L.idx_keys) + slot * kIdxDim;
+      dst[u] = k0;
+      dst[u + 32] = k1;
+    } else {
+      uint16_t *dst = static_cast<uint16_t *>(L.idx_keys) + slot * kIdxDim;
+      dst[u] = (uint16_t)k0;
+      dst[u + 32] = (uint16_t)k1;
     }
   }
 }
