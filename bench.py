@@ -302,6 +302,7 @@ class DecoderX20(Decode1M):
                     self.rings[r][l].codes.copy_(self.rings[0][l].codes)
                     self.rings[r][l].scales.copy_(self.rings[0][l].scales)
             self.win_new = [torch.from_numpy(self.win_lat[l][127:128].copy()).to(dev) for l in range(self.L)]
+            self.attn_swa_ws = csa2.workspace(csa2.attn_swa_workspace_bytes(1, self.H, self.K), dev)
             torch.cuda.synchronize()
 
     def step(self, r):
@@ -317,13 +318,14 @@ class DecoderX20(Decode1M):
                                        pool_blocks=self.P, ws=self.sel_ws, indices=self.gidx[g],
                                        w_idx=self.w_idx_d[l0])
             for l in range(l0, l0 + self.G):  # the lead and its Reuse layers
-                if self.swa:  # the layer's own window entry of the new token
+                if self.swa:  # the layer's own window entry of the new token, then both branches in one softmax
                     csa2.csa2_swa_append(self.rings[r][l], self.batch_prev.seq_lens, self.win_new[l])
-                csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
-                                                 ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
-                if self.swa:
-                    csa2.csa2_swa_attn_merge(self.rings[r][l], self.batch.seq_lens, self.q_d[l], self.w.sigma,
-                                             self.out[l], self.lse[l])
+                    csa2.csa2_sparse_fp4_decode_attn_swa(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
+                                                         self.rings[r][l], ws=self.attn_swa_ws, out=self.out[l],
+                                                         lse=self.lse[l])
+                else:
+                    csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
+                                                     ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
 
     def algorithmic_bytes(self):
         n, K, P, H, L = self.n, self.K, self.P, self.H, self.L
@@ -332,9 +334,9 @@ class DecoderX20(Decode1M):
         kv = L * K * 288
         qio = L * (H * 512 * 2 + H * 512 * 4 + H * 4)
         append = 512 * 4 + 288 + 72 + (512 * 4 + 128 * 512 * 2 if self.finish else 128 * 4)
-        if self.swa:  # per layer: the new window entry, and the window read twice (QK, then PV)
+        if self.swa:  # per layer: the new window entry, and the window read once
             append += L * (512 * 4 + 512 + 4)
-            kv += L * 2 * 128 * (512 + 4)
+            kv += L * 128 * (512 + 4)
         return scan + reindex + kv + qio + append
 
     def oracle_step(self):
@@ -361,7 +363,8 @@ class DecoderX20(Decode1M):
         c = super().config()
         c["layers"] = "20 in 5 groups of 4: Full + 3 Reuse, then 4 x (Reindex + 3 Reuse), one KV source"
         if self.swa:
-            c["swa"] = "per layer: FP8 window of 128 (E4M3 + fp32 per-token scale), merged with the global branch"
+            c["swa"] = ("per layer: FP8 window of 128 (E4M3 + fp32 per-token scale) in one softmax with the global "
+                        "branch (the window slots run as extra splits of the attention kernel)")
         return c
 
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 4
+#define CSA2_ABI_VERSION 5
 
 typedef enum {
   CSA2_OK = 0,
@@ -308,6 +308,26 @@ csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_s
                                         const uint16_t *q, int32_t heads, const int32_t *indices,
                                         int32_t top_k, float softmax_scale, float *out, float *lse,
                                         void *ws, size_t ws_bytes, csa2_stream stream);
+
+/* ---- The same attention with the sliding-window branch in one softmax
+ * ([P1] "KV bottleneck" and "Causal Encoder-Decoder": a local window of 128
+ * beside the global branch; "FP4 KV cache": the window stays FP8).  The
+ * result equals csa2_sparse_fp4_decode_attn followed by csa2_swa_attn_merge
+ * with seq_lens = seqs->seq_lens (up to rounding): out and lse are the
+ * attention over the union of the selected entries and the window slots
+ * holding positions max(0, n - 128) .. n - 1, n = seqs->seq_lens[b]; the
+ * window contributes logits to the latent part of q only.  The window's 128
+ * slots run as four more split workgroups of the same kernel, so no second
+ * attention pass and no in-place merge are needed.  win: the ring (win->batch
+ * >= seqs->batch); other arguments and limits as for
+ * csa2_sparse_fp4_decode_attn; workspace from csa2_attn_swa_workspace_size. */
+csa2_status csa2_attn_swa_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim,
+                                         size_t *bytes);
+csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const csa2_seqs *seqs,
+                                            const uint16_t *q, int32_t heads, const int32_t *indices,
+                                            int32_t top_k, float softmax_scale, const csa2_swa_window *win,
+                                            float *out, float *lse, void *ws, size_t ws_bytes,
+                                            csa2_stream stream);
 
 /* ---- Host-side page allocator (no device memory): a free list of block ids
  * [0, num_blocks).  Not thread-safe; one instance per owner. */

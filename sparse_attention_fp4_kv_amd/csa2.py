@@ -104,6 +104,9 @@ SIGNATURES = {
     "csa2_index_select": (ctypes.c_int, [_PKV, _PSQ, _P, _P, _I32, _I32, _P, _P, _I32, _I32, _P, _P, _SZ, _P]),
     "csa2_attn_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_sparse_fp4_decode_attn": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "csa2_attn_swa_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "csa2_sparse_fp4_decode_attn_swa": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float,
+                                                       ctypes.POINTER(SwaWindow), _P, _P, _P, _SZ, _P]),
     "csa2_block_pool_create": (_P, [_I32]),
     "csa2_block_alloc": (ctypes.c_int, [_P, _I32, _P]),
     "csa2_block_free": (ctypes.c_int, [_P, _I32, _P]),
@@ -439,6 +442,31 @@ def csa2_sparse_fp4_decode_attn(layer, batch, q, indices, softmax_scale, ws=None
     _check(lib().csa2_sparse_fp4_decode_attn(ctypes.byref(kv), ctypes.byref(sq), _ptr(q), H, _ptr(indices), K,
                                              float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                              _stream()), "csa2_sparse_fp4_decode_attn")
+    return out, lse
+
+
+def attn_swa_workspace_bytes(batch, heads, top_k):
+    n = ctypes.c_size_t()
+    _check(lib().csa2_attn_swa_workspace_size(batch, heads, top_k, 512, ctypes.byref(n)),
+           "csa2_attn_swa_workspace_size")
+    return n.value
+
+
+def csa2_sparse_fp4_decode_attn_swa(layer, batch, q, indices, softmax_scale, ring, ws=None, out=None, lse=None):
+    """csa2_sparse_fp4_decode_attn with the sliding-window ring in the same softmax -> (out, lse)."""
+    B, H, _ = q.shape
+    K = indices.shape[1]
+    dev = q.device
+    if ws is None:
+        ws = workspace(attn_swa_workspace_bytes(B, H, K), dev)
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    kv, sq, w = layer.struct(), batch.struct(), ring.struct()
+    _check(lib().csa2_sparse_fp4_decode_attn_swa(ctypes.byref(kv), ctypes.byref(sq), _ptr(q), H, _ptr(indices), K,
+                                                 float(softmax_scale), ctypes.byref(w), _ptr(out), _ptr(lse),
+                                                 _ptr(ws), ws.numel(), _stream()), "csa2_sparse_fp4_decode_attn_swa")
     return out, lse
 
 

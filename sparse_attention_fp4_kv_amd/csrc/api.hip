@@ -380,7 +380,16 @@ csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k
   if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
       top_k > kMaxTopK || latent_dim != 512)
     return CSA2_ERR_INVALID_ARG;
-  *bytes = attn_workspace_bytes(batch, heads, top_k);
+  *bytes = attn_workspace_bytes(batch, heads, top_k, false);
+  return CSA2_OK;
+}
+
+csa2_status csa2_attn_swa_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim,
+                                         size_t *bytes) {
+  if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
+      top_k > kMaxTopK || latent_dim != 512)
+    return CSA2_ERR_INVALID_ARG;
+  *bytes = attn_workspace_bytes(batch, heads, top_k, true);
   return CSA2_OK;
 }
 
@@ -397,9 +406,33 @@ csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_s
   if (S.batch == 0) return CSA2_OK;
   if (q == nullptr || indices == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16))
     return CSA2_ERR_INVALID_ARG;
-  const size_t need = attn_workspace_bytes(S.batch, heads, top_k);
+  const size_t need = attn_workspace_bytes(S.batch, heads, top_k, false);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, out, lse, ws, as_stream(stream)));
+  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, nullptr, nullptr, out, lse, ws,
+                                     as_stream(stream)));
+}
+
+csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const csa2_seqs *seqs, const uint16_t *q,
+                                            int32_t heads, const int32_t *indices, int32_t top_k,
+                                            float softmax_scale, const csa2_swa_window *win, float *out, float *lse,
+                                            void *ws, size_t ws_bytes, csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(layer, true, false, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return CSA2_ERR_INVALID_ARG;
+  if (win == nullptr || win->batch < S.batch) return CSA2_ERR_INVALID_ARG;
+  if (S.batch == 0) return CSA2_OK;
+  if (q == nullptr || indices == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16))
+    return CSA2_ERR_INVALID_ARG;
+  if (win->codes == nullptr || win->scales == nullptr || !aligned(win->codes, 16) || !aligned(win->scales, 4))
+    return CSA2_ERR_INVALID_ARG;
+  const size_t need = attn_workspace_bytes(S.batch, heads, top_k, true);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, win->codes, win->scales, out,
+                                     lse, ws, as_stream(stream)));
 }
 
 csa2_block_pool *csa2_block_pool_create(int32_t num_blocks) {

@@ -30,6 +30,16 @@
 //     (m, l, O) are merged by an lse-weighted combine kernel (one wave per
 //     256 channels when there are few splits, one workgroup per 64 channels
 //     that loads all splits at once when there are many).
+//   * The sliding-window branch (sections "KV bottleneck" and "FP4 KV
+//     cache": a local window of 128 FP8 entries beside the global selection;
+//     merged as one softmax over the union of both entry sets, this library's
+//     reading) can ride along: its 128 ring slots are four more split
+//     workgroups of one 32-entry tile each.  Their tile holds the E4M3 codes
+//     as fp16 (exact) with a zero rope part (window keys have none); the
+//     per-token fp32 scale multiplies the logit, and P times that scale
+//     (normalized by a power of two into [1, 2) over the tile, undone on the
+//     partial) enters PV, so the combine merges window and global partials
+//     alike.
 #include "common.h"
 #include "kernels.h"
 
@@ -44,6 +54,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 32;         // split-K workgroups per (sequence, head group)
 constexpr int kSlotCap = 2048;         // entries one workgroup resolves up front
 constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+constexpr int kWinSlots = 128;          // sliding-window ring slots per sequence
+constexpr int kWinSplits = kWinSlots / kT;  // window tiles = extra split workgroups
 
 struct AttnArgs {
   KvLayerDev L;
@@ -52,13 +64,16 @@ struct AttnArgs {
   const int32_t *idx;     // [B][K]
   int heads;              // H
   int top_k;
-  int splits;             // workgroups per (b, head group) along the entries
+  int splits;             // workgroups per (b, head group) along the selected entries
+  int parts;              // partials per (b, head): splits, plus kWinSplits with the window
   int tiles_per_split;
+  const uint8_t *win_codes;  // [B][128][512] E4M3 window entries, or null
+  const float *win_scales;   // [B][128] per-token scales
   float scale_log2;       // softmax scale * log2(e)
   float *out;             // [B][H][512]  (splits == 1)
   float *lse;             // [B][H] or null
-  float *part_o;          // [B][H][splits][512]  (splits > 1)
-  float *part_ml;         // [B][H][splits][2]
+  float *part_o;          // [B][H][parts][512]  (parts > 1)
+  float *part_ml;         // [B][H][parts][2]
 };
 
 template <int MT>
@@ -69,6 +84,8 @@ struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile 
   __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
   float m_run[16 * MT], l_run[16 * MT], alpha[16 * MT];
   uint32_t slot[kSlotCap];       // physical rows of this workgroup's entries (kNoSlot: skipped)
+  float wts[kT], wp[kT];         // window tile: token scales, and times the P normalization
+  float unnorm;                  // window tile: the P normalization, inverted
 };
 
 __device__ __forceinline__ f16x8 lds_f16x8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
@@ -138,12 +155,18 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int h0 = hg * HG;
   const int n = min(max(a.S.seq_lens[b], 0), a.S.max_len);
+  // workgroups past the selection's splits take window tile split - splits:
+  // ring slots 32 wt .. 32 wt + 31, valid below min(seq_len, 128)
+  const bool win = split >= a.splits;
+  const int wt = split - a.splits;
+  const int nwin = min(max(a.S.seq_lens[b], 0), kWinSlots);
 
   const int n_tiles_all = (a.top_k + kT - 1) / kT;
-  const int tile_begin = split * a.tiles_per_split;
-  const int tile_end = min(tile_begin + a.tiles_per_split, n_tiles_all);
+  const int tile_begin = win ? 0 : split * a.tiles_per_split;
+  const int tile_end = win ? (nwin > kT * wt ? 1 : 0) : min(tile_begin + a.tiles_per_split, n_tiles_all);
   const int e_begin = tile_begin * kT;
-  const int e_count = max(0, min(tile_end * kT, a.top_k) - e_begin);  // <= kSlotCap (host-chosen splits)
+  // <= kSlotCap (host-chosen splits)
+  const int e_count = win ? kT : max(0, min(tile_end * kT, a.top_k) - e_begin);
   const int32_t *idx_row = a.idx + (size_t)b * a.top_k;
 
   // ---- QK^T work of this wave: one M-tile (16 heads) and 1 or 2 N-tiles of 16 entries
@@ -160,10 +183,14 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   // reads for all entries at once; the q loads below overlap them)
   int pos[kSlotCap / 256];
 #pragma unroll
-  for (int j = 0; j < kSlotCap / 256; ++j) {
-    const int i = 256 * j + tid;
-    const int p = idx_row[min(e_begin + i, a.top_k - 1)];  // clamped read, masked below
-    pos[j] = i < e_count ? p : -1;
+  for (int j = 0; j < kSlotCap / 256; ++j) pos[j] = -1;
+  if (!win) {
+#pragma unroll
+    for (int j = 0; j < kSlotCap / 256; ++j) {
+      const int i = 256 * j + tid;
+      const int p = idx_row[min(e_begin + i, a.top_k - 1)];  // clamped read, masked below
+      pos[j] = i < e_count ? p : -1;
+    }
   }
 
   // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*(qk_k0 + ks) + 8*(lane/16) .. +7
@@ -178,7 +205,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     for (int ks = 0; ks < QKS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
   }
 
-  {
+  if (!win) {
     int blk[kSlotCap / 256];
 #pragma unroll
     for (int j = 0; j < kSlotCap / 256; ++j) {
@@ -194,6 +221,21 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < a.L.num_blocks;
       sm.slot[i] = ok ? (uint32_t)blk[j] * kPage + (uint32_t)(pos[j] % kPage) : kNoSlot;
     }
+  } else if (tid < kT) {
+    // window tile: ring slots, token scales, and a power of two that brings the
+    // tile's largest token scale into [1, 2) (P times the scale stays in fp16's
+    // normal range)
+    const int s = kT * wt + tid;
+    const bool ok = s < nwin;
+    sm.slot[tid] = ok ? (uint32_t)s : kNoSlot;
+    const float ts = ok ? a.win_scales[(size_t)b * kWinSlots + s] : 0.0f;
+    float mx = ts;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+    const float norm = mx > 0.0f ? __uint_as_float((254u - ((__float_as_uint(mx) >> 23) & 0xFFu)) << 23) : 1.0f;
+    sm.wts[tid] = ts;
+    sm.wp[tid] = ts * norm;
+    if (tid == 0) sm.unnorm = 1.0f / norm;
   }
 
   // ---- PV accumulators: wave owns channels [128*wave, 128*wave+128) for all HG heads
@@ -276,9 +318,11 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const int ent = 16 * nt + (lane & 15);
       const int li = tile * kT + ent - e_begin;
       const bool valid = qk_half == 1 || (li < e_count && sm.slot[li] != kNoSlot);  // masked once
+      float es = a.scale_log2;
+      if (win) es *= sm.wts[ent];  // window entries: the token scale of the E4M3 codes
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
-        sm.s[qk_half][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * a.scale_log2 : -INFINITY;
+        sm.s[qk_half][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * es : -INFINITY;
     }
     if (next != nullptr) dequant(*next, cq_next);
     __syncthreads();
@@ -302,8 +346,9 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       for (int i = 0; i < EPT; ++i) {
         const float pv = (m_new == -INFINITY) ? 0.f : exp2f(v[i] - m_new);
         sum += pv;
-        const f16 ph = (f16)pv;
-        const f16 pl = (f16)(pv - (float)ph);
+        const float pw = win ? pv * sm.wp[sm_part * EPT + i] : pv;  // window: P times the token scale
+        const f16 ph = (f16)pw;
+        const f16 pl = (f16)(pw - (float)ph);
         sm.p_hi[sm_h][sm_part * EPT + i] = ph;
         sm.p_lo[sm_h][sm_part * EPT + i] = pl;
       }
@@ -355,7 +400,30 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   // ---- tiles: three register sets of raw rows (each tile's loads are issued
   // three tiles ahead; loads past the last tile re-read the last tile) and
   // three tile buffers, so the unrolled loop keeps both in step
-  if (tile_begin < tile_end && a.L.num_blocks > 0) {
+  if (win) {
+    if (tile_begin < tile_end) {
+      // the window tile: thread -> entry tile_entry, channels 64 tile_block .. + 63
+      // (64 E4M3 bytes), converted to fp16 (exact); skipped slots and the rope
+      // part are zero
+      const uint32_t slot = sm.slot[tile_entry];
+      const uint4 *cp = reinterpret_cast<const uint4 *>(
+          a.win_codes + ((size_t)b * kWinSlots + (slot == kNoSlot ? 0 : slot)) * kLatent + 64 * tile_block);
+      uint4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = cp[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x8 lo = fp8x8_to_f16(make_uint2(w[i].x, w[i].y));
+        f16x8 hi = fp8x8_to_f16(make_uint2(w[i].z, w[i].w));
+        if (slot == kNoSlot) lo = hi = f16x8{};
+        *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][64 * tile_block + 16 * i]) = lo;
+        *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][64 * tile_block + 16 * i + 8]) = hi;
+      }
+      if constexpr (ROPE) *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][kLatent + 8 * tile_block]) = f16x8{};
+      __syncthreads();
+      step(0, sm.cq[0], nullptr, sm.cq[1]);
+    }
+  } else if (tile_begin < tile_end && a.L.num_blocks > 0) {
     const int last = tile_end - 1;
     Raw ra, rb, rc;
     load_raw(tile_begin, ra);
@@ -386,15 +454,15 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   // ---- write the result straight from the accumulators (PV column = channel):
   // final rows when unsplit, else a partial for the combine; the 16 lanes of a
   // row group write 64 contiguous bytes.
-  const bool final_out = a.splits == 1;
+  const bool final_out = a.parts == 1;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int hl = 16 * mt + 4 * (lane >> 4) + r;
       const size_t h = (size_t)b * a.heads + h0 + hl;
-      float sc = 1.0f;
-      float *dst = a.part_o + (h * a.splits + split) * kLatent;
+      float sc = win ? sm.unnorm : 1.0f;
+      float *dst = a.part_o + (h * a.parts + split) * kLatent;
       if (final_out) {
         const float l = sm.l_run[hl];
         sc = l > 0.f ? 1.0f / l : 0.f;
@@ -410,7 +478,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       a.lse[(size_t)b * a.heads + h0 + tid] = l > 0.f ? (sm.m_run[tid] + log2f(l)) / kLog2e : -INFINITY;
     }
   } else if (tid < HG) {
-    float *ml = a.part_ml + (((size_t)b * a.heads + h0 + tid) * a.splits + split) * 2;
+    float *ml = a.part_ml + (((size_t)b * a.heads + h0 + tid) * a.parts + split) * 2;
     ml[0] = sm.m_run[tid];
     ml[1] = sm.l_run[tid];
   }
@@ -467,17 +535,18 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const flo
   if (lse != nullptr && quarter == 0 && tid == 0) lse[bh] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
 }
 
-// The same merge for many splits and few heads (batch-1 decode): workgroup
-// (b*H + h, q) covers 64 channels of one head with 256 threads, 16 float4
-// columns x 16 split groups (splits g and g + 16 each), then one merge of the
-// 16 groups through LDS: one round of loads instead of 32 in sequence.
+// The same merge for many splits (batch-1 decode): workgroup (b*H + h, q)
+// covers 64 channels of one head with 256 threads, 16 float4 columns x 16
+// split groups (splits g, g + 16, g + 32 each), then one merge of the 16
+// groups through LDS: one round of loads instead of a long chain per thread.
 constexpr int kWideThreads = 256;
 constexpr int kWideCols = 16;  // float4 columns per workgroup
+constexpr int kWidePer = 3;    // splits per thread
 __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
                                                           float *__restrict__ out, float *__restrict__ lse) {
   constexpr int kGroups = kWideThreads / kWideCols;  // 16
-  static_assert(kMaxSplits <= 2 * kGroups, "two splits per thread");
+  static_assert(kMaxSplits + kWinSplits <= kWidePer * kGroups, "splits per thread");
   __shared__ float4 so[kGroups][kWideCols];
   __shared__ float gm[kGroups], sl[kGroups];
   const int bh = blockIdx.x, q = blockIdx.y;
@@ -485,17 +554,34 @@ __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const f
   const int c4 = kWideCols * q + col;
   const float2 *ml = reinterpret_cast<const float2 *>(part_ml + (size_t)bh * splits * 2);
   const float4 *po = reinterpret_cast<const float4 *>(part_o + (size_t)bh * splits * kLatent);
-  const int s0 = g, s1 = g + kGroups;
-  const bool v0 = s0 < splits, v1 = s1 < splits;
-  const float2 a0 = ml[v0 ? s0 : 0], a1 = ml[v1 ? s1 : 0];
-  const float4 p0 = po[(size_t)(v0 ? s0 : 0) * (kLatent / 4) + c4];
-  const float4 p1 = po[(size_t)(v1 ? s1 : 0) * (kLatent / 4) + c4];
-  const float m0 = v0 ? a0.x : -INFINITY, m1 = v1 ? a1.x : -INFINITY;
-  const float m = fmaxf(m0, m1);
-  const float w0 = m0 == -INFINITY ? 0.f : exp2f(m0 - m), w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - m);
-  const float l = w0 * (v0 ? a0.y : 0.f) + w1 * (v1 ? a1.y : 0.f);
-  so[g][col] = make_float4(w0 * p0.x + w1 * p1.x, w0 * p0.y + w1 * p1.y, w0 * p0.z + w1 * p1.z,
-                           w0 * p0.w + w1 * p1.w);
+  float2 a[kWidePer];
+  float4 p[kWidePer];
+#pragma unroll
+  for (int j = 0; j < kWidePer; ++j) {  // unconditional loads (clamped split index), masked below
+    const int s = g + kGroups * j;
+    const int sc = s < splits ? s : 0;
+    a[j] = ml[sc];
+    p[j] = po[(size_t)sc * (kLatent / 4) + c4];
+  }
+  float mj[kWidePer];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kWidePer; ++j) {
+    mj[j] = g + kGroups * j < splits ? a[j].x : -INFINITY;
+    m = fmaxf(m, mj[j]);
+  }
+  float l = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int j = 0; j < kWidePer; ++j) {
+    const float w = mj[j] == -INFINITY ? 0.f : exp2f(mj[j] - m);  // empty splits: m = -inf, l = 0, O = 0
+    l += w * a[j].y;
+    o.x += w * p[j].x;
+    o.y += w * p[j].y;
+    o.z += w * p[j].z;
+    o.w += w * p[j].w;
+  }
+  so[g][col] = o;
   if (col == 0) {
     gm[g] = m;
     sl[g] = l;
@@ -506,20 +592,20 @@ __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const f
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) mx = fmaxf(mx, gm[i]);
     float lt = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < kGroups; ++i) {
       const float w = gm[i] == -INFINITY ? 0.f : exp2f(gm[i] - mx);
       const float4 x = so[i][tid];
       lt += w * sl[i];
-      o.x += w * x.x;
-      o.y += w * x.y;
-      o.z += w * x.z;
-      o.w += w * x.w;
+      r.x += w * x.x;
+      r.y += w * x.y;
+      r.z += w * x.z;
+      r.w += w * x.w;
     }
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[kWideCols * q + tid] =
-        make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
     if (lse != nullptr && q == 0 && tid == 0) lse[bh] = lt > 0.f ? (mx + log2f(lt)) / kLog2e : -INFINITY;
   }
 }
@@ -547,20 +633,22 @@ int choose_splits(int batch, int heads, int top_k) {
 
 }  // namespace
 
-size_t attn_workspace_bytes(int batch, int heads, int top_k) {
-  const int splits = choose_splits(batch, heads, top_k);
-  if (splits == 1) return 256;
-  const size_t o = (size_t)batch * heads * splits * kLatent * sizeof(float);
-  const size_t ml = (size_t)batch * heads * splits * 2 * sizeof(float);
+size_t attn_workspace_bytes(int batch, int heads, int top_k, bool window) {
+  const int parts = choose_splits(batch, heads, top_k) + (window ? kWinSplits : 0);
+  if (parts == 1) return 256;
+  const size_t o = (size_t)batch * heads * parts * kLatent * sizeof(float);
+  const size_t ml = (size_t)batch * heads * parts * 2 * sizeof(float);
   return ((o + 255) & ~(size_t)255) + ((ml + 255) & ~(size_t)255);
 }
 
 hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
-                              const int32_t *indices, int top_k, float scale, float *out, float *lse, void *ws,
-                              hipStream_t st) {
+                              const int32_t *indices, int top_k, float scale, const uint8_t *win_codes,
+                              const float *win_scales, float *out, float *lse, void *ws, hipStream_t st) {
   if (S.batch == 0) return hipSuccess;
+  const bool window = win_codes != nullptr;
   const int hgsz = heads_per_group(S.batch, heads);
   const int splits = choose_splits(S.batch, heads, top_k);
+  const int parts = splits + (window ? kWinSplits : 0);
   const int tiles = (top_k + kT - 1) / kT;
   AttnArgs a;
   a.L = L;
@@ -570,14 +658,17 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   a.heads = heads;
   a.top_k = top_k;
   a.splits = splits;
+  a.parts = parts;
   a.tiles_per_split = (tiles + splits - 1) / splits;
+  a.win_codes = win_codes;
+  a.win_scales = win_scales;
   a.scale_log2 = scale * kLog2e;
   a.out = out;
   a.lse = lse;
-  const size_t o_bytes = (size_t)S.batch * heads * splits * kLatent * sizeof(float);
+  const size_t o_bytes = (size_t)S.batch * heads * parts * kLatent * sizeof(float);
   a.part_o = static_cast<float *>(ws);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o_bytes + 255) & ~(size_t)255));
-  const dim3 grid(splits, heads / hgsz, S.batch);
+  const dim3 grid(parts, heads / hgsz, S.batch);
   timer_before(kKernSparseAttn, st);
   const bool rope = L.rope_dim != 0;
   if (hgsz == 64) {
@@ -589,14 +680,14 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   }
   timer_after(kKernSparseAttn, st);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || splits == 1) return e;
+  if (e != hipSuccess || parts == 1) return e;
   timer_before(kKernAttnCombine, st);
-  if (splits > 8)
+  if (parts > 8)
     attn_combine_wide_kernel<<<dim3(S.batch * heads, kLatent / 4 / kWideCols), dim3(kWideThreads), 0, st>>>(
-        a.part_o, a.part_ml, splits, out, lse);
+        a.part_o, a.part_ml, parts, out, lse);
   else
     attn_combine_kernel<<<dim3(S.batch * heads, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
-        a.part_o, a.part_ml, splits, out, lse);
+        a.part_o, a.part_ml, parts, out, lse);
   timer_after(kKernAttnCombine, st);
   return hipGetLastError();
 }

@@ -104,6 +104,18 @@ __device__ __forceinline__ f16x2 deq2(uint32_t word, f16x2 s2) {
   return v * s2;
 }
 
+// 8 FP8 codes (two words) -> f16x8, exact.
+__device__ __forceinline__ f16x8 fp8x8_to_f16(uint2 w) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true);
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
 // 8 nibbles (one 32-bit word) -> f16x8 scaled by s.
 __device__ __forceinline__ f16x8 deq8(uint32_t word, f16 s) {
   const f16x2 s2 = {s, s};

@@ -61,18 +61,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// 8 FP8 codes (two words) -> f16x8, exact.
-__device__ __forceinline__ f16x8 fp8x8_to_f16(uint2 w) {
-  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, false);
-  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.x, 1.0f, true);
-  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, false);
-  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.y, 1.0f, true);
-  f16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
 // PV operand (B of v_mfma_f32_16x16x32_f16: k = entries, n = channels) from
 // the row-major window with two transposing loads: within 16 lanes,
 // ds_read_b64_tr_b16 gives lane i element i % 4 of the 8-byte chunks read by

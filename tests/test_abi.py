@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(csa2.LIB_PATH)
     for name in header_functions():
         assert hasattr(raw, name), name
-    assert csa2.lib().csa2_abi_version() == 4
+    assert csa2.lib().csa2_abi_version() == 5
     assert csa2.lib().csa2_status_string(3) == b"workspace missing or too small"
 
 
@@ -128,6 +128,29 @@ def test_swa_validation_rejects_before_launch():
         assert L.csa2_swa_attn_merge(P(w), 16, 1, 16, heads, qd, 0.1, 16, 16, None) == csa2.ERR_INVALID_ARG
     assert L.csa2_swa_attn_merge(P(w), 16, 1, 16, 16, 512, 0.0, 16, 16, None) == csa2.ERR_INVALID_ARG
     assert L.csa2_swa_attn_merge(P(w), 16, 1, 16, 16, 512, 0.1, 16, None, None) == csa2.ERR_INVALID_ARG
+
+
+@needs_lib
+def test_attn_swa_validation_rejects_before_launch():
+    L = csa2.lib()
+    P = ctypes.byref
+    n, m = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.csa2_attn_swa_workspace_size(1, 20, 64, 512, P(n)) == csa2.ERR_INVALID_ARG
+    # the window adds four partials per head: batch 1 needs more workspace than the plain attention
+    assert L.csa2_attn_swa_workspace_size(1, 64, 2048, 512, P(n)) == csa2.OK
+    assert L.csa2_attn_workspace_size(1, 64, 2048, 512, P(m)) == csa2.OK and n.value > m.value
+    kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=16, num_blocks=1, block_tokens=64, latent_dim=512,
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
+    sq = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=2, max_seq_len=64)
+    f = L.csa2_sparse_fp4_decode_attn_swa
+    w = csa2.SwaWindow(codes=16, scales=16, batch=2)
+    small = csa2.SwaWindow(codes=16, scales=16, batch=1)
+    nocodes = csa2.SwaWindow(codes=None, scales=16, batch=2)
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, None, 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(small), 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(nocodes), 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 24, 16, 64, 0.1, P(w), 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(w), 16, None, 256, 64, None) == csa2.ERR_WORKSPACE
 
 
 @needs_lib

@@ -1,5 +1,6 @@
-"""GPU parity of the sliding-window branch: FP8 window append (bit-exact) and the window attention merged
-with the global branch (one softmax over both sets of entries) against the oracle."""
+"""GPU parity of the sliding-window branch: FP8 window append (bit-exact), the window attention merged
+with the global branch (one softmax over both sets of entries) against the oracle, and the same result from
+the attention call that takes the window as extra splits."""
 
 import math
 
@@ -94,3 +95,67 @@ def test_swa_merge_empty_window_leaves_result():
     csa2.csa2_swa_attn_merge(ring, to_dev(np.array([0, -3], dtype=np.int32)), q, 0.05, out, lse)
     torch.cuda.synchronize()
     assert torch.equal(out, o0) and torch.equal(lse, l0)
+
+
+def _union_case(seed, seq_lens, K, rope_dim, heads, empty_global=()):
+    """A paged layer, a window ring and a selection; returns the GPU inputs and the oracle's union result."""
+    st = wl.Streams(seed)
+    B = len(seq_lens)
+    tables, nb = build_tables(st, seq_lens, True)
+    lat = [wl.latent_rows(st, 0, b, n) for b, n in enumerate(seq_lens)]
+    ropes = [wl.rope_rows(st, 0, b, n, rope_dim) for b, n in enumerate(seq_lens)] if rope_dim else None
+    layer = csa2.PagedLayer(nb, rope_dim=rope_dim, device="cuda")
+    fill_layer(layer, tables, seq_lens, latents=lat, ropes=ropes)
+    q = wl.q_heads(st, 0, B, heads, 512 + rope_dim)
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, K), -1, dtype=np.int32)
+    for b, n in enumerate(seq_lens):
+        if b in empty_global:
+            continue
+        m = min(n, K)
+        idx[b, :m] = rng.choice(n, size=m, replace=False)
+    sigma = 1 / math.sqrt(512 + rope_dim)
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    lat_win = [wl.latent_rows(st, 1, b, min(n, 128)) for b, n in enumerate(seq_lens)]
+    ring = csa2.SwaRing(B)
+    _fill_window(ring, lat_win, seq_lens)
+    expect = []
+    for b, n in enumerate(seq_lens):
+        og, lg = oracle_attention_rows(lat[b], ropes[b] if ropes else None, q[b], idx[b], n, sigma)
+        codes, scales = oracle.swa.swa_pack(lat_win[b])
+        os_, ls = oracle.swa.swa_attention(q[b], oracle.swa.swa_unpack(codes, scales), sigma)
+        expect.append(oracle.swa.merge(og, lg, os_, ls))
+    return layer, batch, to_dev(q), to_dev(idx), sigma, ring, expect
+
+
+# (rope_dim, heads, seq_lens, K): batch-1 decode at K 2048 (32 + 4 partials, wide combine) and at the
+# decoder's K 512 (16 + 4), mixed lengths
+# with windows of 1 .. 128 entries and an empty global selection, 128 heads, and a batch of 40 at 128 heads
+# (64 heads per workgroup, 2 + 4 partials, the narrow combine)
+UNION_CASES = [
+    (0, 64, [20000], 2048),
+    (0, 64, [70000], 512),
+    (0, 64, [1000, 50, 128, 3000, 1], 256),
+    (64, 128, [1000, 50, 128, 3000, 1], 256),
+    (64, 16, [33, 200, 97], 512),
+    (0, 128, [64 + 37 * i for i in range(40)], 64),
+]
+
+
+@pytest.mark.parametrize("rope_dim,heads,seq_lens,K", UNION_CASES)
+def test_attention_with_window_matches_union_attention(rope_dim, heads, seq_lens, K):
+    empty = (3,) if len(seq_lens) > 3 else ()
+    layer, batch, q, idx, sigma, ring, expect = _union_case(300 + heads + K + rope_dim, seq_lens, K, rope_dim, heads,
+                                                            empty_global=empty)
+    out, lse = csa2.csa2_sparse_fp4_decode_attn_swa(layer, batch, q, idx, sigma, ring)
+    # the two-call path on the same inputs
+    out2, lse2 = csa2.csa2_sparse_fp4_decode_attn(layer, batch, q, idx, sigma)
+    csa2.csa2_swa_attn_merge(ring, batch.seq_lens, q, sigma, out2, lse2)
+    torch.cuda.synchronize()
+    out, lse, out2, lse2 = out.cpu().numpy(), lse.cpu().numpy(), out2.cpu().numpy(), lse2.cpu().numpy()
+    for b in range(len(seq_lens)):
+        om, lm = expect[b]
+        err = float(np.max(np.abs(out[b] - om)))
+        assert err <= ATTN_TOL, (b, err)
+        assert float(np.max(np.abs(lse[b] - lm))) <= LSE_TOL, b
+        assert float(np.max(np.abs(out[b] - out2[b]))) <= 2 * ATTN_TOL, b
