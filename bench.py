@@ -318,11 +318,10 @@ class DecoderX20(Decode1M):
                                        pool_blocks=self.P, ws=self.sel_ws, indices=self.gidx[g],
                                        w_idx=self.w_idx_d[l0])
             for l in range(l0, l0 + self.G):  # the lead and its Reuse layers
-                if self.swa:  # the layer's own window entry of the new token, then both branches in one softmax
-                    csa2.csa2_swa_append(self.rings[r][l], self.batch_prev.seq_lens, self.win_new[l])
+                if self.swa:  # the layer's own window entry of the new token appended, both branches in one softmax
                     csa2.csa2_sparse_fp4_decode_attn_swa(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
-                                                         self.rings[r][l], ws=self.attn_swa_ws, out=self.out[l],
-                                                         lse=self.lse[l])
+                                                         self.rings[r][l], new_latent=self.win_new[l],
+                                                         ws=self.attn_swa_ws, out=self.out[l], lse=self.lse[l])
                 else:
                     csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
                                                      ws=self.attn_ws, out=self.out[l], lse=self.lse[l])

@@ -319,15 +319,19 @@ csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_s
  * window contributes logits to the latent part of q only.  The window's 128
  * slots run as four more split workgroups of the same kernel, so no second
  * attention pass and no in-place merge are needed.  win: the ring (win->batch
- * >= seqs->batch); other arguments and limits as for
- * csa2_sparse_fp4_decode_attn; workspace from csa2_attn_swa_workspace_size. */
+ * >= seqs->batch).  new_latent: NULL, or device fp32 [batch][512], the
+ * current token's window entry: it is packed into slot (n - 1) mod 128 of
+ * the ring first (as csa2_swa_append with positions n - 1 would; sequences
+ * with n <= 0 take none) and attended in the same call.  Other arguments and
+ * limits as for csa2_sparse_fp4_decode_attn; workspace from
+ * csa2_attn_swa_workspace_size. */
 csa2_status csa2_attn_swa_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim,
                                          size_t *bytes);
 csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const csa2_seqs *seqs,
                                             const uint16_t *q, int32_t heads, const int32_t *indices,
                                             int32_t top_k, float softmax_scale, const csa2_swa_window *win,
-                                            float *out, float *lse, void *ws, size_t ws_bytes,
-                                            csa2_stream stream);
+                                            const float *new_latent, float *out, float *lse, void *ws,
+                                            size_t ws_bytes, csa2_stream stream);
 
 /* ---- Host-side page allocator (no device memory): a free list of block ids
  * [0, num_blocks).  Not thread-safe; one instance per owner. */

@@ -106,7 +106,7 @@ SIGNATURES = {
     "csa2_sparse_fp4_decode_attn": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "csa2_attn_swa_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_sparse_fp4_decode_attn_swa": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float,
-                                                       ctypes.POINTER(SwaWindow), _P, _P, _P, _SZ, _P]),
+                                                       ctypes.POINTER(SwaWindow), _P, _P, _P, _P, _SZ, _P]),
     "csa2_block_pool_create": (_P, [_I32]),
     "csa2_block_alloc": (ctypes.c_int, [_P, _I32, _P]),
     "csa2_block_free": (ctypes.c_int, [_P, _I32, _P]),
@@ -452,8 +452,11 @@ def attn_swa_workspace_bytes(batch, heads, top_k):
     return n.value
 
 
-def csa2_sparse_fp4_decode_attn_swa(layer, batch, q, indices, softmax_scale, ring, ws=None, out=None, lse=None):
-    """csa2_sparse_fp4_decode_attn with the sliding-window ring in the same softmax -> (out, lse)."""
+def csa2_sparse_fp4_decode_attn_swa(layer, batch, q, indices, softmax_scale, ring, new_latent=None, ws=None, out=None,
+                                    lse=None):
+    """csa2_sparse_fp4_decode_attn with the sliding-window ring in the same softmax -> (out, lse).
+
+    new_latent: fp32 [B, 512] (device), the current token's window entry appended in the same call, or None."""
     B, H, _ = q.shape
     K = indices.shape[1]
     dev = q.device
@@ -465,7 +468,8 @@ def csa2_sparse_fp4_decode_attn_swa(layer, batch, q, indices, softmax_scale, rin
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     kv, sq, w = layer.struct(), batch.struct(), ring.struct()
     _check(lib().csa2_sparse_fp4_decode_attn_swa(ctypes.byref(kv), ctypes.byref(sq), _ptr(q), H, _ptr(indices), K,
-                                                 float(softmax_scale), ctypes.byref(w), _ptr(out), _ptr(lse),
+                                                 float(softmax_scale), ctypes.byref(w), _ptr(new_latent), _ptr(out),
+                                                 _ptr(lse),
                                                  _ptr(ws), ws.numel(), _stream()), "csa2_sparse_fp4_decode_attn_swa")
     return out, lse
 

@@ -408,14 +408,14 @@ csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_s
     return CSA2_ERR_INVALID_ARG;
   const size_t need = attn_workspace_bytes(S.batch, heads, top_k, false);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, nullptr, nullptr, out, lse, ws,
-                                     as_stream(stream)));
+  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, nullptr, nullptr, nullptr, out,
+                                     lse, ws, as_stream(stream)));
 }
 
 csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const csa2_seqs *seqs, const uint16_t *q,
                                             int32_t heads, const int32_t *indices, int32_t top_k,
-                                            float softmax_scale, const csa2_swa_window *win, float *out, float *lse,
-                                            void *ws, size_t ws_bytes, csa2_stream stream) {
+                                            float softmax_scale, const csa2_swa_window *win, const float *new_latent,
+                                            float *out, float *lse, void *ws, size_t ws_bytes, csa2_stream stream) {
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(layer, true, false, &L);
@@ -429,10 +429,11 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
     return CSA2_ERR_INVALID_ARG;
   if (win->codes == nullptr || win->scales == nullptr || !aligned(win->codes, 16) || !aligned(win->scales, 4))
     return CSA2_ERR_INVALID_ARG;
+  if (new_latent != nullptr && !aligned(new_latent, 8)) return CSA2_ERR_INVALID_ARG;
   const size_t need = attn_workspace_bytes(S.batch, heads, top_k, true);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, win->codes, win->scales, out,
-                                     lse, ws, as_stream(stream)));
+  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, win->codes, win->scales,
+                                     new_latent, out, lse, ws, as_stream(stream)));
 }
 
 csa2_block_pool *csa2_block_pool_create(int32_t num_blocks) {

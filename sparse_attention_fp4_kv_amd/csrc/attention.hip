@@ -39,7 +39,10 @@
 //     per-token fp32 scale multiplies the logit, and P times that scale
 //     (normalized by a power of two into [1, 2) over the tile, undone on the
 //     partial) enters PV, so the combine merges window and global partials
-//     alike.
+//     alike.  The current token's window entry can be appended in the same
+//     launch: the window workgroups of the tile holding its slot pack it to
+//     FP8 (the same rounding as the standalone append) into LDS and use it
+//     from there, and the first head group's one writes it to the ring.
 #include "common.h"
 #include "kernels.h"
 
@@ -67,8 +70,9 @@ struct AttnArgs {
   int splits;             // workgroups per (b, head group) along the selected entries
   int parts;              // partials per (b, head): splits, plus kWinSplits with the window
   int tiles_per_split;
-  const uint8_t *win_codes;  // [B][128][512] E4M3 window entries, or null
-  const float *win_scales;   // [B][128] per-token scales
+  uint8_t *win_codes;        // [B][128][512] E4M3 window entries, or null
+  float *win_scales;         // [B][128] per-token scales
+  const float *win_latent;   // [B][512] the current token's window entry to append first, or null
   float scale_log2;       // softmax scale * log2(e)
   float *out;             // [B][H][512]  (splits == 1)
   float *lse;             // [B][H] or null
@@ -86,6 +90,8 @@ struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile 
   uint32_t slot[kSlotCap];       // physical rows of this workgroup's entries (kNoSlot: skipped)
   float wts[kT], wp[kT];         // window tile: token scales, and times the P normalization
   float unnorm;                  // window tile: the P normalization, inverted
+  float wamax[4];                // appended window entry: per-wave amax
+  __attribute__((aligned(16))) uint8_t newc[kLatent];  // appended window entry: E4M3 codes
 };
 
 __device__ __forceinline__ f16x8 lds_f16x8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
@@ -160,6 +166,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   const bool win = split >= a.splits;
   const int wt = split - a.splits;
   const int nwin = min(max(a.S.seq_lens[b], 0), kWinSlots);
+  const int s_new = nwin > 0 ? (a.S.seq_lens[b] - 1) % kWinSlots : -1;  // the current token's slot
+  const bool pack_new = win && a.win_latent != nullptr && s_new >= 0 && s_new / kT == wt;
 
   const int n_tiles_all = (a.top_k + kT - 1) / kT;
   const int tile_begin = win ? 0 : split * a.tiles_per_split;
@@ -221,21 +229,47 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < a.L.num_blocks;
       sm.slot[i] = ok ? (uint32_t)blk[j] * kPage + (uint32_t)(pos[j] % kPage) : kNoSlot;
     }
-  } else if (tid < kT) {
-    // window tile: ring slots, token scales, and a power of two that brings the
-    // tile's largest token scale into [1, 2) (P times the scale stays in fp16's
-    // normal range)
-    const int s = kT * wt + tid;
-    const bool ok = s < nwin;
-    sm.slot[tid] = ok ? (uint32_t)s : kNoSlot;
-    const float ts = ok ? a.win_scales[(size_t)b * kWinSlots + s] : 0.0f;
-    float mx = ts;
+  } else {
+    // appending the current token's entry (slot (n - 1) mod 128) when this tile holds it: FP8 pack with
+    // s = amax / 448, code = E4M3(x / s); each thread packs channels 2 tid, 2 tid + 1
+    float snew = 0.0f;
+    if (pack_new) {
+      const float2 x = reinterpret_cast<const float2 *>(a.win_latent + (size_t)b * kLatent)[tid];
+      float m = fmaxf(fabsf(x.x), fabsf(x.y));
 #pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-    const float norm = mx > 0.0f ? __uint_as_float((254u - ((__float_as_uint(mx) >> 23) & 0xFFu)) << 23) : 1.0f;
-    sm.wts[tid] = ts;
-    sm.wp[tid] = ts * norm;
-    if (tid == 0) sm.unnorm = 1.0f / norm;
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane == 0) sm.wamax[wave] = m;
+      __syncthreads();  // uniform: the whole workgroup packs
+      const float amax = fmaxf(fmaxf(sm.wamax[0], sm.wamax[1]), fmaxf(sm.wamax[2], sm.wamax[3]));
+      snew = __fdiv_rn(amax, 448.0f);
+      uint32_t c0 = 0u, c1 = 0u;
+      if (snew > 0.0f) {
+        c0 = e4m3_encode(fabsf(__fdiv_rn(x.x, snew))) | ((__float_as_uint(x.x) >> 31) << 7);
+        c1 = e4m3_encode(fabsf(__fdiv_rn(x.y, snew))) | ((__float_as_uint(x.y) >> 31) << 7);
+      }
+      const uint16_t c = (uint16_t)(c0 | (c1 << 8));
+      reinterpret_cast<uint16_t *>(sm.newc)[tid] = c;
+      if (hg == 0) {  // one head group writes the ring
+        reinterpret_cast<uint16_t *>(a.win_codes + ((size_t)b * kWinSlots + s_new) * kLatent)[tid] = c;
+        if (tid == 0) a.win_scales[(size_t)b * kWinSlots + s_new] = snew;
+      }
+    }
+    if (tid < kT) {
+      // window tile: ring slots, token scales, and a power of two that brings the
+      // tile's largest token scale into [1, 2) (P times the scale stays in fp16's
+      // normal range)
+      const int s = kT * wt + tid;
+      const bool ok = s < nwin;
+      sm.slot[tid] = ok ? (uint32_t)s : kNoSlot;
+      const float ts = !ok ? 0.0f : (pack_new && s == s_new) ? snew : a.win_scales[(size_t)b * kWinSlots + s];
+      float mx = ts;
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+      const float norm = mx > 0.0f ? __uint_as_float((254u - ((__float_as_uint(mx) >> 23) & 0xFFu)) << 23) : 1.0f;
+      sm.wts[tid] = ts;
+      sm.wp[tid] = ts * norm;
+      if (tid == 0) sm.unnorm = 1.0f / norm;
+    }
   }
 
   // ---- PV accumulators: wave owns channels [128*wave, 128*wave+128) for all HG heads
@@ -406,8 +440,12 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       // (64 E4M3 bytes), converted to fp16 (exact); skipped slots and the rope
       // part are zero
       const uint32_t slot = sm.slot[tile_entry];
-      const uint4 *cp = reinterpret_cast<const uint4 *>(
-          a.win_codes + ((size_t)b * kWinSlots + (slot == kNoSlot ? 0 : slot)) * kLatent + 64 * tile_block);
+      const uint4 *cp = pack_new && slot == (uint32_t)s_new  // the appended entry, from LDS
+                            ? reinterpret_cast<const uint4 *>(sm.newc + 64 * tile_block)
+                            : reinterpret_cast<const uint4 *>(a.win_codes +
+                                                              ((size_t)b * kWinSlots + (slot == kNoSlot ? 0 : slot)) *
+                                                                  kLatent +
+                                                              64 * tile_block);
       uint4 w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = cp[i];
@@ -642,8 +680,9 @@ size_t attn_workspace_bytes(int batch, int heads, int top_k, bool window) {
 }
 
 hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
-                              const int32_t *indices, int top_k, float scale, const uint8_t *win_codes,
-                              const float *win_scales, float *out, float *lse, void *ws, hipStream_t st) {
+                              const int32_t *indices, int top_k, float scale, uint8_t *win_codes,
+                              float *win_scales, const float *win_latent, float *out, float *lse, void *ws,
+                              hipStream_t st) {
   if (S.batch == 0) return hipSuccess;
   const bool window = win_codes != nullptr;
   const int hgsz = heads_per_group(S.batch, heads);
@@ -662,6 +701,7 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   a.tiles_per_split = (tiles + splits - 1) / splits;
   a.win_codes = win_codes;
   a.win_scales = win_scales;
+  a.win_latent = win_latent;
   a.scale_log2 = scale * kLog2e;
   a.out = out;
   a.lse = lse;

@@ -80,11 +80,13 @@ hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, Id
                                        hipStream_t st);
 
 // ---- attention (attention.hip)
-// window: the sliding-window ring's codes / scales join the softmax as kWinSplits more splits
+// window: the sliding-window ring's codes / scales join the softmax as four more splits; win_latent, if
+// given, is the current token's window entry, appended to the ring in the same launch
 size_t attn_workspace_bytes(int batch, int heads, int top_k, bool window);
 hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
-                              const int32_t *indices, int top_k, float scale, const uint8_t *win_codes,
-                              const float *win_scales, float *out, float *lse, void *ws, hipStream_t st);
+                              const int32_t *indices, int top_k, float scale, uint8_t *win_codes,
+                              float *win_scales, const float *win_latent, float *out, float *lse, void *ws,
+                              hipStream_t st);
 
 // ---- CED projection (ced.hip)
 // Latent finish (RMSNorm, RoPE, FP4 pack) and the FP4 indexer key projected

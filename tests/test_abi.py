@@ -146,11 +146,13 @@ def test_attn_swa_validation_rejects_before_launch():
     w = csa2.SwaWindow(codes=16, scales=16, batch=2)
     small = csa2.SwaWindow(codes=16, scales=16, batch=1)
     nocodes = csa2.SwaWindow(codes=None, scales=16, batch=2)
-    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, None, 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
-    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(small), 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
-    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(nocodes), 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
-    assert f(P(kv), P(sq), 16, 24, 16, 64, 0.1, P(w), 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
-    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(w), 16, None, 256, 64, None) == csa2.ERR_WORKSPACE
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, None, None, 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(small), None, 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(nocodes), None, 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 24, 16, 64, 0.1, P(w), None, 16, None, 256, 64, None) == csa2.ERR_INVALID_ARG
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(w), None, 16, None, 256, 64, None) == csa2.ERR_WORKSPACE
+    # a misaligned appended entry
+    assert f(P(kv), P(sq), 16, 64, 16, 64, 0.1, P(w), 4, 16, None, 256, 1 << 20, None) == csa2.ERR_INVALID_ARG
 
 
 @needs_lib

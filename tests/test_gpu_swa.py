@@ -37,12 +37,14 @@ def test_swa_append_bit_exact():
     assert not codes[~touched].any() and not scales[~touched].any()
 
 
-def _fill_window(ring, lat_win, seq_lens):
-    """Append every window position of every sequence through the GPU append (one call per position index)."""
+def _fill_window(ring, lat_win, seq_lens, skip_last=False):
+    """Append every window position of every sequence through the GPU append (one call per position index);
+    skip_last leaves out each sequence's last position (n - 1)."""
     B = len(seq_lens)
     W = max(min(n, 128) for n in seq_lens)
     for j in range(W):
-        pos = np.array([n - min(n, 128) + j if j < min(n, 128) else -1 for n in seq_lens], dtype=np.int32)
+        pos = np.array([n - min(n, 128) + j if j < min(n, 128) - (1 if skip_last else 0) else -1 for n in seq_lens],
+                       dtype=np.int32)
         rows = np.stack([lat_win[b][j] if pos[b] >= 0 else np.zeros(512, np.float32) for b in range(B)])
         csa2.csa2_swa_append(ring, to_dev(pos), to_dev(rows))
 
@@ -97,7 +99,7 @@ def test_swa_merge_empty_window_leaves_result():
     assert torch.equal(out, o0) and torch.equal(lse, l0)
 
 
-def _union_case(seed, seq_lens, K, rope_dim, heads, empty_global=()):
+def _union_case(seed, seq_lens, K, rope_dim, heads, empty_global=(), skip_last=False):
     """A paged layer, a window ring and a selection; returns the GPU inputs and the oracle's union result."""
     st = wl.Streams(seed)
     B = len(seq_lens)
@@ -118,14 +120,14 @@ def _union_case(seed, seq_lens, K, rope_dim, heads, empty_global=()):
     batch = make_batch(tables, seq_lens, max(seq_lens))
     lat_win = [wl.latent_rows(st, 1, b, min(n, 128)) for b, n in enumerate(seq_lens)]
     ring = csa2.SwaRing(B)
-    _fill_window(ring, lat_win, seq_lens)
+    _fill_window(ring, lat_win, seq_lens, skip_last)
     expect = []
     for b, n in enumerate(seq_lens):
         og, lg = oracle_attention_rows(lat[b], ropes[b] if ropes else None, q[b], idx[b], n, sigma)
         codes, scales = oracle.swa.swa_pack(lat_win[b])
         os_, ls = oracle.swa.swa_attention(q[b], oracle.swa.swa_unpack(codes, scales), sigma)
         expect.append(oracle.swa.merge(og, lg, os_, ls))
-    return layer, batch, to_dev(q), to_dev(idx), sigma, ring, expect
+    return layer, batch, to_dev(q), to_dev(idx), sigma, ring, expect, lat_win
 
 
 # (rope_dim, heads, seq_lens, K): batch-1 decode at K 2048 (32 + 4 partials, wide combine) and at the
@@ -145,8 +147,8 @@ UNION_CASES = [
 @pytest.mark.parametrize("rope_dim,heads,seq_lens,K", UNION_CASES)
 def test_attention_with_window_matches_union_attention(rope_dim, heads, seq_lens, K):
     empty = (3,) if len(seq_lens) > 3 else ()
-    layer, batch, q, idx, sigma, ring, expect = _union_case(300 + heads + K + rope_dim, seq_lens, K, rope_dim, heads,
-                                                            empty_global=empty)
+    layer, batch, q, idx, sigma, ring, expect, _ = _union_case(300 + heads + K + rope_dim, seq_lens, K, rope_dim,
+                                                               heads, empty_global=empty)
     out, lse = csa2.csa2_sparse_fp4_decode_attn_swa(layer, batch, q, idx, sigma, ring)
     # the two-call path on the same inputs
     out2, lse2 = csa2.csa2_sparse_fp4_decode_attn(layer, batch, q, idx, sigma)
@@ -159,3 +161,24 @@ def test_attention_with_window_matches_union_attention(rope_dim, heads, seq_lens
         assert err <= ATTN_TOL, (b, err)
         assert float(np.max(np.abs(lse[b] - lm))) <= LSE_TOL, b
         assert float(np.max(np.abs(out[b] - out2[b]))) <= 2 * ATTN_TOL, b
+
+
+@pytest.mark.parametrize("rope_dim,heads,seq_lens,K", [(0, 64, [20000], 2048), (64, 16, [33, 200, 97, 128, 1], 512)])
+def test_attention_with_window_appends_current_entry(rope_dim, heads, seq_lens, K):
+    """The ring holds positions up to n - 2; the call appends position n - 1 and attends over the full window:
+    the same result as above, and the ring's new slot equals the standalone pack bit for bit."""
+    layer, batch, q, idx, sigma, ring, expect, lat_win = _union_case(400 + heads + K, seq_lens, K, rope_dim, heads,
+                                                                     skip_last=True)
+    new = np.stack([lw[-1] for lw in lat_win])
+    out, lse = csa2.csa2_sparse_fp4_decode_attn_swa(layer, batch, q, idx, sigma, ring, new_latent=to_dev(new))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    codes, scales = ring.codes.cpu().numpy(), ring.scales.cpu().numpy()
+    oc, os_ = oracle.swa.swa_pack(new)
+    for b, n in enumerate(seq_lens):
+        om, lm = expect[b]
+        err = float(np.max(np.abs(out[b] - om)))
+        assert err <= ATTN_TOL, (b, err)
+        assert float(np.max(np.abs(lse[b] - lm))) <= LSE_TOL, b
+        slot = int(oracle.swa.window_slot(n - 1))
+        assert np.array_equal(codes[b, slot], oc[b]) and scales[b, slot] == os_[b], b
