@@ -132,8 +132,9 @@ def _union_case(seed, seq_lens, K, rope_dim, heads, empty_global=(), skip_last=F
 
 # (rope_dim, heads, seq_lens, K): batch-1 decode at K 2048 (32 + 4 partials, wide combine) and at the
 # decoder's K 512 (16 + 4), mixed lengths
-# with windows of 1 .. 128 entries and an empty global selection, 128 heads, and a batch of 40 at 128 heads
-# (64 heads per workgroup, 2 + 4 partials, the narrow combine)
+# with windows of 1 .. 128 entries and an empty global selection, 128 heads, a batch of 40 at 128 heads
+# (64 heads per workgroup, 2 + 4 partials, the narrow combine) and a batch of 32 with rope at 64 heads per
+# workgroup (a ragged last tile of 96 entries)
 UNION_CASES = [
     (0, 64, [20000], 2048),
     (0, 64, [70000], 512),
@@ -141,6 +142,7 @@ UNION_CASES = [
     (64, 128, [1000, 50, 128, 3000, 1], 256),
     (64, 16, [33, 200, 97], 512),
     (0, 128, [64 + 37 * i for i in range(40)], 64),
+    (64, 64, [40 + 53 * i for i in range(32)], 96),
 ]
 
 
