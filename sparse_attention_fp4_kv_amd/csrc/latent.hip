@@ -109,14 +109,29 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
   float g[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) g[i] = gam[i];
-  // RoPE frequencies of this lane's 4 pairs (lanes 56..63), fl32(theta^(-2i/64))
-  float f[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const bool rot = a.theta != 0.0f && lane >= kRopeFirst / 8;
-  if (rot) {
+  // RoPE cos / sin of the wave's 8 rows spread over all its lanes: lane 8 j + m
+  // computes pairs 4 m .. 4 m + 3 of row j (angle fl32(p * fl32(theta^(-2i/64)))),
+  // and the rotating lanes 56 + m fetch them when row j is finished
+  const bool rope = a.theta != 0.0f;
+  const bool rot = rope && lane >= kRopeFirst / 8;
+  float rc[4] = {1.0f, 1.0f, 1.0f, 1.0f}, rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (rope) {
+    const int64_t r = row0 + 4 * (lane >> 3) + wave;
+    int64_t p = 0;
+    if (r < row_end) {
+      if (a.m.paged) {
+        const int sp = a.m.S.seq_lens[r];
+        p = sp < 0 ? 0 : sp;
+      } else {
+        p = a.m.pos0 + r % a.m.tokens;
+      }
+    }
+    const float pf = (float)p;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int i = 4 * (lane - kRopeFirst / 8) + q;
-      f[q] = (float)pow((double)a.theta, -2.0 * i / 64.0);
+      const int i = 4 * (lane & 7) + q;
+      const float fq = (float)pow((double)a.theta, -2.0 * i / 64.0);
+      sincosf(pf * fq, &rs[q], &rc[q]);
     }
   }
   for (int j = 0; j < kRows / 4; ++j) {
@@ -140,15 +155,16 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
     const float inv = __fdiv_rn(1.0f, __fsqrt_rn(ss * (1.0f / kLatent) + a.eps));
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (x[i] * inv) * g[i];
-    if (rot) {
-      const float pf = (float)pos;
+    if (rope) {  // uniform: every lane takes part in the fetch
+      const int src = 8 * j + (lane & 7);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float s, c;
-        sincosf(pf * f[q], &s, &c);
-        const float u = x[2 * q], v = x[2 * q + 1];
-        x[2 * q] = u * c - v * s;
-        x[2 * q + 1] = u * s + v * c;
+        const float c = __shfl(rc[q], src), s = __shfl(rs[q], src);
+        if (rot) {
+          const float u = x[2 * q], v = x[2 * q + 1];
+          x[2 * q] = u * c - v * s;
+          x[2 * q + 1] = u * s + v * c;
+        }
       }
     }
     // pack: group 16 channels = lanes 2m, 2m+1
