@@ -21,7 +21,10 @@
 // token's scale (normalized by a power of two so it stays in fp16's normal
 // range) as fp16 hi + lo parts against the window staged in LDS as fp16, 256
 // channels at a time, read through transposing LDS loads.  The epilogue
-// merges with the global result (out, lse) in place.
+// merges with the global result (out, lse) in place.  This pair of kernels
+// serves a caller that already holds the global result; the decode path runs
+// the window inside the global attention launch instead (attention.hip: the
+// ring's tiles as extra split workgroups, the append done there too).
 #include "common.h"
 #include "kernels.h"
 

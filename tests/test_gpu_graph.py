@@ -66,3 +66,56 @@ def test_captured_step_replays_match_eager():
         torch.cuda.synchronize()
         for a, r in zip((idx, pool, out, lse), ref):
             assert torch.equal(a, r), f"replay {rep}"
+
+
+def test_captured_window_attention_replays_match_eager():
+    """The attention call that takes the sliding window as extra splits and appends the current token's window
+    entry (a ring write inside the kernel) replays from a graph with the eager bytes, ring included."""
+    st = wl.Streams(111)
+    seq_lens = [20000, 3001]
+    B, H, K = len(seq_lens), 64, 2048
+    tables, nb = build_tables(st, seq_lens, True)
+    lat = [wl.latent_rows(st, 0, b, n) for b, n in enumerate(seq_lens)]
+    layer = csa2.PagedLayer(nb, device="cuda")
+    fill_layer(layer, tables, seq_lens, latents=lat)
+    batch = make_batch(tables, seq_lens, max(seq_lens))
+    rng = np.random.default_rng(5)
+    idx = to_dev(np.stack([rng.choice(n, size=K, replace=False).astype(np.int32) for n in seq_lens]))
+    q = to_dev(wl.q_heads(st, 0, B, H, 512))
+    ring = csa2.SwaRing(B)
+    for j in range(127):  # positions n - 128 .. n - 2; the call appends n - 1
+        pos = to_dev(np.array([n - 128 + j for n in seq_lens], dtype=np.int32))
+        csa2.csa2_swa_append(ring, pos, to_dev(wl.latent_rows(st, 1, j, B)))
+    new = to_dev(wl.latent_rows(st, 1, 127, B))
+    ws = csa2.workspace(csa2.attn_swa_workspace_bytes(B, H, K))
+    out = torch.empty((B, H, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    sigma = 1 / math.sqrt(512)
+
+    def step():
+        csa2.csa2_sparse_fp4_decode_attn_swa(layer, batch, q, idx, sigma, ring, new_latent=new, ws=ws, out=out,
+                                             lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out, lse, ring.codes, ring.scales)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    slots = [(n - 1) % 128 for n in seq_lens]
+    for rep in range(3):
+        out.fill_(-7)
+        lse.fill_(-7)
+        for b, sl in enumerate(slots):  # the appended slot is written again by every replay
+            ring.codes[b, sl].fill_(0)
+            ring.scales[b, sl] = -1.0
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, r in zip((out, lse, ring.codes, ring.scales), ref):
+            assert torch.equal(a, r), f"replay {rep}"
