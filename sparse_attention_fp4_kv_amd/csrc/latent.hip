@@ -96,6 +96,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ uint16_t exact_bf16(float v) { return (uint16_t)(__float_as_uint(v) >> 16); }
 
+// EARLY: every W_idx fragment of the key projection is loaded at the start,
+// in flight together with the rows (the decode-time append of a few rows,
+// where those loads are the critical path); otherwise they stream 8 k-steps
+// ahead of the MFMA chain, which keeps registers for occupancy in bulk runs.
+template <bool EARLY>
 __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kRows][kLdX];
   __shared__ __attribute__((aligned(16))) float ks[kRows][kLdK];
@@ -105,6 +110,16 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
                                  : (int64_t)blockIdx.y * a.m.tokens + (int64_t)blockIdx.x * kRows;
   const int64_t row_end = a.m.paged ? a.rows : (int64_t)(blockIdx.y + 1) * a.m.tokens;
   const int layer = a.m.paged ? 0 : (int)blockIdx.y;
+  constexpr int kSteps = kLatent / 16;  // 32 k-steps of the key projection
+  constexpr int kAhead = EARLY ? kSteps : 8;
+  // k[r][n] = sum_c x_hat[r][c] W[n][c]: wave w owns n in [32w, 32w + 32)
+  const uint16_t *wrow = a.w_idx == nullptr ? nullptr
+                         : a.w_idx + ((size_t)layer * kKeyDim + 32 * wave + (lane & 31)) * kLatent + 8 * (lane >> 5);
+  uint4 wb[kAhead];
+  if (EARLY && wrow != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) wb[i] = *reinterpret_cast<const uint4 *>(wrow + 16 * i);
+  }
   const float *gam = a.gamma + (size_t)layer * kLatent + 8 * lane;
   float g[8];
 #pragma unroll
@@ -115,7 +130,7 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
   const bool rope = a.theta != 0.0f;
   const bool rot = rope && lane >= kRopeFirst / 8;
   float rc[4] = {1.0f, 1.0f, 1.0f, 1.0f}, rs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (rope) {
+  if (rope && row0 + wave < row_end) {  // (uniform: a wave whose rows are all past the end skips it)
     const int64_t r = row0 + 4 * (lane >> 3) + wave;
     int64_t p = 0;
     if (r < row_end) {
@@ -131,23 +146,41 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int i = 4 * (lane & 7) + q;
       const float fq = (float)pow((double)a.theta, -2.0 * i / 64.0);
-      sincosf(pf * fq, &rs[q], &rc[q]);
+      const float t = pf * fq;
+      if constexpr (EARLY) {
+        // few rows: the fp32 angle reduced by 2 pi in double (2 pi as a double
+        // plus its remainder; |k| < 2^23) and the small-argument double
+        // sincos, so no large-argument reduction table is read from memory
+        constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
+        const double td = (double)t;
+        const double k = rint(td * (1.0 / kTwoPiHi));
+        const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, td));
+        double sd, cd;
+        sincos(r, &sd, &cd);
+        rs[q] = (float)sd;
+        rc[q] = (float)cd;
+      } else {
+        sincosf(t, &rs[q], &rc[q]);
+      }
     }
   }
   for (int j = 0; j < kRows / 4; ++j) {
     const int lr = 4 * j + wave;  // local row
     const int64_t r = row0 + lr;
+    if (r >= row_end) {  // uniform over the wave; the row's keys are computed from stale LDS and never stored
+      if (lane == 0) slots[lr] = -1;
+      continue;
+    }
     int64_t pos = 0;
     int lay = 0;
-    int64_t slot = -1;
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (r < row_end) {
-      slot = row_slot(a, r, &pos, &lay);
+    const int64_t slot = row_slot(a, r, &pos, &lay);
+    float x[8];
+    {
       const float4 *src = reinterpret_cast<const float4 *>(a.c + r * kLatent + 8 * lane);
       const float4 u = src[0], v = src[1];
       x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
     }
-    if (lane == 0) slots[lr] = r < row_end ? slot : -1;
+    if (lane == 0) slots[lr] = slot;
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
@@ -202,16 +235,13 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
   }
   if (a.w_idx == nullptr) return;  // uniform over the workgroup
   __syncthreads();
-  // k[r][n] = sum_c x_hat[r][c] W[n][c]: wave w owns n in [32w, 32w + 32)
   {
-    const uint16_t *wrow = a.w_idx + ((size_t)layer * kKeyDim + 32 * wave + (lane & 31)) * kLatent + 8 * (lane >> 5);
     const uint16_t *xrow = &xs[lane & 31][8 * (lane >> 5)];
     f32x16 acc = {};
-    constexpr int kSteps = kLatent / 16;  // 32
-    constexpr int kAhead = 8;
-    uint4 wb[kAhead];
+    if (!EARLY) {
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) wb[i] = *reinterpret_cast<const uint4 *>(wrow + 16 * i);
+      for (int i = 0; i < kAhead; ++i) wb[i] = *reinterpret_cast<const uint4 *>(wrow + 16 * i);
+    }
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
       const uint4 wv = wb[ks % kAhead];
@@ -269,7 +299,7 @@ hipError_t launch_kv_finish_rows(const float *c, int64_t tokens, int n_layers, i
   a.m.paged = 0;
   const dim3 grid((unsigned)((tokens + kRows - 1) / kRows), (unsigned)n_layers);
   timer_before(kKernKvFinish, st);
-  finish_kernel<<<grid, dim3(256), 0, st>>>(a);
+  finish_kernel<false><<<grid, dim3(256), 0, st>>>(a);
   timer_after(kKernKvFinish, st);
   return hipGetLastError();
 }
@@ -289,7 +319,7 @@ hipError_t launch_kv_append_finish(const KvLayerDev &L, const SeqsDev &S, const 
   a.m.S = S;
   const dim3 grid((unsigned)((S.batch + kRows - 1) / kRows));
   timer_before(kKernKvAppend, st);
-  finish_kernel<<<grid, dim3(256), 0, st>>>(a);
+  finish_kernel<true><<<grid, dim3(256), 0, st>>>(a);
   timer_after(kKernKvAppend, st);
   return hipGetLastError();
 }
