@@ -13,7 +13,8 @@
 // A workgroup computes a 256 x 128 output tile with 4 waves (128 x 64 each,
 // 4 x 2 MFMA tiles of 32 x 32), k-steps of 64 staged through one LDS buffer
 // with a register prefetch of the next step (the loads have a whole k-step of
-// 32 MFMAs per wave to arrive); two workgroups share a CU.  The epilogue parks the fp32 tile in
+// 32 MFMAs per wave to arrive); two workgroups share a CU, and the tiles are
+// dealt so that each XCD's L2 serves a block of neighbouring tiles.  The epilogue parks the fp32 tile in
 // LDS and packs each 16-channel group of C straight to E2M1 + E4M3 (the same
 // rounding rules as the standalone pack) and rounds Z to bf16, so C never
 // reaches HBM in fp32 (unless the optional debug copy is asked for).
@@ -28,6 +29,8 @@ constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int kLdA = BK + 8;   // bf16 per LDS row (pad breaks bank conflicts)
 constexpr int kWM = 128, kWN = 64;  // wave tile: 4 x 2 MFMA tiles of 32 x 32
 constexpr int kLdC = BN + 4;   // fp32 per epilogue row (128 rows at a time)
+constexpr int kGroupM = 8;     // row tiles an XCD sweeps across the columns together
+constexpr int kXcds = 8;
 // output columns per layer: 512 of C, then 64 of Z when W^Z is given
 __device__ __forceinline__ int per_layer(const void *w_z) { return w_z != nullptr ? kLatent + kIdxDim : kLatent; }
 
@@ -67,8 +70,20 @@ union SmemCed {
 __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
   __shared__ __attribute__((aligned(16))) SmemCed sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  // Tile order: the hardware deals workgroups to the 8 XCDs round-robin by
+  // linear id, so the id is first renumbered to give each XCD a contiguous
+  // range of tiles, which is then walked kGroupM row tiles at a time across
+  // the columns: the workgroups an XCD runs together share A row tiles and B
+  // column tiles in its L2.  (A bijection on the tiles; without a multiple of
+  // 8 tiles the XCD step is left out.)
+  const int nt = gridDim.x, mt = gridDim.y, total = nt * mt;
+  const int pid = blockIdx.y * nt + blockIdx.x;
+  const int t = total % kXcds == 0 ? (pid % kXcds) * (total / kXcds) + pid / kXcds : pid;
+  const int first_m = (t / (kGroupM * nt)) * kGroupM;
+  const int gm = min(mt - first_m, kGroupM);
+  const int u = t % (kGroupM * nt);
+  const int64_t m0 = (int64_t)(first_m + u % gm) * BM;
+  const int n0 = (u / gm) * BN;
   const int n_total = a.n_layers * per_layer(a.w_z);
   const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
 
