@@ -148,6 +148,14 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
+    // scheduling: spread the k-step's 24 LDS reads and 12 global loads between its 32 MFMAs
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __syncthreads();  // every wave is done reading the tile
     if (ks + 1 < k_steps) stash(0);
     __syncthreads();
