@@ -575,16 +575,17 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const flo
 
 // The same merge for many splits (batch-1 decode): workgroup (b*H + h, q)
 // covers 64 channels of one head with 256 threads, 16 float4 columns x 16
-// split groups (splits g, g + 16, g + 32 each), then one merge of the 16
+// split groups (splits g, g + 16, .. : PER each), then one merge of the 16
 // groups through LDS: one round of loads instead of a long chain per thread.
 constexpr int kWideThreads = 256;
 constexpr int kWideCols = 16;  // float4 columns per workgroup
-constexpr int kWidePer = 3;    // splits per thread
+constexpr int kWideMaxPer = 3;  // splits per thread at most
+template <int kWidePer>
 __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
                                                           float *__restrict__ out, float *__restrict__ lse) {
   constexpr int kGroups = kWideThreads / kWideCols;  // 16
-  static_assert(kMaxSplits + kWinSplits <= kWidePer * kGroups, "splits per thread");
+  static_assert(kMaxSplits + kWinSplits <= kWideMaxPer * kGroups, "splits per thread");
   __shared__ float4 so[kGroups][kWideCols];
   __shared__ float gm[kGroups], sl[kGroups];
   const int bh = blockIdx.x, q = blockIdx.y;
@@ -722,9 +723,13 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || parts == 1) return e;
   timer_before(kKernAttnCombine, st);
-  if (parts > 8)
-    attn_combine_wide_kernel<<<dim3(S.batch * heads, kLatent / 4 / kWideCols), dim3(kWideThreads), 0, st>>>(
-        a.part_o, a.part_ml, parts, out, lse);
+  const dim3 wide_grid(S.batch * heads, kLatent / 4 / kWideCols);
+  if (parts > 32)
+    attn_combine_wide_kernel<3><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, out, lse);
+  else if (parts > 16)
+    attn_combine_wide_kernel<2><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, out, lse);
+  else if (parts > 8)
+    attn_combine_wide_kernel<1><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, out, lse);
   else
     attn_combine_kernel<<<dim3(S.batch * heads, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
         a.part_o, a.part_ml, parts, out, lse);
