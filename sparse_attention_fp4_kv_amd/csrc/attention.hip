@@ -523,13 +523,13 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 }
 
 // Merges the splits' partials: workgroup (b*H + h, half) of one full wave
-// covers 256 channels of one head, one float4 per thread.  Splits are read 32
+// covers 256 channels of one head, one float4 per thread.  Splits are read 8
 // at a time (all loads of a chunk issued together) and merged online.
 constexpr int kCombineThreads = 64;
 __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
                                                           float *__restrict__ out, float *__restrict__ lse) {
-  constexpr int kChunk = 32;
+  constexpr int kChunk = 8;  // the launch sends this kernel at most 8 splits (more go to the wide merge)
   const int bh = blockIdx.x, quarter = blockIdx.y;  // quarter: which kCombineThreads float4s
   const int tid = threadIdx.x;
   const int c4 = kCombineThreads * quarter + tid;  // float4 index within the 512 channels
