@@ -195,6 +195,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   if (!win) {
 #pragma unroll
     for (int j = 0; j < kSlotCap / 256; ++j) {
+      if (256 * j >= e_count) break;  // uniform: rounds past this workgroup's entries are not read
       const int i = 256 * j + tid;
       const int p = idx_row[min(e_begin + i, a.top_k - 1)];  // clamped read, masked below
       pos[j] = i < e_count ? p : -1;
@@ -217,6 +218,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     int blk[kSlotCap / 256];
 #pragma unroll
     for (int j = 0; j < kSlotCap / 256; ++j) {
+      if (256 * j >= e_count) break;  // (slots past e_count are never read)
       const int p = pos[j];
       const bool ok = p >= 0 && p < n && p / kPage < a.S.max_blocks;
       // clamped read, masked below (a table without columns maps nothing)
@@ -225,6 +227,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < kSlotCap / 256; ++j) {
+      if (256 * j >= e_count) break;
       const int i = 256 * j + tid;
       const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < a.L.num_blocks;
       sm.slot[i] = ok ? (uint32_t)blk[j] * kPage + (uint32_t)(pos[j] % kPage) : kNoSlot;
