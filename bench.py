@@ -67,6 +67,16 @@ def kernel_source_sha(kernel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return None
+
+
 def usable_cores():
     n = len(os.sched_getaffinity(0))
     try:
@@ -170,7 +180,7 @@ class Decode1M(Decode):
         self.w_idx_d = [torch.from_numpy(x).to(dev) if x is not None else None for x in self.w_idx]
         self.q_d = [torch.from_numpy(q.view(np.int16)).to(dev) for q in self.q]
         self.sel_ws = csa2.workspace(csa2.index_select_workspace_bytes(1, n, self.K, self.P), dev)
-        self.attn_ws = csa2.workspace(csa2.attn_workspace_bytes(1, self.H, self.K), dev)
+        self.lead_layers = list(range(self.L))  # every layer selects (Full, then Reindex)
         self.idx = torch.empty((self.L, 1, self.K), dtype=torch.int32, device=dev)
         self.pool = torch.empty((1, self.P), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.L, 1, self.H, 512), dtype=torch.float32, device=dev)
@@ -192,10 +202,40 @@ class Decode1M(Decode):
                 self.kf64 = oracle.indexer.fp4_keys_to_f64(*oracle.fp4.fp4_pack(self.keys))
             else:
                 self.kf64 = oracle.indexer.keys_to_f64(self.keys, "bf16")
+        if type(self) is Decode1M:
+            self._workspaces()
         torch.cuda.synchronize()
 
     queries_per_step = property(lambda self: self.L)
     dominant = "index_scan"
+
+    def _workspaces(self):
+        """Reindex and multi-layer attention workspaces (after the subclass has fixed its layer plan)."""
+        csa2, dev = self.csa2, self.dev
+        nre = max(1, len(self.lead_layers) - 1)
+        self.reidx_ws = csa2.workspace(csa2.reindex_layers_workspace_bytes(nre, 1, self.K, self.P), dev)
+        self.attn_ws = csa2.workspace(csa2.attn_layers_workspace_bytes(self.L, 1, self.H, self.K,
+                                                                       getattr(self, "swa", False)), dev)
+
+    def _select(self, layer, idx_of_lead):
+        """Full selection with the pool (the new token's row appended in the scan's launch, or by the
+        finishing append before it), then every Reindex layer over that pool in two launches."""
+        csa2 = self.csa2
+        l0 = self.lead_layers[0]
+        if self.finish:
+            self._append(layer)
+            csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l0], self.K, csa2.FULL, pool_blocks=self.P,
+                                   want_pool=True, ws=self.sel_ws, indices=idx_of_lead[0], pool_out=self.pool,
+                                   w_idx=self.w_idx_d[l0])
+        else:
+            csa2.csa2_index_select_append(layer, self.batch, self.q_idx_d[l0], self.K,
+                                          [(layer, self.new_latent, None, self.new_key)], pool_blocks=self.P,
+                                          want_pool=True, ws=self.sel_ws, indices=idx_of_lead[0], pool_out=self.pool,
+                                          w_idx=self.w_idx_d[l0])
+        rest = self.lead_layers[1:]
+        if rest:
+            csa2.csa2_index_reindex_layers(layer, self.batch, [(self.q_idx_d[l], self.w_idx_d[l]) for l in rest],
+                                           self.K, self.pool, self.P, ws=self.reidx_ws, indices=idx_of_lead[1:])
 
     def _fill_finished(self, layer, n, chunk=1 << 17):
         """Identity page table: finish raw latents of positions [s, e) straight into rows [s, e)."""
@@ -224,18 +264,21 @@ class Decode1M(Decode):
         return oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(self.latent[v]))
 
     def step(self, r):
+        """append + Full select with the pool (one scan launch, one select launch), the 3 Reindex layers
+        (one pool-scoring launch, one select launch), the 4 attentions (one launch, one combine)."""
         csa2, layer = self.csa2, self.layers[r]
-        self._append(layer)
-        for l in range(self.L):
-            if l == 0:
-                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[0], self.K, csa2.FULL, pool_blocks=self.P,
-                                       want_pool=True, ws=self.sel_ws, indices=self.idx[0], pool_out=self.pool,
-                                       w_idx=self.w_idx_d[0])
-            else:
-                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l], self.K, csa2.REINDEX, pool_in=self.pool,
-                                       pool_blocks=self.P, ws=self.sel_ws, indices=self.idx[l], w_idx=self.w_idx_d[l])
-            csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.idx[l], self.w.sigma,
-                                             ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
+        self._select(layer, [self.idx[l] for l in range(self.L)])
+        csa2.csa2_sparse_fp4_decode_attn_layers([(layer, self.q_d[l], self.idx[l]) for l in range(self.L)],
+                                                self.batch, self.w.sigma, ws=self.attn_ws,
+                                                outs=[self.out[l] for l in range(self.L)],
+                                                lses=[self.lse[l] for l in range(self.L)])
+
+    def attn_bytes(self):
+        """Algorithmic bytes of the step's attention launch: every layer's gathered entries, query, indices,
+        output and lse (the windows too when the layers have them)."""
+        L, K, H = self.L, self.K, self.H
+        win = L * 128 * (512 + 4) + L * (512 * 4) if getattr(self, "swa", False) else 0
+        return L * (K * 288 + H * 512 * 2 + K * 4 + H * 512 * 4 + H * 4) + win
 
     # indexer key bytes per token (FP4: 64 B of codes + 8 scales) and query bytes per selection
     key_bytes = property(lambda self: 72 if self.fp4 else 128)
@@ -286,6 +329,7 @@ class DecoderX20(Decode1M):
         super().__init__(w, replicas, dev, cpu_needed)
         self.G = w.extra["group_size"]
         self.leads = list(range(0, self.L, self.G))
+        self.lead_layers = self.leads
         self.gidx = self.torch.empty((len(self.leads), 1, self.K), dtype=self.torch.int32, device=dev)
         self.swa = w.extra.get("swa", False)
         if self.swa:  # every layer's own window of 128 local latents (FP8), one ring per layer and replica
@@ -302,29 +346,25 @@ class DecoderX20(Decode1M):
                     self.rings[r][l].codes.copy_(self.rings[0][l].codes)
                     self.rings[r][l].scales.copy_(self.rings[0][l].scales)
             self.win_new = [torch.from_numpy(self.win_lat[l][127:128].copy()).to(dev) for l in range(self.L)]
-            self.attn_swa_ws = csa2.workspace(csa2.attn_swa_workspace_bytes(1, self.H, self.K), dev)
-            torch.cuda.synchronize()
+        self._workspaces()
+        self.torch.cuda.synchronize()
 
     def step(self, r):
+        """The finishing append, the Full select with the pool, the 4 Reindex leads (two launches), then all
+        20 layers' attention in one launch (each lead's Reuse layers take its indices; with windows, every
+        layer's new window entry is appended in that launch)."""
         csa2, layer = self.csa2, self.layers[r]
-        self._append(layer)
+        self._select(layer, [self.gidx[g] for g in range(len(self.leads))])
+        jobs = []
         for g, l0 in enumerate(self.leads):
-            if g == 0:
-                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l0], self.K, csa2.FULL, pool_blocks=self.P,
-                                       want_pool=True, ws=self.sel_ws, indices=self.gidx[g], pool_out=self.pool,
-                                       w_idx=self.w_idx_d[l0])
-            else:
-                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l0], self.K, csa2.REINDEX, pool_in=self.pool,
-                                       pool_blocks=self.P, ws=self.sel_ws, indices=self.gidx[g],
-                                       w_idx=self.w_idx_d[l0])
             for l in range(l0, l0 + self.G):  # the lead and its Reuse layers
-                if self.swa:  # the layer's own window entry of the new token appended, both branches in one softmax
-                    csa2.csa2_sparse_fp4_decode_attn_swa(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
-                                                         self.rings[r][l], new_latent=self.win_new[l],
-                                                         ws=self.attn_swa_ws, out=self.out[l], lse=self.lse[l])
+                if self.swa:
+                    jobs.append((layer, self.q_d[l], self.gidx[g], self.rings[r][l], self.win_new[l]))
                 else:
-                    csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.gidx[g], self.w.sigma,
-                                                     ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
+                    jobs.append((layer, self.q_d[l], self.gidx[g]))
+        csa2.csa2_sparse_fp4_decode_attn_layers(jobs, self.batch, self.w.sigma, ws=self.attn_ws,
+                                                outs=[self.out[l] for l in range(self.L)],
+                                                lses=[self.lse[l] for l in range(self.L)])
 
     def algorithmic_bytes(self):
         n, K, P, H, L = self.n, self.K, self.P, self.H, self.L
@@ -428,6 +468,11 @@ class DecodeBatch(Decode):
     def dominant_bytes(self):
         return sum(n * self.key_bytes() for n in self.lens) + self.B * 64 * 4
 
+    def attn_bytes(self):
+        entry = 288 + 2 * self.R
+        return sum(min(n, self.K) * entry for n in self.lens) + self.B * (
+            self.H * (512 + self.R) * 2 + self.K * 4 + self.H * 512 * 4 + self.H * 4)
+
     def oracle_step(self, rows=None):
         import oracle
 
@@ -484,25 +529,38 @@ class MixedServing(Decode):
         self.q_idx_d = torch.from_numpy(self.q_idx).to(dev)
         self.q_d = [torch.from_numpy(q.view(np.int16)).to(dev) for q in self.q]
         self.sel_ws = csa2.workspace(csa2.index_select_workspace_bytes(self.B, maxn, self.K), dev)
-        self.attn_ws = csa2.workspace(csa2.attn_workspace_bytes(self.B, self.H, self.K), dev)
+        self.attn_ws = csa2.workspace(csa2.attn_layers_workspace_bytes(self.L, self.B, self.H, self.K), dev)
         self.idx = torch.empty((self.B, self.K), dtype=torch.int32, device=dev)
         self.out = torch.empty((self.L, self.B, self.H, 512), dtype=torch.float32, device=dev)
         self.lse = torch.empty((self.L, self.B, self.H), dtype=torch.float32, device=dev)
+        self.oracle_rows = {}
+        if cpu_needed:  # the CPU sample's inputs, generated here, outside its timed loop
+            import oracle
+
+            for b in range(min(self.B, self.ORACLE_SEQS)):
+                n = self.lens[b] + 1
+                kf = oracle.indexer.keys_to_f64(self.keys[b], "bf16")
+                idx, _ = oracle.indexer.full_select(self.q_idx[b], kf, self.K)
+                v = oracle.attention.valid_slots(idx, n)
+                self.oracle_rows[b] = (kf, idx, [wl.latent_rows(self.st, l, b, n)[v] for l in range(self.L)])
         torch.cuda.synchronize()
 
+    ORACLE_SEQS = 8  # sequences whose oracle inputs are prepared for the CPU baseline
     queries_per_step = property(lambda self: self.B * self.L)
     dominant = "index_scan"
 
     def step(self, r):
+        """The new token's key (key pool) and its latent (each layer's own KV pool) appended in the scan's
+        launch, one Full selection, then the 4 Reuse layers' attention over their own KV in one launch."""
         csa2 = self.csa2
-        for l in range(self.L):  # the new token's latent into each layer's own KV pool
-            csa2.csa2_kv_append(self.kv[r][l], self.batch_prev, self.new_lat[l])
-        csa2.csa2_kv_append(self.key_pools[r], self.batch_prev, None, idx_key=self.new_key)  # key only
-        csa2.csa2_index_select(self.key_pools[r], self.batch, self.q_idx_d, self.K, csa2.FULL, ws=self.sel_ws,
-                               indices=self.idx)
-        for l in range(self.L):  # Reuse: one selection, each layer's own KV
-            csa2.csa2_sparse_fp4_decode_attn(self.kv[r][l], self.batch, self.q_d[l], self.idx, self.w.sigma,
-                                             ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
+        rows = [(self.key_pools[r], None, None, self.new_key)] + [(self.kv[r][l], self.new_lat[l], None, None)
+                                                                  for l in range(self.L)]
+        csa2.csa2_index_select_append(self.key_pools[r], self.batch, self.q_idx_d, self.K, rows, ws=self.sel_ws,
+                                      indices=self.idx)
+        csa2.csa2_sparse_fp4_decode_attn_layers([(self.kv[r][l], self.q_d[l], self.idx) for l in range(self.L)],
+                                                self.batch, self.w.sigma, ws=self.attn_ws,
+                                                outs=[self.out[l] for l in range(self.L)],
+                                                lses=[self.lse[l] for l in range(self.L)])
 
     def algorithmic_bytes(self):
         per = sum((n + 1) * 128 for n in self.lens) + self.L * sum(min(n + 1, self.K) for n in self.lens) * 288
@@ -513,19 +571,22 @@ class MixedServing(Decode):
     def dominant_bytes(self):
         return sum((n + 1) * 128 for n in self.lens) + self.B * 64 * 4
 
+    def attn_bytes(self):
+        return self.L * (sum(min(n + 1, self.K) for n in self.lens) * 288 + self.B * (
+            self.H * 512 * 2 + self.K * 4 + self.H * 512 * 4 + self.H * 4))
+
     def oracle_step(self, rows=None):
+        """The oracle on sequences whose inputs __init__ prepared: the Full selection over every key, then
+        each layer's pack of the selected latents and its attention."""
         import oracle
 
-        wl = self.wl
         outs = []
-        for b in (rows if rows is not None else range(self.B)):
-            n = self.lens[b] + 1
-            kf = oracle.indexer.keys_to_f64(self.keys[b], "bf16")
+        for b in (rows if rows is not None else sorted(self.oracle_rows)):
+            kf, idx0, lat_sel = self.oracle_rows[b]
             idx, _ = oracle.indexer.full_select(self.q_idx[b], kf, self.K)
-            v = oracle.attention.valid_slots(idx, n)
+            assert np.array_equal(idx, idx0)
             for l in range(self.L):
-                lat = wl.latent_rows(self.st, l, b, n)
-                c = oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(lat[v]))
+                c = oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(lat_sel[l]))
                 outs.append(oracle.attention.sparse_attention(self.q[l][b], c, self.w.sigma))
         return outs
 
@@ -664,7 +725,7 @@ def cpu_baseline(wk, budget_s):
             fl = wk.flops() * rows * reps / wk.T
             return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
                     "sample": f"{reps} x {rows}-token slices x 20 layers of the CED projection + pack (float64)",
-                    "usable_cores": cores_avail}
+                    "usable_cores": cores_avail, "cpu_model": cpu_model()}
         per_call_queries = None
         t0 = time.time()
         calls = 0
@@ -678,16 +739,18 @@ def cpu_baseline(wk, budget_s):
                       if isinstance(wk, DecoderX20) else
                       f"{calls} full 4-layer steps (1M-token scan, pool, 3 Reindex, 4 attentions)")
         else:
+            seqs = sorted(wk.oracle_rows) if getattr(wk, "oracle_rows", None) else list(range(wk.B))
             b = 0
             while calls < 1 or time.time() - t0 < budget_s:
-                wk.oracle_step(rows=[b % wk.B])
+                wk.oracle_step(rows=[seqs[b % len(seqs)]])
                 calls += 1
                 queries += getattr(wk, "L", 1)
                 b += 1
-            sample = f"{calls} sequences of the batch (selection + attention per sequence, float64)"
+            sample = (f"{calls} sequences of the batch (selection + attention per sequence, float64; "
+                      f"cycling over sequences {seqs[0]}..{seqs[-1]})")
         dt = time.time() - t0
         return {"value": queries / dt, "unit": "queries/s", "cores": 1, "kind": "oracle", "sample": sample,
-                "seconds": round(dt, 2), "usable_cores": cores_avail}
+                "seconds": round(dt, 2), "usable_cores": cores_avail, "cpu_model": cpu_model()}
     finally:
         if ctx is not None:
             ctx.unregister() if hasattr(ctx, "unregister") else None
@@ -699,7 +762,7 @@ def cpu_baseline(wk, budget_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_hierarchical", choices=WORKLOADS)
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated for cold reads (0: auto)")
@@ -776,16 +839,36 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {args.steps} steps timed: {ms * 1e3:.1f} us per step")
 
-    # dominant kernel: HIP events around each of its launches in eager steps
-    pairs = []
-    for i in range(args.steps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        csa2.csa2_time_next_launch(wk.dominant, a, b)
-        wk.step(i % R)
-        pairs.append((a, b))
+    # the distribution of single steps (an event pair around each replay, a separate pass)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        run(i)
+        b.record()
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+    per = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3
+    step_us = {"p10": float(np.percentile(per, 10)), "median": float(np.median(per)),
+               "p90": float(np.percentile(per, 90)), "steps": len(per)}
+
+    # a kernel's own time: HIP events around each of its launches (on the stream it is launched on) in
+    # eager steps over the same rotated replicas
+    def kernel_ms(name, n):
+        pairs = []
+        for i in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            csa2.csa2_time_next_launch(name, a, b)
+            wk.step(i % R)
+            if csa2.lib().csa2_timer_pending():  # the step never launched this kernel
+                csa2.csa2_time_next_launch(None)
+                return None
+            pairs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs]))
+
+    n_eager = min(args.steps, 50)
+    kern_ms = kernel_ms(wk.dominant, n_eager)
 
     alg = wk.algorithmic_bytes()
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -811,6 +894,16 @@ def main():
         roof["mfma_tflops"], roof["mfma_frac"] = tf, tf / BF16_PEAK_TFLOPS  # fp16 dense peak = bf16's
     roof["kernel"] = wk.dominant
     roof["kernel_ms"] = kern_ms
+    if hasattr(wk, "attn_bytes"):
+        # the attention launch of the step: its algorithmic bytes over its own time (latency-bound at batch 1)
+        a_ms = kernel_ms("sparse_attn", n_eager)
+        c_ms = kernel_ms("attn_combine", n_eager)
+        if a_ms:
+            ab = wk.attn_bytes()
+            res["attn_roofline"] = {"kernel": "sparse_attn", "bound": "hbm", "achieved": ab / (a_ms * 1e-3) / 1e9,
+                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                    "frac": ab / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "bytes": ab,
+                                    "kernel_ms": a_ms, "combine_ms": c_ms}
     roof["traffic"] = None
     try:  # counter-derived bytes, only while the kernel source is the one they were taken on
         with open(args.traffic_file) as f:
@@ -821,6 +914,19 @@ def main():
         pass
     res["roofline"] = roof
     res["graph"] = graphs is not None
+    res["step_us"] = step_us
+    # context: what a plain device copy reaches on this GPU (1 GiB read + 1 GiB written)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    res["copy_gbps"] = 5 * 2 * src.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
     if want_cpu:
         log("[bench] timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(wk, args.cpu_seconds)

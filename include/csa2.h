@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define CSA2_ABI_VERSION 5
+#define CSA2_ABI_VERSION 6
 
 typedef enum {
   CSA2_OK = 0,
@@ -109,6 +109,33 @@ const char *csa2_status_string(csa2_status status);
  * "attn_combine", "ced_project", "fp4_pack", "kv_append", "index_scores".
  * kernel == NULL disarms.  Returns CSA2_ERR_INVALID_ARG for an unknown name. */
 csa2_status csa2_time_next_launch(const char *kernel, void *start_event, void *stop_event);
+/* 1 while a timer armed by csa2_time_next_launch has not fired yet (its kernel
+ * has not been launched since), else 0. */
+int32_t csa2_timer_pending(void);
+
+/* ---- Debug checks: device-side checks of the documented input contracts.
+ * Off unless the environment variable CSA2_DEBUG_CHECKS is a non-zero number
+ * when the library first launches, or csa2_debug_checks(1) is called (0 turns
+ * them off).  While on, kernels OR these bits into a per-device flag word
+ * (inputs are still treated as documented: skipped entries stay skipped):
+ *   CSA2_DBG_Q_RANGE    an attention query or rope value of magnitude above
+ *                       65504 (fp16 overflow) or NaN
+ *   CSA2_DBG_INDEX      a selected index below -1 or at or past seq_len
+ *   CSA2_DBG_PAGE       a visible position whose page id is outside
+ *                       [0, num_blocks) or past max_blocks_per_seq
+ *   CSA2_DBG_NONFINITE  a NaN or infinite value given to the FP4 pack or append
+ *   CSA2_DBG_SCORE      a NaN or infinite score given to csa2_topk
+ *   CSA2_DBG_SEQ_LEN    a sequence length outside [0, max_seq_len]
+ * csa2_debug_flags waits for the device, returns the bits raised on the
+ * current device since the last call and clears them. */
+#define CSA2_DBG_Q_RANGE 1u
+#define CSA2_DBG_INDEX 2u
+#define CSA2_DBG_PAGE 4u
+#define CSA2_DBG_NONFINITE 8u
+#define CSA2_DBG_SCORE 16u
+#define CSA2_DBG_SEQ_LEN 32u
+csa2_status csa2_debug_checks(int32_t enable);
+csa2_status csa2_debug_flags(uint32_t *flags);
 
 /* Zero `bytes` of a workspace on `stream` (a fill kernel, no memset node). */
 csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream);
@@ -290,6 +317,54 @@ csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
                               int32_t pool_blocks, int32_t pool_block_tokens, int32_t *indices,
                               void *ws, size_t ws_bytes, csa2_stream stream);
 
+/* ---- Full-mode selection with this step's appends in the same launch
+ * ([P1] "CSA2" Full mode and "Hierarchical Sparse Indexer"; the appended row
+ * is the [P1] "FP4 KV cache" entry of the token being decoded, which is
+ * visible to this step's selection).  seqs->seq_lens count the new token:
+ * for every sequence b with n = seq_lens[b] >= 1, each of the n_appends rows
+ * is written at position n - 1 of its layer exactly as csa2_kv_append writes
+ * it at position seq_lens[b] (csa2_kv_append with lengths n - 1), and then
+ * indices (and pool_out, when not NULL) are what csa2_index_select in FULL
+ * mode returns over positions 0 .. n - 1.  When an append writes the scanned
+ * layer's keys (the same idx_keys storage, with idx_key given), the new key is
+ * scored from that input directly; otherwise the key at n - 1 is read from the
+ * cache.  The append workgroups ride in the scan's launch, so no launch is
+ * added.  Appends write disjoint storage (no two share codes, or key storage,
+ * that both write); 0 <= n_appends <= 8.  Other arguments, limits and the
+ * workspace (csa2_index_select_workspace_size) as for csa2_index_select. */
+typedef struct {
+  const csa2_kv_layer *layer;
+  const float *latent;      /* device fp32 [batch][512] or NULL */
+  const uint16_t *rope;     /* device bf16 [batch][rope_dim] or NULL */
+  const void *idx_key;      /* device [batch][idx_dim] (fp32 for CSA2_FP4 keys, packed here) or NULL */
+} csa2_append;
+csa2_status csa2_index_select_append(const csa2_kv_layer *keys, const csa2_seqs *seqs, const csa2_append *appends,
+                                     int32_t n_appends, const void *q_idx, const float *w_idx, int32_t top_k,
+                                     int32_t *pool_out, int32_t pool_blocks, int32_t pool_block_tokens,
+                                     int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream);
+
+/* ---- Reindex for several layers at once ([P1] "CSA2" Reindex mode and
+ * "Hierarchical Sparse Indexer": every later selecting layer rescores only
+ * the candidate pool of the first Full layer with its own query).  Each entry
+ * of `queries` is one REINDEX call of csa2_index_select over the same keys,
+ * seqs, pool_in, pool_blocks and top_k: its q_idx / w_idx as defined there and
+ * its own indices (device int32 [batch][top_k]).  Results equal those of one
+ * csa2_index_select call per layer; the layers' pool scoring runs in one
+ * launch and their selections in one more.  1 <= n_layers <= 8.  Workspace
+ * from csa2_index_reindex_layers_workspace_size (it holds no per-position
+ * keys, so it does not grow with the sequence length). */
+typedef struct {
+  const void *q_idx;
+  const float *w_idx;
+  int32_t *indices;
+} csa2_reindex_query;
+csa2_status csa2_index_reindex_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t top_k,
+                                                    int32_t pool_blocks, int32_t pool_block_tokens, size_t *bytes);
+csa2_status csa2_index_reindex_layers(const csa2_kv_layer *keys, const csa2_seqs *seqs,
+                                      const csa2_reindex_query *queries, int32_t n_layers, int32_t top_k,
+                                      const int32_t *pool_in, int32_t pool_blocks, int32_t pool_block_tokens,
+                                      void *ws, size_t ws_bytes, csa2_stream stream);
+
 /* ---- Sparse FP4 decode attention ([P1] "CSA2": all heads share one latent;
  * "FP4 KV cache": entries are dequantized before attention; [P4] section 2:
  * 64 heads, 1 KV head).  For each sequence b and head h, over the valid
@@ -301,7 +376,12 @@ csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
  * indices: device int32 [batch][top_k]; out: device fp32 [batch][heads][512];
  * lse: device fp32 [batch][heads] or NULL.  heads must be a positive multiple
  * of 16 (at most 128); top_k in [1, 4096].  The logits and the softmax run in
- * fp32; q and rope enter the matrix cores as fp16. */
+ * fp32; q and rope enter the matrix cores as fp16, which holds every bf16
+ * value of magnitude 2^-14 .. 65504 (and zero) exactly: inside that range the
+ * conversion loses nothing.  Smaller magnitudes become fp16 subnormals (an
+ * absolute error below 2^-25 per element); larger ones become infinite and
+ * make that head's results NaN, so q and rope must stay below 65504 in
+ * magnitude (with debug checks on, such values set a device error flag). */
 csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim,
                                      size_t *bytes);
 csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_seqs *seqs,
@@ -332,6 +412,38 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
                                             int32_t top_k, float softmax_scale, const csa2_swa_window *win,
                                             const float *new_latent, float *out, float *lse, void *ws,
                                             size_t ws_bytes, csa2_stream stream);
+
+/* ---- The attention of several layers in one launch ([P1] "CSA2": the
+ * decoder's layers each attend over their own KV with indices that a Full or
+ * Reindex layer selected, a Reuse layer taking another layer's indices
+ * unchanged; [P1] "Hierarchical Sparse Indexer": a step runs one Full and
+ * several Reindex layers).  Every entry of `layers` is one problem exactly as
+ * csa2_sparse_fp4_decode_attn defines it -- its own KV pool, query (device
+ * bf16 [batch][heads][512 + rope_dim]), indices (device int32
+ * [batch][top_k]), out (device fp32 [batch][heads][512]) and lse (device fp32
+ * [batch][heads] or NULL) -- or, with `win` set, as
+ * csa2_sparse_fp4_decode_attn_swa defines it (its own ring; new_latent NULL
+ * or that layer's current window entry).  All layers share seqs, heads,
+ * top_k and softmax_scale; their pools have the same rope_dim; either every
+ * layer has a window or none has.  1 <= n_layers <= 20.  Results equal those
+ * of one call per layer (the same kernels; only the launch is shared), so the
+ * layers' problems are independent: no output may alias another layer's
+ * input.  Workspace from csa2_attn_layers_workspace_size (with_window: 1 when
+ * the layers have windows). */
+typedef struct {
+  const csa2_kv_layer *layer;
+  const uint16_t *q;
+  const int32_t *indices;
+  float *out;
+  float *lse;
+  const csa2_swa_window *win; /* NULL: no sliding-window branch */
+  const float *new_latent;    /* with win: NULL or device fp32 [batch][512] */
+} csa2_attn_layer;
+csa2_status csa2_attn_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t heads, int32_t top_k,
+                                            int32_t latent_dim, int32_t with_window, size_t *bytes);
+csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, int32_t n_layers,
+                                               const csa2_seqs *seqs, int32_t heads, int32_t top_k,
+                                               float softmax_scale, void *ws, size_t ws_bytes, csa2_stream stream);
 
 /* ---- Host-side page allocator (no device memory): a free list of block ids
  * [0, num_blocks).  Not thread-safe; one instance per owner. */

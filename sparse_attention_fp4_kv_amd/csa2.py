@@ -72,6 +72,27 @@ class SwaWindow(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("batch", ctypes.c_int32)]
 
 
+class AppendRowC(ctypes.Structure):
+    """csa2_append: one row appended in the scan's launch."""
+
+    _fields_ = [("layer", ctypes.POINTER(KvLayer)), ("latent", ctypes.c_void_p), ("rope", ctypes.c_void_p),
+                ("idx_key", ctypes.c_void_p)]
+
+
+class ReindexQueryC(ctypes.Structure):
+    """csa2_reindex_query: one Reindex layer's query and output."""
+
+    _fields_ = [("q_idx", ctypes.c_void_p), ("w_idx", ctypes.c_void_p), ("indices", ctypes.c_void_p)]
+
+
+class AttnLayerC(ctypes.Structure):
+    """csa2_attn_layer: one layer's attention problem in a multi-layer launch."""
+
+    _fields_ = [("layer", ctypes.POINTER(KvLayer)), ("q", ctypes.c_void_p), ("indices", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("win", ctypes.POINTER(SwaWindow)),
+                ("new_latent", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -84,6 +105,9 @@ SIGNATURES = {
     "csa2_abi_version": (ctypes.c_int, []),
     "csa2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "csa2_time_next_launch": (ctypes.c_int, [ctypes.c_char_p, _P, _P]),
+    "csa2_timer_pending": (_I32, []),
+    "csa2_debug_checks": (ctypes.c_int, [_I32]),
+    "csa2_debug_flags": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
     "csa2_workspace_clear": (ctypes.c_int, [_P, _SZ, _P]),
     "csa2_fp4_pack": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _P]),
     "csa2_fp4_unpack": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P]),
@@ -107,6 +131,14 @@ SIGNATURES = {
     "csa2_attn_swa_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_sparse_fp4_decode_attn_swa": (ctypes.c_int, [_PKV, _PSQ, _P, _I32, _P, _I32, ctypes.c_float,
                                                        ctypes.POINTER(SwaWindow), _P, _P, _P, _P, _SZ, _P]),
+    "csa2_index_select_append": (ctypes.c_int, [_PKV, _PSQ, ctypes.POINTER(AppendRowC), _I32, _P, _P, _I32, _P, _I32,
+                                                _I32, _P, _P, _SZ, _P]),
+    "csa2_index_reindex_layers_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "csa2_index_reindex_layers": (ctypes.c_int, [_PKV, _PSQ, ctypes.POINTER(ReindexQueryC), _I32, _I32, _P, _I32,
+                                                 _I32, _P, _SZ, _P]),
+    "csa2_attn_layers_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
+    "csa2_sparse_fp4_decode_attn_layers": (ctypes.c_int, [ctypes.POINTER(AttnLayerC), _I32, _PSQ, _I32, _I32,
+                                                          ctypes.c_float, _P, _SZ, _P]),
     "csa2_block_pool_create": (_P, [_I32]),
     "csa2_block_alloc": (ctypes.c_int, [_P, _I32, _P]),
     "csa2_block_free": (ctypes.c_int, [_P, _I32, _P]),
@@ -472,6 +504,103 @@ def csa2_sparse_fp4_decode_attn_swa(layer, batch, q, indices, softmax_scale, rin
                                                  _ptr(lse),
                                                  _ptr(ws), ws.numel(), _stream()), "csa2_sparse_fp4_decode_attn_swa")
     return out, lse
+
+
+def csa2_index_select_append(layer, batch, q_idx, top_k, appends, pool_blocks=0, want_pool=False, ws=None,
+                             indices=None, pool_out=None, w_idx=None):
+    """Full selection (optionally with the pool) over seq_lens positions, with this step's rows appended at
+    position seq_lens[b] - 1 in the same launch.  appends: list of (layer, latent | None, rope | None,
+    idx_key | None) -> (indices, pool_out or None)."""
+    B = batch.batch
+    dev = q_idx.device
+    max_len = batch.max_seq_len or batch.block_table.shape[1] * PAGE
+    if ws is None:
+        ws = workspace(index_select_workspace_bytes(B, max_len, top_k, pool_blocks if want_pool else 0), dev)
+    if indices is None:
+        indices = torch.empty((B, top_k), dtype=torch.int32, device=dev)
+    if want_pool and pool_out is None:
+        pool_out = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
+    kvs = [a[0].struct() for a in appends]  # kept alive for the call
+    rows = (AppendRowC * max(len(appends), 1))(
+        *[AppendRowC(ctypes.pointer(kv), _ptr(a[1]), _ptr(a[2]), _ptr(a[3])) for kv, a in zip(kvs, appends)])
+    kv, sq = layer.struct(), batch.struct()
+    _check(lib().csa2_index_select_append(ctypes.byref(kv), ctypes.byref(sq), rows, len(appends), _ptr(q_idx),
+                                          _ptr(w_idx), top_k, _ptr(pool_out) if want_pool else None, pool_blocks,
+                                          8 if want_pool else 0, _ptr(indices), _ptr(ws), ws.numel(), _stream()),
+           "csa2_index_select_append")
+    return indices, (pool_out if want_pool else None)
+
+
+def reindex_layers_workspace_bytes(n_layers, batch, top_k, pool_blocks):
+    n = ctypes.c_size_t()
+    _check(lib().csa2_index_reindex_layers_workspace_size(n_layers, batch, top_k, pool_blocks, 8, ctypes.byref(n)),
+           "csa2_index_reindex_layers_workspace_size")
+    return n.value
+
+
+def csa2_index_reindex_layers(layer, batch, queries, top_k, pool_in, pool_blocks, ws=None, indices=None):
+    """Reindex of several layers over one pool.  queries: list of (q_idx, w_idx | None); indices: list of
+    int32 [B, K] outputs or None -> list of indices."""
+    B = batch.batch
+    dev = pool_in.device
+    L = len(queries)
+    if ws is None:
+        ws = workspace(reindex_layers_workspace_bytes(L, B, top_k, pool_blocks), dev)
+    if indices is None:
+        indices = [torch.empty((B, top_k), dtype=torch.int32, device=dev) for _ in range(L)]
+    qs = (ReindexQueryC * L)(*[ReindexQueryC(_ptr(q), _ptr(w), _ptr(o)) for (q, w), o in zip(queries, indices)])
+    kv, sq = layer.struct(), batch.struct()
+    _check(lib().csa2_index_reindex_layers(ctypes.byref(kv), ctypes.byref(sq), qs, L, top_k, _ptr(pool_in),
+                                           pool_blocks, 8, _ptr(ws), ws.numel(), _stream()),
+           "csa2_index_reindex_layers")
+    return indices
+
+
+def attn_layers_workspace_bytes(n_layers, batch, heads, top_k, window=False):
+    n = ctypes.c_size_t()
+    _check(lib().csa2_attn_layers_workspace_size(n_layers, batch, heads, top_k, 512, 1 if window else 0,
+                                                 ctypes.byref(n)), "csa2_attn_layers_workspace_size")
+    return n.value
+
+
+def csa2_sparse_fp4_decode_attn_layers(jobs, batch, softmax_scale, ws=None, outs=None, lses=None):
+    """Several layers' attention in one launch.  jobs: list of (layer, q bf16 bits [B, H, 512+rope], indices
+    int32 [B, K]) or (layer, q, indices, ring, new_latent | None) with a sliding window -> (outs, lses)."""
+    B, H, _ = jobs[0][1].shape
+    K = jobs[0][2].shape[1]
+    dev = jobs[0][1].device
+    L = len(jobs)
+    window = len(jobs[0]) > 3
+    if ws is None:
+        ws = workspace(attn_layers_workspace_bytes(L, B, H, K, window), dev)
+    if outs is None:
+        outs = [torch.empty((B, H, 512), dtype=torch.float32, device=dev) for _ in range(L)]
+    if lses is None:
+        lses = [torch.empty((B, H), dtype=torch.float32, device=dev) for _ in range(L)]
+    kvs = [j[0].struct() for j in jobs]  # kept alive for the call
+    wins = [j[3].struct() if window else None for j in jobs]
+    arr = (AttnLayerC * L)(*[
+        AttnLayerC(ctypes.pointer(kv), _ptr(j[1]), _ptr(j[2]), _ptr(o), _ptr(ls),
+                   ctypes.pointer(w) if w is not None else None, _ptr(j[4]) if window else None)
+        for kv, w, j, o, ls in zip(kvs, wins, jobs, outs, lses)])
+    sq = batch.struct()
+    _check(lib().csa2_sparse_fp4_decode_attn_layers(arr, L, ctypes.byref(sq), H, K, float(softmax_scale), _ptr(ws),
+                                                    ws.numel(), _stream()), "csa2_sparse_fp4_decode_attn_layers")
+    return outs, lses
+
+
+DBG_Q_RANGE, DBG_INDEX, DBG_PAGE, DBG_NONFINITE, DBG_SCORE, DBG_SEQ_LEN = 1, 2, 4, 8, 16, 32
+
+
+def csa2_debug_checks(enable):
+    _check(lib().csa2_debug_checks(1 if enable else 0), "csa2_debug_checks")
+
+
+def csa2_debug_flags():
+    """Waits for the device; returns and clears the debug bits raised since the last call."""
+    v = ctypes.c_uint32()
+    _check(lib().csa2_debug_flags(ctypes.byref(v)), "csa2_debug_flags")
+    return v.value
 
 
 class BlockPool:

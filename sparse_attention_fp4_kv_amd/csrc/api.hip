@@ -3,13 +3,54 @@
 // arguments before launching anything and never lets a C++ exception out.
 #include "../../include/csa2.h"
 
+#include <atomic>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "kernels.h"
 
 using namespace csa2;
+
+// The debug flag word of every device (word 0 is used; the rest pads it to
+// its own cache line).
+static __device__ __align__(256) uint32_t dbg_word[64];
+
+namespace {
+std::atomic<int> g_debug{-1};  // -1: the environment has not been read yet
+std::mutex g_dbg_mu;
+void *g_dbg_addr[kMaxDevices] = {};
+
+bool debug_on() {
+  int v = g_debug.load();
+  if (v < 0) {
+    const char *e = std::getenv("CSA2_DEBUG_CHECKS");
+    int want = (e != nullptr && std::atoi(e) != 0) ? 1 : 0;
+    g_debug.compare_exchange_strong(v, want);
+    v = g_debug.load();
+  }
+  return v > 0;
+}
+
+// The flag word's address on the current device (resolved once per device).
+void *dbg_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_dbg_mu);
+  if (g_dbg_addr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(dbg_word)) != hipSuccess) return nullptr;
+    g_dbg_addr[dev] = p;
+  }
+  return g_dbg_addr[dev];
+}
+}  // namespace
+
+namespace csa2 {
+uint32_t *debug_flags() { return debug_on() ? static_cast<uint32_t *>(dbg_address()) : nullptr; }
+}  // namespace csa2
 
 namespace {
 
@@ -143,6 +184,26 @@ csa2_status csa2_time_next_launch(const char *kernel, void *start_event, void *s
     }
   }
   return CSA2_ERR_INVALID_ARG;
+}
+
+int32_t csa2_timer_pending(void) { return g_timer.id >= 0 ? 1 : 0; }
+
+csa2_status csa2_debug_checks(int32_t enable) {
+  g_debug.store(enable != 0 ? 1 : 0);
+  if (enable != 0 && dbg_address() == nullptr) return CSA2_ERR_HIP;
+  return CSA2_OK;
+}
+
+csa2_status csa2_debug_flags(uint32_t *flags) {
+  if (flags == nullptr) return CSA2_ERR_INVALID_ARG;
+  *flags = 0;
+  void *p = dbg_address();
+  if (p == nullptr) return CSA2_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return CSA2_ERR_HIP;
+  const uint32_t zero = 0;
+  if (hipMemcpy(flags, p, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess) return CSA2_ERR_HIP;
+  if (hipMemcpy(p, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess) return CSA2_ERR_HIP;
+  return CSA2_OK;
 }
 
 csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream) {
@@ -376,11 +437,102 @@ csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
   return from_hip(e);
 }
 
+namespace {
+// Validates one row of csa2_index_select_append (the checks of csa2_kv_append).
+csa2_status check_append(const csa2_append &a, AppendRow *out) {
+  KvLayerDev L;
+  csa2_status st = check_layer(a.layer, a.latent != nullptr, false, &L);
+  if (st != CSA2_OK) return st;
+  if (a.latent == nullptr && a.rope == nullptr && a.idx_key == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (a.rope != nullptr && (L.rope_dim == 0 || a.layer->rope == nullptr)) return CSA2_ERR_INVALID_ARG;
+  if (a.latent != nullptr && L.rope_dim != 0 && a.rope == nullptr) return CSA2_ERR_INVALID_ARG;
+  if (a.idx_key != nullptr && !keys_ok(a.layer)) return CSA2_ERR_INVALID_ARG;
+  if (a.idx_key != nullptr && !aligned(a.idx_key, 16)) return CSA2_ERR_INVALID_ARG;
+  *out = AppendRow{L, a.latent, a.rope, a.idx_key};
+  return CSA2_OK;
+}
+}  // namespace
+
+csa2_status csa2_index_select_append(const csa2_kv_layer *keys, const csa2_seqs *seqs, const csa2_append *appends,
+                                     int32_t n_appends, const void *q_idx, const float *w_idx, int32_t top_k,
+                                     int32_t *pool_out, int32_t pool_blocks, int32_t pool_block_tokens,
+                                     int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(keys, false, true, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (pool_out != nullptr && (pool_block_tokens != 8 || pool_blocks < 1 || pool_blocks > kMaxPoolBlocks))
+    return CSA2_ERR_INVALID_ARG;
+  if (n_appends < 0 || n_appends > kMaxAppendRows || (n_appends > 0 && appends == nullptr))
+    return CSA2_ERR_INVALID_ARG;
+  AppendRow rows[kMaxAppendRows];
+  const void *new_key = nullptr;
+  for (int i = 0; i < n_appends; ++i) {
+    if ((st = check_append(appends[i], &rows[i])) != CSA2_OK) return st;
+    // rows write disjoint storage: no two appends may share codes or key storage
+    for (int j = 0; j < i; ++j) {
+      if (appends[i].latent && appends[j].latent && appends[i].layer->codes == appends[j].layer->codes)
+        return CSA2_ERR_INVALID_ARG;
+      if (appends[i].idx_key && appends[j].idx_key && appends[i].layer->idx_keys == appends[j].layer->idx_keys)
+        return CSA2_ERR_INVALID_ARG;
+    }
+    if (appends[i].idx_key != nullptr && appends[i].layer->idx_keys == keys->idx_keys) {
+      const csa2_kv_layer *a = appends[i].layer;  // the scanned keys: the same kind of key
+      if (a->idx_dtype != keys->idx_dtype || a->idx_scales != keys->idx_scales) return CSA2_ERR_INVALID_ARG;
+      new_key = appends[i].idx_key;
+    }
+  }
+  if (S.batch == 0) return CSA2_OK;
+  if (!query_ok(keys, q_idx, w_idx) || indices == nullptr) return CSA2_ERR_INVALID_ARG;
+  const size_t need = index_select_workspace_bytes(S.batch, S.max_len, top_k, pool_out ? pool_blocks : 0);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_index_select_full(L, S, IdxQuery{q_idx, w_idx}, top_k, pool_out, pool_out ? pool_blocks : 0,
+                                           indices, ws, as_stream(stream), rows, n_appends, new_key));
+}
+
+csa2_status csa2_index_reindex_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t top_k,
+                                                    int32_t pool_blocks, int32_t pool_block_tokens, size_t *bytes) {
+  if (bytes == nullptr || n_layers < 1 || n_layers > kMaxIdxLayers || batch < 0 || top_k < 1 || top_k > kMaxTopK)
+    return CSA2_ERR_INVALID_ARG;
+  if (pool_block_tokens != 8 || pool_blocks < 1 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
+  *bytes = reindex_layers_workspace_bytes(n_layers, batch);
+  return CSA2_OK;
+}
+
+csa2_status csa2_index_reindex_layers(const csa2_kv_layer *keys, const csa2_seqs *seqs,
+                                      const csa2_reindex_query *queries, int32_t n_layers, int32_t top_k,
+                                      const int32_t *pool_in, int32_t pool_blocks, int32_t pool_block_tokens,
+                                      void *ws, size_t ws_bytes, csa2_stream stream) {
+  KvLayerDev L;
+  SeqsDev S;
+  csa2_status st = check_layer(keys, false, true, &L);
+  if (st != CSA2_OK) return st;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (queries == nullptr || n_layers < 1 || n_layers > kMaxIdxLayers) return CSA2_ERR_INVALID_ARG;
+  if (top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (pool_block_tokens != 8 || pool_blocks < 1 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
+  if (S.batch == 0) return CSA2_OK;
+  if (pool_in == nullptr) return CSA2_ERR_INVALID_ARG;
+  IdxQuery q[kMaxIdxLayers];
+  int32_t *out[kMaxIdxLayers];
+  for (int j = 0; j < n_layers; ++j) {
+    if (!query_ok(keys, queries[j].q_idx, queries[j].w_idx) || queries[j].indices == nullptr)
+      return CSA2_ERR_INVALID_ARG;
+    q[j] = IdxQuery{queries[j].q_idx, queries[j].w_idx};
+    out[j] = queries[j].indices;
+  }
+  const size_t need = reindex_layers_workspace_bytes(n_layers, S.batch);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_reindex_layers(L, S, q, out, n_layers, top_k, pool_in, pool_blocks, ws, as_stream(stream)));
+}
+
 csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim, size_t *bytes) {
   if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
       top_k > kMaxTopK || latent_dim != 512)
     return CSA2_ERR_INVALID_ARG;
-  *bytes = attn_workspace_bytes(batch, heads, top_k, false);
+  *bytes = attn_workspace_bytes(1, batch, heads, top_k, false);
   return CSA2_OK;
 }
 
@@ -389,7 +541,7 @@ csa2_status csa2_attn_swa_workspace_size(int32_t batch, int32_t heads, int32_t t
   if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
       top_k > kMaxTopK || latent_dim != 512)
     return CSA2_ERR_INVALID_ARG;
-  *bytes = attn_workspace_bytes(batch, heads, top_k, true);
+  *bytes = attn_workspace_bytes(1, batch, heads, top_k, true);
   return CSA2_OK;
 }
 
@@ -406,10 +558,10 @@ csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_s
   if (S.batch == 0) return CSA2_OK;
   if (q == nullptr || indices == nullptr || out == nullptr || !aligned(q, 16) || !aligned(out, 16))
     return CSA2_ERR_INVALID_ARG;
-  const size_t need = attn_workspace_bytes(S.batch, heads, top_k, false);
+  const size_t need = attn_workspace_bytes(1, S.batch, heads, top_k, false);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, nullptr, nullptr, nullptr, out,
-                                     lse, ws, as_stream(stream)));
+  const AttnLaunchJob job{L, q, indices, nullptr, nullptr, nullptr, out, lse};
+  return from_hip(launch_sparse_attn(&job, 1, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
 }
 
 csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const csa2_seqs *seqs, const uint16_t *q,
@@ -430,10 +582,62 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
   if (win->codes == nullptr || win->scales == nullptr || !aligned(win->codes, 16) || !aligned(win->scales, 4))
     return CSA2_ERR_INVALID_ARG;
   if (new_latent != nullptr && !aligned(new_latent, 8)) return CSA2_ERR_INVALID_ARG;
-  const size_t need = attn_workspace_bytes(S.batch, heads, top_k, true);
+  const size_t need = attn_workspace_bytes(1, S.batch, heads, top_k, true);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  return from_hip(launch_sparse_attn(L, S, q, heads, indices, top_k, softmax_scale, win->codes, win->scales,
-                                     new_latent, out, lse, ws, as_stream(stream)));
+  const AttnLaunchJob job{L, q, indices, win->codes, win->scales, new_latent, out, lse};
+  return from_hip(launch_sparse_attn(&job, 1, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
+}
+
+csa2_status csa2_attn_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t heads, int32_t top_k,
+                                            int32_t latent_dim, int32_t with_window, size_t *bytes) {
+  if (bytes == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs || batch < 0 || heads <= 0 || heads % 16 != 0 ||
+      heads > 128 || top_k < 1 || top_k > kMaxTopK || latent_dim != 512)
+    return CSA2_ERR_INVALID_ARG;
+  *bytes = attn_workspace_bytes(n_layers, batch, heads, top_k, with_window != 0);
+  return CSA2_OK;
+}
+
+csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, int32_t n_layers,
+                                               const csa2_seqs *seqs, int32_t heads, int32_t top_k,
+                                               float softmax_scale, void *ws, size_t ws_bytes, csa2_stream stream) {
+  SeqsDev S;
+  csa2_status st;
+  if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
+  if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return CSA2_ERR_INVALID_ARG;
+  AttnLaunchJob jobs[kMaxAttnJobs];
+  const bool window = layers[0].win != nullptr;
+  for (int j = 0; j < n_layers; ++j) {
+    const csa2_attn_layer &x = layers[j];
+    KvLayerDev L;
+    if ((st = check_layer(x.layer, true, false, &L)) != CSA2_OK) return st;
+    if (j > 0 && L.rope_dim != jobs[0].L.rope_dim) return CSA2_ERR_INVALID_ARG;  // one kernel variant per launch
+    if ((x.win != nullptr) != window) return CSA2_ERR_INVALID_ARG;
+    if (x.win == nullptr && x.new_latent != nullptr) return CSA2_ERR_INVALID_ARG;
+    if (x.win != nullptr) {
+      if (x.win->batch < S.batch) return CSA2_ERR_INVALID_ARG;
+      if (S.batch > 0 && (x.win->codes == nullptr || x.win->scales == nullptr || !aligned(x.win->codes, 16) ||
+                          !aligned(x.win->scales, 4)))
+        return CSA2_ERR_INVALID_ARG;
+      if (x.new_latent != nullptr && !aligned(x.new_latent, 8)) return CSA2_ERR_INVALID_ARG;
+    }
+    if (S.batch > 0 && (x.q == nullptr || x.indices == nullptr || x.out == nullptr || !aligned(x.q, 16) ||
+                        !aligned(x.out, 16)))
+      return CSA2_ERR_INVALID_ARG;
+    jobs[j] = AttnLaunchJob{L,
+                            x.q,
+                            x.indices,
+                            x.win ? x.win->codes : nullptr,
+                            x.win ? x.win->scales : nullptr,
+                            x.new_latent,
+                            x.out,
+                            x.lse};
+  }
+  if (S.batch == 0) return CSA2_OK;
+  const size_t need = attn_workspace_bytes(n_layers, S.batch, heads, top_k, window);
+  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_sparse_attn(jobs, n_layers, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
 }
 
 csa2_block_pool *csa2_block_pool_create(int32_t num_blocks) {

@@ -48,6 +48,7 @@
 
 namespace csa2 {
 
+
 namespace {
 
 constexpr int kT = 32;                 // entries per tile
@@ -60,24 +61,31 @@ constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
 constexpr int kWinSlots = 128;          // sliding-window ring slots per sequence
 constexpr int kWinSplits = kWinSlots / kT;  // window tiles = extra split workgroups
 
-struct AttnArgs {
+// One attention problem of a launch: a layer's KV pool, its query, the
+// selected positions and where the result goes (the batch view is shared).
+struct AttnJob {
   KvLayerDev L;
-  SeqsDev S;
-  const uint16_t *q;      // [B][H][512 + rope]
-  const int32_t *idx;     // [B][K]
-  int heads;              // H
-  int top_k;
-  int splits;             // workgroups per (b, head group) along the selected entries
-  int parts;              // partials per (b, head): splits, plus kWinSplits with the window
-  int tiles_per_split;
+  const uint16_t *q;         // [B][H][512 + rope]
+  const int32_t *idx;        // [B][K]
   uint8_t *win_codes;        // [B][128][512] E4M3 window entries, or null
   float *win_scales;         // [B][128] per-token scales
   const float *win_latent;   // [B][512] the current token's window entry to append first, or null
+  float *out;                // [B][H][512]
+  float *lse;                // [B][H] or null
+};
+
+struct AttnArgs {
+  AttnJob job[kMaxAttnJobs];
+  SeqsDev S;
+  int heads;              // H
+  int top_k;
+  int splits;             // workgroups per (job, b, head group) along the selected entries
+  int parts;              // partials per (job, b, head): splits, plus kWinSplits with the window
+  int tiles_per_split;
   float scale_log2;       // softmax scale * log2(e)
-  float *out;             // [B][H][512]  (splits == 1)
-  float *lse;             // [B][H] or null
-  float *part_o;          // [B][H][parts][512]  (parts > 1)
-  float *part_ml;         // [B][H][parts][2]
+  float *part_o;          // [jobs][B][H][parts][512]  (parts > 1)
+  float *part_ml;         // [jobs][B][H][parts][2]
+  uint32_t *dbg;          // debug flag word, or null
 };
 
 template <int MT>
@@ -158,8 +166,11 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   constexpr int KS = QW / 32;                  // 16 or 18 k-steps of 32 channels
   __shared__ Smem<MT> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, hg = blockIdx.y;
+  const int jz = blockIdx.z, jn = jz / a.S.batch, b = jz - jn * a.S.batch;  // job, sequence
+  const AttnJob &J = a.job[jn];
   const int h0 = hg * HG;
+  const size_t hrow0 = (size_t)jz * a.heads + h0;  // first (job, b, head) row of this workgroup
   const int n = min(max(a.S.seq_lens[b], 0), a.S.max_len);
   // workgroups past the selection's splits take window tile split - splits:
   // ring slots 32 wt .. 32 wt + 31, valid below min(seq_len, 128)
@@ -167,7 +178,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   const int wt = split - a.splits;
   const int nwin = min(max(a.S.seq_lens[b], 0), kWinSlots);
   const int s_new = nwin > 0 ? (a.S.seq_lens[b] - 1) % kWinSlots : -1;  // the current token's slot
-  const bool pack_new = win && a.win_latent != nullptr && s_new >= 0 && s_new / kT == wt;
+  const bool pack_new = win && J.win_latent != nullptr && s_new >= 0 && s_new / kT == wt;
 
   const int n_tiles_all = (a.top_k + kT - 1) / kT;
   const int tile_begin = win ? 0 : split * a.tiles_per_split;
@@ -175,7 +186,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   const int e_begin = tile_begin * kT;
   // <= kSlotCap (host-chosen splits)
   const int e_count = win ? kT : max(0, min(tile_end * kT, a.top_k) - e_begin);
-  const int32_t *idx_row = a.idx + (size_t)b * a.top_k;
+  const int32_t *idx_row = J.idx + (size_t)b * a.top_k;
 
   // ---- QK^T work of this wave: one M-tile (16 heads) and 1 or 2 N-tiles of 16 entries
   // (16 heads: every wave takes one N-tile and half of the k-steps; the two
@@ -199,6 +210,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const int i = 256 * j + tid;
       const int p = idx_row[min(e_begin + i, a.top_k - 1)];  // clamped read, masked below
       pos[j] = i < e_count ? p : -1;
+      if (a.dbg != nullptr && i < e_count && (p < -1 || p >= n)) dbg_raise(a.dbg, kDbgIndex);
     }
   }
 
@@ -206,12 +218,23 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   f16x8 qf[QKS];
   {
     const uint16_t *qrow =
-        a.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 32 * qk_k0 + 8 * (lane >> 4);
+        J.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 32 * qk_k0 + 8 * (lane >> 4);
     uint4 raw[QKS];
 #pragma unroll
     for (int ks = 0; ks < QKS; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
 #pragma unroll
     for (int ks = 0; ks < QKS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
+    if (a.dbg != nullptr) {  // a bf16 magnitude above fp16's largest finite value (65504)
+      bool big = false;
+#pragma unroll
+      for (int ks = 0; ks < QKS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) big |= !(fabsf((float)qf[ks][e]) <= 65504.0f);
+      if (big) dbg_raise(a.dbg, kDbgQRange);
+      if (split == 0 && hg == 0 && tid == 0 && (J.L.num_blocks < 0 || a.S.seq_lens[b] < 0 ||
+                                                  a.S.seq_lens[b] > a.S.max_len))
+        dbg_raise(a.dbg, kDbgSeqLen);
+    }
   }
 
   if (!win) {
@@ -229,7 +252,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     for (int j = 0; j < kSlotCap / 256; ++j) {
       if (256 * j >= e_count) break;
       const int i = 256 * j + tid;
-      const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < a.L.num_blocks;
+      const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < J.L.num_blocks;
+      if (a.dbg != nullptr && pos[j] >= 0 && !ok) dbg_raise(a.dbg, kDbgPage);
       sm.slot[i] = ok ? (uint32_t)blk[j] * kPage + (uint32_t)(pos[j] % kPage) : kNoSlot;
     }
   } else {
@@ -237,7 +261,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     // s = amax / 448, code = E4M3(x / s); each thread packs channels 2 tid, 2 tid + 1
     float snew = 0.0f;
     if (pack_new) {
-      const float2 x = reinterpret_cast<const float2 *>(a.win_latent + (size_t)b * kLatent)[tid];
+      const float2 x = reinterpret_cast<const float2 *>(J.win_latent + (size_t)b * kLatent)[tid];
       float m = fmaxf(fabsf(x.x), fabsf(x.y));
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -253,8 +277,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const uint16_t c = (uint16_t)(c0 | (c1 << 8));
       reinterpret_cast<uint16_t *>(sm.newc)[tid] = c;
       if (hg == 0) {  // one head group writes the ring
-        reinterpret_cast<uint16_t *>(a.win_codes + ((size_t)b * kWinSlots + s_new) * kLatent)[tid] = c;
-        if (tid == 0) a.win_scales[(size_t)b * kWinSlots + s_new] = snew;
+        reinterpret_cast<uint16_t *>(J.win_codes + ((size_t)b * kWinSlots + s_new) * kLatent)[tid] = c;
+        if (tid == 0) J.win_scales[(size_t)b * kWinSlots + s_new] = snew;
       }
     }
     if (tid < kT) {
@@ -264,7 +288,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const int s = kT * wt + tid;
       const bool ok = s < nwin;
       sm.slot[tid] = ok ? (uint32_t)s : kNoSlot;
-      const float ts = !ok ? 0.0f : (pack_new && s == s_new) ? snew : a.win_scales[(size_t)b * kWinSlots + s];
+      const float ts = !ok ? 0.0f : (pack_new && s == s_new) ? snew : J.win_scales[(size_t)b * kWinSlots + s];
       float mx = ts;
 #pragma unroll
       for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
@@ -297,11 +321,11 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     const int li = tile * kT + e - e_begin;
     const uint32_t slot = li < e_count ? sm.slot[li] : kNoSlot;
     const size_t rs = slot == kNoSlot ? 0 : slot;
-    const uint4 *cp = reinterpret_cast<const uint4 *>(a.L.codes + rs * (kLatent / 2) + 32 * cb);
+    const uint4 *cp = reinterpret_cast<const uint4 *>(J.L.codes + rs * (kLatent / 2) + 32 * cb);
     r.c0 = cp[0];
     r.c1 = cp[1];
-    r.sc4 = *reinterpret_cast<const uint32_t *>(a.L.scales + rs * (kLatent / kGroup) + 4 * cb);
-    if constexpr (ROPE) r.rp = *reinterpret_cast<const uint4 *>(a.L.rope + rs * 64 + 8 * cb);
+    r.sc4 = *reinterpret_cast<const uint32_t *>(J.L.scales + rs * (kLatent / kGroup) + 4 * cb);
+    if constexpr (ROPE) r.rp = *reinterpret_cast<const uint4 *>(J.L.rope + rs * 64 + 8 * cb);
     r.valid = slot != kNoSlot;
   };
 
@@ -322,7 +346,14 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       *reinterpret_cast<f16x8 *>(&cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc[wi >> 1]);
     if constexpr (ROPE) {
       const uint4 rp = make_uint4(r.rp.x & vmask, r.rp.y & vmask, r.rp.z & vmask, r.rp.w & vmask);
-      *reinterpret_cast<f16x8 *>(&cq[e][kLatent + 8 * cb]) = bf16x8_to_f16x8(rp);
+      const f16x8 rh = bf16x8_to_f16x8(rp);
+      *reinterpret_cast<f16x8 *>(&cq[e][kLatent + 8 * cb]) = rh;
+      if (a.dbg != nullptr) {
+        bool big = false;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) big |= !(fabsf((float)rh[i]) <= 65504.0f);
+        if (big) dbg_raise(a.dbg, kDbgQRange);
+      }
     }
   };
 
@@ -445,7 +476,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       const uint32_t slot = sm.slot[tile_entry];
       const uint4 *cp = pack_new && slot == (uint32_t)s_new  // the appended entry, from LDS
                             ? reinterpret_cast<const uint4 *>(sm.newc + 64 * tile_block)
-                            : reinterpret_cast<const uint4 *>(a.win_codes +
+                            : reinterpret_cast<const uint4 *>(J.win_codes +
                                                               ((size_t)b * kWinSlots + (slot == kNoSlot ? 0 : slot)) *
                                                                   kLatent +
                                                               64 * tile_block);
@@ -464,7 +495,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       __syncthreads();
       step(0, sm.cq[0], nullptr, sm.cq[1]);
     }
-  } else if (tile_begin < tile_end && a.L.num_blocks > 0) {
+  } else if (tile_begin < tile_end && J.L.num_blocks > 0) {
     const int last = tile_end - 1;
     Raw ra, rb, rc;
     load_raw(tile_begin, ra);
@@ -501,25 +532,25 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int hl = 16 * mt + 4 * (lane >> 4) + r;
-      const size_t h = (size_t)b * a.heads + h0 + hl;
+      const size_t h = hrow0 + hl;  // partial row (job, b, head)
       float sc = win ? sm.unnorm : 1.0f;
       float *dst = a.part_o + (h * a.parts + split) * kLatent;
       if (final_out) {
         const float l = sm.l_run[hl];
         sc = l > 0.f ? 1.0f / l : 0.f;
-        dst = a.out + h * kLatent;
+        dst = J.out + ((size_t)b * a.heads + h0 + hl) * kLatent;
       }
       dst += 128 * wave + (lane & 15);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) dst[16 * nt] = acc[mt][nt][r] * sc;
     }
   if (final_out) {
-    if (a.lse != nullptr && tid < HG) {
+    if (J.lse != nullptr && tid < HG) {
       const float l = sm.l_run[tid];
-      a.lse[(size_t)b * a.heads + h0 + tid] = l > 0.f ? (sm.m_run[tid] + log2f(l)) / kLog2e : -INFINITY;
+      J.lse[(size_t)b * a.heads + h0 + tid] = l > 0.f ? (sm.m_run[tid] + log2f(l)) / kLog2e : -INFINITY;
     }
   } else if (tid < HG) {
-    float *ml = a.part_ml + (((size_t)b * a.heads + h0 + tid) * a.parts + split) * 2;
+    float *ml = a.part_ml + ((hrow0 + tid) * a.parts + split) * 2;
     ml[0] = sm.m_run[tid];
     ml[1] = sm.l_run[tid];
   }
@@ -529,9 +560,17 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 // covers 256 channels of one head, one float4 per thread.  Splits are read 8
 // at a time (all loads of a chunk issued together) and merged online.
 constexpr int kCombineThreads = 64;
+// Where the merged rows go: partial row r = (job, b, head) belongs to job
+// r / rows_per_job and is row r % rows_per_job of that job's out / lse.
+struct CombineOut {
+  float *out[kMaxAttnJobs];
+  float *lse[kMaxAttnJobs];
+  int rows_per_job;  // B * H
+};
+
 __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
-                                                          float *__restrict__ out, float *__restrict__ lse) {
+                                                          CombineOut co) {
   constexpr int kChunk = 8;  // the launch sends this kernel at most 8 splits (more go to the wide merge)
   const int bh = blockIdx.x, quarter = blockIdx.y;  // quarter: which kCombineThreads float4s
   const int tid = threadIdx.x;
@@ -572,8 +611,11 @@ __global__ void __launch_bounds__(kCombineThreads) attn_combine_kernel(const flo
     m = mc;
   }
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[c4] = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
-  if (lse != nullptr && quarter == 0 && tid == 0) lse[bh] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
+  const int jn = bh / co.rows_per_job, row = bh - jn * co.rows_per_job;
+  reinterpret_cast<float4 *>(co.out[jn] + (size_t)row * kLatent)[c4] =
+      make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+  float *lse = co.lse[jn];
+  if (lse != nullptr && quarter == 0 && tid == 0) lse[row] = l > 0.f ? (m + log2f(l)) / kLog2e : -INFINITY;
 }
 
 // The same merge for many splits (batch-1 decode): workgroup (b*H + h, q)
@@ -586,7 +628,7 @@ constexpr int kWideMaxPer = 3;  // splits per thread at most
 template <int kWidePer>
 __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_ml, int splits,
-                                                          float *__restrict__ out, float *__restrict__ lse) {
+                                                          CombineOut co) {
   constexpr int kGroups = kWideThreads / kWideCols;  // 16
   static_assert(kMaxSplits + kWinSplits <= kWideMaxPer * kGroups, "splits per thread");
   __shared__ float4 so[kGroups][kWideCols];
@@ -646,9 +688,11 @@ __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const f
       r.w += w * x.w;
     }
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    reinterpret_cast<float4 *>(out + (size_t)bh * kLatent)[kWideCols * q + tid] =
+    const int jn = bh / co.rows_per_job, row = bh - jn * co.rows_per_job;
+    reinterpret_cast<float4 *>(co.out[jn] + (size_t)row * kLatent)[kWideCols * q + tid] =
         make_float4(r.x * inv, r.y * inv, r.z * inv, r.w * inv);
-    if (lse != nullptr && q == 0 && tid == 0) lse[bh] = lt > 0.f ? (mx + log2f(lt)) / kLog2e : -INFINITY;
+    float *lse = co.lse[jn];
+    if (lse != nullptr && q == 0 && tid == 0) lse[row] = lt > 0.f ? (mx + log2f(lt)) / kLog2e : -INFINITY;
   }
 }
 
@@ -656,13 +700,14 @@ __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const f
 // when that leaves the chip short of workgroups (small batches) 16 heads per
 // workgroup give 4x the workgroups, each with a quarter of the MFMA work per
 // tile (the tile is then dequantized once per head group, from L2).
-int heads_per_group(int batch, int heads) {
-  if (heads % 64 == 0 && (int64_t)batch * (heads / 64) >= 32) return 64;
+// `problems` counts (job, sequence) pairs of the launch.
+int heads_per_group(int problems, int heads) {
+  if (heads % 64 == 0 && (int64_t)problems * (heads / 64) >= 32) return 64;
   return 16;
 }
 
-int choose_splits(int batch, int heads, int top_k) {
-  const int groups = batch * (heads / heads_per_group(batch, heads));
+int choose_splits(int problems, int heads, int top_k) {
+  const int groups = problems * (heads / heads_per_group(problems, heads));
   const int tiles = (top_k + kT - 1) / kT;
   int splits = (256 + groups - 1) / groups;  // about one workgroup per CU
   if (splits > tiles) splits = tiles;
@@ -675,46 +720,44 @@ int choose_splits(int batch, int heads, int top_k) {
 
 }  // namespace
 
-size_t attn_workspace_bytes(int batch, int heads, int top_k, bool window) {
-  const int parts = choose_splits(batch, heads, top_k) + (window ? kWinSplits : 0);
+size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window) {
+  const int parts = choose_splits(jobs * batch, heads, top_k) + (window ? kWinSplits : 0);
   if (parts == 1) return 256;
-  const size_t o = (size_t)batch * heads * parts * kLatent * sizeof(float);
-  const size_t ml = (size_t)batch * heads * parts * 2 * sizeof(float);
+  const size_t rows = (size_t)jobs * batch * heads * parts;
+  const size_t o = rows * kLatent * sizeof(float);
+  const size_t ml = rows * 2 * sizeof(float);
   return ((o + 255) & ~(size_t)255) + ((ml + 255) & ~(size_t)255);
 }
 
-hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
-                              const int32_t *indices, int top_k, float scale, uint8_t *win_codes,
-                              float *win_scales, const float *win_latent, float *out, float *lse, void *ws,
-                              hipStream_t st) {
-  if (S.batch == 0) return hipSuccess;
-  const bool window = win_codes != nullptr;
-  const int hgsz = heads_per_group(S.batch, heads);
-  const int splits = choose_splits(S.batch, heads, top_k);
+hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsDev &S, int heads, int top_k,
+                              float scale, void *ws, hipStream_t st) {
+  if (S.batch == 0 || n_jobs == 0) return hipSuccess;
+  const bool window = jobs[0].win_codes != nullptr;
+  const int problems = n_jobs * S.batch;
+  const int hgsz = heads_per_group(problems, heads);
+  const int splits = choose_splits(problems, heads, top_k);
   const int parts = splits + (window ? kWinSplits : 0);
   const int tiles = (top_k + kT - 1) / kT;
   AttnArgs a;
-  a.L = L;
+  for (int j = 0; j < n_jobs; ++j) {
+    const AttnLaunchJob &x = jobs[j];
+    a.job[j] = AttnJob{x.L, x.q, x.indices, x.win_codes, x.win_scales, x.win_latent, x.out, x.lse};
+  }
   a.S = S;
-  a.q = q;
-  a.idx = indices;
   a.heads = heads;
   a.top_k = top_k;
   a.splits = splits;
   a.parts = parts;
   a.tiles_per_split = (tiles + splits - 1) / splits;
-  a.win_codes = win_codes;
-  a.win_scales = win_scales;
-  a.win_latent = win_latent;
   a.scale_log2 = scale * kLog2e;
-  a.out = out;
-  a.lse = lse;
-  const size_t o_bytes = (size_t)S.batch * heads * parts * kLatent * sizeof(float);
+  a.dbg = debug_flags();
+  const size_t rows = (size_t)problems * heads * parts;
+  const size_t o_bytes = rows * kLatent * sizeof(float);
   a.part_o = static_cast<float *>(ws);
   a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + ((o_bytes + 255) & ~(size_t)255));
-  const dim3 grid(parts, heads / hgsz, S.batch);
+  const dim3 grid(parts, heads / hgsz, problems);
   timer_before(kKernSparseAttn, st);
-  const bool rope = L.rope_dim != 0;
+  const bool rope = jobs[0].L.rope_dim != 0;
   if (hgsz == 64) {
     if (rope) sparse_attn_kernel<4, true><<<grid, dim3(256), 0, st>>>(a);
     else sparse_attn_kernel<4, false><<<grid, dim3(256), 0, st>>>(a);
@@ -725,17 +768,24 @@ hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint1
   timer_after(kKernSparseAttn, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || parts == 1) return e;
+  CombineOut co;
+  for (int j = 0; j < n_jobs; ++j) {
+    co.out[j] = jobs[j].out;
+    co.lse[j] = jobs[j].lse;
+  }
+  co.rows_per_job = S.batch * heads;
+  const int prow = problems * heads;
   timer_before(kKernAttnCombine, st);
-  const dim3 wide_grid(S.batch * heads, kLatent / 4 / kWideCols);
+  const dim3 wide_grid(prow, kLatent / 4 / kWideCols);
   if (parts > 32)
-    attn_combine_wide_kernel<3><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, out, lse);
+    attn_combine_wide_kernel<3><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, co);
   else if (parts > 16)
-    attn_combine_wide_kernel<2><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, out, lse);
+    attn_combine_wide_kernel<2><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, co);
   else if (parts > 8)
-    attn_combine_wide_kernel<1><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, out, lse);
+    attn_combine_wide_kernel<1><<<wide_grid, dim3(kWideThreads), 0, st>>>(a.part_o, a.part_ml, parts, co);
   else
-    attn_combine_kernel<<<dim3(S.batch * heads, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
-        a.part_o, a.part_ml, parts, out, lse);
+    attn_combine_kernel<<<dim3(prow, kLatent / 4 / kCombineThreads), dim3(kCombineThreads), 0, st>>>(
+        a.part_o, a.part_ml, parts, co);
   timer_after(kKernAttnCombine, st);
   return hipGetLastError();
 }

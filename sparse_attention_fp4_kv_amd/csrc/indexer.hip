@@ -40,6 +40,7 @@
 //   layer's own top-K over all positions) run as two workgroups side by side.
 //   Reindex: 16-block producer workgroups score the pool with the layer's own
 //   query; the select runs as above.
+#include "append.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -60,6 +61,7 @@ constexpr int kPoolItemsPerWg = kPoolBlocksPerWg * kBlk;
 constexpr int kMaxPoolItems = 2048 * kBlk;     // 16,384
 constexpr int kMaxSeg = 4096;                  // segments per row (8M positions, host-validated)
 constexpr int kSegPerThread = kMaxSeg / kSelThreads;  // 8
+constexpr int kMaxIdxJobs = kMaxIdxLayers;     // Reindex layers scored by one launch
 
 enum SelMode { kFullPos = 0, kFullHier = 1, kReindex = 2, kGiven = 3 };
 
@@ -131,6 +133,27 @@ SelWs carve(void *ws, int batch, const WsShape &s) {
   w.cap_keys = s.cap_keys;
   w.cap_blocks = s.cap_blocks;
   w.max_seg = s.max_seg;
+  return w;
+}
+
+// Workspace of one Reindex layer of a multi-layer call: only the pool items,
+// candidates and segment infos (no per-position keys).
+constexpr int kPoolSegs = kMaxPoolItems / kPoolItemsPerWg;  // 128
+size_t reindex_job_bytes(int batch) {
+  const size_t B = (size_t)batch;
+  return align256(8 * B * kMaxPoolItems) + align256(8 * B * kCandCap) + align256(sizeof(SegInfo) * B * kPoolSegs);
+}
+
+SelWs carve_reindex(void *ws, int batch) {
+  const size_t B = (size_t)batch;
+  char *p = static_cast<char *>(ws);
+  SelWs w{};
+  w.pool_full = reinterpret_cast<uint2 *>(p);
+  p += align256(8 * B * kMaxPoolItems);
+  w.cand_pos = reinterpret_cast<uint2 *>(p);
+  p += align256(8 * B * kCandCap);
+  w.seg_pos = reinterpret_cast<SegInfo *>(p);
+  w.max_seg = kPoolSegs;
   return w;
 }
 
@@ -545,6 +568,15 @@ struct ScanArgs {
   IdxQuery q;
   int K, P;  // top-K, pool blocks (hierarchical)
   SelWs w;
+  // Rows appended in the same launch (workgroups x >= scan_wgs, one per
+  // append and sequence) at position seq_lens[b] - 1.  When one of them
+  // writes the scanned keys, new_key is its key input: the scan workgroup
+  // covering that position scores it from there (the cache row may not be
+  // written yet).
+  int scan_wgs, n_app;
+  AppendRow app[kMaxAppendRows];
+  const void *new_key;
+  uint32_t *dbg;  // debug flag word, or null
 };
 
 template <int KF, bool HIER>
@@ -559,12 +591,22 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (wg >= a.scan_wgs) {  // an append workgroup (uniform)
+    const AppendRow &r = a.app[wg - a.scan_wgs];
+    if (tid < 64) append_row(r.L, a.S, b, -1, r.latent, r.rope, r.idx_key, tid, a.dbg);
+    return;
+  }
   const int n = row_len(a.S, b);
   const int64_t base = (int64_t)wg * kScanPos;
+  if (a.dbg != nullptr && wg == 0 && tid == 0 && (a.S.seq_lens[b] < 0 || a.S.seq_lens[b] > a.S.max_len))
+    dbg_raise(a.dbg, kDbgSeqLen);
   if (base >= n) return;  // segments past the row are never read
   zero_hists<HIER ? 4 : 2>(hist);
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
-  if (tid < kScanPages) pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
+  if (tid < kScanPages) {
+    pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
+    if (a.dbg != nullptr && base + 64 * tid < n && pg[tid] < 0) dbg_raise(a.dbg, kDbgPage);
+  }
   float q[8];
   Fp4Query Q;
   if constexpr (KF == kKeyFp4) {
@@ -633,6 +675,44 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   }
   }
   __syncthreads();
+  if (a.new_key != nullptr && a.S.seq_lens[b] - 1 >= base && a.S.seq_lens[b] - 1 < base + kScanPos &&
+      a.S.seq_lens[b] <= n) {  // uniform: this workgroup holds the appended position
+    const int lp = a.S.seq_lens[b] - 1 - (int)base;
+    if (wave == 0 && pg[lp / kPage] >= 0) {
+      // the same lane layout and arithmetic as the streaming loop, on the input key
+      if constexpr (KF == kKeyFp4) {
+        Fp4Half kh = Fp4Half{u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, 0u};
+        if ((lane & 31) == (lp & 31)) {
+          const float *src = static_cast<const float *>(a.new_key) + (size_t)b * kFp4IdxDim + 64 * (lane >> 5);
+          uint32_t wd[8], sc = 0;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = src[16 * g + i];
+            sc |= pack_group16(v, &wd[2 * g], &wd[2 * g + 1]) << (8 * g);
+          }
+          kh = Fp4Half{u32x4{wd[0], wd[1], wd[2], wd[3]}, u32x4{wd[4], wd[5], wd[6], wd[7]}, sc};
+        }
+        const float sc = fp4_tile_score(kh, Q);
+        if (lane == (lp & 31)) pkey[lp] = score_key(sc);
+      } else {
+        KeyLoad kl;
+        if constexpr (F32) {
+          const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const float *>(a.new_key) +
+                                                           (size_t)b * kIdxDim + 8 * (lane & 7));
+          kl = KeyLoad{p[0], p[1]};
+        } else {
+          const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.new_key) +
+                                                           (size_t)b * kIdxDim + 8 * (lane & 7));
+          kl = KeyLoad{p[0], u32x4{0, 0, 0, 0}};
+        }
+        const float sc = unit_score<F32>(kl, q);
+        if (lane == 0) pkey[lp] = score_key(sc);
+      }
+    }
+    __syncthreads();
+  }
   if constexpr (HIER) {
     // block key = largest key of its 8 positions (unmapped or past-the-end positions hold key 0)
     const u32x4 *p4 = reinterpret_cast<const u32x4 *>(pkey + kBlk * tid);
@@ -673,6 +753,7 @@ struct GivenArgs {
   int max_len;
   int K;
   SelWs w;
+  uint32_t *dbg;  // debug flag word, or null
 };
 
 __global__ void __launch_bounds__(256) given_kernel(GivenArgs a) {
@@ -692,6 +773,12 @@ __global__ void __launch_bounds__(256) given_kernel(GivenArgs a) {
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) pkey[8 * tid + j] = (base + 8 * tid + j < n) ? score_key(v[j]) : 0u;
+  if (a.dbg != nullptr) {
+    bool fin = true;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fin &= (base + 8 * tid + j >= n) || isfinite(v[j]);
+    if (!fin) dbg_raise(a.dbg, kDbgScore);
+  }
   __syncthreads();
   uint32_t *kout = a.w.keys + (size_t)b * a.w.cap_keys + base;
 #pragma unroll
@@ -707,11 +794,11 @@ __global__ void __launch_bounds__(256) given_kernel(GivenArgs a) {
 struct PoolArgs {
   KvLayerDev L;
   SeqsDev S;
-  IdxQuery q;
   const int32_t *pool;  // [B][pool_blocks]
   int pool_blocks;
   int K;
-  SelWs w;
+  IdxQuery q[kMaxIdxJobs];  // one query and one workspace per layer (blockIdx.z)
+  SelWs w[kMaxIdxJobs];
 };
 
 // Workgroup w scores pool blocks [16w, 16w+16) of its row (wave v: blocks
@@ -726,6 +813,8 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   __shared__ uint32_t red[256 / 64 + 24];
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const IdxQuery qj = a.q[blockIdx.z];
+  const SelWs &w = a.w[blockIdx.z];
   const int n = row_len(a.S, b);
   if (tid < kPoolBlocksPerWg) {
     const int j = wg * kPoolBlocksPerWg + tid;
@@ -749,7 +838,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   if constexpr (KF == kKeyFp4) {
     // wave v: its 4 blocks are one tile of 32 positions (lane % 32 -> block 4 v + p / 8, position p % 8)
     Fp4Query Q;
-    load_fp4_query(a.q, b, a.L.idx_heads, lane, Q);
+    load_fp4_query(qj, b, a.L.idx_heads, lane, Q);
     __syncthreads();
     const int p = lane & 31, blk = 4 * wave + (p >> 3);
     const int64_t s0 = slot0[blk];
@@ -762,7 +851,7 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   } else {
   float q[8];
   {
-    const float *qp = static_cast<const float *>(a.q.q) + (size_t)b * kIdxDim + 8 * (lane & 7);
+    const float *qp = static_cast<const float *>(qj.q) + (size_t)b * kIdxDim + 8 * (lane & 7);
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = qp[e];
   }
@@ -791,18 +880,17 @@ __global__ void __launch_bounds__(256) pool_kernel(PoolArgs a) {
   auto pos_of = [&](int i) { return (uint32_t)(tok0[i >> 3] + (i & 7)); };
   if (tid < kPoolItemsPerWg) {
     const uint32_t k = key_l[tid];
-    a.w.pool_full[(size_t)b * kMaxPoolItems + (size_t)wg * kPoolItemsPerWg + tid] =
+    w.pool_full[(size_t)b * kMaxPoolItems + (size_t)wg * kPoolItemsPerWg + tid] =
         make_uint2(k, k ? pos_of(tid) : 0u);
   }
   const int nseg = (a.pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
   const int cap = seg_budget(a.K, nseg, kPoolItemsPerWg);
-  emit_segment<256, 1>(key_l, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
-                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red, pos_of);
+  emit_segment<256, 1>(key_l, cap, w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                       w.seg_pos + (size_t)b * w.max_seg + wg, hist, red, pos_of);
 }
 
 // ------------------------------------------------------------------ select
 struct SelArgs {
-  SelWs w;
   SeqsDev S;
   const int32_t *lens;   // kGiven
   int max_len;           // kGiven
@@ -810,7 +898,8 @@ struct SelArgs {
   int K;                 // indices per row
   int P;                 // pool blocks per row (kFullHier: output size; kReindex: input size)
   int32_t *pool_out;     // kFullHier
-  int32_t *out;          // [B][K]
+  int32_t *out[kMaxIdxJobs];  // [B][K] per job (blockIdx.z; one job except Reindex layers)
+  SelWs w[kMaxIdxJobs];
 };
 
 struct SelSmem {
@@ -1519,17 +1608,18 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelArgs a) {
   __shared__ SelSmem sm;
   const int b = blockIdx.y;
   const bool re = a.mode == kReindex, blk = blockIdx.x != 0;
+  const SelWs &w = a.w[blockIdx.z];
   const int n = re ? 0 : (a.mode == kGiven ? min(max(a.lens[b], 0), a.max_len) : row_len(a.S, b));
   Stream st;
-  st.cand = (blk ? a.w.cand_blk : a.w.cand_pos) + (size_t)b * kCandCap;
-  st.info = (blk ? a.w.seg_blk : a.w.seg_pos) + (size_t)b * a.w.max_seg;
-  st.full_keys = re ? nullptr : (blk ? a.w.bkeys + (size_t)b * a.w.cap_blocks : a.w.keys + (size_t)b * a.w.cap_keys);
-  st.full_pairs = re ? a.w.pool_full + (size_t)b * kMaxPoolItems : nullptr;
+  st.cand = (blk ? w.cand_blk : w.cand_pos) + (size_t)b * kCandCap;
+  st.info = (blk ? w.seg_blk : w.seg_pos) + (size_t)b * w.max_seg;
+  st.full_keys = re ? nullptr : (blk ? w.bkeys + (size_t)b * w.cap_blocks : w.keys + (size_t)b * w.cap_keys);
+  st.full_pairs = re ? w.pool_full + (size_t)b * kMaxPoolItems : nullptr;
   st.nseg = re ? (a.P + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg : (n + kScanPos - 1) / kScanPos;
   st.ips = re ? kPoolItemsPerWg : (blk ? kScanBlocks : kScanPos);
   st.items = re ? (int64_t)a.P * kBlk : (blk ? (n + kBlk - 1) / kBlk : n);
   const int need = blk ? a.P : a.K;
-  int32_t *out = blk ? a.pool_out + (size_t)b * a.P : a.out + (size_t)b * a.K;
+  int32_t *out = blk ? a.pool_out + (size_t)b * a.P : a.out[blockIdx.z] + (size_t)b * a.K;
   st.cap = seg_budget(need, st.nseg, st.ips);
   select_stream(sm, st, need, out);
 }
@@ -1582,11 +1672,47 @@ __global__ void __launch_bounds__(256) scores_fp4_kernel(KvLayerDev L, SeqsDev S
   }
 }
 
-hipError_t run_select(const SelArgs &a, int outputs, int batch, hipStream_t st) {
+hipError_t run_select(const SelArgs &a, int outputs, int batch, int jobs, hipStream_t st) {
   timer_before(kKernTopkCompact, st);
-  select_kernel<<<dim3(outputs, batch), dim3(kSelThreads), 0, st>>>(a);
+  select_kernel<<<dim3(outputs, batch, jobs), dim3(kSelThreads), 0, st>>>(a);
   timer_after(kKernTopkCompact, st);
   return hipGetLastError();
+}
+
+// Reindex of `jobs` layers over one pool: pool scoring and the select, each
+// one launch with a grid dimension over the layers.
+hipError_t run_reindex(const KvLayerDev &L, const SeqsDev &S, const IdxQuery *q, const SelWs *w,
+                       int32_t *const *indices, int jobs, int top_k, const int32_t *pool_in, int pool_blocks,
+                       hipStream_t st) {
+  PoolArgs p{};
+  p.L = L;
+  p.S = S;
+  p.pool = pool_in;
+  p.pool_blocks = pool_blocks;
+  p.K = top_k;
+  for (int j = 0; j < jobs; ++j) {
+    p.q[j] = q[j];
+    p.w[j] = w[j];
+  }
+  const int gx = (pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
+  const dim3 grid(gx, S.batch, jobs);
+  timer_before(kKernPoolScore, st);
+  if (L.idx_fp4) pool_kernel<kKeyFp4><<<grid, dim3(256), 0, st>>>(p);
+  else if (L.idx_f32) pool_kernel<kKeyF32><<<grid, dim3(256), 0, st>>>(p);
+  else pool_kernel<kKeyBf16><<<grid, dim3(256), 0, st>>>(p);
+  timer_after(kKernPoolScore, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SelArgs s{};
+  for (int j = 0; j < jobs; ++j) {
+    s.w[j] = w[j];
+    s.out[j] = indices[j];
+  }
+  s.S = S;
+  s.mode = kReindex;
+  s.K = top_k;
+  s.P = pool_blocks;
+  return run_select(s, 1, S.batch, jobs, st);
 }
 
 }  // namespace
@@ -1629,7 +1755,7 @@ hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t
   if (batch <= 0) return hipSuccess;
   const WsShape sh = ws_shape(max_len, 0);
   SelWs w = carve(ws, batch, sh);
-  GivenArgs g{scores, stride, lens, max_len, top_k, w};
+  GivenArgs g{scores, stride, lens, max_len, top_k, w, debug_flags()};
   const int gx = (int)(sh.cap_keys / kScanPos);
   timer_before(kKernTopkGiven, st);
   given_kernel<<<dim3(gx, batch), dim3(256), 0, st>>>(g);
@@ -1637,26 +1763,37 @@ hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelArgs s{};
-  s.w = w;
+  s.w[0] = w;
   s.lens = lens;
   s.max_len = max_len;
   s.mode = kGiven;
   s.K = top_k;
-  s.out = indices;
-  return run_select(s, 1, batch, st);
+  s.out[0] = indices;
+  return run_select(s, 1, batch, 1, st);
 }
 
 hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                     int32_t *pool_out, int pool_blocks, int32_t *indices, void *ws,
-                                    hipStream_t st) {
+                                    hipStream_t st, const AppendRow *app, int n_app, const void *new_key) {
   if (S.batch <= 0) return hipSuccess;
   const bool hier = pool_out != nullptr;
   const WsShape sh = ws_shape(S.max_len, hier ? pool_blocks : 0);
   SelWs w = carve(ws, S.batch, sh);
-  ScanArgs a{L, S, q_idx, top_k, pool_blocks, w};
+  ScanArgs a{};
+  a.L = L;
+  a.S = S;
+  a.q = q_idx;
+  a.K = top_k;
+  a.P = pool_blocks;
+  a.w = w;
   const int gx = (int)(sh.cap_keys / kScanPos);
+  a.scan_wgs = gx;
+  a.n_app = n_app;
+  for (int i = 0; i < n_app; ++i) a.app[i] = app[i];
+  a.new_key = new_key;
+  a.dbg = debug_flags();
   timer_before(kKernIndexScan, st);
-  const dim3 grid(gx, S.batch);
+  const dim3 grid(gx + n_app, S.batch);
   if (L.idx_fp4) {
     if (hier) scan_kernel<kKeyFp4, true><<<grid, dim3(256), 0, st>>>(a);
     else scan_kernel<kKeyFp4, false><<<grid, dim3(256), 0, st>>>(a);
@@ -1671,14 +1808,14 @@ hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQu
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   SelArgs s{};
-  s.w = w;
+  s.w[0] = w;
   s.S = S;
   s.mode = hier ? kFullHier : kFullPos;
   s.K = top_k;
   s.P = pool_blocks;
   s.pool_out = pool_out;
-  s.out = indices;
-  return run_select(s, hier ? 2 : 1, S.batch, st);
+  s.out[0] = indices;
+  return run_select(s, hier ? 2 : 1, S.batch, 1, st);
 }
 
 hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
@@ -1687,23 +1824,20 @@ hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, Id
   if (S.batch <= 0) return hipSuccess;
   const WsShape sh = ws_shape(S.max_len, pool_blocks);
   SelWs w = carve(ws, S.batch, sh);
-  PoolArgs p{L, S, q_idx, pool_in, pool_blocks, top_k, w};
-  const int gx = (pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
-  timer_before(kKernPoolScore, st);
-  if (L.idx_fp4) pool_kernel<kKeyFp4><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
-  else if (L.idx_f32) pool_kernel<kKeyF32><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
-  else pool_kernel<kKeyBf16><<<dim3(gx, S.batch), dim3(256), 0, st>>>(p);
-  timer_after(kKernPoolScore, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  SelArgs s{};
-  s.w = w;
-  s.S = S;
-  s.mode = kReindex;
-  s.K = top_k;
-  s.P = pool_blocks;
-  s.out = indices;
-  return run_select(s, 1, S.batch, st);
+  return run_reindex(L, S, &q_idx, &w, &indices, 1, top_k, pool_in, pool_blocks, st);
+}
+
+size_t reindex_layers_workspace_bytes(int jobs, int batch) {
+  return (size_t)jobs * reindex_job_bytes(batch);
+}
+
+hipError_t launch_reindex_layers(const KvLayerDev &L, const SeqsDev &S, const IdxQuery *q_idx, int32_t *const *indices,
+                                 int jobs, int top_k, const int32_t *pool_in, int pool_blocks, void *ws,
+                                 hipStream_t st) {
+  if (S.batch <= 0 || jobs <= 0) return hipSuccess;
+  SelWs w[kMaxIdxJobs];
+  for (int j = 0; j < jobs; ++j) w[j] = carve_reindex(static_cast<char *>(ws) + (size_t)j * reindex_job_bytes(S.batch), S.batch);
+  return run_reindex(L, S, q_idx, w, indices, jobs, top_k, pool_in, pool_blocks, st);
 }
 
 }  // namespace csa2

@@ -28,6 +28,18 @@ enum KernelId {
 void timer_before(KernelId id, hipStream_t st);
 void timer_after(KernelId id, hipStream_t st);
 
+// Debug checks: while they are on, kernels OR these bits (the public
+// CSA2_DBG_* values) into a per-device flag word; debug_flags() is that
+// word's device address on the current device, or null when the checks are
+// off (then every check is skipped).
+constexpr uint32_t kDbgQRange = 1u, kDbgIndex = 2u, kDbgPage = 4u, kDbgNonFinite = 8u, kDbgScore = 16u,
+                   kDbgSeqLen = 32u;
+constexpr int kMaxDevices = 64;  // devices whose per-device library state is kept
+uint32_t *debug_flags();
+__device__ __forceinline__ void dbg_raise(uint32_t *dbg, uint32_t bit) {
+  if (dbg != nullptr) atomicOr(dbg, bit);
+}
+
 // Device view of one KV layer's paged pool (validated copy of csa2_kv_layer).
 struct KvLayerDev {
   uint8_t *codes;
@@ -72,21 +84,54 @@ hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, IdxQuery q
 hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t *lens, int batch, int max_len,
                               int top_k, int32_t *indices, void *ws, hipStream_t st);
 size_t index_select_workspace_bytes(int batch, int max_len, int top_k, int pool_blocks);
+// A row appended at position seq_lens[b] - 1 of every sequence in the same
+// launch as a Full-mode scan (the append workgroups ride along).
+constexpr int kMaxAppendRows = 8;
+struct AppendRow {
+  KvLayerDev L;
+  const float *latent;
+  const uint16_t *rope;
+  const void *idx_key;
+};
+// new_key: the key input of the append that writes the scanned keys (scored
+// from there), or null.
 hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                     int32_t *pool_out, int pool_blocks, int32_t *indices, void *ws,
-                                    hipStream_t st);
+                                    hipStream_t st, const AppendRow *app = nullptr, int n_app = 0,
+                                    const void *new_key = nullptr);
 hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, IdxQuery q_idx, int top_k,
                                        const int32_t *pool_in, int pool_blocks, int32_t *indices, void *ws,
                                        hipStream_t st);
+// Reindex of several layers (own query and output each) over one key pool and
+// one candidate pool: two launches in all.  At most kMaxIdxLayers layers.
+constexpr int kMaxIdxLayers = 8;
+size_t reindex_layers_workspace_bytes(int jobs, int batch);
+hipError_t launch_reindex_layers(const KvLayerDev &L, const SeqsDev &S, const IdxQuery *q_idx, int32_t *const *indices,
+                                 int jobs, int top_k, const int32_t *pool_in, int pool_blocks, void *ws,
+                                 hipStream_t st);
 
 // ---- attention (attention.hip)
-// window: the sliding-window ring's codes / scales join the softmax as four more splits; win_latent, if
-// given, is the current token's window entry, appended to the ring in the same launch
-size_t attn_workspace_bytes(int batch, int heads, int top_k, bool window);
-hipError_t launch_sparse_attn(const KvLayerDev &L, const SeqsDev &S, const uint16_t *q, int heads,
-                              const int32_t *indices, int top_k, float scale, uint8_t *win_codes,
-                              float *win_scales, const float *win_latent, float *out, float *lse, void *ws,
-                              hipStream_t st);
+// One launch serves up to kMaxAttnJobs attention problems over one batch view
+// (e.g. the layers of a step, each with its own KV pool, query, indices and
+// output).  window: the sliding-window ring's codes / scales join the softmax
+// as four more splits (all jobs of a launch have a window, or none);
+// win_latent, if given, is the current token's window entry, appended to the
+// ring in the same launch.
+constexpr int kMaxAttnJobs = 20;
+struct AttnLaunchJob {
+  KvLayerDev L;
+  const uint16_t *q;
+  const int32_t *indices;
+  uint8_t *win_codes;
+  float *win_scales;
+  const float *win_latent;
+  float *out;
+  float *lse;
+};
+size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window);
+
+hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsDev &S, int heads, int top_k,
+                              float scale, void *ws, hipStream_t st);
 
 // ---- CED projection (ced.hip)
 // Latent finish (RMSNorm, RoPE, FP4 pack) and the FP4 indexer key projected

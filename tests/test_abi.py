@@ -11,8 +11,21 @@ import pytest
 from sparse_attention_fp4_kv_amd import csa2
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HAVE_LIB = os.path.exists(csa2.LIB_PATH)
-needs_lib = pytest.mark.skipif(not HAVE_LIB, reason="libcsa2.so not built")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    """These checks need the built library: build it when it is missing (hipcc cross-compiles without a GPU),
+    and fail, not skip, when that is impossible."""
+    if not os.path.exists(csa2.LIB_PATH):
+        from sparse_attention_fp4_kv_amd import build_lib
+
+        build_lib.build()
+    assert os.path.exists(csa2.LIB_PATH), "libcsa2.so could not be built"
+
+
+def needs_lib(f):
+    return f
 
 
 def header_functions():
@@ -34,7 +47,7 @@ def test_library_exports_every_declared_symbol():
     raw = ctypes.CDLL(csa2.LIB_PATH)
     for name in header_functions():
         assert hasattr(raw, name), name
-    assert csa2.lib().csa2_abi_version() == 5
+    assert csa2.lib().csa2_abi_version() == 6
     assert csa2.lib().csa2_status_string(3) == b"workspace missing or too small"
 
 
@@ -171,3 +184,59 @@ def test_block_pool():
     p.free([1])
     assert p.num_free == 3 and p.alloc(1) == [1]
     p.close()
+
+
+@needs_lib
+def test_multi_layer_validation_rejects_before_launch():
+    L = csa2.lib()
+    P = ctypes.byref
+    n = ctypes.c_size_t()
+    kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=16, num_blocks=1, block_tokens=64, latent_dim=512,
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
+    sq = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=1, max_seq_len=64)
+    # attention over layers: 1..20 layers, one rope width, windows on all layers or none
+    assert L.csa2_attn_layers_workspace_size(0, 1, 64, 2048, 512, 0, P(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_attn_layers_workspace_size(21, 1, 64, 2048, 512, 0, P(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_attn_layers_workspace_size(4, 1, 64, 2048, 512, 0, P(n)) == csa2.OK
+    four = n.value
+    assert L.csa2_attn_layers_workspace_size(1, 1, 64, 2048, 512, 0, P(n)) == csa2.OK and n.value <= four
+    rope = csa2.KvLayer(codes=16, scales=16, rope=16, idx_keys=None, num_blocks=1, block_tokens=64, latent_dim=512,
+                        rope_dim=64, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
+    w = csa2.SwaWindow(codes=16, scales=16, batch=1)
+    mk = lambda layer, win=None, nl=None: csa2.AttnLayerC(ctypes.pointer(layer), 16, 16, 16, None,
+                                                           ctypes.pointer(win) if win else None, nl)
+    f = L.csa2_sparse_fp4_decode_attn_layers
+    arr = (csa2.AttnLayerC * 2)(mk(kv), mk(rope))
+    assert f(arr, 2, P(sq), 64, 64, 0.1, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG  # mixed rope widths
+    arr = (csa2.AttnLayerC * 2)(mk(kv), mk(kv, w))
+    assert f(arr, 2, P(sq), 64, 64, 0.1, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG  # window on one layer only
+    arr = (csa2.AttnLayerC * 1)(mk(kv, None, 16))
+    assert f(arr, 1, P(sq), 64, 64, 0.1, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG  # new entry without a window
+    arr = (csa2.AttnLayerC * 2)(mk(kv), mk(kv))
+    assert f(arr, 0, P(sq), 64, 64, 0.1, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    assert f(arr, 2, P(sq), 24, 64, 0.1, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    assert f(arr, 2, P(sq), 64, 64, 0.1, 256, 1, None) == csa2.ERR_WORKSPACE
+    # Reindex over layers: 1..8 layers, a pool, the keys' query kind
+    assert L.csa2_index_reindex_layers_workspace_size(9, 1, 64, 2048, 8, P(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_reindex_layers_workspace_size(3, 1, 64, 2048, 4, P(n)) == csa2.ERR_INVALID_ARG
+    assert L.csa2_index_reindex_layers_workspace_size(3, 1, 64, 2048, 8, P(n)) == csa2.OK
+    three = n.value
+    assert L.csa2_index_reindex_layers_workspace_size(1, 1, 64, 2048, 8, P(n)) == csa2.OK and 3 * n.value == three
+    g = L.csa2_index_reindex_layers
+    qs = (csa2.ReindexQueryC * 2)(csa2.ReindexQueryC(16, None, 16), csa2.ReindexQueryC(16, None, 16))
+    assert g(P(kv), P(sq), qs, 2, 64, None, 2048, 8, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG  # no pool
+    assert g(P(kv), P(sq), qs, 2, 64, 16, 2048, 8, 256, 1, None) == csa2.ERR_WORKSPACE
+    qs[1].w_idx = 16  # weights belong to FP4 keys
+    assert g(P(kv), P(sq), qs, 2, 64, 16, 2048, 8, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    # select with appends: at most 8 rows, disjoint storage, rows valid as for csa2_kv_append
+    h = L.csa2_index_select_append
+    row = lambda layer, lat=None, rp=None, key=None: csa2.AppendRowC(ctypes.pointer(layer), lat, rp, key)
+    rows = (csa2.AppendRowC * 2)(row(kv, 16, None, 16), row(kv, 16, None, None))
+    assert h(P(kv), P(sq), rows, 2, 16, None, 8, None, 0, 0, 16, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    rows = (csa2.AppendRowC * 1)(row(kv))
+    assert h(P(kv), P(sq), rows, 1, 16, None, 8, None, 0, 0, 16, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    rows = (csa2.AppendRowC * 1)(row(rope, 16))  # a rope layer's latent needs its rope row
+    assert h(P(kv), P(sq), rows, 1, 16, None, 8, None, 0, 0, 16, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    rows = (csa2.AppendRowC * 1)(row(kv, 16, None, 16))
+    assert h(P(kv), P(sq), rows, 9, 16, None, 8, None, 0, 0, 16, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
+    assert h(P(kv), P(sq), rows, 1, 16, None, 8, None, 0, 0, 16, 256, 1, None) == csa2.ERR_WORKSPACE

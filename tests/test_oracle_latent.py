@@ -109,3 +109,31 @@ def test_finished_entry_range_bound():
     x = lt.finish_latent(c, np.arange(64) * 977, g, 1e-6, 10000.0)
     assert np.all(np.linalg.norm(x, axis=1) <= math.sqrt(512) * (1 + 1e-12))
     assert np.max(np.abs(x)) <= 22.63
+
+
+def test_rope_angle_rounded_to_fp32():
+    """The angle is the fp32 product fl32(p * fl32(f)), not the exact product.  Worked by hand for pair
+    16 (f = 10000^(-1/2) = 0.01) at p = 7: fl32(0.01) = 5368709 * 2^-29 (an odd 23-bit integer); 7 times
+    that is 37580963 * 2^-29, a 26-bit integer that fp32 cannot hold; its 24-bit rounding is
+    37580963 / 4 = 9395240.75 -> 9395241 (nearest), so the angle is 9395241 * 2^-27 =
+    0.070000000298023223876953125, while the exact product is 0.06999999843537807..."""
+    f = lt.rope_frequencies(10000.0)
+    assert int(f[16].view(np.uint32)) == 0x3C23D70A  # 5368709 * 2^-29
+    t = lt.rope_angles([7], 10000.0)[0, 16]
+    assert float(t) == 9395241 * 2.0 ** -27 == 0.070000000298023223876953125
+    exact = 37580963 * 2.0 ** -29
+    assert float(t) != exact  # a float64 product would fail this
+    x = np.zeros((1, 512))
+    x[0, 480], x[0, 481] = 1.0, 0.0
+    y = lt.rope(x, [7], 10000.0)
+    assert abs(y[0, 480] - math.cos(9395241 * 2.0 ** -27)) < 1e-16
+    assert abs(y[0, 481] - math.sin(9395241 * 2.0 ** -27)) < 1e-16
+    assert abs(y[0, 481] - math.sin(exact)) > 1e-10  # the two readings are told apart
+    # a large position: p = 2^20 + 3 on pair 1 (f = fl32(10000^(-1/32)))
+    f1 = int(f[1].view(np.uint32))
+    mant, ex = (f1 & 0x7FFFFF) | 0x800000, ((f1 >> 23) & 0xFF) - 150  # f = mant * 2^ex
+    prod = ((1 << 20) + 3) * mant  # exact integer product, 44 bits
+    sh = prod.bit_length() - 24
+    q, r = divmod(prod, 1 << sh)
+    q += 1 if (2 * r > (1 << sh) or (2 * r == (1 << sh) and q & 1)) else 0  # round to nearest even
+    assert float(lt.rope_angles([(1 << 20) + 3], 10000.0)[0, 1]) == q * 2.0 ** (ex + sh)
