@@ -445,6 +445,24 @@ csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, in
                                                const csa2_seqs *seqs, int32_t heads, int32_t top_k,
                                                float softmax_scale, void *ws, size_t ws_bytes, csa2_stream stream);
 
+/* ---- For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * csa2_sparse_fp4_decode_attn_layers without a workspace argument.  The split
+ * partials go to a scratch array the library holds on every device it runs on
+ * (32 MiB each, held until the process ends); a problem whose partials need
+ * more (the size csa2_attn_layers_workspace_size reports) returns
+ * CSA2_ERR_WORKSPACE and launches nothing.  Every call on one device shares
+ * that device's scratch: calls that overlap in time on one device (on
+ * different streams) race, so serialize them.  The scratch needs no clearing
+ * (every partial is written before it is read).  The first call on a device
+ * resolves the scratch's address there (not a stream operation; make that
+ * first call outside graph capture).  Results equal those of
+ * csa2_sparse_fp4_decode_attn_layers on the same arguments.  Nothing is
+ * allocated by this call. */
+csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *layers, int32_t n_layers,
+                                                       const csa2_seqs *seqs, int32_t heads, int32_t top_k,
+                                                       float softmax_scale, csa2_stream stream);
+
 /* ---- Host-side page allocator (no device memory): a free list of block ids
  * [0, num_blocks).  Not thread-safe; one instance per owner. */
 typedef struct csa2_block_pool csa2_block_pool;

@@ -139,6 +139,8 @@ SIGNATURES = {
     "csa2_attn_layers_workspace_size": (ctypes.c_int, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
     "csa2_sparse_fp4_decode_attn_layers": (ctypes.c_int, [ctypes.POINTER(AttnLayerC), _I32, _PSQ, _I32, _I32,
                                                           ctypes.c_float, _P, _SZ, _P]),
+    "csa2_sparse_fp4_decode_attn_layers_noalloc": (ctypes.c_int, [ctypes.POINTER(AttnLayerC), _I32, _PSQ, _I32,
+                                                                  _I32, ctypes.c_float, _P]),
     "csa2_block_pool_create": (_P, [_I32]),
     "csa2_block_alloc": (ctypes.c_int, [_P, _I32, _P]),
     "csa2_block_free": (ctypes.c_int, [_P, _I32, _P]),

@@ -640,6 +640,22 @@ csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, in
   return from_hip(launch_sparse_attn(jobs, n_layers, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
 }
 
+csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *layers, int32_t n_layers,
+                                                       const csa2_seqs *seqs, int32_t heads, int32_t top_k,
+                                                       float softmax_scale, csa2_stream stream) {
+  SeqsDev S;
+  csa2_status st = check_seqs(seqs, &S);
+  if (st != CSA2_OK) return st;
+  if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
+  if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
+  const bool window = layers[0].win != nullptr;
+  if (attn_workspace_bytes(n_layers, S.batch, heads, top_k, window) > kAttnScratchBytes) return CSA2_ERR_WORKSPACE;
+  void *scratch_ptr = nullptr;
+  if (attn_scratch(&scratch_ptr) != hipSuccess) return CSA2_ERR_HIP;
+  return csa2_sparse_fp4_decode_attn_layers(layers, n_layers, seqs, heads, top_k, softmax_scale, scratch_ptr,
+                                            kAttnScratchBytes, stream);
+}
+
 csa2_block_pool *csa2_block_pool_create(int32_t num_blocks) {
   if (num_blocks < 0) return nullptr;
   csa2_block_pool *p = new (std::nothrow) csa2_block_pool;

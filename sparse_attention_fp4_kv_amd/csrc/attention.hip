@@ -43,10 +43,37 @@
 //     launch: the window workgroups of the tile holding its slot pack it to
 //     FP8 (the same rounding as the standalone append) into LDS and use it
 //     from there, and the first head group's one writes it to the ring.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace csa2 {
+
+// Scratch of the allocation-free attention entry point: the split partials of
+// one launch live here instead of in a caller workspace.  Every device the
+// library runs on holds its own copy until the process ends; its address is
+// resolved once per device (hipGetSymbolAddress) and only that address is
+// handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+hipError_t attn_scratch(void **ptr) {
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 
 namespace {

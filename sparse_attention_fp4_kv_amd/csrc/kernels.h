@@ -129,6 +129,11 @@ struct AttnLaunchJob {
   float *lse;
 };
 size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window);
+// The library-held scratch of the allocation-free entry point (device memory
+// of this many bytes on every device it runs on) and its address on the
+// current device.
+constexpr size_t kAttnScratchBytes = (size_t)32 << 20;
+hipError_t attn_scratch(void **ptr);
 
 hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsDev &S, int heads, int top_k,
                               float scale, void *ws, hipStream_t st);
