@@ -10,16 +10,21 @@
 // with c_s the dequantized 512-channel latent (K = V).
 //
 // Design (ours):
-//   * One workgroup (4 waves) serves up to 64 heads of one sequence, so each
-//     dequantized entry feeds every head: QK^T and PV are MFMA contractions
-//     with M = heads (v_mfma_f32_16x16x32_f16, fp32 accumulation).
+//   * One workgroup (8 waves, two per SIMD) serves 16 or 64 heads of one
+//     sequence, so each dequantized entry feeds all of them: QK^T and PV are
+//     MFMA contractions with M = heads (v_mfma_f32_16x16x32_f16, fp32
+//     accumulation).  QK^T splits each 16 x 16 logit tile's 512 (+64)
+//     channels over 2 or 4 waves (partial logits added in the softmax), with
+//     2 or 4 independent accumulator chains per wave; PV gives each wave 64
+//     output channels of every head.
 //   * Entries are processed in tiles of 32.  A tile's FP4 codes are gathered
-//     straight into registers (8 lanes per 256-byte row), dequantized with the
-//     hardware E2M1 -> fp16 convert plus one packed multiply by the E4M3 scale
-//     (exact), and written once to LDS, row-major.  QK^T reads its operand
-//     (channels contiguous) with 16-byte loads; PV reads its operand (entries
-//     contiguous) with gfx950's transposing LDS loads, so no transposed copy
-//     of the tile is made.
+//     straight into registers (16 bytes per lane, 4 lanes per 64 contiguous
+//     bytes of a row), dequantized with the hardware E2M1 -> fp16 convert
+//     times the E4M3 scale (exact), and written once to LDS, row-major, each
+//     16-byte store of a half-wave on 16 different bank groups.  QK^T reads
+//     its operand (channels contiguous) with 16-byte loads; PV reads its
+//     operand (entries contiguous) with gfx950's transposing LDS loads, so no
+//     transposed copy of the tile is made.
 //   * Online softmax in fp32 (exp2 domain) against a reference max that
 //     moves only when a logit exceeds it by more than 8 (so most tiles skip
 //     rescaling the accumulators).  P enters the PV contraction as
@@ -79,8 +84,13 @@ hipError_t attn_scratch(void **ptr) {
 namespace {
 
 constexpr int kT = 32;                 // entries per tile
-constexpr int kQkLd = kLatent + 64 + 8;  // row-major tile row (f16): 512 latent + 64 rope + pad
+constexpr int kThreads = 512;          // 8 waves per workgroup (two per SIMD)
+constexpr int kWaves = kThreads / 64;
 constexpr int kPLd = kT + 8;
+// waves splitting the k-steps (channels) of one 16 x 16 logit tile: with 16
+// heads the 8 waves take 2 N-tiles x 4 k-parts, else M-tiles x N-tiles x 2
+template <int MT>
+constexpr int kKParts = MT == 1 ? 4 : 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 32;         // split-K workgroups per (sequence, head group)
 constexpr int kSlotCap = 2048;         // entries one workgroup resolves up front
@@ -115,17 +125,21 @@ struct AttnArgs {
   uint32_t *dbg;          // debug flag word, or null
 };
 
-template <int MT>
+// LDS of one workgroup.  LD is the tile row (f16): 512 latent channels (+ 64
+// rope) + 8 of padding, so a row is an odd number of 16-byte units (65 or 73)
+// and the 16 lanes of a 16-byte access that differ in their entry fall on 16
+// different bank groups.
+template <int MT, int LD>
 struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile access is a 128-bit LDS op
-  __attribute__((aligned(16))) f16 cq[3][kT][kQkLd];   // row-major dequantized tiles (+ rope), used in turn
-  float s[2][16 * MT][kT + 1];   // logits of the tile (two k-halves when 16 heads; padded rows)
+  __attribute__((aligned(16))) f16 cq[3][kT][LD];   // row-major dequantized tiles (+ rope), used in turn
+  float s[kKParts<MT>][16 * MT][kT + 1];             // partial logits of the k-parts (padded rows)
   __attribute__((aligned(16))) f16 p_hi[16 * MT][kPLd];
   __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
   float m_run[16 * MT], l_run[16 * MT], alpha[16 * MT];
   uint32_t slot[kSlotCap];       // physical rows of this workgroup's entries (kNoSlot: skipped)
   float wts[kT], wp[kT];         // window tile: token scales, and times the P normalization
   float unnorm;                  // window tile: the P normalization, inverted
-  float wamax[4];                // appended window entry: per-wave amax
+  float wamax[kWaves];           // appended window entry: per-wave amax
   __attribute__((aligned(16))) uint8_t newc[kLatent];  // appended window entry: E4M3 codes
 };
 
@@ -142,9 +156,10 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // g = L / 16 therefore points at row 8 g + (L / 4) % 4 (+ 4 for the second
 // load), channels n0 + 4 (L % 4) .. + 3, and receives rows 8 g .. 8 g + 7 of
 // channel n0 + L % 16.  p: that lane's first-load address.
+template <int LD>
 __device__ __forceinline__ f16x8 pv_operand(const f16 *p) {
   const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * kQkLd));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 4 * LD));
   const s16x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(f16x8, ab);
 }
@@ -178,20 +193,26 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Raw FP4 row fragment of one entry: 64 channels of codes, their 4 scales and
-// (with rope) 8 rope values.
+// Raw row fragment of one entry held by one thread: 32 channels of FP4 codes
+// (16 bytes), their 2 E4M3 scales and (with rope) 4 rope values.
 struct Raw {
-  uint4 c0, c1, rp;
-  uint32_t sc4;
+  uint4 c;
+  uint2 rp;
+  uint32_t sc2;
   bool valid;
 };
 
 template <int MT, bool ROPE>
-__global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
   constexpr int HG = 16 * MT;                  // heads in this workgroup
   constexpr int QW = kLatent + (ROPE ? 64 : 0);  // q row width
+  constexpr int LD = ROPE ? kLatent + 64 + 8 : kLatent + 8;  // tile row (f16)
   constexpr int KS = QW / 32;                  // 16 or 18 k-steps of 32 channels
-  __shared__ Smem<MT> sm;
+  constexpr int KP = kKParts<MT>;              // waves splitting the k-steps of one logit tile
+  constexpr int QKS = (KS + KP - 1) / KP;      // k-steps per wave (the last part may be shorter)
+  constexpr int QNT = MT == 4 ? 2 : 1;         // N-tiles of 16 entries per wave
+  constexpr bool kEvenParts = KS % KP == 0;    // every k-part has QKS k-steps
+  __shared__ Smem<MT, LD> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int split = blockIdx.x, hg = blockIdx.y;
   const int jz = blockIdx.z, jn = jz / a.S.batch, b = jz - jn * a.S.batch;  // job, sequence
@@ -215,26 +236,27 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   const int e_count = win ? kT : max(0, min(tile_end * kT, a.top_k) - e_begin);
   const int32_t *idx_row = J.idx + (size_t)b * a.top_k;
 
-  // ---- QK^T work of this wave: one M-tile (16 heads) and 1 or 2 N-tiles of 16 entries
-  // (16 heads: every wave takes one N-tile and half of the k-steps; the two
-  // halves of a logit are added when the softmax reads them)
-  constexpr int QKS = MT == 1 ? KS / 2 : KS;  // k-steps per wave
-  int qk_mt, qk_nt0, qk_ntn, qk_half;
-  if constexpr (MT == 4) { qk_mt = wave; qk_nt0 = 0; qk_ntn = 2; qk_half = 0; }
-  else if constexpr (MT == 2) { qk_mt = wave >> 1; qk_nt0 = wave & 1; qk_ntn = 1; qk_half = 0; }
-  else { qk_mt = 0; qk_nt0 = wave & 1; qk_ntn = 1; qk_half = wave >> 1; }
-  const int qk_k0 = qk_half * QKS;
+  // ---- QK^T work of this wave: M-tile qk_mt (16 heads), N-tiles qk_nt0 ..
+  // qk_nt0 + QNT - 1 (16 entries each), k-part qk_kp (k-steps qk_k0 .. qk_k1 - 1);
+  // the KP partial logits of an entry are added when the softmax reads them
+  int qk_mt, qk_nt0, qk_kp;
+  if constexpr (MT == 4) { qk_mt = wave & 3; qk_nt0 = 0; qk_kp = wave >> 2; }
+  else if constexpr (MT == 2) { qk_mt = wave & 1; qk_nt0 = (wave >> 1) & 1; qk_kp = wave >> 2; }
+  else { qk_mt = 0; qk_nt0 = wave & 1; qk_kp = wave >> 1; }
+  const int qk_k0 = qk_kp * QKS;
+  const int qk_kn = min(QKS, KS - qk_k0);  // k-steps of this part (uniform)
 
   // ---- entry indices of this workgroup, then their physical rows (two dependent
   // reads for all entries at once; the q loads below overlap them)
-  int pos[kSlotCap / 256];
+  constexpr int kRounds = kSlotCap / kThreads;
+  int pos[kRounds];
 #pragma unroll
-  for (int j = 0; j < kSlotCap / 256; ++j) pos[j] = -1;
+  for (int j = 0; j < kRounds; ++j) pos[j] = -1;
   if (!win) {
 #pragma unroll
-    for (int j = 0; j < kSlotCap / 256; ++j) {
-      if (256 * j >= e_count) break;  // uniform: rounds past this workgroup's entries are not read
-      const int i = 256 * j + tid;
+    for (int j = 0; j < kRounds; ++j) {
+      if (kThreads * j >= e_count) break;  // uniform: rounds past this workgroup's entries are not read
+      const int i = kThreads * j + tid;
       const int p = idx_row[min(e_begin + i, a.top_k - 1)];  // clamped read, masked below
       pos[j] = i < e_count ? p : -1;
       if (a.dbg != nullptr && i < e_count && (p < -1 || p >= n)) dbg_raise(a.dbg, kDbgIndex);
@@ -248,7 +270,8 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         J.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 32 * qk_k0 + 8 * (lane >> 4);
     uint4 raw[QKS];
 #pragma unroll
-    for (int ks = 0; ks < QKS; ++ks) raw[ks] = *reinterpret_cast<const uint4 *>(qrow + 32 * ks);
+    for (int ks = 0; ks < QKS; ++ks) raw[ks] = (kEvenParts || ks < qk_kn) ? *reinterpret_cast<const uint4 *>(qrow + 32 * ks)
+                                                                         : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int ks = 0; ks < QKS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
     if (a.dbg != nullptr) {  // a bf16 magnitude above fp16's largest finite value (65504)
@@ -265,10 +288,10 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   }
 
   if (!win) {
-    int blk[kSlotCap / 256];
+    int blk[kRounds];
 #pragma unroll
-    for (int j = 0; j < kSlotCap / 256; ++j) {
-      if (256 * j >= e_count) break;  // (slots past e_count are never read)
+    for (int j = 0; j < kRounds; ++j) {
+      if (kThreads * j >= e_count) break;  // (slots past e_count are never read)
       const int p = pos[j];
       const bool ok = p >= 0 && p < n && p / kPage < a.S.max_blocks;
       // clamped read, masked below (a table without columns maps nothing)
@@ -276,35 +299,33 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       pos[j] = ok ? p : -1;
     }
 #pragma unroll
-    for (int j = 0; j < kSlotCap / 256; ++j) {
-      if (256 * j >= e_count) break;
-      const int i = 256 * j + tid;
+    for (int j = 0; j < kRounds; ++j) {
+      if (kThreads * j >= e_count) break;
+      const int i = kThreads * j + tid;
       const bool ok = pos[j] >= 0 && blk[j] >= 0 && blk[j] < J.L.num_blocks;
       if (a.dbg != nullptr && pos[j] >= 0 && !ok) dbg_raise(a.dbg, kDbgPage);
       sm.slot[i] = ok ? (uint32_t)blk[j] * kPage + (uint32_t)(pos[j] % kPage) : kNoSlot;
     }
   } else {
     // appending the current token's entry (slot (n - 1) mod 128) when this tile holds it: FP8 pack with
-    // s = amax / 448, code = E4M3(x / s); each thread packs channels 2 tid, 2 tid + 1
+    // s = amax / 448, code = E4M3(x / s); thread t packs channel t
     float snew = 0.0f;
     if (pack_new) {
-      const float2 x = reinterpret_cast<const float2 *>(J.win_latent + (size_t)b * kLatent)[tid];
-      float m = fmaxf(fabsf(x.x), fabsf(x.y));
+      const float x = J.win_latent[(size_t)b * kLatent + tid];
+      float m = fabsf(x);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
       if (lane == 0) sm.wamax[wave] = m;
       __syncthreads();  // uniform: the whole workgroup packs
-      const float amax = fmaxf(fmaxf(sm.wamax[0], sm.wamax[1]), fmaxf(sm.wamax[2], sm.wamax[3]));
+      float amax = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, sm.wamax[w]);
       snew = __fdiv_rn(amax, 448.0f);
-      uint32_t c0 = 0u, c1 = 0u;
-      if (snew > 0.0f) {
-        c0 = e4m3_encode(fabsf(__fdiv_rn(x.x, snew))) | ((__float_as_uint(x.x) >> 31) << 7);
-        c1 = e4m3_encode(fabsf(__fdiv_rn(x.y, snew))) | ((__float_as_uint(x.y) >> 31) << 7);
-      }
-      const uint16_t c = (uint16_t)(c0 | (c1 << 8));
-      reinterpret_cast<uint16_t *>(sm.newc)[tid] = c;
+      uint32_t c = 0u;
+      if (snew > 0.0f) c = e4m3_encode(fabsf(__fdiv_rn(x, snew))) | ((__float_as_uint(x) >> 31) << 7);
+      sm.newc[tid] = (uint8_t)c;
       if (hg == 0) {  // one head group writes the ring
-        reinterpret_cast<uint16_t *>(J.win_codes + ((size_t)b * kWinSlots + s_new) * kLatent)[tid] = c;
+        J.win_codes[((size_t)b * kWinSlots + s_new) * kLatent + tid] = (uint8_t)c;
         if (tid == 0) J.win_scales[(size_t)b * kWinSlots + s_new] = snew;
       }
     }
@@ -326,59 +347,58 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
     }
   }
 
-  // ---- PV accumulators: wave owns channels [128*wave, 128*wave+128) for all HG heads
-  f32x4 acc[MT][8];
+  // ---- PV accumulators: wave owns channels [64*wave, 64*wave+64) for all HG heads
+  f32x4 acc[MT][4];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   __syncthreads();  // slot[] is complete
 
-  // gather of one tile: thread -> entry tile_entry, channel block tile_block
-  // (channels 64 tile_block .. + 63).  A wave covers 8 entries; its
-  // lanes 16 i .. 16 i + 15 take the 8 entries at blocks 2 i and 2 i + 1, so
-  // each 16-byte LDS store of the dequantized tile (row stride 73 x 16 bytes)
-  // lands the 16 lanes on 16 different bank groups.  Every load is issued
-  // unconditionally (a skipped entry reads row 0 and is zeroed when
-  // dequantized; an empty pool never launches a tile).
-  const int tile_entry = (tid & 7) + 8 * wave, tile_block = (lane >> 3) & 7;
+  // gather of one tile: thread -> entry tile_entry, channels 32 tile_chunk ..
+  // + 31 (16 bytes of codes, 2 scales, 4 rope values).  Within a wave the 16
+  // lanes of one chunk hold 16 different entries, so each 16-byte LDS store of
+  // the dequantized tile (rows of an odd number of 16-byte units) hits 16
+  // different bank groups; the 4 lanes l, l + 16, l + 32, l + 48 read 64
+  // contiguous bytes of one row.  Every load is issued unconditionally (a
+  // skipped entry reads row 0 and is zeroed when dequantized; an empty pool
+  // never launches a tile).
+  const int tile_entry = (lane & 15) + 16 * (wave & 1), tile_chunk = (lane >> 4) + 4 * (wave >> 1);
   auto load_raw = [&](int tile, Raw &r) {
-    const int e = tile_entry, cb = tile_block;
-    const int li = tile * kT + e - e_begin;
+    const int li = tile * kT + tile_entry - e_begin;
     const uint32_t slot = li < e_count ? sm.slot[li] : kNoSlot;
     const size_t rs = slot == kNoSlot ? 0 : slot;
-    const uint4 *cp = reinterpret_cast<const uint4 *>(J.L.codes + rs * (kLatent / 2) + 32 * cb);
-    r.c0 = cp[0];
-    r.c1 = cp[1];
-    r.sc4 = *reinterpret_cast<const uint32_t *>(J.L.scales + rs * (kLatent / kGroup) + 4 * cb);
-    if constexpr (ROPE) r.rp = *reinterpret_cast<const uint4 *>(J.L.rope + rs * 64 + 8 * cb);
+    r.c = *reinterpret_cast<const uint4 *>(J.L.codes + rs * (kLatent / 2) + 16 * tile_chunk);
+    r.sc2 = *reinterpret_cast<const uint16_t *>(J.L.scales + rs * (kLatent / kGroup) + 2 * tile_chunk);
+    if constexpr (ROPE) r.rp = *reinterpret_cast<const uint2 *>(J.L.rope + rs * 64 + 4 * tile_chunk);
     r.valid = slot != kNoSlot;
   };
 
   // dequantize one tile's row fragments into a row-major tile buffer
   // (branch-free: a skipped entry is masked to scale 0 and rope 0, so its
-  // channels are all zero; the four E4M3 scales go through the hardware fp8
+  // channels are all zero; the two E4M3 scales go through the hardware fp8
   // convert, exact in fp16)
-  auto dequant = [&](const Raw &r, f16 (*cq)[kQkLd]) {
-    const int e = tile_entry, cb = tile_block;
+  auto dequant = [&](const Raw &r, f16 (*cq)[LD]) {
     const uint32_t vmask = 0u - (uint32_t)r.valid;
-    const uint32_t words[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-    const uint32_t sc4 = r.sc4 & vmask;
-    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, false);  // scale bytes 0, 1
-    const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc4, 1.0f, true);   // scale bytes 2, 3
-    const f16 sc[4] = {s01[0], s01[1], s23[0], s23[1]};
+    const uint32_t words[4] = {r.c.x, r.c.y, r.c.z, r.c.w};
+    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc2 & vmask, 1.0f, false);  // scale bytes 0, 1
 #pragma unroll
-    for (int wi = 0; wi < 8; ++wi)
-      *reinterpret_cast<f16x8 *>(&cq[e][64 * cb + 8 * wi]) = deq8(words[wi], sc[wi >> 1]);
+    for (int wi = 0; wi < 4; ++wi)
+      *reinterpret_cast<f16x8 *>(&cq[tile_entry][32 * tile_chunk + 8 * wi]) = deq8(words[wi], s01[wi >> 1]);
     if constexpr (ROPE) {
-      const uint4 rp = make_uint4(r.rp.x & vmask, r.rp.y & vmask, r.rp.z & vmask, r.rp.w & vmask);
-      const f16x8 rh = bf16x8_to_f16x8(rp);
-      *reinterpret_cast<f16x8 *>(&cq[e][kLatent + 8 * cb]) = rh;
+      const uint2 rp = make_uint2(r.rp.x & vmask, r.rp.y & vmask);
+      f16 rh[4];
+      rh[0] = (f16)__uint_as_float(rp.x << 16);
+      rh[1] = (f16)__uint_as_float(rp.x & 0xFFFF0000u);
+      rh[2] = (f16)__uint_as_float(rp.y << 16);
+      rh[3] = (f16)__uint_as_float(rp.y & 0xFFFF0000u);
+      typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<f16x4 *>(&cq[tile_entry][kLatent + 4 * tile_chunk]) = f16x4{rh[0], rh[1], rh[2], rh[3]};
       if (a.dbg != nullptr) {
         bool big = false;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) big |= !(fabsf((float)rh[i]) <= 65504.0f);
+        for (int i = 0; i < 4; ++i) big |= !(fabsf((float)rh[i]) <= 65504.0f);
         if (big) dbg_raise(a.dbg, kDbgQRange);
       }
     }
@@ -386,49 +406,70 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 
   // online-softmax state: thread -> head tid / TPH, entries (tid % TPH) * EPT ..
   // + EPT - 1 of a tile; the TPH threads of a head keep the same running max
-  // and sum in registers
-  constexpr int TPH = 256 / HG;   // threads per head (4, 8 or 16)
-  constexpr int EPT = kT / TPH;   // entries per thread (8, 4 or 2)
+  // and sum in registers (threads past HG * TPH take no part)
+  constexpr int TPH = (kThreads / HG) < 16 ? (kThreads / HG) : 16;  // threads per head (8 or 16)
+  constexpr int EPT = kT / TPH;   // entries per thread (4 or 2)
   const int sm_h = tid / TPH, sm_part = tid % TPH;
+  const bool sm_on = tid < HG * TPH;
   float m_run = -INFINITY, l_run = 0.f;
 
   // One tile from buffer cq, with the next tile's dequantization into cq_next
   // (three buffers in turn) in the same phase.  Two barriers per tile: the
   // buffer a phase writes was last read two barriers earlier.
-  auto step = [&](int tile, f16 (*cq)[kQkLd], const Raw *next, f16 (*cq_next)[kQkLd]) {
-    // 1. logits S = scale * Q C^T  (this wave's M-tile, 1 or 2 N-tiles)
-    for (int j = 0; j < qk_ntn; ++j) {
+  auto step = [&](int tile, f16 (*cq)[LD], const Raw *next, f16 (*cq_next)[LD]) {
+    // 1. partial logits S_kp = Q C^T over this wave's k-part; even and odd
+    // k-steps of every N-tile accumulate separately (2 or 4 independent MFMA
+    // chains), the B fragments of 4 k-steps read together ahead of them
+    f32x4 sacc[QNT][2];
+    const f16 *brow[QNT];
+#pragma unroll
+    for (int j = 0; j < QNT; ++j) {
+      sacc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      brow[j] = &cq[16 * (qk_nt0 + j) + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < QKS; k0 += 4) {
+      f16x8 bq[QNT][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < QNT; ++j)
+          if (k0 + kk < QKS)
+            bq[j][kk] = (kEvenParts || k0 + kk < qk_kn) ? lds_f16x8(brow[j] + 32 * (k0 + kk)) : f16x8{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < QNT; ++j)
+          if (k0 + kk < QKS)
+            sacc[j][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[k0 + kk], bq[j][kk], sacc[j][kk & 1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < QNT; ++j) {
       const int nt = qk_nt0 + j;
-      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-      const f16 *brow = &cq[16 * nt + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
-      f16x8 bq[QKS];  // B fragments read 4 k-steps ahead of the MFMA that consumes them
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bq[ks] = lds_f16x8(brow + 32 * ks);
-#pragma unroll
-      for (int ks = 0; ks < QKS; ++ks) {
-        if (ks + 4 < QKS) bq[ks + 4] = lds_f16x8(brow + 32 * (ks + 4));
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], bq[ks], sacc, 0, 0, 0);
-      }
-      // lane holds S[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16] (this wave's k-half)
+      const f32x4 sa = sacc[j][0] + sacc[j][1];
+      // lane holds S_kp[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
       const int ent = 16 * nt + (lane & 15);
-      const int li = tile * kT + ent - e_begin;
-      const bool valid = qk_half == 1 || (li < e_count && sm.slot[li] != kNoSlot);  // masked once
-      float es = a.scale_log2;
-      if (win) es *= sm.wts[ent];  // window entries: the token scale of the E4M3 codes
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        sm.s[qk_half][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = valid ? sacc[rr] * es : -INFINITY;
+      for (int rr = 0; rr < 4; ++rr) sm.s[qk_kp][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = sa[rr];
     }
     if (next != nullptr) dequant(*next, cq_next);
     __syncthreads();
-    // 2. online softmax
-    {
+    // 2. online softmax: logit = scale * (sum of the k-parts), masked entries -inf
+    if (sm_on) {
       float v[EPT];
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        v[i] = sm.s[0][sm_h][sm_part * EPT + i];
-        if constexpr (MT == 1) v[i] += sm.s[1][sm_h][sm_part * EPT + i];
+        const int ent = sm_part * EPT + i;
+        float x = sm.s[0][sm_h][ent];
+#pragma unroll
+        for (int kp = 1; kp < KP; ++kp) x += sm.s[kp][sm_h][ent];
+        const int li = tile * kT + ent - e_begin;
+        const bool valid = li < e_count && sm.slot[li] != kNoSlot;
+        float es = a.scale_log2;
+        if (win) es *= sm.wts[ent];  // window entries: the token scale of the E4M3 codes
+        v[i] = valid ? x * es : -INFINITY;
         mx = fmaxf(mx, v[i]);
       }
       mx = group_max<TPH>(mx);
@@ -437,16 +478,18 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       // unscaled on most tiles, and O / l is the same ratio.
       const float m_new = mx > m_run + 8.f ? mx : m_run;
       float sum = 0.f;
+      typedef f16 f16xE __attribute__((ext_vector_type(EPT)));
+      f16xE ph, pl;
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
         const float pv = (m_new == -INFINITY) ? 0.f : exp2f(v[i] - m_new);
         sum += pv;
         const float pw = win ? pv * sm.wp[sm_part * EPT + i] : pv;  // window: P times the token scale
-        const f16 ph = (f16)pw;
-        const f16 pl = (f16)(pw - (float)ph);
-        sm.p_hi[sm_h][sm_part * EPT + i] = ph;
-        sm.p_lo[sm_h][sm_part * EPT + i] = pl;
+        ph[i] = (f16)pw;
+        pl[i] = (f16)(pw - (float)ph[i]);
       }
+      *reinterpret_cast<f16xE *>(&sm.p_hi[sm_h][sm_part * EPT]) = ph;
+      *reinterpret_cast<f16xE *>(&sm.p_lo[sm_h][sm_part * EPT]) = pl;
       sum = group_sum<TPH>(sum);
       // (from an empty state O and l are zero: no rescaling either)
       const float al = (m_new == m_run || m_run == -INFINITY) ? 1.f : exp2f(m_run - m_new);
@@ -455,7 +498,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       if (sm_part == 0) sm.alpha[sm_h] = al;
     }
     __syncthreads();
-    // 3. O = alpha * O + P V  (wave: channels 128*wave .. +127, all heads)
+    // 3. O = alpha * O + P V  (wave: channels 64*wave .. +63, all heads)
     {
       float al[MT][4];
       bool rescale = false;
@@ -472,23 +515,24 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) acc[mt][nt][rr] *= al[mt][rr];
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt][rr] *= al[mt][rr];
       }
-      f16x8 ph[MT], pl[MT];
+      f16x8 ph[MT], pl[MT], bv[4];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         ph[mt] = lds_f16x8(&sm.p_hi[16 * mt + (lane & 15)][8 * (lane >> 4)]);
         pl[mt] = lds_f16x8(&sm.p_lo[16 * mt + (lane & 15)][8 * (lane >> 4)]);
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const f16x8 bv = pv_operand(&cq[8 * (lane >> 4) + ((lane >> 2) & 3)][128 * wave + 16 * nt + 4 * (lane & 3)]);
+      for (int nt = 0; nt < 4; ++nt)
+        bv[nt] = pv_operand<LD>(&cq[8 * (lane >> 4) + ((lane >> 2) & 3)][64 * wave + 16 * nt + 4 * (lane & 3)]);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv, acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[mt], bv, acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[mt], bv[nt], acc[mt][nt], 0, 0, 0);
         }
-      }
     }
   };
 
@@ -497,28 +541,31 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
   // three tile buffers, so the unrolled loop keeps both in step
   if (win) {
     if (tile_begin < tile_end) {
-      // the window tile: thread -> entry tile_entry, channels 64 tile_block .. + 63
-      // (64 E4M3 bytes), converted to fp16 (exact); skipped slots and the rope
+      // the window tile: thread -> entry tile_entry, channels 32 tile_chunk .. + 31
+      // (32 E4M3 bytes), converted to fp16 (exact); skipped slots and the rope
       // part are zero
       const uint32_t slot = sm.slot[tile_entry];
       const uint4 *cp = pack_new && slot == (uint32_t)s_new  // the appended entry, from LDS
-                            ? reinterpret_cast<const uint4 *>(sm.newc + 64 * tile_block)
+                            ? reinterpret_cast<const uint4 *>(sm.newc + 32 * tile_chunk)
                             : reinterpret_cast<const uint4 *>(J.win_codes +
                                                               ((size_t)b * kWinSlots + (slot == kNoSlot ? 0 : slot)) *
                                                                   kLatent +
-                                                              64 * tile_block);
-      uint4 w[4];
+                                                              32 * tile_chunk);
+      uint4 w[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = cp[i];
+      for (int i = 0; i < 2; ++i) w[i] = cp[i];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         f16x8 lo = fp8x8_to_f16(make_uint2(w[i].x, w[i].y));
         f16x8 hi = fp8x8_to_f16(make_uint2(w[i].z, w[i].w));
         if (slot == kNoSlot) lo = hi = f16x8{};
-        *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][64 * tile_block + 16 * i]) = lo;
-        *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][64 * tile_block + 16 * i + 8]) = hi;
+        *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][32 * tile_chunk + 16 * i]) = lo;
+        *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][32 * tile_chunk + 16 * i + 8]) = hi;
       }
-      if constexpr (ROPE) *reinterpret_cast<f16x8 *>(&sm.cq[0][tile_entry][kLatent + 8 * tile_block]) = f16x8{};
+      if constexpr (ROPE) {
+        typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<f16x4 *>(&sm.cq[0][tile_entry][kLatent + 4 * tile_chunk]) = f16x4{};
+      }
       __syncthreads();
       step(0, sm.cq[0], nullptr, sm.cq[1]);
     }
@@ -544,7 +591,7 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
       }
     }
   }
-  if (sm_part == 0) {
+  if (sm_on && sm_part == 0) {
     sm.m_run[sm_h] = m_run;
     sm.l_run[sm_h] = l_run;
   }
@@ -567,9 +614,9 @@ __global__ void __launch_bounds__(256) sparse_attn_kernel(AttnArgs a) {
         sc = l > 0.f ? 1.0f / l : 0.f;
         dst = J.out + ((size_t)b * a.heads + h0 + hl) * kLatent;
       }
-      dst += 128 * wave + (lane & 15);
+      dst += 64 * wave + (lane & 15);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) dst[16 * nt] = acc[mt][nt][r] * sc;
+      for (int nt = 0; nt < 4; ++nt) dst[16 * nt] = acc[mt][nt][r] * sc;
     }
   if (final_out) {
     if (J.lse != nullptr && tid < HG) {
@@ -786,11 +833,11 @@ hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsD
   timer_before(kKernSparseAttn, st);
   const bool rope = jobs[0].L.rope_dim != 0;
   if (hgsz == 64) {
-    if (rope) sparse_attn_kernel<4, true><<<grid, dim3(256), 0, st>>>(a);
-    else sparse_attn_kernel<4, false><<<grid, dim3(256), 0, st>>>(a);
+    if (rope) sparse_attn_kernel<4, true><<<grid, dim3(kThreads), 0, st>>>(a);
+    else sparse_attn_kernel<4, false><<<grid, dim3(kThreads), 0, st>>>(a);
   } else {
-    if (rope) sparse_attn_kernel<1, true><<<grid, dim3(256), 0, st>>>(a);
-    else sparse_attn_kernel<1, false><<<grid, dim3(256), 0, st>>>(a);
+    if (rope) sparse_attn_kernel<1, true><<<grid, dim3(kThreads), 0, st>>>(a);
+    else sparse_attn_kernel<1, false><<<grid, dim3(kThreads), 0, st>>>(a);
   }
   timer_after(kKernSparseAttn, st);
   hipError_t e = hipGetLastError();
