@@ -263,6 +263,23 @@ class Decode1M(Decode):
             return oracle.fp4.fp4_unpack(self.o_entries[0][v], self.o_entries[1][v])
         return oracle.fp4.fp4_unpack(*oracle.fp4.fp4_pack(self.latent[v]))
 
+    def step_sequential(self, r):
+        """The same step as one call per layer and kind, as a decoder that runs other work between its layers
+        would issue it: append, then per layer its selection (Full with the pool, or Reindex) and its
+        attention, each its own launches."""
+        csa2, layer = self.csa2, self.layers[r]
+        csa2.csa2_kv_append(layer, self.batch_prev, self.new_latent, idx_key=self.new_key)
+        for l in range(self.L):
+            if l == 0:
+                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[0], self.K, csa2.FULL, pool_blocks=self.P,
+                                       want_pool=True, ws=self.sel_ws, indices=self.idx[0], pool_out=self.pool,
+                                       w_idx=self.w_idx_d[0])
+            else:
+                csa2.csa2_index_select(layer, self.batch, self.q_idx_d[l], self.K, csa2.REINDEX, pool_in=self.pool,
+                                       pool_blocks=self.P, ws=self.sel_ws, indices=self.idx[l], w_idx=self.w_idx_d[l])
+            csa2.csa2_sparse_fp4_decode_attn(layer, self.batch, self.q_d[l], self.idx[l], self.w.sigma,
+                                             ws=self.attn_ws, out=self.out[l], lse=self.lse[l])
+
     def step(self, r):
         """append + Full select with the pool (one scan launch, one select launch), the 3 Reindex layers
         (one pool-scoring launch, one select launch), the 4 attentions (one launch, one combine)."""
@@ -767,6 +784,9 @@ def main():
     ap.add_argument("--workload", default="decode_1m_hierarchical", choices=WORKLOADS)
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas rotated for cold reads (0: auto)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--sequential", action="store_true",
+                    help="1M-token workloads: issue the step one layer at a time (separate selection and attention "
+                         "calls per layer), the latency a decoder with other work between its layers would see")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-file", default=os.path.join(ROOT, "profiles", "traffic.json"))
@@ -803,6 +823,9 @@ def main():
     want_cpu = not args.no_cpu_baseline
     wk = make(args.workload, replicas, dev, want_cpu)
     R = wk.replicas
+    if args.sequential:
+        assert type(wk) is Decode1M and not wk.fp4, "--sequential applies to decode_1m_hierarchical"
+        wk.step = wk.step_sequential
 
     # one eager step per replica (also checks that the library runs)
     for r in range(R):
@@ -914,6 +937,8 @@ def main():
         pass
     res["roofline"] = roof
     res["graph"] = graphs is not None
+    if args.sequential:
+        res["config"]["issue"] = "sequential: one selection and one attention call per layer"
     res["step_us"] = step_us
     # context: what a plain device copy reaches on this GPU (1 GiB read + 1 GiB written)
     src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
