@@ -484,7 +484,12 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
       for (int i = 0; i < EPT; ++i) {
         const float pv = (m_new == -INFINITY) ? 0.f : exp2f(v[i] - m_new);
         sum += pv;
-        const float pw = win ? pv * sm.wp[sm_part * EPT + i] : pv;  // window: P times the token scale
+        // window: P times the token scale.  pw is rounded to fp32 once and
+        // both parts are split from that value: left visible, the product
+        // gets folded into one fp16 conversion (rounded once from the exact
+        // product) but not the other, and hi + lo can miss pw by one fp16 ulp
+        float pw = win ? pv * sm.wp[sm_part * EPT + i] : pv;
+        asm volatile("" : "+v"(pw));
         ph[i] = (f16)pw;
         pl[i] = (f16)(pw - (float)ph[i]);
       }

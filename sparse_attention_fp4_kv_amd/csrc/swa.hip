@@ -192,7 +192,11 @@ __global__ void __launch_bounds__(256) swa_attn_kernel(SwaArgs a) {
     for (int i = 0; i < 8; ++i) {
       const float p = e0 + i < nwin ? exp2f(sv[i] - mx) : 0.0f;
       l += p;
-      const float pv = p * (ts[i] * norm);
+      // pv is rounded to fp32 once and both parts are split from that value
+      // (left visible, the product gets folded into one fp16 conversion but
+      // not the other, and hi + lo can miss pv by one fp16 ulp of hi)
+      float pv = p * (ts[i] * norm);
+      asm volatile("" : "+v"(pv));
       ph[i] = (f16)pv;
       pl[i] = (f16)(pv - (float)ph[i]);
     }
