@@ -22,6 +22,8 @@ FLAGS = [
     # keep hipcc from emitting packed-fp32 VALU ops (v_pk_{add,mul,fma}_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# roctx (range markers around the C ABI calls, off unless CSA2_ROCTX is set)
+LIBS = ["-lrocprofiler-sdk-roctx"]
 
 
 def hipcc():
@@ -34,7 +36,7 @@ def hipcc():
 def build(verbose=False):
     """Compile every HIP source into libcsa2.so next to this file (always rebuilds)."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc()] + FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES] + LIBS
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)

@@ -10,9 +10,36 @@
 #include <new>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "kernels.h"
 
 using namespace csa2;
+
+namespace {
+// roctx ranges around every call that launches work, named after the call,
+// for profilers (rocprofv3 --marker-trace); on when the environment variable
+// CSA2_ROCTX is set to a nonzero value, read once.
+bool roctx_on() {
+  static const bool on = [] {
+    const char *e = std::getenv("CSA2_ROCTX");
+    return e != nullptr && std::atoi(e) != 0;
+  }();
+  return on;
+}
+struct TraceRange {
+  bool on;
+  explicit TraceRange(const char *name) : on(roctx_on()) {
+    if (on) roctxRangePushA(name);
+  }
+  ~TraceRange() {
+    if (on) roctxRangePop();
+  }
+  TraceRange(const TraceRange &) = delete;
+  TraceRange &operator=(const TraceRange &) = delete;
+};
+}  // namespace
+#define CSA2_TRACE TraceRange trace_range_(__func__)
 
 // The debug flag word of every device (word 0 is used; the rest pads it to
 // its own cache line).
@@ -207,6 +234,7 @@ csa2_status csa2_debug_flags(uint32_t *flags) {
 }
 
 csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream) {
+  CSA2_TRACE;
   if (bytes == 0) return CSA2_OK;
   if (ws == nullptr || !aligned(ws, 4) || bytes % 4 != 0) return CSA2_ERR_INVALID_ARG;
   return from_hip(launch_fill_zero(ws, bytes, as_stream(stream)));
@@ -214,6 +242,7 @@ csa2_status csa2_workspace_clear(void *ws, size_t bytes, csa2_stream stream) {
 
 csa2_status csa2_fp4_pack(const float *x, int64_t rows, int32_t channels, uint8_t *codes, uint8_t *scales,
                           csa2_stream stream) {
+  CSA2_TRACE;
   if (rows < 0 || channels <= 0 || channels % 16 != 0) return CSA2_ERR_INVALID_ARG;
   if (rows == 0) return CSA2_OK;
   if (x == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_INVALID_ARG;
@@ -223,6 +252,7 @@ csa2_status csa2_fp4_pack(const float *x, int64_t rows, int32_t channels, uint8_
 
 csa2_status csa2_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t rows, int32_t channels, float *y,
                             csa2_stream stream) {
+  CSA2_TRACE;
   if (rows < 0 || channels <= 0 || channels % 16 != 0) return CSA2_ERR_INVALID_ARG;
   if (rows == 0) return CSA2_OK;
   if (y == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_INVALID_ARG;
@@ -232,6 +262,7 @@ csa2_status csa2_fp4_unpack(const uint8_t *codes, const uint8_t *scales, int64_t
 
 csa2_status csa2_kv_append(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
                            const uint16_t *rope, const void *idx_key, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(layer, latent != nullptr, false, &L);
@@ -276,6 +307,7 @@ csa2_status check_finish_rows(int64_t tokens, int32_t n_layers, int64_t pos0, co
 csa2_status csa2_kv_finish_rows(const float *c, int64_t tokens, int32_t n_layers, int64_t pos0,
                                 const csa2_kv_finish *fin, uint8_t *codes, uint8_t *scales, uint8_t *idx_codes,
                                 uint8_t *idx_scales, float *x_f32, float *k_f32, csa2_stream stream) {
+  CSA2_TRACE;
   KvFinish f;
   csa2_status st = check_finish_rows(tokens, n_layers, pos0, fin, codes, scales, idx_codes, idx_scales, x_f32,
                                      k_f32, &f);
@@ -290,6 +322,7 @@ csa2_status csa2_ced_kv_project_finished(const uint16_t *h, int64_t tokens, int3
                                          const uint16_t *w_kv, const csa2_kv_finish *fin, int64_t pos0,
                                          float *c_f32, uint8_t *codes, uint8_t *scales, uint8_t *idx_codes,
                                          uint8_t *idx_scales, csa2_stream stream) {
+  CSA2_TRACE;
   if (hidden <= 0 || hidden % 64 != 0 || tokens > (int64_t)1 << 31) return CSA2_ERR_INVALID_ARG;
   KvFinish f;
   csa2_status st = check_finish_rows(tokens, n_layers, pos0, fin, codes, scales, idx_codes, idx_scales, nullptr,
@@ -307,6 +340,7 @@ csa2_status csa2_ced_kv_project_finished(const uint16_t *h, int64_t tokens, int3
 
 csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs *seqs, const float *latent,
                                     const csa2_kv_finish *fin, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   KvFinish f;
@@ -326,6 +360,7 @@ csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs 
 
 csa2_status csa2_swa_append(const csa2_swa_window *win, const int32_t *positions, int32_t batch,
                             const float *latent, csa2_stream stream) {
+  CSA2_TRACE;
   if (win == nullptr || batch < 0 || batch > win->batch) return CSA2_ERR_INVALID_ARG;
   if (batch == 0) return CSA2_OK;
   if (win->codes == nullptr || win->scales == nullptr || positions == nullptr || latent == nullptr)
@@ -337,6 +372,7 @@ csa2_status csa2_swa_append(const csa2_swa_window *win, const int32_t *positions
 csa2_status csa2_swa_attn_merge(const csa2_swa_window *win, const int32_t *seq_lens, int32_t batch,
                                 const uint16_t *q, int32_t heads, int32_t q_dim, float softmax_scale, float *out,
                                 float *lse, csa2_stream stream) {
+  CSA2_TRACE;
   if (win == nullptr || batch < 0 || batch > win->batch) return CSA2_ERR_INVALID_ARG;
   if (heads < 16 || heads > 128 || heads % 16 != 0 || (q_dim != 512 && q_dim != 576)) return CSA2_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !(softmax_scale < 3.0e38f)) return CSA2_ERR_INVALID_ARG;
@@ -352,6 +388,7 @@ csa2_status csa2_swa_attn_merge(const csa2_swa_window *win, const int32_t *seq_l
 csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidden, int32_t n_layers,
                                 const uint16_t *w_kv, const uint16_t *w_z, uint8_t *codes, uint8_t *scales,
                                 uint16_t *z, float *c_f32, csa2_stream stream) {
+  CSA2_TRACE;
   if (tokens < 0 || n_layers < 0 || hidden <= 0 || hidden % 64 != 0) return CSA2_ERR_INVALID_ARG;
   if (tokens > (int64_t)1 << 31 || n_layers > 4096) return CSA2_ERR_INVALID_ARG;
   if (tokens == 0 || n_layers == 0) return CSA2_OK;
@@ -366,6 +403,7 @@ csa2_status csa2_ced_kv_project(const uint16_t *h, int64_t tokens, int32_t hidde
 
 csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, const void *q_idx,
                               const float *w_idx, float *scores, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(keys, false, true, &L);
@@ -385,6 +423,7 @@ csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top
 
 csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *lens, int32_t batch, int32_t max_len,
                       int32_t top_k, int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
   if (batch < 0 || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 || top_k > kMaxTopK || row_stride < max_len)
     return CSA2_ERR_INVALID_ARG;
   if (batch == 0) return CSA2_OK;
@@ -410,6 +449,7 @@ csa2_status csa2_index_select(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
                               int32_t *pool_out, int32_t pool_blocks,
                               int32_t pool_block_tokens, int32_t *indices, void *ws, size_t ws_bytes,
                               csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(keys, false, true, &L);
@@ -457,6 +497,7 @@ csa2_status csa2_index_select_append(const csa2_kv_layer *keys, const csa2_seqs 
                                      int32_t n_appends, const void *q_idx, const float *w_idx, int32_t top_k,
                                      int32_t *pool_out, int32_t pool_blocks, int32_t pool_block_tokens,
                                      int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(keys, false, true, &L);
@@ -505,6 +546,7 @@ csa2_status csa2_index_reindex_layers(const csa2_kv_layer *keys, const csa2_seqs
                                       const csa2_reindex_query *queries, int32_t n_layers, int32_t top_k,
                                       const int32_t *pool_in, int32_t pool_blocks, int32_t pool_block_tokens,
                                       void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(keys, false, true, &L);
@@ -548,6 +590,7 @@ csa2_status csa2_attn_swa_workspace_size(int32_t batch, int32_t heads, int32_t t
 csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_seqs *seqs, const uint16_t *q,
                                         int32_t heads, const int32_t *indices, int32_t top_k, float softmax_scale,
                                         float *out, float *lse, void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(layer, true, false, &L);
@@ -568,6 +611,7 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
                                             int32_t heads, const int32_t *indices, int32_t top_k,
                                             float softmax_scale, const csa2_swa_window *win, const float *new_latent,
                                             float *out, float *lse, void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
   KvLayerDev L;
   SeqsDev S;
   csa2_status st = check_layer(layer, true, false, &L);
@@ -600,6 +644,7 @@ csa2_status csa2_attn_layers_workspace_size(int32_t n_layers, int32_t batch, int
 csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, int32_t n_layers,
                                                const csa2_seqs *seqs, int32_t heads, int32_t top_k,
                                                float softmax_scale, void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
   SeqsDev S;
   csa2_status st;
   if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
@@ -643,6 +688,7 @@ csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, in
 csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *layers, int32_t n_layers,
                                                        const csa2_seqs *seqs, int32_t heads, int32_t top_k,
                                                        float softmax_scale, csa2_stream stream) {
+  CSA2_TRACE;
   SeqsDev S;
   csa2_status st = check_seqs(seqs, &S);
   if (st != CSA2_OK) return st;

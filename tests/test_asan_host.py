@@ -23,7 +23,7 @@ def test_host_code_under_asan():
         cmd = [hipcc, "--offload-arch=gfx950", "-O1", "-g", "-std=c++17",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
-               "-o", exe, os.path.join(ROOT, "tests", "asan", "abi_host_check.cpp")] + srcs
+               "-o", exe, os.path.join(ROOT, "tests", "asan", "abi_host_check.cpp")] + srcs + build_lib.LIBS
         res = subprocess.run(cmd, capture_output=True, text=True)
         noise = "is not a recognized feature for this target"
         assert res.returncode == 0, "\n".join(l for l in res.stderr.splitlines() if noise not in l)[-4000:]
