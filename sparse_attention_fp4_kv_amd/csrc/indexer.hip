@@ -419,11 +419,12 @@ __device__ __forceinline__ void zero_hists(uint32_t (*hist)[kBins]) {
   for (int i = 0; i < NH * kBins / 4 / 256; ++i) h4[256 * i + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
 }
 
-// hist[0], hist[1]: level-1 and level-2 histograms, zeroed by the caller
-// before a barrier that precedes the call (zero_hists).
+// Absolute digits (the key's top 11 bits, then the next 11 inside the
+// boundary bin).  hist[0], hist[1]: level-1 and level-2 histograms, zeroed by
+// the caller before a barrier that precedes the call (zero_hists).
 template <int NT, int IPT, class PosOf>
-__device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
-                                             uint32_t (*hist)[kBins], uint32_t *red, PosOf pos_of) {
+__device__ __forceinline__ void emit_segment_abs(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
+                                                 uint32_t (*hist)[kBins], uint32_t *red, PosOf pos_of) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i0 = 64 * IPT * wave + lane;  // this lane's items: i0 + 64 j
   uint32_t k[IPT];
@@ -471,10 +472,10 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
 // hist[0..3]: level-1 and level-2 histograms of positions and blocks, zeroed
 // by the caller before a barrier that precedes the call.
 template <class PosP, class PosB>
-__device__ __forceinline__ void emit_segment_pair(const uint32_t *pkeys, int cap_p, uint2 *cand_p, SegInfo *info_p,
-                                                  PosP pos_p, const uint32_t *bkeys, int cap_b, uint2 *cand_b,
-                                                  SegInfo *info_b, PosB pos_b, uint32_t (*hist)[kBins],
-                                                  uint32_t *red) {
+__device__ __forceinline__ void emit_segment_pair_abs(const uint32_t *pkeys, int cap_p, uint2 *cand_p,
+                                                      SegInfo *info_p, PosP pos_p, const uint32_t *bkeys, int cap_b,
+                                                      uint2 *cand_b, SegInfo *info_b, PosB pos_b,
+                                                      uint32_t (*hist)[kBins], uint32_t *red) {
   constexpr int NT = 256;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ip0 = 64 * 8 * wave + lane, ib = 64 * wave + lane;
@@ -561,6 +562,223 @@ __device__ __forceinline__ void emit_segment_pair(const uint32_t *pkeys, int cap
   }
 }
 
+// Relative digits.  Bin of a key below the segment's largest key M: bins of
+// 2^12 key units counted down from M (bin 2047 holds M); keys 2047 or more
+// bins below M are "far" (bin 0) and are only counted, not binned.  Keys are
+// order-preserving images of fp32 scores, close to logarithmic in the score,
+// so the window spans about a factor of 2 below the largest score at any
+// scale, which holds a segment's best few items for the score distributions
+// of an indexer, at 2^12-unit resolution.  The cut keeps whole bins from the
+// top (at most cap items); everything left has a key below the edge.  When
+// the window holds fewer than cap items and far items remain, the absolute
+// two-level emission runs instead (it can use more of the budget there).
+constexpr int kRelShift = 12;
+__device__ __forceinline__ uint32_t rel_bin(uint32_t key, uint32_t m) {
+  const uint32_t d = (m - key) >> kRelShift;
+  return d >= (uint32_t)(kBins - 1) ? 0u : (uint32_t)(kBins - 1) - d;
+}
+// Every key in bins <= d is below this (a key of bin d > 0 is at most
+// M - (2047 - d) 2^12; a far key at most M - 2047 2^12; both >= 1 when such
+// a key exists).
+__device__ __forceinline__ uint32_t rel_edge(uint32_t m, uint32_t d) {
+  return m - (((uint32_t)(kBins - 1) - d) << kRelShift) + 1u;
+}
+
+// Relative-digit histogram of one lane's keys (far keys only counted) and
+// its wave's count of far keys in far_w[wave] (0 or the count; lane 0 writes).
+template <int IPT>
+__device__ __forceinline__ void rel_hist(const uint32_t (&k)[IPT], uint32_t m, uint32_t *hist, uint32_t *far_w) {
+  uint32_t far = 0u;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const uint32_t bin = rel_bin(k[j], m);
+    const bool is_far = k[j] != 0u && bin == 0u;
+    far += (uint32_t)__popcll(__ballot(is_far));
+    if (k[j] != 0u && bin != 0u) atomicAdd(&hist[bin], 1u);
+  }
+  if ((threadIdx.x & 63) == 0) far_w[threadIdx.x >> 6] = far;
+}
+
+// The cut of one relative-digit segment from its threshold search (for
+// cap + 1 over the binned keys) and its far count: returns false when the
+// absolute emission must run instead; else *cut / *d say which bins are kept
+// (all when !cut, else bins > d) and *edge the segment's edge.
+__device__ __forceinline__ bool rel_cut(const uint32_t *res, uint32_t far, int cap, uint32_t m, bool *cut,
+                                        uint32_t *d, uint32_t *edge) {
+  const bool found = res[2] != 0u;
+  if (found) {  // the boundary lies in the window (bin >= 1)
+    *cut = true;
+    *d = res[0];
+    *edge = rel_edge(m, res[0]);
+    return true;
+  }
+  const uint32_t binned = res[1];  // total of bins 1 .. 2047 (bin 0 is never binned)
+  if (far == 0u) {                 // everything fits
+    *cut = false;
+    *d = 0u;
+    *edge = 0u;
+    return true;
+  }
+  if (binned == (uint32_t)cap) {  // exactly the budget in the window, the rest far
+    *cut = true;
+    *d = 0u;
+    *edge = rel_edge(m, 0u);
+    return true;
+  }
+  return false;
+}
+
+// Largest of this lane's keys over the workgroup (every thread gets it).
+// red: NT/64 words; ends with a barrier.
+template <int NT, int IPT>
+__device__ __forceinline__ uint32_t block_max_key(const uint32_t (&k)[IPT], uint32_t *red) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t m = 0u;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) m = max(m, k[j]);
+  m = wave_last(wave_inclusive_max(m));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  uint32_t r = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) r = max(r, red[w]);
+  return r;
+}
+
+// emit_segment with relative digits below a known largest key m of the
+// segment's keys (same contract as emit_segment_abs; hist[0], hist[1] zeroed
+// by the caller before a barrier that precedes the call; red: NT/64 + 24
+// words).
+template <int NT, int IPT, class PosOf>
+__device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_l, int cap, uint2 *cand_seg,
+                                               SegInfo *info, uint32_t (*hist)[kBins], uint32_t *red,
+                                               PosOf pos_of) {
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int i0 = 64 * IPT * wave + lane;  // this lane's items: i0 + 64 j
+  uint32_t k[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) k[j] = keys_l[i0 + 64 * j];
+  rel_hist<IPT>(k, m, hist[0], red + 24 - NW);
+  __syncthreads();
+  find_threshold(hist[0], (uint32_t)cap + 1u, red + 16);
+  uint32_t far = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) far += red[24 - NW + w];
+  bool cut;
+  uint32_t d1, edge;
+  if (!rel_cut(red + 16, far, cap, m, &cut, &d1, &edge)) {  // uniform
+    zero_hists<1>(hist);
+    __syncthreads();
+    emit_segment_abs<NT, IPT>(keys_l, cap, cand_seg, info, hist, red, pos_of);
+    return;
+  }
+  uint32_t flags = 0;
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const bool em = k[j] != 0u && (!cut || rel_bin(k[j], m) > d1);
+    flags |= em ? (1u << j) : 0u;
+  }
+  const uint32_t total = ordered_emit<NT, IPT>(flags, red, 0u, [&](int j, uint32_t slot, bool keep) {
+    if (keep) cand_seg[slot] = make_uint2(k[j], pos_of(i0 + 64 * j));
+  });
+  for (int i = (int)total + t; i < cap; i += NT) cand_seg[i] = make_uint2(0u, 0u);  // unused slots: no item
+  if (t == 0) *info = SegInfo{total, edge};
+}
+
+// The same, finding the largest key first (one more barrier).
+template <int NT, int IPT, class PosOf>
+__device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
+                                             uint32_t (*hist)[kBins], uint32_t *red, PosOf pos_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t k[IPT];
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) k[j] = keys_l[64 * IPT * wave + lane + 64 * j];
+  const uint32_t m = block_max_key<NT, IPT>(k, red + 8);
+  emit_segment_m<NT, IPT>(m, keys_l, cap, cand_seg, info, hist, red, pos_of);
+}
+
+// emit_segment_pair with relative digits below m, the largest position key
+// (which is also the largest block key): both histograms and both threshold
+// searches (waves 0 and 1) share their barriers.  hist[0..3] zeroed by the
+// caller before a barrier that precedes the call; red: 36 words.
+template <class PosP, class PosB>
+__device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pkeys, int cap_p, uint2 *cand_p,
+                                                  SegInfo *info_p, PosP pos_p, const uint32_t *bkeys, int cap_b,
+                                                  uint2 *cand_b, SegInfo *info_b, PosB pos_b,
+                                                  uint32_t (*hist)[kBins], uint32_t *red) {
+  constexpr int NT = 256;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int ip0 = 64 * 8 * wave + lane, ib = 64 * wave + lane;
+  uint32_t kp[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kp[j] = pkeys[ip0 + 64 * j];
+  const uint32_t kb1[1] = {bkeys[ib]};
+  const uint32_t kb = kb1[0];
+  const uint32_t mp = m, mb = m;
+  rel_hist<8>(kp, mp, hist[0], red + 24);
+  rel_hist<1>(kb1, mb, hist[1], red + 28);
+  __syncthreads();
+  if (wave == 0) find_threshold_wave(hist[0], (uint32_t)cap_p + 1u, red + 16);
+  if (wave == 1) find_threshold_wave(hist[1], (uint32_t)cap_b + 1u, red + 20);
+  __syncthreads();
+  uint32_t far_p = 0u, far_b = 0u;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    far_p += red[24 + w];
+    far_b += red[28 + w];
+  }
+  bool cut_p, cut_b;
+  uint32_t d1p, d1b, edge_p, edge_b;
+  const bool ok_p = rel_cut(red + 16, far_p, cap_p, mp, &cut_p, &d1p, &edge_p);
+  const bool ok_b = rel_cut(red + 20, far_b, cap_b, mb, &cut_b, &d1b, &edge_b);
+  if (!ok_p || !ok_b) {  // uniform: the absolute emission for both
+    __syncthreads();     // every thread has read red[]
+    zero_hists<2>(hist);
+    __syncthreads();
+    emit_segment_pair_abs(pkeys, cap_p, cand_p, info_p, pos_p, bkeys, cap_b, cand_b, info_b, pos_b, hist, red);
+    return;
+  }
+  // ordered compaction of both segments with one exchange of wave totals
+  const uint64_t below = __lanemask_lt();
+  uint64_t bal[8];
+  uint32_t wtot_p = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bal[j] = __ballot(kp[j] != 0u && (!cut_p || rel_bin(kp[j], mp) > d1p));
+    wtot_p += (uint32_t)__popcll(bal[j]);
+  }
+  const bool keep_b = kb != 0u && (!cut_b || rel_bin(kb, mb) > d1b);
+  const uint64_t bal_b = __ballot(keep_b);
+  if (lane == 0) {  // (red[0..7] is free here: the values read above live in red[8..31])
+    red[wave] = wtot_p;
+    red[4 + wave] = (uint32_t)__popcll(bal_b);
+  }
+  __syncthreads();
+  uint32_t run = 0, total_p = 0, slot_b = 0, total_b = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t xp = red[w], xb = red[4 + w];
+    run += w < wave ? xp : 0u;
+    slot_b += w < wave ? xb : 0u;
+    total_p += xp;
+    total_b += xb;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if ((bal[j] >> lane) & 1u) cand_p[run + (uint32_t)__popcll(bal[j] & below)] = make_uint2(kp[j], pos_p(ip0 + 64 * j));
+    run += (uint32_t)__popcll(bal[j]);
+  }
+  if (keep_b) cand_b[slot_b + (uint32_t)__popcll(bal_b & below)] = make_uint2(kb, pos_b(ib));
+  for (int i = (int)total_p + t; i < cap_p; i += NT) cand_p[i] = make_uint2(0u, 0u);  // unused slots: no item
+  for (int i = (int)total_b + t; i < cap_b; i += NT) cand_b[i] = make_uint2(0u, 0u);
+  if (t == 0) {
+    *info_p = SegInfo{total_p, edge_p};
+    *info_b = SegInfo{total_b, edge_b};
+  }
+}
+
 // ------------------------------------------------------------------ producer: full scan
 struct ScanArgs {
   KvLayerDev L;
@@ -588,7 +806,8 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   // histograms of the emission: positions (level 1, 2) and, hierarchical,
   // blocks (level 1, 2); zeroed while the first loads are in flight
   __shared__ __attribute__((aligned(16))) uint32_t hist[HIER ? 4 : 2][kBins];
-  __shared__ uint32_t red[256 / 64 + 24];
+  __shared__ uint32_t red[36];
+  __shared__ uint32_t kmax_l;  // largest key of the segment (LDS atomic max of the waves' maxima)
   const int b = blockIdx.y, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (wg >= a.scan_wgs) {  // an append workgroup (uniform)
@@ -596,12 +815,14 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     if (tid < 64) append_row(r.L, a.S, b, -1, r.latent, r.rope, r.idx_key, tid, a.dbg);
     return;
   }
-  const int n = row_len(a.S, b);
+  const int sl = a.S.seq_lens[b];  // read once: a reload after the key loads would cost a memory round trip
+  const int n = sl < 0 ? 0 : (sl > a.S.max_len ? a.S.max_len : sl);
   const int64_t base = (int64_t)wg * kScanPos;
-  if (a.dbg != nullptr && wg == 0 && tid == 0 && (a.S.seq_lens[b] < 0 || a.S.seq_lens[b] > a.S.max_len))
-    dbg_raise(a.dbg, kDbgSeqLen);
+  if (a.dbg != nullptr && wg == 0 && tid == 0 && (sl < 0 || sl > a.S.max_len)) dbg_raise(a.dbg, kDbgSeqLen);
   if (base >= n) return;  // segments past the row are never read
   zero_hists<HIER ? 4 : 2>(hist);
+  if (tid == 0) kmax_l = 0u;
+  uint32_t kmax = 0u;  // this lane's largest key
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
   if (tid < kScanPages) {
     pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
@@ -641,7 +862,9 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
         for (int j = 0; j < 2; ++j) {
           const int lp = page * kPage + 32 * j + (lane & 31);  // local position
           const float sc = fp4_tile_score(kt[pp % kDepth][j], Q);
-          if (lane < 32) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
+          const uint32_t key = (lane < 32 && mapped && base + lp < n) ? score_key(sc) : 0u;
+          kmax = max(kmax, key);
+          if (lane < 32) pkey[lp] = key;
         }
       }
     } else {
@@ -667,17 +890,21 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
       for (int u = 0; u < 8; ++u) {
         const int lp = page * kPage + 8 * u + (lane >> 3);  // local position
         const float sc = unit_score<F32>(kl[pp % kDepth][u], q);
-        if ((lane & 7) == 0) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
+        const uint32_t key = (mapped && base + lp < n) ? score_key(sc) : 0u;
+        kmax = max(kmax, key);
+        if ((lane & 7) == 0) pkey[lp] = key;
       }
     }
   } else {
     for (int i = tid; i < kScanPos; i += 256) pkey[i] = 0u;
   }
   }
+  kmax = wave_last(wave_inclusive_max(kmax));
+  if (lane == 0) atomicMax(&kmax_l, kmax);
   __syncthreads();
-  if (a.new_key != nullptr && a.S.seq_lens[b] - 1 >= base && a.S.seq_lens[b] - 1 < base + kScanPos &&
-      a.S.seq_lens[b] <= n) {  // uniform: this workgroup holds the appended position
-    const int lp = a.S.seq_lens[b] - 1 - (int)base;
+  if (a.new_key != nullptr && sl - 1 >= base && sl - 1 < base + kScanPos &&
+      sl <= n) {  // uniform: this workgroup holds the appended position
+    const int lp = sl - 1 - (int)base;
     if (wave == 0 && pg[lp / kPage] >= 0) {
       // the same lane layout and arithmetic as the streaming loop, on the input key
       if constexpr (KF == kKeyFp4) {
@@ -695,7 +922,10 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
           kh = Fp4Half{u32x4{wd[0], wd[1], wd[2], wd[3]}, u32x4{wd[4], wd[5], wd[6], wd[7]}, sc};
         }
         const float sc = fp4_tile_score(kh, Q);
-        if (lane == (lp & 31)) pkey[lp] = score_key(sc);
+        if (lane == (lp & 31)) {
+          pkey[lp] = score_key(sc);
+          atomicMax(&kmax_l, score_key(sc));
+        }
       } else {
         KeyLoad kl;
         if constexpr (F32) {
@@ -708,7 +938,10 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
           kl = KeyLoad{p[0], u32x4{0, 0, 0, 0}};
         }
         const float sc = unit_score<F32>(kl, q);
-        if (lane == 0) pkey[lp] = score_key(sc);
+        if (lane == 0) {
+          pkey[lp] = score_key(sc);
+          atomicMax(&kmax_l, score_key(sc));
+        }
       }
     }
     __syncthreads();
@@ -718,8 +951,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     const u32x4 *p4 = reinterpret_cast<const u32x4 *>(pkey + kBlk * tid);
     const u32x4 x = p4[0], y = p4[1];
     uint32_t m = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(y[0], y[1]), max(y[2], y[3])));
-    bkey[tid] = m;
-    __syncthreads();
+    bkey[tid] = m;  // (read back only by this thread: the key store and the emission's block item tid)
   }
   // store every key (the select re-reads segments that overflow their budget)
   {
@@ -733,15 +965,15 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   const int cap = seg_budget(a.K, nseg, kScanPos);
   if constexpr (HIER) {
     const int cap_b = seg_budget(a.P, nseg, kScanBlocks);
-    emit_segment_pair(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+    emit_segment_pair(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
                       bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
                       a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
                       hist, red);
   } else {
-    emit_segment<256, 8>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
-                         a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
-                         [&](int i) { return (uint32_t)(base + i); });
+    emit_segment_m<256, 8>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                           a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
+                           [&](int i) { return (uint32_t)(base + i); });
   }
 }
 
