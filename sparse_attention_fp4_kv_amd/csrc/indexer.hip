@@ -49,7 +49,7 @@ namespace csa2 {
 namespace {
 
 constexpr int kBins = 2048;                    // 11-bit radix digits
-constexpr int kScanPos = 2048;                 // positions per producer workgroup
+constexpr int kScanPos = 2048;                 // positions per producer workgroup (1024 for small grids)
 constexpr int kScanPages = kScanPos / kPage;   // 32
 constexpr int kBlk = 8;                        // positions per pool block
 constexpr int kScanBlocks = kScanPos / kBlk;   // 256
@@ -81,6 +81,7 @@ struct SelWs {
   SegInfo *seg_blk;  // [B][max_seg]
   int64_t cap_keys, cap_blocks;
   int max_seg;
+  int slice;         // positions per producer segment (scan: 1024 or 2048; given scores: 2048)
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -89,14 +90,20 @@ inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 struct WsShape {
   int64_t cap_keys, cap_blocks;
   int max_seg;
+  int slice;
   bool pool;
 };
 
-WsShape ws_shape(int max_len, int pool_blocks) {
+// Producer segments of a full scan are 2048 positions, or 1024 when 2048
+// would leave at most one scan workgroup per CU (256): two workgroups per CU
+// then overlap one's emission with the other's key loads.  Given scores
+// always use 2048.
+WsShape ws_shape(int batch, int max_len, int pool_blocks, bool scan) {
   WsShape s;
   s.cap_keys = round_up(max_len > 0 ? max_len : 1, kScanPos);
   s.cap_blocks = round_up((s.cap_keys + kBlk - 1) / kBlk, kScanBlocks);
-  const int seg_scan = (int)(s.cap_keys / kScanPos);
+  s.slice = (scan && (int64_t)(batch > 0 ? batch : 1) * (s.cap_keys / kScanPos) <= 256) ? kScanPos / 2 : kScanPos;
+  const int seg_scan = (int)(s.cap_keys / s.slice);
   const int seg_pool = (pool_blocks + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg;
   s.max_seg = seg_scan > seg_pool ? seg_scan : seg_pool;
   s.pool = pool_blocks > 0;
@@ -133,6 +140,7 @@ SelWs carve(void *ws, int batch, const WsShape &s) {
   w.cap_keys = s.cap_keys;
   w.cap_blocks = s.cap_blocks;
   w.max_seg = s.max_seg;
+  w.slice = s.slice;
   return w;
 }
 
@@ -465,27 +473,28 @@ __device__ __forceinline__ void emit_segment_abs(const uint32_t *keys_l, int cap
   if (t == 0) *info = SegInfo{total, edge};
 }
 
-// Both segments of a hierarchical scan workgroup at once (positions: 2048
-// keys, 8 per thread; blocks: 256 keys, 1 per thread), with the same cut rule
-// as emit_segment: the two histograms share each barrier and their threshold
-// searches run side by side in waves 0 and 1.
+// Both segments of a hierarchical scan workgroup at once (positions: 256 IPT
+// keys, IPT per thread; blocks: 32 IPT keys, one per thread of the first
+// 32 IPT), with the same cut rule as emit_segment: the two histograms share
+// each barrier and their threshold searches run side by side in waves 0 and
+// 1.
 // hist[0..3]: level-1 and level-2 histograms of positions and blocks, zeroed
 // by the caller before a barrier that precedes the call.
-template <class PosP, class PosB>
+template <int IPT, class PosP, class PosB>
 __device__ __forceinline__ void emit_segment_pair_abs(const uint32_t *pkeys, int cap_p, uint2 *cand_p,
                                                       SegInfo *info_p, PosP pos_p, const uint32_t *bkeys, int cap_b,
                                                       uint2 *cand_b, SegInfo *info_b, PosB pos_b,
                                                       uint32_t (*hist)[kBins], uint32_t *red) {
   constexpr int NT = 256;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int ip0 = 64 * 8 * wave + lane, ib = 64 * wave + lane;
+  const int ip0 = 64 * IPT * wave + lane, ib = 64 * wave + lane;
   uint32_t *hist_p = hist[0], *hist_b = hist[1];
-  uint32_t kp[8];
+  uint32_t kp[IPT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kp[j] = pkeys[ip0 + 64 * j];
-  const uint32_t kb = bkeys[ib];
+  for (int j = 0; j < IPT; ++j) kp[j] = pkeys[ip0 + 64 * j];
+  const uint32_t kb = ib < 32 * IPT ? bkeys[ib] : 0u;
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < IPT; ++j)
     if (kp[j]) atomicAdd(&hist_p[kp[j] >> 21], 1u);
   if (kb) atomicAdd(&hist_b[kb >> 21], 1u);
   __syncthreads();
@@ -501,7 +510,7 @@ __device__ __forceinline__ void emit_segment_pair_abs(const uint32_t *pkeys, int
     hist_b = hist[3];
     if (cut_p) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < IPT; ++j)
         if (kp[j] && (kp[j] >> 21) == d1p) atomicAdd(&hist_p[(kp[j] >> 10) & 0x7FFu], 1u);
     }
     if (cut_b && kb && (kb >> 21) == d1b) atomicAdd(&hist_b[(kb >> 10) & 0x7FFu], 1u);
@@ -525,10 +534,10 @@ __device__ __forceinline__ void emit_segment_pair_abs(const uint32_t *pkeys, int
   };
   // ordered compaction of both segments with one exchange of wave totals
   const uint64_t below = __lanemask_lt();
-  uint64_t bal[8];
+  uint64_t bal[IPT];
   uint32_t wtot_p = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     bal[j] = __ballot(emit(kp[j], cut_p, d1p, d2p));
     wtot_p += (uint32_t)__popcll(bal[j]);
   }
@@ -549,7 +558,7 @@ __device__ __forceinline__ void emit_segment_pair_abs(const uint32_t *pkeys, int
     total_b += xb;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     if ((bal[j] >> lane) & 1u) cand_p[run + (uint32_t)__popcll(bal[j] & below)] = make_uint2(kp[j], pos_p(ip0 + 64 * j));
     run += (uint32_t)__popcll(bal[j]);
   }
@@ -573,6 +582,11 @@ __device__ __forceinline__ void emit_segment_pair_abs(const uint32_t *pkeys, int
 // the window holds fewer than cap items and far items remain, the absolute
 // two-level emission runs instead (it can use more of the budget there).
 constexpr int kRelShift = 12;
+// The relative digits are used when the budget is a small share of the
+// segment (at most 1/50 of its items, e.g. 12 of 2048 at 1M positions);
+// larger budgets reach further below the maximum than the window does for
+// Gaussian-like scores and go straight to the absolute emission.
+__device__ __forceinline__ bool rel_fits(int cap, int items) { return 50 * cap <= items; }
 __device__ __forceinline__ uint32_t rel_bin(uint32_t key, uint32_t m) {
   const uint32_t d = (m - key) >> kRelShift;
   return d >= (uint32_t)(kBins - 1) ? 0u : (uint32_t)(kBins - 1) - d;
@@ -657,6 +671,10 @@ __device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_
   constexpr int NW = NT / 64;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int i0 = 64 * IPT * wave + lane;  // this lane's items: i0 + 64 j
+  if (!rel_fits(cap, NT * IPT)) {  // uniform
+    emit_segment_abs<NT, IPT>(keys_l, cap, cand_seg, info, hist, red, pos_of);
+    return;
+  }
   uint32_t k[IPT];
 #pragma unroll
   for (int j = 0; j < IPT; ++j) k[j] = keys_l[i0 + 64 * j];
@@ -691,6 +709,10 @@ __device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_
 template <int NT, int IPT, class PosOf>
 __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, uint2 *cand_seg, SegInfo *info,
                                              uint32_t (*hist)[kBins], uint32_t *red, PosOf pos_of) {
+  if (!rel_fits(cap, NT * IPT)) {  // uniform
+    emit_segment_abs<NT, IPT>(keys_l, cap, cand_seg, info, hist, red, pos_of);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t k[IPT];
 #pragma unroll
@@ -703,21 +725,27 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
 // (which is also the largest block key): both histograms and both threshold
 // searches (waves 0 and 1) share their barriers.  hist[0..3] zeroed by the
 // caller before a barrier that precedes the call; red: 36 words.
-template <class PosP, class PosB>
+template <int IPT, class PosP, class PosB>
 __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pkeys, int cap_p, uint2 *cand_p,
                                                   SegInfo *info_p, PosP pos_p, const uint32_t *bkeys, int cap_b,
                                                   uint2 *cand_b, SegInfo *info_b, PosB pos_b,
                                                   uint32_t (*hist)[kBins], uint32_t *red) {
   constexpr int NT = 256;
+  // (a block key is the largest of its 8 positions: the best blocks' keys are
+  // among the best positions' keys, so blocks are measured against positions)
+  if (!rel_fits(cap_p, NT * IPT) || !rel_fits(cap_b, NT * IPT)) {  // uniform
+    emit_segment_pair_abs<IPT>(pkeys, cap_p, cand_p, info_p, pos_p, bkeys, cap_b, cand_b, info_b, pos_b, hist, red);
+    return;
+  }
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int ip0 = 64 * 8 * wave + lane, ib = 64 * wave + lane;
-  uint32_t kp[8];
+  const int ip0 = 64 * IPT * wave + lane, ib = 64 * wave + lane;
+  uint32_t kp[IPT];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) kp[j] = pkeys[ip0 + 64 * j];
-  const uint32_t kb1[1] = {bkeys[ib]};
+  for (int j = 0; j < IPT; ++j) kp[j] = pkeys[ip0 + 64 * j];
+  const uint32_t kb1[1] = {ib < 32 * IPT ? bkeys[ib] : 0u};
   const uint32_t kb = kb1[0];
   const uint32_t mp = m, mb = m;
-  rel_hist<8>(kp, mp, hist[0], red + 24);
+  rel_hist<IPT>(kp, mp, hist[0], red + 24);
   rel_hist<1>(kb1, mb, hist[1], red + 28);
   __syncthreads();
   if (wave == 0) find_threshold_wave(hist[0], (uint32_t)cap_p + 1u, red + 16);
@@ -737,15 +765,15 @@ __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pk
     __syncthreads();     // every thread has read red[]
     zero_hists<2>(hist);
     __syncthreads();
-    emit_segment_pair_abs(pkeys, cap_p, cand_p, info_p, pos_p, bkeys, cap_b, cand_b, info_b, pos_b, hist, red);
+    emit_segment_pair_abs<IPT>(pkeys, cap_p, cand_p, info_p, pos_p, bkeys, cap_b, cand_b, info_b, pos_b, hist, red);
     return;
   }
   // ordered compaction of both segments with one exchange of wave totals
   const uint64_t below = __lanemask_lt();
-  uint64_t bal[8];
+  uint64_t bal[IPT];
   uint32_t wtot_p = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     bal[j] = __ballot(kp[j] != 0u && (!cut_p || rel_bin(kp[j], mp) > d1p));
     wtot_p += (uint32_t)__popcll(bal[j]);
   }
@@ -766,7 +794,7 @@ __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pk
     total_b += xb;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < IPT; ++j) {
     if ((bal[j] >> lane) & 1u) cand_p[run + (uint32_t)__popcll(bal[j] & below)] = make_uint2(kp[j], pos_p(ip0 + 64 * j));
     run += (uint32_t)__popcll(bal[j]);
   }
@@ -797,12 +825,17 @@ struct ScanArgs {
   uint32_t *dbg;  // debug flag word, or null
 };
 
-template <int KF, bool HIER>
+// SLICE: positions per workgroup (segment), 2048 or 1024.
+template <int KF, bool HIER, int SLICE>
 __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   constexpr bool F32 = KF == kKeyF32;
-  __shared__ int32_t pg[kScanPages];
-  __shared__ __attribute__((aligned(16))) uint32_t pkey[kScanPos];
-  __shared__ __attribute__((aligned(16))) uint32_t bkey[kScanBlocks];
+  constexpr int kPages = SLICE / kPage;   // 32 or 16
+  constexpr int kPagesPerWave = kPages / 4;
+  constexpr int kBlocks = SLICE / kBlk;   // 256 or 128
+  constexpr int kIpt = SLICE / 256;       // positions per thread in the emission
+  __shared__ int32_t pg[kPages];
+  __shared__ __attribute__((aligned(16))) uint32_t pkey[SLICE];
+  __shared__ __attribute__((aligned(16))) uint32_t bkey[kBlocks];
   // histograms of the emission: positions (level 1, 2) and, hierarchical,
   // blocks (level 1, 2); zeroed while the first loads are in flight
   __shared__ __attribute__((aligned(16))) uint32_t hist[HIER ? 4 : 2][kBins];
@@ -817,14 +850,14 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   }
   const int sl = a.S.seq_lens[b];  // read once: a reload after the key loads would cost a memory round trip
   const int n = sl < 0 ? 0 : (sl > a.S.max_len ? a.S.max_len : sl);
-  const int64_t base = (int64_t)wg * kScanPos;
+  const int64_t base = (int64_t)wg * SLICE;
   if (a.dbg != nullptr && wg == 0 && tid == 0 && (sl < 0 || sl > a.S.max_len)) dbg_raise(a.dbg, kDbgSeqLen);
   if (base >= n) return;  // segments past the row are never read
   zero_hists<HIER ? 4 : 2>(hist);
   if (tid == 0) kmax_l = 0u;
   uint32_t kmax = 0u;  // this lane's largest key
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
-  if (tid < kScanPages) {
+  if (tid < kPages) {
     pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
     if (a.dbg != nullptr && base + 64 * tid < n && pg[tid] < 0) dbg_raise(a.dbg, kDbgPage);
   }
@@ -842,7 +875,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   // four neighbouring pages at a time), one page at a time (8 loads of 1 KB,
   // or for FP4 keys two tiles of 32 positions) with the next page's loads in
   // flight
-  constexpr int kDepth = 2;  // pages whose loads are in flight (deeper measured slower)
+  constexpr int kDepth = 2;  // pages whose loads are in flight (deeper measured slower, also at one workgroup per CU)
   if constexpr (KF == kKeyFp4) {
     if (can_load) {
       Fp4Half kt[kDepth][2];
@@ -854,8 +887,8 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
       };
       issue4(0, kt[0]);
 #pragma unroll
-      for (int pp = 0; pp < 8; ++pp) {
-        if (pp + 1 < 8) issue4(pp + 1, kt[(pp + 1) % kDepth]);
+      for (int pp = 0; pp < kPagesPerWave; ++pp) {
+        if (pp + 1 < kPagesPerWave) issue4(pp + 1, kt[(pp + 1) % kDepth]);
         const int page = 4 * pp + wave;
         const bool mapped = pg[page] >= 0;
 #pragma unroll
@@ -868,7 +901,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
         }
       }
     } else {
-      for (int i = tid; i < kScanPos; i += 256) pkey[i] = 0u;
+      for (int i = tid; i < SLICE; i += 256) pkey[i] = 0u;
     }
   } else {
   KeyLoad kl[kDepth][8];
@@ -882,8 +915,8 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
 #pragma unroll
     for (int pp = 0; pp < kDepth - 1; ++pp) issue(pp, kl[pp]);
 #pragma unroll
-    for (int pp = 0; pp < 8; ++pp) {
-      if (pp + kDepth - 1 < 8) issue(pp + kDepth - 1, kl[(pp + kDepth - 1) % kDepth]);
+    for (int pp = 0; pp < kPagesPerWave; ++pp) {
+      if (pp + kDepth - 1 < kPagesPerWave) issue(pp + kDepth - 1, kl[(pp + kDepth - 1) % kDepth]);
       const int page = 4 * pp + wave;
       const bool mapped = pg[page] >= 0;
 #pragma unroll
@@ -896,13 +929,13 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
       }
     }
   } else {
-    for (int i = tid; i < kScanPos; i += 256) pkey[i] = 0u;
+    for (int i = tid; i < SLICE; i += 256) pkey[i] = 0u;
   }
   }
   kmax = wave_last(wave_inclusive_max(kmax));
   if (lane == 0) atomicMax(&kmax_l, kmax);
   __syncthreads();
-  if (a.new_key != nullptr && sl - 1 >= base && sl - 1 < base + kScanPos &&
+  if (a.new_key != nullptr && sl - 1 >= base && sl - 1 < base + SLICE &&
       sl <= n) {  // uniform: this workgroup holds the appended position
     const int lp = sl - 1 - (int)base;
     if (wave == 0 && pg[lp / kPage] >= 0) {
@@ -948,30 +981,34 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   }
   if constexpr (HIER) {
     // block key = largest key of its 8 positions (unmapped or past-the-end positions hold key 0)
-    const u32x4 *p4 = reinterpret_cast<const u32x4 *>(pkey + kBlk * tid);
-    const u32x4 x = p4[0], y = p4[1];
-    uint32_t m = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(y[0], y[1]), max(y[2], y[3])));
-    bkey[tid] = m;  // (read back only by this thread: the key store and the emission's block item tid)
+    if (tid < kBlocks) {
+      const u32x4 *p4 = reinterpret_cast<const u32x4 *>(pkey + kBlk * tid);
+      const u32x4 x = p4[0], y = p4[1];
+      uint32_t m = max(max(max(x[0], x[1]), max(x[2], x[3])), max(max(y[0], y[1]), max(y[2], y[3])));
+      bkey[tid] = m;  // (read back only by this thread: the key store and the emission's block item tid)
+    }
   }
   // store every key (the select re-reads segments that overflow their budget)
   {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(pkey);
     u32x4 *dst = reinterpret_cast<u32x4 *>(a.w.keys + (size_t)b * a.w.cap_keys + base);
-    dst[tid] = src[tid];
-    dst[tid + 256] = src[tid + 256];
-    if constexpr (HIER) a.w.bkeys[(size_t)b * a.w.cap_blocks + base / kBlk + tid] = bkey[tid];
+#pragma unroll
+    for (int i = 0; i < SLICE / 4 / 256; ++i) dst[tid + 256 * i] = src[tid + 256 * i];
+    if constexpr (HIER) {
+      if (tid < kBlocks) a.w.bkeys[(size_t)b * a.w.cap_blocks + base / kBlk + tid] = bkey[tid];
+    }
   }
-  const int nseg = (n + kScanPos - 1) / kScanPos;
-  const int cap = seg_budget(a.K, nseg, kScanPos);
+  const int nseg = (n + SLICE - 1) / SLICE;
+  const int cap = seg_budget(a.K, nseg, SLICE);
   if constexpr (HIER) {
-    const int cap_b = seg_budget(a.P, nseg, kScanBlocks);
-    emit_segment_pair(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+    const int cap_b = seg_budget(a.P, nseg, kBlocks);
+    emit_segment_pair<kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
                       bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
                       a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
                       hist, red);
   } else {
-    emit_segment_m<256, 8>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+    emit_segment_m<256, kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                            a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
                            [&](int i) { return (uint32_t)(base + i); });
   }
@@ -1547,8 +1584,9 @@ __device__ __forceinline__ uint32_t wave_exclusive_scan(uint32_t v, uint32_t *to
 
 // One wave walks every stored item of segment s in position order and counts
 // (FILL false) or writes to ck/cp from dst on (FILL true) those with a
-// non-zero key >= floor_key.  Key segments hold ips = 256 or 2048 keys (one
-// 16-byte load per lane per 256), pair segments ips = 128 pairs.
+// non-zero key >= floor_key.  Key segments hold ips = 128, 256, 1024 or 2048
+// keys (one 16-byte load per lane per 256; with 128, lanes 0..31 only), pair
+// segments ips = 128 pairs.
 template <bool FILL>
 __device__ __forceinline__ uint32_t wave_segment(SelSmem &sm, const Stream &st, int s, uint32_t floor_key, uint32_t dst) {
   const int lane = threadIdx.x & 63;
@@ -1576,24 +1614,26 @@ __device__ __forceinline__ uint32_t wave_segment(SelSmem &sm, const Stream &st, 
     }
   } else {
     const u32x4 *src = reinterpret_cast<const u32x4 *>(st.full_keys + (size_t)s * st.ips);
-    const int steps = st.ips / 256;  // 1 or 8
+    const int steps = (st.ips + 255) / 256;   // 1, 4 or 8
+    const bool lane_ok = st.ips >= 256 || 4 * lane < st.ips;  // 128 keys: lanes 0..31
     for (int u0 = 0; u0 < steps; u0 += 4) {
     u32x4 v[4];
 #pragma unroll
-    for (int du = 0; du < 4; ++du) v[du] = src[64 * (u0 + du < steps ? u0 + du : u0) + lane];  // loads first
+    for (int du = 0; du < 4; ++du)  // loads first (a masked lane reads the segment's first keys)
+      v[du] = src[lane_ok ? 64 * (u0 + du < steps ? u0 + du : u0) + lane : 0];
 #pragma unroll
     for (int du = 0; du < 4; ++du) {
       const int u = u0 + du;
       if (u >= steps) break;
       uint32_t c = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c += (v[du][e] != 0u && v[du][e] >= floor_key) ? 1u : 0u;
+      for (int e = 0; e < 4; ++e) c += (lane_ok && v[du][e] != 0u && v[du][e] >= floor_key) ? 1u : 0u;
       uint32_t tot;
       uint32_t o = run + wave_exclusive_scan(c, &tot);
       if constexpr (FILL) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (v[du][e] != 0u && v[du][e] >= floor_key) {
+          if (lane_ok && v[du][e] != 0u && v[du][e] >= floor_key) {
             sm.ck[dst + o] = v[du][e];
             sm.cp[dst + o] = (uint32_t)((int64_t)s * st.ips + 256 * u + 4 * lane + e);
             ++o;
@@ -1847,8 +1887,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelArgs a) {
   st.info = (blk ? w.seg_blk : w.seg_pos) + (size_t)b * w.max_seg;
   st.full_keys = re ? nullptr : (blk ? w.bkeys + (size_t)b * w.cap_blocks : w.keys + (size_t)b * w.cap_keys);
   st.full_pairs = re ? w.pool_full + (size_t)b * kMaxPoolItems : nullptr;
-  st.nseg = re ? (a.P + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg : (n + kScanPos - 1) / kScanPos;
-  st.ips = re ? kPoolItemsPerWg : (blk ? kScanBlocks : kScanPos);
+  st.nseg = re ? (a.P + kPoolBlocksPerWg - 1) / kPoolBlocksPerWg : (n + w.slice - 1) / w.slice;
+  st.ips = re ? kPoolItemsPerWg : (blk ? w.slice / kBlk : w.slice);
   st.items = re ? (int64_t)a.P * kBlk : (blk ? (n + kBlk - 1) / kBlk : n);
   const int need = blk ? a.P : a.K;
   int32_t *out = blk ? a.pool_out + (size_t)b * a.P : a.out[blockIdx.z] + (size_t)b * a.K;
@@ -1951,12 +1991,12 @@ hipError_t run_reindex(const KvLayerDev &L, const SeqsDev &S, const IdxQuery *q,
 
 size_t topk_workspace_bytes(int batch, int max_items, int top_k) {
   (void)top_k;
-  return ws_bytes_for(batch, ws_shape(max_items, 0));
+  return ws_bytes_for(batch, ws_shape(batch, max_items, 0, false));
 }
 
 size_t index_select_workspace_bytes(int batch, int max_len, int top_k, int pool_blocks) {
   (void)top_k;
-  return ws_bytes_for(batch, ws_shape(max_len, pool_blocks));
+  return ws_bytes_for(batch, ws_shape(batch, max_len, pool_blocks, true));
 }
 
 hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, IdxQuery q, float *scores, hipStream_t st) {
@@ -1985,7 +2025,7 @@ hipError_t launch_index_scores(const KvLayerDev &L, const SeqsDev &S, IdxQuery q
 hipError_t launch_topk_scores(const float *scores, int64_t stride, const int32_t *lens, int batch, int max_len,
                               int top_k, int32_t *indices, void *ws, hipStream_t st) {
   if (batch <= 0) return hipSuccess;
-  const WsShape sh = ws_shape(max_len, 0);
+  const WsShape sh = ws_shape(batch, max_len, 0, false);
   SelWs w = carve(ws, batch, sh);
   GivenArgs g{scores, stride, lens, max_len, top_k, w, debug_flags()};
   const int gx = (int)(sh.cap_keys / kScanPos);
@@ -2009,7 +2049,7 @@ hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQu
                                     hipStream_t st, const AppendRow *app, int n_app, const void *new_key) {
   if (S.batch <= 0) return hipSuccess;
   const bool hier = pool_out != nullptr;
-  const WsShape sh = ws_shape(S.max_len, hier ? pool_blocks : 0);
+  const WsShape sh = ws_shape(S.batch, S.max_len, hier ? pool_blocks : 0, true);
   SelWs w = carve(ws, S.batch, sh);
   ScanArgs a{};
   a.L = L;
@@ -2018,7 +2058,7 @@ hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQu
   a.K = top_k;
   a.P = pool_blocks;
   a.w = w;
-  const int gx = (int)(sh.cap_keys / kScanPos);
+  const int gx = (int)(sh.cap_keys / sh.slice);
   a.scan_wgs = gx;
   a.n_app = n_app;
   for (int i = 0; i < n_app; ++i) a.app[i] = app[i];
@@ -2026,16 +2066,23 @@ hipError_t launch_index_select_full(const KvLayerDev &L, const SeqsDev &S, IdxQu
   a.dbg = debug_flags();
   timer_before(kKernIndexScan, st);
   const dim3 grid(gx + n_app, S.batch);
+  const bool half = sh.slice != kScanPos;
+#define CSA2_SCAN(KF, H)                                                        \
+  do {                                                                          \
+    if (half) scan_kernel<KF, H, kScanPos / 2><<<grid, dim3(256), 0, st>>>(a);  \
+    else scan_kernel<KF, H, kScanPos><<<grid, dim3(256), 0, st>>>(a);           \
+  } while (0)
   if (L.idx_fp4) {
-    if (hier) scan_kernel<kKeyFp4, true><<<grid, dim3(256), 0, st>>>(a);
-    else scan_kernel<kKeyFp4, false><<<grid, dim3(256), 0, st>>>(a);
+    if (hier) CSA2_SCAN(kKeyFp4, true);
+    else CSA2_SCAN(kKeyFp4, false);
   } else if (L.idx_f32) {
-    if (hier) scan_kernel<kKeyF32, true><<<grid, dim3(256), 0, st>>>(a);
-    else scan_kernel<kKeyF32, false><<<grid, dim3(256), 0, st>>>(a);
+    if (hier) CSA2_SCAN(kKeyF32, true);
+    else CSA2_SCAN(kKeyF32, false);
   } else {
-    if (hier) scan_kernel<kKeyBf16, true><<<grid, dim3(256), 0, st>>>(a);
-    else scan_kernel<kKeyBf16, false><<<grid, dim3(256), 0, st>>>(a);
+    if (hier) CSA2_SCAN(kKeyBf16, true);
+    else CSA2_SCAN(kKeyBf16, false);
   }
+#undef CSA2_SCAN
   timer_after(kKernIndexScan, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -2054,7 +2101,7 @@ hipError_t launch_index_select_reindex(const KvLayerDev &L, const SeqsDev &S, Id
                                        const int32_t *pool_in, int pool_blocks, int32_t *indices, void *ws,
                                        hipStream_t st) {
   if (S.batch <= 0) return hipSuccess;
-  const WsShape sh = ws_shape(S.max_len, pool_blocks);
+  const WsShape sh = ws_shape(S.batch, S.max_len, pool_blocks, true);
   SelWs w = carve(ws, S.batch, sh);
   return run_reindex(L, S, &q_idx, &w, &indices, 1, top_k, pool_in, pool_blocks, st);
 }
