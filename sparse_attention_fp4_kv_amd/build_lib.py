@@ -7,6 +7,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -33,15 +34,47 @@ def hipcc():
     raise RuntimeError("hipcc not found: libcsa2 needs the ROCm toolchain to build")
 
 
-def build(verbose=False):
-    """Compile every HIP source into libcsa2.so next to this file (always rebuilds)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES] + LIBS
+# Per-source device flags.  The indexer's MFMA results feed VALU epilogues
+# (ReLU and head weights), so its MFMAs write VGPRs instead of AGPRs (no
+# v_accvgpr_read per result); the attention and CED kernels keep their
+# accumulators in AGPRs.
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (res.stderr or "").splitlines() if noise not in l)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + err)
+    return err
+
+
+def build(verbose=False):
+    """Compile every HIP source into libcsa2.so next to this file (always rebuilds): one object
+    per source (compiled in parallel, with its own flags), then one link."""
+    tmp = LIB + ".tmp"
+    objdir = tempfile.mkdtemp(prefix="csa2_build_")
+    try:
+        compile_flags = [f for f in FLAGS if f != "-shared"]
+        procs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(objdir, src + ".o")
+            objs.append(obj)
+            cmd = [hipcc()] + compile_flags + FILE_FLAGS.get(src, []) + ["-c", "-o", obj, os.path.join(CSRC, src)]
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        noise = "is not a recognized feature for this target"
+        errs = []
+        for cmd, p in procs:
+            out, err = p.communicate()
+            err = "\n".join(l for l in (err or "").splitlines() if noise not in l)
+            if p.returncode != 0:
+                raise RuntimeError("hipcc failed:\n" + err)
+            errs.append(err)
+        errs.append(_run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs + LIBS))
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    err = "\n".join(e for e in errs if e.strip())
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)

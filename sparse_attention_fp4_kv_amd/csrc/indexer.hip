@@ -288,9 +288,12 @@ __device__ __forceinline__ float fp4_tile_score(const Fp4Half &k, const Fp4Query
   f32x16 acc = {};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(Q.qa[ks], deq8(words[ks], sc[ks >> 1]), acc, 0, 0, 0);
+  // max(x, 0) as the signed-integer maximum of the fp32 bits (negative values
+  // and -0 have the sign bit set, so they become +0): one instruction, where
+  // fmaxf also canonicalizes its input
   float part = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) part = fmaf(Q.wr[e], fmaxf(acc[e], 0.0f), part);
+  for (int e = 0; e < 16; ++e) part = fmaf(Q.wr[e], __int_as_float(max(__float_as_int(acc[e]), 0)), part);
   return part + __shfl_xor(part, 32);
 }
 
@@ -833,6 +836,10 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   constexpr int kPagesPerWave = kPages / 4;
   constexpr int kBlocks = SLICE / kBlk;   // 256 or 128
   constexpr int kIpt = SLICE / 256;       // positions per thread in the emission
+  // relative-digit emission for bf16 / fp32 keys; the FP4 multi-head scan is
+  // bound by VALU issue in its loads, where tracking the maximum cost more
+  // than the emission saved (two-level emission there)
+  constexpr bool kRel = KF != kKeyFp4;
   __shared__ int32_t pg[kPages];
   __shared__ __attribute__((aligned(16))) uint32_t pkey[SLICE];
   __shared__ __attribute__((aligned(16))) uint32_t bkey[kBlocks];
@@ -895,9 +902,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
         for (int j = 0; j < 2; ++j) {
           const int lp = page * kPage + 32 * j + (lane & 31);  // local position
           const float sc = fp4_tile_score(kt[pp % kDepth][j], Q);
-          const uint32_t key = (lane < 32 && mapped && base + lp < n) ? score_key(sc) : 0u;
-          kmax = max(kmax, key);
-          if (lane < 32) pkey[lp] = key;
+          if (lane < 32) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
         }
       }
     } else {
@@ -932,8 +937,10 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     for (int i = tid; i < SLICE; i += 256) pkey[i] = 0u;
   }
   }
-  kmax = wave_last(wave_inclusive_max(kmax));
-  if (lane == 0) atomicMax(&kmax_l, kmax);
+  if constexpr (kRel) {
+    kmax = wave_last(wave_inclusive_max(kmax));
+    if (lane == 0) atomicMax(&kmax_l, kmax);
+  }
   __syncthreads();
   if (a.new_key != nullptr && sl - 1 >= base && sl - 1 < base + SLICE &&
       sl <= n) {  // uniform: this workgroup holds the appended position
@@ -1002,15 +1009,28 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   const int cap = seg_budget(a.K, nseg, SLICE);
   if constexpr (HIER) {
     const int cap_b = seg_budget(a.P, nseg, kBlocks);
-    emit_segment_pair<kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+    if constexpr (kRel) {
+      emit_segment_pair<kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
                       bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
                       a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
                       hist, red);
+    } else {
+      emit_segment_pair_abs<kIpt>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                      a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
+                      bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
+                      a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
+                      hist, red);
+    }
   } else {
-    emit_segment_m<256, kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
-                           a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
-                           [&](int i) { return (uint32_t)(base + i); });
+    if constexpr (kRel)
+      emit_segment_m<256, kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                                a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
+                                [&](int i) { return (uint32_t)(base + i); });
+    else
+      emit_segment_abs<256, kIpt>(pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+                                  a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
+                                  [&](int i) { return (uint32_t)(base + i); });
   }
 }
 
