@@ -210,7 +210,13 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
   constexpr int KS = QW / 32;                  // 16 or 18 k-steps of 32 channels
   constexpr int KP = kKParts<MT>;              // waves splitting the k-steps of one logit tile
   constexpr int QKS = (KS + KP - 1) / KP;      // k-steps per wave (the last part may be shorter)
-  constexpr int QNT = MT == 4 ? 2 : 1;         // N-tiles of 16 entries per wave
+  // M-tiles (16 heads) x N-tiles (16 entries) of one wave's QK^T: with 64
+  // heads and no rope a wave takes 2 M-tiles of one N-tile, so each K
+  // fragment it reads from LDS feeds two MFMAs (the tile is read twice per
+  // pass, not 4x); with rope the second M-tile's q fragments would not fit in
+  // registers, so a wave takes one M-tile of both N-tiles
+  constexpr int QMT = MT == 4 && !ROPE ? 2 : 1;
+  constexpr int QNT = MT == 4 && ROPE ? 2 : 1;
   constexpr bool kEvenParts = KS % KP == 0;    // every k-part has QKS k-steps
   __shared__ Smem<MT, LD> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -236,11 +242,13 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
   const int e_count = win ? kT : max(0, min(tile_end * kT, a.top_k) - e_begin);
   const int32_t *idx_row = J.idx + (size_t)b * a.top_k;
 
-  // ---- QK^T work of this wave: M-tile qk_mt (16 heads), N-tiles qk_nt0 ..
-  // qk_nt0 + QNT - 1 (16 entries each), k-part qk_kp (k-steps qk_k0 .. qk_k1 - 1);
+  // ---- QK^T work of this wave: M-tiles qk_mt .. qk_mt + QMT - 1 (16 heads
+  // each), N-tiles qk_nt0 .. qk_nt0 + QNT - 1 (16 entries each), k-part qk_kp
+  // (k-steps qk_k0 .. qk_k1 - 1);
   // the KP partial logits of an entry are added when the softmax reads them
   int qk_mt, qk_nt0, qk_kp;
-  if constexpr (MT == 4) { qk_mt = wave & 3; qk_nt0 = 0; qk_kp = wave >> 2; }
+  if constexpr (MT == 4 && QMT == 2) { qk_mt = 2 * (wave & 1); qk_nt0 = (wave >> 1) & 1; qk_kp = wave >> 2; }
+  else if constexpr (MT == 4) { qk_mt = wave & 3; qk_nt0 = 0; qk_kp = wave >> 2; }
   else if constexpr (MT == 2) { qk_mt = wave & 1; qk_nt0 = (wave >> 1) & 1; qk_kp = wave >> 2; }
   else { qk_mt = 0; qk_nt0 = wave & 1; qk_kp = wave >> 1; }
   const int qk_k0 = qk_kp * QKS;
@@ -263,23 +271,32 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
     }
   }
 
-  // q fragments (A operand): head 16*qk_mt + lane%16, channels 32*(qk_k0 + ks) + 8*(lane/16) .. +7
-  f16x8 qf[QKS];
+  // q fragments (A operand) of M-tile qk_mt + i: head 16*(qk_mt + i) + lane%16,
+  // channels 32*(qk_k0 + ks) + 8*(lane/16) .. +7
+  f16x8 qf[QMT][QKS];
   {
-    const uint16_t *qrow =
-        J.q + ((size_t)b * a.heads + h0 + 16 * qk_mt + (lane & 15)) * QW + 32 * qk_k0 + 8 * (lane >> 4);
-    uint4 raw[QKS];
+    uint4 raw[QMT][QKS];
 #pragma unroll
-    for (int ks = 0; ks < QKS; ++ks) raw[ks] = (kEvenParts || ks < qk_kn) ? *reinterpret_cast<const uint4 *>(qrow + 32 * ks)
-                                                                         : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < QMT; ++i) {
+      const uint16_t *qrow =
+          J.q + ((size_t)b * a.heads + h0 + 16 * (qk_mt + i) + (lane & 15)) * QW + 32 * qk_k0 + 8 * (lane >> 4);
 #pragma unroll
-    for (int ks = 0; ks < QKS; ++ks) qf[ks] = bf16x8_to_f16x8(raw[ks]);
+      for (int ks = 0; ks < QKS; ++ks)
+        raw[i][ks] = (kEvenParts || ks < qk_kn) ? *reinterpret_cast<const uint4 *>(qrow + 32 * ks)
+                                                : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < QMT; ++i)
+#pragma unroll
+      for (int ks = 0; ks < QKS; ++ks) qf[i][ks] = bf16x8_to_f16x8(raw[i][ks]);
     if (a.dbg != nullptr) {  // a bf16 magnitude above fp16's largest finite value (65504)
       bool big = false;
 #pragma unroll
-      for (int ks = 0; ks < QKS; ++ks)
+      for (int i = 0; i < QMT; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) big |= !(fabsf((float)qf[ks][e]) <= 65504.0f);
+        for (int ks = 0; ks < QKS; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) big |= !(fabsf((float)qf[i][ks][e]) <= 65504.0f);
       if (big) dbg_raise(a.dbg, kDbgQRange);
       if (split == 0 && hg == 0 && tid == 0 && (J.L.num_blocks < 0 || a.S.seq_lens[b] < 0 ||
                                                   a.S.seq_lens[b] > a.S.max_len))
@@ -420,12 +437,15 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
     // 1. partial logits S_kp = Q C^T over this wave's k-part; even and odd
     // k-steps of every N-tile accumulate separately (2 or 4 independent MFMA
     // chains), the B fragments of 4 k-steps read together ahead of them
-    f32x4 sacc[QNT][2];
+    f32x4 sacc[QMT][QNT][2];
     const f16 *brow[QNT];
 #pragma unroll
     for (int j = 0; j < QNT; ++j) {
-      sacc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < QMT; ++i) {
+        sacc[i][j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[i][j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       brow[j] = &cq[16 * (qk_nt0 + j) + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
     }
 #pragma unroll
@@ -441,18 +461,23 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int j = 0; j < QNT; ++j)
-          if (k0 + kk < QKS)
-            sacc[j][kk & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[k0 + kk], bq[j][kk], sacc[j][kk & 1], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < QMT; ++i)
+            if (k0 + kk < QKS)
+              sacc[i][j][kk & 1] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[i][k0 + kk], bq[j][kk], sacc[i][j][kk & 1], 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < QNT; ++j) {
-      const int nt = qk_nt0 + j;
-      const f32x4 sa = sacc[j][0] + sacc[j][1];
-      // lane holds S_kp[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
-      const int ent = 16 * nt + (lane & 15);
+    for (int j = 0; j < QNT; ++j)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) sm.s[qk_kp][16 * qk_mt + 4 * (lane >> 4) + rr][ent] = sa[rr];
-    }
+      for (int i = 0; i < QMT; ++i) {
+        const int nt = qk_nt0 + j;
+        const f32x4 sa = sacc[i][j][0] + sacc[i][j][1];
+        // lane holds S_kp[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
+        const int ent = 16 * nt + (lane & 15);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sm.s[qk_kp][16 * (qk_mt + i) + 4 * (lane >> 4) + rr][ent] = sa[rr];
+      }
     if (next != nullptr) dequant(*next, cq_next);
     __syncthreads();
     // 2. online softmax: logit = scale * (sum of the k-parts), masked entries -inf
