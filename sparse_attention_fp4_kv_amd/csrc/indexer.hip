@@ -14,13 +14,15 @@
 // item order is (key descending, position ascending), so ties go to the lower
 // position.  No global atomics, fences or inter-workgroup waits are used: on
 // gfx950 they cost more than a kernel boundary.
-//   producers  Each workgroup owns a fixed slice of a row (2048 positions of a
-//              full scan, 2048 given scores, or 16 pool blocks), keeps its keys
-//              in LDS and stores all of them.  It then emits its best items as
-//              a candidate segment, cut exactly with two 11-bit radix levels to
-//              a budget of about 3x its expected share of the top-K, plus the
-//              segment's edge: every item it did not emit has a key below the
-//              edge.  The full scan streams the keys with non-temporal 16-byte
+//   producers  Each workgroup owns a fixed slice of a row (2048 or 1024
+//              positions of a full scan, 2048 given scores, or 16 pool blocks),
+//              keeps its keys in LDS and stores all of them.  It then emits its
+//              best items as a candidate segment, cut exactly to a budget of
+//              about 3x its expected share of the top-K, plus the segment's
+//              edge: every item it did not emit has a key below the edge.  The
+//              cut uses one histogram level of 2^12-unit bins counted down from
+//              the slice's largest key when the budget is small (the common
+//              decode case), else two 11-bit radix levels of the absolute key.  The full scan streams the keys with non-temporal 16-byte
 //              loads, 16 in flight per lane, after one page-table lookup per
 //              64 positions; loads are never guarded by branches (unmapped
 //              pages read slot 0 and are masked).  In hierarchical mode it
