@@ -25,11 +25,13 @@ namespace csa2 {
 
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int kLdA = BK + 8;   // bf16 per LDS row (pad breaks bank conflicts)
-constexpr int kWM = 128, kWN = 64;  // wave tile: 4 x 2 MFMA tiles of 32 x 32
-constexpr int kLdC = BN + 4;   // fp32 per epilogue row (128 rows at a time)
-constexpr int kGroupM = 8;     // row tiles an XCD sweeps across the columns together
+constexpr int BM = 256, BN = 256, BK = 32;  // workgroup tile, k-step
+constexpr int kStages = 4;                   // LDS stages in flight
+constexpr int kWM = 128, kWN = 64;           // wave tile: 4 x 2 MFMA tiles of 32 x 32
+constexpr int kThreads = 512;                // 8 waves: 2 (rows) x 4 (columns)
+constexpr int kRowsEpi = 64;                 // output rows parked in LDS per epilogue round
+constexpr int kLdC = BN + 4;                 // fp32 per epilogue row
+constexpr int kGroupM = 8;                   // row tiles an XCD sweeps across the columns together
 constexpr int kXcds = 8;
 // output columns per layer: 512 of C, then 64 of Z when W^Z is given
 __device__ __forceinline__ int per_layer(const void *w_z) { return w_z != nullptr ? kLatent + kIdxDim : kLatent; }
@@ -47,27 +49,48 @@ struct CedArgs {
   float *c_f32;
 };
 
-// Row n of the combined weight matrix, or null for a Z row without weights.
+// Row n (< the total column count) of the combined weight matrix.
 __device__ __forceinline__ const uint16_t *weight_row(const CedArgs &a, int n) {
   const int npl = per_layer(a.w_z);
   const int l = n / npl, c = n % npl;
   if (c < kLatent) return a.w_kv + ((size_t)l * kLatent + c) * a.hidden;
-  if (a.w_z == nullptr) return nullptr;
   return a.w_z + ((size_t)l * kIdxDim + (c - kLatent)) * a.hidden;
 }
 
+// One k-step stage: rows 0..255 hold the A tile (tokens), 256..511 the B tile
+// (output columns), 32 bf16 of k each (64 bytes = four 16-byte chunks).  The
+// chunks of a row are stored in a row-dependent order (chunk c at position
+// c ^ swz(row)), so that the 16 lanes of one phase of a fragment read (16
+// consecutive rows, one logical chunk) hit 16 different 16-byte bank groups
+// with 64 banks, and 8 lanes hit 8 with 32.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 union SmemCed {
-  struct {
-    uint16_t a[1][BM][kLdA];  // one buffer: the next k-step waits in registers
-    uint16_t b[1][BN][kLdA];
-  } ab;
-  float c[kWM][kLdC];  // half of the output tile at a time in the epilogue
+  uint16_t st[kStages][BM + BN][BK];  // 4 x 32 KB
+  float c[kRowsEpi][kLdC];            // one epilogue round (66.5 KB)
 };
 
-// 256 x 128 output tile per workgroup, 4 waves of 128 x 64 (8 independent
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: expcnt and
+// lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+// Workgroup barrier that orders the LDS accesses around it (the compiler may
+// not move memory operations across it) without waiting for outstanding
+// global-to-LDS loads the way a fenced barrier would.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
+
+// 256 x 256 output tile per workgroup, 8 waves of 128 x 64 (8 independent
 // 32 x 32 accumulators per wave: each A fragment feeds 2 MFMAs, each B
-// fragment 4); two workgroups fit one CU.
-__global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
+// fragment 4).  The tiles travel from global memory straight into LDS
+// (global_load_lds_dwordx4: 16 bytes per lane, a wave's 64 lanes fill 1 KB =
+// 16 rows of a stage), three k-steps ahead of the one being multiplied.
+__global__ void __launch_bounds__(kThreads) ced_kernel(CedArgs a) {
   __shared__ __attribute__((aligned(16))) SmemCed sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Tile order: the hardware deals workgroups to the 8 XCDs round-robin by
@@ -85,38 +108,44 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
   const int64_t m0 = (int64_t)(first_m + u % gm) * BM;
   const int n0 = (u / gm) * BN;
   const int n_total = a.n_layers * per_layer(a.w_z);
-  const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
+  const int wm = (wave >> 2) * kWM, wn = (wave & 3) * kWN;
 
-  // global -> register staging: a thread loads rows (tid / 8) + 32 i of A (i < 8) and of
-  // B (i < 4), 16-byte column chunk tid % 8
-  const int ld_row = tid >> 3, ld_col = 8 * (tid & 7);
-  const uint16_t *a_src[8];
-  const uint16_t *b_src[4];
+  // ---- loads: the 32 row groups of 16 rows of a stage, 4 per wave; lane i
+  // fetches row 16 g + i / 4, stored chunk i % 4 = logical chunk (i % 4) ^ swz
+  const uint16_t *src[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + ld_row + 32 * i;
-    a_src[i] = m < a.tokens ? a.h + m * a.hidden + ld_col : nullptr;
+  for (int q = 0; q < 4; ++q) {
+    const int g = 4 * wave + q;         // row group (0..15: A, 16..31: B)
+    const int r = 16 * (g & 15) + (lane >> 2);
+    const int chunk = (lane & 3) ^ swz(r);
+    if (g < 16) {
+      const int64_t m = min(m0 + r, a.tokens - 1);  // rows past the end are read from the last one, not stored
+      src[q] = a.h + m * a.hidden + 8 * chunk;
+    } else {
+      const int n = min(n0 + r, n_total - 1);
+      src[q] = weight_row(a, n) + 8 * chunk;
+    }
   }
+  auto issue = [&](int stage, int k0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = n0 + ld_row + 32 * i;
-    b_src[i] = n < n_total ? weight_row(a, n) : nullptr;
-    if (b_src[i]) b_src[i] += ld_col;
-  }
-  uint4 ra[8], rb[4];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      const int g = 4 * wave + q;
+      __builtin_amdgcn_global_load_lds((glb_void *)(src[q] + k0), (lds_void *)&sm.st[stage][16 * g][0], 16, 0, 0);
+    }
+  };
+
+  // fragment reads: lane l takes row (l % 32) of a 32-row tile and logical
+  // chunk 2 kk + l / 32 of k-step half kk, stored at chunk ^ swz(row), and
+  // swz(row) depends only on l % 16 here
+  const int fsw = swz(lane & 15);
+  auto frags = [&](int stage, int kk, bf16x8 (&fa)[4], bf16x8 (&fb)[2]) {
+    const int ch = (2 * kk + (lane >> 5)) ^ fsw;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      rb[i] = b_src[i] ? *reinterpret_cast<const uint4 *>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
-  };
-  auto stash = [&](int buf) {
+      fa[i] = *reinterpret_cast<const bf16x8 *>(&sm.st[stage][wm + 32 * i + (lane & 31)][8 * ch]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4 *>(&sm.ab.a[buf][ld_row + 32 * i][ld_col]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4 *>(&sm.ab.b[buf][ld_row + 32 * i][ld_col]) = rb[i];
+    for (int j = 0; j < 2; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8 *>(&sm.st[stage][BM + wn + 32 * j + (lane & 31)][8 * ch]);
   };
 
   f32x16 acc[4][2];
@@ -126,61 +155,100 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
 
+  // ---- pipeline (k_steps = hidden / 32 >= 2).  Stage s lives in buffer
+  // s % 4.  Iteration s: read the second half of stage s, multiply the first;
+  // wait for this wave's loads of stage s + 1 and pass a barrier (then every
+  // wave's stage s + 1 has landed and every wave is done with stage s - 1);
+  // start the loads of stage s + 3 into stage s - 1's buffer; read the first
+  // half of stage s + 1; multiply the second half of stage s.
   const int k_steps = a.hidden / BK;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int ks = 0; ks < k_steps; ++ks) {
-    const int buf = 0;
-    if (ks + 1 < k_steps) fetch((ks + 1) * BK);
+  issue(0, 0);
+  issue(1, BK);
+  if (k_steps > 2) {
+    issue(2, 2 * BK);
+    wait_vm<8>();
+  } else {
+    wait_vm<4>();
+  }
+  barrier_lds();
+  bf16x8 fa0[4], fb0[2], fa1[4], fb1[2];
+  frags(0, 0, fa0, fb0);
+  int s = 0;
+  // steady state: no conditions in the body, so the fragment reads of the
+  // next stage stay in flight while the second half's MFMAs wait only for
+  // their own reads
+  for (; s + 3 < k_steps; ++s) {
+    frags(s & (kStages - 1), 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    // schedule: the second half's 6 fragment reads go out between the first
+    // MFMAs, so they land while the rest of the first half runs
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[4], fb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8 *>(&sm.ab.a[buf][wm + 32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8 *>(&sm.ab.b[buf][wn + 32 * j + (lane & 31)][kk + 8 * (lane >> 5)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    // scheduling: spread the k-step's 24 LDS reads and 12 global loads between its 32 MFMAs
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __syncthreads();  // every wave is done reading the tile
-    if (ks + 1 < k_steps) stash(0);
-    __syncthreads();
+    __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+    wait_vm<4>();  // stage s + 2's loads may still be in flight
+    barrier_lds();
+    issue((s + 3) & (kStages - 1), (s + 3) * BK);
+    frags((s + 1) & (kStages - 1), 0, fa0, fb0);
+    mfmas(fa1, fb1);
+    // schedule: the 4 loads and the next stage's 6 fragment reads between
+    // the second half's MFMAs
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  for (; s < k_steps; ++s) {  // the last (at most 3) stages: nothing left to load
+    frags(s & (kStages - 1), 1, fa1, fb1);
+    mfmas(fa0, fb0);
+    if (s + 1 < k_steps) {
+      if (s + 2 < k_steps) wait_vm<4>();
+      else wait_vm<0>();
+      barrier_lds();
+      frags((s + 1) & (kStages - 1), 0, fa0, fb0);
+    }
+    mfmas(fa1, fb1);
   }
 
-  // ---- epilogue: 128 rows at a time -> LDS -> pack / round / store
+  // ---- epilogue: 64 rows at a time -> LDS -> pack / round / store
   // lane holds out[wm + 32i + 8*(e/4) + 4*(lane/32) + e%4][wn + 32j + lane%32]
+  __syncthreads();  // the last stage's fragment reads are done before the union is reused
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if ((wave >> 1) == half) {
+  for (int q = 0; q < BM / kRowsEpi; ++q) {
+    if ((wave >> 2) == (q >> 1)) {  // the waves holding rows 64 q .. 64 q + 63
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * (q & 1) + ii;
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            sm.c[32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][wn + 32 * j + (lane & 31)] = acc[i][j][e];
+            sm.c[32 * ii + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][wn + 32 * j + (lane & 31)] = acc[i][j][e];
+      }
     }
     __syncthreads();
-    // 128 rows x 8 groups of 16 columns = 1024 groups, 4 per thread
+    // 64 rows x 16 groups of 16 columns = 1024 groups, 2 per thread
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int g = tid + 256 * it;
-      const int r = g >> 3, cg = g & 7;
-      const int64_t t = m0 + kWM * half + r;
+    for (int it = 0; it < 2; ++it) {
+      const int g = tid + kThreads * it;
+      const int r = g >> 4, cg = g & 15;
+      const int64_t t = m0 + kRowsEpi * q + r;
       const int n = n0 + 16 * cg;
       if (t >= a.tokens || n >= n_total) continue;
       float v[16];
@@ -200,7 +268,7 @@ __global__ void __launch_bounds__(256) ced_kernel(CedArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
         }
-      } else if (a.z != nullptr && a.w_z != nullptr) {
+      } else if (a.z != nullptr) {
         uint32_t packed[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -228,7 +296,7 @@ hipError_t launch_ced_project(const uint16_t *h, int64_t tokens, int hidden, int
   const int n_total = n_layers * (w_z != nullptr ? kLatent + kIdxDim : kLatent);
   const dim3 grid((n_total + BN - 1) / BN, (unsigned)((tokens + BM - 1) / BM));
   timer_before(kKernCedProject, st);
-  ced_kernel<<<grid, dim3(256), 0, st>>>(a);
+  ced_kernel<<<grid, dim3(kThreads), 0, st>>>(a);
   timer_after(kKernCedProject, st);
   return hipGetLastError();
 }
