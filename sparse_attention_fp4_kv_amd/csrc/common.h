@@ -49,17 +49,20 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
 // The decision points between neighbouring grid values are .25 .75 1.25 1.75
 // 2.5 3.5 5 (times s; every product is exact in fp32).  On a tie the even
 // code wins, which makes the comparison strict below an even code and
-// inclusive below an odd one.
+// inclusive below an odd one.  The code is the number of decision points
+// passed; it is found by a three-level binary search (bit 2: 1.75, bit 1:
+// 0.75 or 3.5, bit 0: .25 1.25 2.5 or 5), three compares instead of seven.
 __device__ __forceinline__ uint32_t e2m1_magnitude(float ax, float s) {
-  uint32_t c = 0;
-  c += ax > 0.25f * s;
-  c += ax >= 0.75f * s;
-  c += ax > 1.25f * s;
-  c += ax >= 1.75f * s;
-  c += ax > 2.5f * s;
-  c += ax >= 3.5f * s;
-  c += ax > 5.0f * s;
-  return c;
+  // the seven products do not depend on ax: callers packing a group share
+  // them (the empty asm keeps the compiler from turning a select of two
+  // products back into a product of a select, one multiply per value)
+  float t0 = 0.25f * s, t1 = 0.75f * s, t2 = 1.25f * s, t3 = 1.75f * s;
+  float t4 = 2.5f * s, t5 = 3.5f * s, t6 = 5.0f * s;
+  asm("" : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t4), "+v"(t5), "+v"(t6));
+  const bool b2 = ax >= t3;
+  const bool b1 = ax >= (b2 ? t5 : t1);
+  const bool b0 = ax > (b2 ? (b1 ? t6 : t4) : (b1 ? t2 : t0));
+  return 4u * b2 + 2u * b1 + (uint32_t)b0;
 }
 
 // Packs 16 consecutive channels: returns the E4M3 scale code and writes the
