@@ -274,9 +274,10 @@ __device__ __forceinline__ void load_fp4_query(IdxQuery q, int b, int heads, int
     Q.qa[ks] = r < heads ? v : f16x8{};
   }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < 16; ++e) {  // unconditional (clamped) loads, masked after
     const int row = 8 * (e >> 2) + 4 * h + (e & 3);
-    Q.wr[e] = row < heads ? q.w[(size_t)b * heads + row] : 0.0f;
+    const float w = q.w[(size_t)b * heads + (row < heads ? row : heads - 1)];
+    Q.wr[e] = row < heads ? w : 0.0f;
   }
 }
 
@@ -293,10 +294,13 @@ __device__ __forceinline__ float fp4_tile_score(const Fp4Half &k, const Fp4Query
   // max(x, 0) as the signed-integer maximum of the fp32 bits (negative values
   // and -0 have the sign bit set, so they become +0): one instruction, where
   // fmaxf also canonicalizes its input
-  float part = 0.0f;
+  // four independent partial sums instead of one chain of 16 dependent FMAs
+  float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int e = 0; e < 16; ++e) part = fmaf(Q.wr[e], __int_as_float(max(__float_as_int(acc[e]), 0)), part);
-  return part + __shfl_xor(part, 32);
+  for (int e = 0; e < 16; ++e)
+    part[e & 3] = fmaf(Q.wr[e], __int_as_float(max(__float_as_int(acc[e]), 0)), part[e & 3]);
+  const float s = (part[0] + part[1]) + (part[2] + part[3]);
+  return s + __shfl_xor(s, 32);
 }
 
 __device__ __forceinline__ int row_len(const SeqsDev &S, int b) {
