@@ -800,20 +800,27 @@ __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const f
   }
 }
 
-// Heads per workgroup.  64 shares each dequantized tile among the most heads;
-// when that leaves the chip short of workgroups (small batches) 16 heads per
-// workgroup give 4x the workgroups, each with a quarter of the MFMA work per
-// tile (the tile is then dequantized once per head group, from L2).
+// Heads per workgroup.  64 shares each dequantized tile (and each window
+// tile) among the most heads; with fewer than 8 (job, sequence) problems in
+// the launch 16 heads per workgroup give 4x the workgroups, each with a
+// quarter of the MFMA work per tile (the tile is then dequantized once per
+// head group, from L2), which measured faster for one sequence over 4
+// layers (73 against 79 us per step) while 64 heads won at 8 sequences (63
+// -> 58 us) and for 20 layers with their windows (99 -> 93 us).
 // `problems` counts (job, sequence) pairs of the launch.
 int heads_per_group(int problems, int heads) {
-  if (heads % 64 == 0 && (int64_t)problems * (heads / 64) >= 32) return 64;
+  if (heads % 64 == 0 && (int64_t)problems * (heads / 64) >= 8) return 64;
   return 16;
 }
 
 int choose_splits(int problems, int heads, int top_k) {
-  const int groups = problems * (heads / heads_per_group(problems, heads));
+  const int hpg = heads_per_group(problems, heads);
+  const int groups = problems * (heads / hpg);
   const int tiles = (top_k + kT - 1) / kT;
   int splits = (256 + groups - 1) / groups;  // about one workgroup per CU
+  // a 64-head workgroup's slot resolution and first gather cost as much as a
+  // tile or two: give each at least two tiles
+  if (hpg == 64 && splits > (tiles + 1) / 2) splits = (tiles + 1) / 2;
   if (splits > tiles) splits = tiles;
   if (splits > kMaxSplits) splits = kMaxSplits;
   const int min_splits = (tiles * kT + kSlotCap - 1) / kSlotCap;  // a workgroup resolves at most kSlotCap entries

@@ -33,7 +33,7 @@ def _random_idx(rng, seq_lens, K):
 ])
 def test_attention_layers_own_kv(seq_lens, K, heads, rope_dim):
     """Four layers, each with its own KV pool (Reuse: layers 0 and 1 share one index set, 2 and 3 have their
-    own): every layer matches the oracle over its own cache, and the single-layer call within 1e-5."""
+    own): every layer matches the oracle over its own cache, and the single-layer call within 5e-5."""
     st = wl.Streams(700 + K + heads + rope_dim)
     B, L = len(seq_lens), 4
     tables, nb = build_tables(st, seq_lens, True)
@@ -58,8 +58,10 @@ def test_attention_layers_own_kv(seq_lens, K, heads, rope_dim):
     for l in range(L):
         out, lse = outs[l].cpu().numpy(), lses[l].cpu().numpy()
         o1, l1 = singles[l][0].cpu().numpy(), singles[l][1].cpu().numpy()
-        # a different split of the entries (the launch holds more problems): rounding of the merge only
-        assert np.all(np.abs(out - o1) <= 1e-5 * np.maximum(1.0, np.abs(o1))), l
+        # the launch holds more problems, so its entries are split differently and its heads may be grouped
+        # differently (64 or 16 per workgroup: each logit's channel sum in 2 or 4 fp32 partials); each result
+        # is within ~2e-5 of the exact one, so the two differ by the rounding of both
+        assert np.all(np.abs(out - o1) <= 5e-5 * np.maximum(1.0, np.abs(o1))), l
         for b, n in enumerate(seq_lens):
             o_out, o_lse = oracle_attention_rows(lat[l][b], ropes[l][b] if rope_dim else None, q[l][b], idx[l][b], n,
                                                  sigma)
@@ -69,7 +71,8 @@ def test_attention_layers_own_kv(seq_lens, K, heads, rope_dim):
 
 def test_attention_layers_with_windows():
     """Three layers, each with its own sliding-window ring and new window entry, in one launch: the same as
-    one csa2_sparse_fp4_decode_attn_swa call per layer (within 1e-5), and the same ring bytes."""
+    one csa2_sparse_fp4_decode_attn_swa call per layer (within 5e-5: the launch of 9 problems groups 64 heads
+    per workgroup, the single calls 16), and the same ring bytes."""
     st = wl.Streams(720)
     seq_lens, K, H, L = [3000, 90, 128], 256, 64, 3
     B = len(seq_lens)
@@ -100,7 +103,7 @@ def test_attention_layers_with_windows():
     for l in range(L):
         assert torch.equal(rings_a[l].codes, rings_b[l].codes) and torch.equal(rings_a[l].scales, rings_b[l].scales)
         o1 = singles[l][0]
-        assert bool(((outs[l] - o1).abs() <= 1e-5 * o1.abs().clamp(min=1.0)).all())
+        assert bool(((outs[l] - o1).abs() <= 5e-5 * o1.abs().clamp(min=1.0)).all())
         assert float((lses[l] - singles[l][1]).abs().max()) <= 1e-5
 
 
