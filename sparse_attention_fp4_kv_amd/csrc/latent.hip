@@ -102,8 +102,14 @@ __device__ __forceinline__ uint16_t exact_bf16(float v) { return (uint16_t)(__fl
 // ahead of the MFMA chain, which keeps registers for occupancy in bulk runs.
 template <bool EARLY>
 __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kRows][kLdX];
-  __shared__ __attribute__((aligned(16))) float ks[kRows][kLdK];
+  // the dequantized rows, then (after every wave's projection has read them)
+  // the projected keys: one LDS area, so four workgroups fit a CU
+  __shared__ __attribute__((aligned(16))) union {
+    uint16_t xs[kRows][kLdX];
+    float ks[kRows][kLdK];
+  } sx;
+  auto &xs = sx.xs;
+  auto &ks = sx.ks;
   __shared__ int64_t slots[kRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row0 = a.m.paged ? (int64_t)blockIdx.x * kRows
@@ -164,22 +170,29 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
       }
     }
   }
+  // a wave's rows are 4 apart; the next one's channels are loaded while this
+  // one is finished
+  auto load_row = [&](int64_t r, float (&x)[8]) {
+    const float4 *src = reinterpret_cast<const float4 *>(a.c + r * kLatent + 8 * lane);
+    const float4 u = src[0], v = src[1];
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+  };
+  float xn[8];
+  if (row0 + wave < row_end) load_row(row0 + wave, xn);
   for (int j = 0; j < kRows / 4; ++j) {
     const int lr = 4 * j + wave;  // local row
     const int64_t r = row0 + lr;
-    if (r >= row_end) {  // uniform over the wave; the row's keys are computed from stale LDS and never stored
+    if (r >= row_end) {  // uniform over the wave (and so are the later rows); their keys come from stale LDS and are never stored
       if (lane == 0) slots[lr] = -1;
       continue;
     }
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = xn[i];
+    if (j + 1 < kRows / 4 && r + 4 < row_end) load_row(r + 4, xn);
     int64_t pos = 0;
     int lay = 0;
     const int64_t slot = row_slot(a, r, &pos, &lay);
-    float x[8];
-    {
-      const float4 *src = reinterpret_cast<const float4 *>(a.c + r * kLatent + 8 * lane);
-      const float4 u = src[0], v = src[1];
-      x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-    }
     if (lane == 0) slots[lr] = slot;
     float ss = 0.0f;
 #pragma unroll
@@ -250,6 +263,7 @@ __global__ void __launch_bounds__(256) finish_kernel(FinishArgs a) {
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, xv), __builtin_bit_cast(bf16x8, wv),
                                                     acc, 0, 0, 0);
     }
+    __syncthreads();  // every wave has read xs (the keys take its place)
 #pragma unroll
     for (int e = 0; e < 16; ++e) ks[8 * (e >> 2) + 4 * (lane >> 5) + (e & 3)][32 * wave + (lane & 31)] = acc[e];
   }
