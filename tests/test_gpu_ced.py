@@ -19,7 +19,7 @@ def _bits(x):
 def test_identity_weights_bit_exact():
     """hidden = 512, W_kv = I: C = H exactly, so the fused pack equals the oracle pack of H."""
     rng = np.random.default_rng(0)
-    T = 300  # ragged against the 128-row tile
+    T = 300  # ragged against the 256-row tile
     h = _bits(rng.standard_normal((T, 512)) * 4)
     w = np.broadcast_to(np.eye(512, dtype=np.float32), (2, 512, 512))
     codes, scales, z, c = csa2.csa2_ced_kv_project(to_dev(h), to_dev(_bits(w)), c_f32=True)
@@ -36,6 +36,24 @@ def test_integer_weights_exact_all_outputs():
     """Small integers: every product and sum is exact in fp32, so C, packed C and Z are exact."""
     rng = np.random.default_rng(1)
     T, hidden, L = 200, 256, 3
+    h = _bits(rng.integers(-3, 4, size=(T, hidden)))
+    wkv = _bits(rng.integers(-2, 3, size=(L, 512, hidden)))
+    wz = _bits(rng.integers(-2, 3, size=(L, 64, hidden)))
+    codes, scales, z, c = csa2.csa2_ced_kv_project(to_dev(h), to_dev(wkv), to_dev(wz), c_f32=True)
+    torch.cuda.synchronize()
+    oc, os_, oz, C = oracle.ced.ced_project_and_pack(h, wkv, wz)
+    assert np.array_equal(c.cpu().numpy(), C.astype(np.float32))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(z.cpu().numpy().view(np.uint16), oz)
+
+
+@pytest.mark.parametrize("hidden,T", [(64, 1), (128, 257), (192, 513)])
+def test_integer_weights_short_k_and_ragged_rows(hidden, T):
+    """The shortest reductions (2, 4 and 6 k-steps of 32: the load pipeline's start-up and drain without a
+    steady state) and row counts of 1, one past a 256-row tile and one past two, with W^Z: exact as above."""
+    rng = np.random.default_rng(2 + hidden)
+    L = 2
     h = _bits(rng.integers(-3, 4, size=(T, hidden)))
     wkv = _bits(rng.integers(-2, 3, size=(L, 512, hidden)))
     wz = _bits(rng.integers(-2, 3, size=(L, 64, hidden)))
