@@ -596,25 +596,27 @@ constexpr int kRelShift = 12;
 // larger budgets reach further below the maximum than the window does for
 // Gaussian-like scores and go straight to the absolute emission.
 __device__ __forceinline__ bool rel_fits(int cap, int items) { return 50 * cap <= items; }
+template <int SH = kRelShift>
 __device__ __forceinline__ uint32_t rel_bin(uint32_t key, uint32_t m) {
-  const uint32_t d = (m - key) >> kRelShift;
+  const uint32_t d = (m - key) >> SH;
   return d >= (uint32_t)(kBins - 1) ? 0u : (uint32_t)(kBins - 1) - d;
 }
 // Every key in bins <= d is below this (a key of bin d > 0 is at most
 // M - (2047 - d) 2^12; a far key at most M - 2047 2^12; both >= 1 when such
 // a key exists).
+template <int SH = kRelShift>
 __device__ __forceinline__ uint32_t rel_edge(uint32_t m, uint32_t d) {
-  return m - (((uint32_t)(kBins - 1) - d) << kRelShift) + 1u;
+  return m - (((uint32_t)(kBins - 1) - d) << SH) + 1u;
 }
 
 // Relative-digit histogram of one lane's keys (far keys only counted) and
 // its wave's count of far keys in far_w[wave] (0 or the count; lane 0 writes).
-template <int IPT>
+template <int IPT, int SH = kRelShift>
 __device__ __forceinline__ void rel_hist(const uint32_t (&k)[IPT], uint32_t m, uint32_t *hist, uint32_t *far_w) {
   uint32_t far = 0u;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    const uint32_t bin = rel_bin(k[j], m);
+    const uint32_t bin = rel_bin<SH>(k[j], m);
     const bool is_far = k[j] != 0u && bin == 0u;
     far += (uint32_t)__popcll(__ballot(is_far));
     if (k[j] != 0u && bin != 0u) atomicAdd(&hist[bin], 1u);
@@ -626,13 +628,14 @@ __device__ __forceinline__ void rel_hist(const uint32_t (&k)[IPT], uint32_t m, u
 // cap + 1 over the binned keys) and its far count: returns false when the
 // absolute emission must run instead; else *cut / *d say which bins are kept
 // (all when !cut, else bins > d) and *edge the segment's edge.
+template <int SH = kRelShift>
 __device__ __forceinline__ bool rel_cut(const uint32_t *res, uint32_t far, int cap, uint32_t m, bool *cut,
                                         uint32_t *d, uint32_t *edge) {
   const bool found = res[2] != 0u;
   if (found) {  // the boundary lies in the window (bin >= 1)
     *cut = true;
     *d = res[0];
-    *edge = rel_edge(m, res[0]);
+    *edge = rel_edge<SH>(m, res[0]);
     return true;
   }
   const uint32_t binned = res[1];  // total of bins 1 .. 2047 (bin 0 is never binned)
@@ -645,7 +648,7 @@ __device__ __forceinline__ bool rel_cut(const uint32_t *res, uint32_t far, int c
   if (binned == (uint32_t)cap) {  // exactly the budget in the window, the rest far
     *cut = true;
     *d = 0u;
-    *edge = rel_edge(m, 0u);
+    *edge = rel_edge<SH>(m, 0u);
     return true;
   }
   return false;
@@ -673,7 +676,7 @@ __device__ __forceinline__ uint32_t block_max_key(const uint32_t (&k)[IPT], uint
 // segment's keys (same contract as emit_segment_abs; hist[0], hist[1] zeroed
 // by the caller before a barrier that precedes the call; red: NT/64 + 24
 // words).
-template <int NT, int IPT, class PosOf>
+template <int NT, int IPT, int SH = kRelShift, class PosOf>
 __device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_l, int cap, uint2 *cand_seg,
                                                SegInfo *info, uint32_t (*hist)[kBins], uint32_t *red,
                                                PosOf pos_of) {
@@ -687,7 +690,7 @@ __device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_
   uint32_t k[IPT];
 #pragma unroll
   for (int j = 0; j < IPT; ++j) k[j] = keys_l[i0 + 64 * j];
-  rel_hist<IPT>(k, m, hist[0], red + 24 - NW);
+  rel_hist<IPT, SH>(k, m, hist[0], red + 24 - NW);
   __syncthreads();
   find_threshold(hist[0], (uint32_t)cap + 1u, red + 16);
   uint32_t far = 0u;
@@ -695,7 +698,7 @@ __device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_
   for (int w = 0; w < NW; ++w) far += red[24 - NW + w];
   bool cut;
   uint32_t d1, edge;
-  if (!rel_cut(red + 16, far, cap, m, &cut, &d1, &edge)) {  // uniform
+  if (!rel_cut<SH>(red + 16, far, cap, m, &cut, &d1, &edge)) {  // uniform
     zero_hists<1>(hist);
     __syncthreads();
     emit_segment_abs<NT, IPT>(keys_l, cap, cand_seg, info, hist, red, pos_of);
@@ -704,7 +707,7 @@ __device__ __forceinline__ void emit_segment_m(uint32_t m, const uint32_t *keys_
   uint32_t flags = 0;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    const bool em = k[j] != 0u && (!cut || rel_bin(k[j], m) > d1);
+    const bool em = k[j] != 0u && (!cut || rel_bin<SH>(k[j], m) > d1);
     flags |= em ? (1u << j) : 0u;
   }
   const uint32_t total = ordered_emit<NT, IPT>(flags, red, 0u, [&](int j, uint32_t slot, bool keep) {
@@ -734,7 +737,7 @@ __device__ __forceinline__ void emit_segment(const uint32_t *keys_l, int cap, ui
 // (which is also the largest block key): both histograms and both threshold
 // searches (waves 0 and 1) share their barriers.  hist[0..3] zeroed by the
 // caller before a barrier that precedes the call; red: 36 words.
-template <int IPT, class PosP, class PosB>
+template <int IPT, int SH, class PosP, class PosB>
 __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pkeys, int cap_p, uint2 *cand_p,
                                                   SegInfo *info_p, PosP pos_p, const uint32_t *bkeys, int cap_b,
                                                   uint2 *cand_b, SegInfo *info_b, PosB pos_b,
@@ -754,8 +757,8 @@ __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pk
   const uint32_t kb1[1] = {ib < 32 * IPT ? bkeys[ib] : 0u};
   const uint32_t kb = kb1[0];
   const uint32_t mp = m, mb = m;
-  rel_hist<IPT>(kp, mp, hist[0], red + 24);
-  rel_hist<1>(kb1, mb, hist[1], red + 28);
+  rel_hist<IPT, SH>(kp, mp, hist[0], red + 24);
+  rel_hist<1, SH>(kb1, mb, hist[1], red + 28);
   __syncthreads();
   if (wave == 0) find_threshold_wave(hist[0], (uint32_t)cap_p + 1u, red + 16);
   if (wave == 1) find_threshold_wave(hist[1], (uint32_t)cap_b + 1u, red + 20);
@@ -768,8 +771,8 @@ __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pk
   }
   bool cut_p, cut_b;
   uint32_t d1p, d1b, edge_p, edge_b;
-  const bool ok_p = rel_cut(red + 16, far_p, cap_p, mp, &cut_p, &d1p, &edge_p);
-  const bool ok_b = rel_cut(red + 20, far_b, cap_b, mb, &cut_b, &d1b, &edge_b);
+  const bool ok_p = rel_cut<SH>(red + 16, far_p, cap_p, mp, &cut_p, &d1p, &edge_p);
+  const bool ok_b = rel_cut<SH>(red + 20, far_b, cap_b, mb, &cut_b, &d1b, &edge_b);
   if (!ok_p || !ok_b) {  // uniform: the absolute emission for both
     __syncthreads();     // every thread has read red[]
     zero_hists<2>(hist);
@@ -783,10 +786,10 @@ __device__ __forceinline__ void emit_segment_pair(uint32_t m, const uint32_t *pk
   uint32_t wtot_p = 0;
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    bal[j] = __ballot(kp[j] != 0u && (!cut_p || rel_bin(kp[j], mp) > d1p));
+    bal[j] = __ballot(kp[j] != 0u && (!cut_p || rel_bin<SH>(kp[j], mp) > d1p));
     wtot_p += (uint32_t)__popcll(bal[j]);
   }
-  const bool keep_b = kb != 0u && (!cut_b || rel_bin(kb, mb) > d1b);
+  const bool keep_b = kb != 0u && (!cut_b || rel_bin<SH>(kb, mb) > d1b);
   const uint64_t bal_b = __ballot(keep_b);
   if (lane == 0) {  // (red[0..7] is free here: the values read above live in red[8..31])
     red[wave] = wtot_p;
@@ -842,10 +845,12 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   constexpr int kPagesPerWave = kPages / 4;
   constexpr int kBlocks = SLICE / kBlk;   // 256 or 128
   constexpr int kIpt = SLICE / 256;       // positions per thread in the emission
-  // relative-digit emission for bf16 / fp32 keys; the FP4 multi-head scan is
-  // bound by VALU issue in its loads, where tracking the maximum cost more
-  // than the emission saved (two-level emission there)
-  constexpr bool kRel = KF != kKeyFp4;
+  // relative-digit emission (the slice's largest key tracked while scoring);
+  // the FP4 multi-head scores (weighted sums of ReLUs) spread further below
+  // the slice maximum than a dot product's, so their bins are 4x wider (the
+  // window spans 4 binades instead of 1)
+  constexpr bool kRel = true;
+  constexpr int kSh = KF == kKeyFp4 ? kRelShift + 2 : kRelShift;
   __shared__ int32_t pg[kPages];
   __shared__ __attribute__((aligned(16))) uint32_t pkey[SLICE];
   __shared__ __attribute__((aligned(16))) uint32_t bkey[kBlocks];
@@ -908,7 +913,9 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
         for (int j = 0; j < 2; ++j) {
           const int lp = page * kPage + 32 * j + (lane & 31);  // local position
           const float sc = fp4_tile_score(kt[pp % kDepth][j], Q);
-          if (lane < 32) pkey[lp] = (mapped && base + lp < n) ? score_key(sc) : 0u;
+          const uint32_t key = (mapped && base + lp < n) ? score_key(sc) : 0u;
+          kmax = max(kmax, key);
+          if (lane < 32) pkey[lp] = key;
         }
       }
     } else {
@@ -1016,7 +1023,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   if constexpr (HIER) {
     const int cap_b = seg_budget(a.P, nseg, kBlocks);
     if constexpr (kRel) {
-      emit_segment_pair<kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+      emit_segment_pair<kIpt, kSh>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                       a.w.seg_pos + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base + i); },
                       bkey, cap_b, a.w.cand_blk + (size_t)b * kCandCap + (size_t)wg * cap_b,
                       a.w.seg_blk + (size_t)b * a.w.max_seg + wg, [&](int i) { return (uint32_t)(base / kBlk + i); },
@@ -1030,7 +1037,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     }
   } else {
     if constexpr (kRel)
-      emit_segment_m<256, kIpt>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
+      emit_segment_m<256, kIpt, kSh>(kmax_l, pkey, cap, a.w.cand_pos + (size_t)b * kCandCap + (size_t)wg * cap,
                                 a.w.seg_pos + (size_t)b * a.w.max_seg + wg, hist, red,
                                 [&](int i) { return (uint32_t)(base + i); });
     else
