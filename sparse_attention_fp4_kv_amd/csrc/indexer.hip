@@ -866,6 +866,14 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
     if (tid < 64) append_row(r.L, a.S, b, -1, r.latent, r.rope, r.idx_key, tid, a.dbg);
     return;
   }
+  // this slice's page-table entries are read together with the length (one
+  // memory round trip before the key loads instead of two); entries of pages
+  // past the length are masked below
+  int blk_raw = -1;
+  if (tid < kPages) {
+    const int64_t page = (int64_t)wg * kPages + tid;
+    if (page < a.S.max_blocks) blk_raw = a.S.block_table[(int64_t)b * a.S.max_blocks + page];
+  }
   const int sl = a.S.seq_lens[b];  // read once: a reload after the key loads would cost a memory round trip
   const int n = sl < 0 ? 0 : (sl > a.S.max_len ? a.S.max_len : sl);
   const int64_t base = (int64_t)wg * SLICE;
@@ -876,7 +884,7 @@ __global__ void __launch_bounds__(256) scan_kernel(ScanArgs a) {
   uint32_t kmax = 0u;  // this lane's largest key
   const bool can_load = a.L.num_blocks > 0;  // an empty pool: every page is unmapped
   if (tid < kPages) {
-    pg[tid] = (base + 64 * tid < n) ? page_block(a.S, a.L.num_blocks, b, base / kPage + tid) : -1;
+    pg[tid] = (base + 64 * tid < n && blk_raw >= 0 && blk_raw < a.L.num_blocks) ? blk_raw : -1;
     if (a.dbg != nullptr && base + 64 * tid < n && pg[tid] < 0) dbg_raise(a.dbg, kDbgPage);
   }
   float q[8];
