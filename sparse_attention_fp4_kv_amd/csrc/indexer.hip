@@ -20,18 +20,21 @@
 //              best items as a candidate segment, cut exactly to a budget of
 //              about 3x its expected share of the top-K, plus the segment's
 //              edge: every item it did not emit has a key below the edge.  The
-//              cut uses one histogram level of 2^12-unit bins counted down from
-//              the slice's largest key when the budget is small (the common
-//              decode case), else two 11-bit radix levels of the absolute key.  The full scan streams the keys with non-temporal 16-byte
-//              loads, 16 in flight per lane, after one page-table lookup per
-//              64 positions; loads are never guarded by branches (unmapped
-//              pages read slot 0 and are masked).  In hierarchical mode it
-//              emits two segments: block maxima and positions.
+//              cut uses one histogram level of bins counted down from the
+//              slice's largest key (2^12 key units wide, 2^14 for the
+//              multi-head FP4 scores) when the budget is small (the common
+//              decode case), else two 11-bit radix levels of the absolute key.
+//              The full scan streams the keys with non-temporal 16-byte loads,
+//              16 in flight per lane, after one page-table lookup per 64
+//              positions; loads are never guarded by branches (unmapped pages
+//              read slot 0 and are masked).  In hierarchical mode it emits two
+//              segments: block maxima and positions.
 //   select     One 512-thread workgroup per row and output loads the segments
-//              into LDS in position order and finds the exact threshold with
-//              32-bit radix levels (11/11/10 key bits, then position bits only
-//              for ties at the boundary; each threshold search runs in one
-//              wave).  A segment whose edge exceeds the threshold's key may
+//              into registers in position order and finds the exact threshold
+//              with a 2048-bin histogram over the candidates' own key range,
+//              a second one inside the boundary bin and an exact rank of the
+//              few items left (radix levels on key then position bits when
+//              heavy ties leave more; each threshold search runs in one wave).  A segment whose edge exceeds the threshold's key may
 //              hold more winners: those segments are re-read in full from the
 //              stored keys (items at or above the threshold key only) and the
 //              threshold is recomputed, which is then exact.  If that would
