@@ -449,15 +449,18 @@ csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, in
  * capture, tight serving loops, harnesses that forbid allocation):
  * csa2_sparse_fp4_decode_attn_layers without a workspace argument.  The split
  * partials go to a scratch array the library holds on every device it runs on
- * (32 MiB each, held until the process ends); a problem whose partials need
- * more (the size csa2_attn_layers_workspace_size reports) returns
- * CSA2_ERR_WORKSPACE and launches nothing.  Every call on one device shares
+ * (32 MiB each, held until the process ends).  When the partials of the usual
+ * split count (the size csa2_attn_layers_workspace_size reports) need more,
+ * the entries are split over fewer workgroups until they fit; a problem that
+ * does not fit even so returns CSA2_ERR_WORKSPACE and launches nothing.  Every
+ * call on one device shares
  * that device's scratch: calls that overlap in time on one device (on
  * different streams) race, so serialize them.  The scratch needs no clearing
  * (every partial is written before it is read).  The first call on a device
  * resolves the scratch's address there (not a stream operation; make that
  * first call outside graph capture).  Results equal those of
- * csa2_sparse_fp4_decode_attn_layers on the same arguments.  Nothing is
+ * csa2_sparse_fp4_decode_attn_layers on the same arguments (within the
+ * rounding of a different split where fewer splits were needed).  Nothing is
  * allocated by this call. */
 csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *layers, int32_t n_layers,
                                                        const csa2_seqs *seqs, int32_t heads, int32_t top_k,

@@ -604,7 +604,7 @@ csa2_status csa2_sparse_fp4_decode_attn(const csa2_kv_layer *layer, const csa2_s
   const size_t need = attn_workspace_bytes(1, S.batch, heads, top_k, false);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
   const AttnLaunchJob job{L, q, indices, nullptr, nullptr, nullptr, out, lse};
-  return from_hip(launch_sparse_attn(&job, 1, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
+  return from_hip(launch_sparse_attn(&job, 1, S, heads, top_k, softmax_scale, ws, ~(size_t)0, as_stream(stream)));
 }
 
 csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const csa2_seqs *seqs, const uint16_t *q,
@@ -629,7 +629,7 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
   const size_t need = attn_workspace_bytes(1, S.batch, heads, top_k, true);
   if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
   const AttnLaunchJob job{L, q, indices, win->codes, win->scales, new_latent, out, lse};
-  return from_hip(launch_sparse_attn(&job, 1, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
+  return from_hip(launch_sparse_attn(&job, 1, S, heads, top_k, softmax_scale, ws, ~(size_t)0, as_stream(stream)));
 }
 
 csa2_status csa2_attn_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t heads, int32_t top_k,
@@ -641,10 +641,13 @@ csa2_status csa2_attn_layers_workspace_size(int32_t n_layers, int32_t batch, int
   return CSA2_OK;
 }
 
-csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, int32_t n_layers,
-                                               const csa2_seqs *seqs, int32_t heads, int32_t top_k,
-                                               float softmax_scale, void *ws, size_t ws_bytes, csa2_stream stream) {
-  CSA2_TRACE;
+namespace {
+// The layered attention with its partials bounded by max_ws bytes (the split
+// count lowered to fit): the workspace entry point passes no bound, the
+// allocation-free one its scratch size.
+csa2_status attn_layers_impl(const csa2_attn_layer *layers, int32_t n_layers, const csa2_seqs *seqs, int32_t heads,
+                             int32_t top_k, float softmax_scale, void *ws, size_t ws_bytes, size_t max_ws,
+                             csa2_stream stream) {
   SeqsDev S;
   csa2_status st;
   if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
@@ -680,9 +683,17 @@ csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, in
                             x.lse};
   }
   if (S.batch == 0) return CSA2_OK;
-  const size_t need = attn_workspace_bytes(n_layers, S.batch, heads, top_k, window);
-  if (ws == nullptr || ws_bytes < need || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
-  return from_hip(launch_sparse_attn(jobs, n_layers, S, heads, top_k, softmax_scale, ws, as_stream(stream)));
+  const size_t need = attn_workspace_bytes(n_layers, S.batch, heads, top_k, window, max_ws);
+  if (ws == nullptr || ws_bytes < need || need > max_ws || !aligned(ws, 256)) return CSA2_ERR_WORKSPACE;
+  return from_hip(launch_sparse_attn(jobs, n_layers, S, heads, top_k, softmax_scale, ws, max_ws, as_stream(stream)));
+}
+}  // namespace
+
+csa2_status csa2_sparse_fp4_decode_attn_layers(const csa2_attn_layer *layers, int32_t n_layers,
+                                               const csa2_seqs *seqs, int32_t heads, int32_t top_k,
+                                               float softmax_scale, void *ws, size_t ws_bytes, csa2_stream stream) {
+  CSA2_TRACE;
+  return attn_layers_impl(layers, n_layers, seqs, heads, top_k, softmax_scale, ws, ws_bytes, ~(size_t)0, stream);
 }
 
 csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *layers, int32_t n_layers,
@@ -695,11 +706,12 @@ csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *la
   if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
   if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
   const bool window = layers[0].win != nullptr;
-  if (attn_workspace_bytes(n_layers, S.batch, heads, top_k, window) > kAttnScratchBytes) return CSA2_ERR_WORKSPACE;
+  if (attn_workspace_bytes(n_layers, S.batch, heads, top_k, window, kAttnScratchBytes) > kAttnScratchBytes)
+    return CSA2_ERR_WORKSPACE;
   void *scratch_ptr = nullptr;
   if (attn_scratch(&scratch_ptr) != hipSuccess) return CSA2_ERR_HIP;
-  return csa2_sparse_fp4_decode_attn_layers(layers, n_layers, seqs, heads, top_k, softmax_scale, scratch_ptr,
-                                            kAttnScratchBytes, stream);
+  return attn_layers_impl(layers, n_layers, seqs, heads, top_k, softmax_scale, scratch_ptr, kAttnScratchBytes,
+                          kAttnScratchBytes, stream);
 }
 
 csa2_block_pool *csa2_block_pool_create(int32_t num_blocks) {

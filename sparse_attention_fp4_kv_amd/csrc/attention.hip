@@ -813,7 +813,19 @@ int heads_per_group(int problems, int heads) {
   return 16;
 }
 
-int choose_splits(int problems, int heads, int top_k) {
+// Bytes of the split partials (out, then m and l) of a launch.
+size_t partial_bytes(int problems, int heads, int parts) {
+  if (parts == 1) return 256;
+  const size_t rows = (size_t)problems * heads * parts;
+  const size_t o = rows * kLatent * sizeof(float);
+  const size_t ml = rows * 2 * sizeof(float);
+  return ((o + 255) & ~(size_t)255) + ((ml + 255) & ~(size_t)255);
+}
+
+// Split-K workgroups per (problem, head group); with a bound on the partials'
+// bytes (the allocation-free entry point's scratch) the count is lowered
+// until they fit, down to the least a workgroup's slot array allows.
+int choose_splits(int problems, int heads, int top_k, bool window, size_t max_bytes) {
   const int hpg = heads_per_group(problems, heads);
   const int groups = problems * (heads / hpg);
   const int tiles = (top_k + kT - 1) / kT;
@@ -826,27 +838,26 @@ int choose_splits(int problems, int heads, int top_k) {
   const int min_splits = (tiles * kT + kSlotCap - 1) / kSlotCap;  // a workgroup resolves at most kSlotCap entries
   if (splits < min_splits) splits = min_splits;
   if (splits < 1) splits = 1;
+  const int win = window ? kWinSplits : 0;
+  while (splits > min_splits && splits > 1 && partial_bytes(problems, heads, splits + win) > max_bytes) --splits;
   return splits;
 }
 
 }  // namespace
 
-size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window) {
-  const int parts = choose_splits(jobs * batch, heads, top_k) + (window ? kWinSplits : 0);
-  if (parts == 1) return 256;
-  const size_t rows = (size_t)jobs * batch * heads * parts;
-  const size_t o = rows * kLatent * sizeof(float);
-  const size_t ml = rows * 2 * sizeof(float);
-  return ((o + 255) & ~(size_t)255) + ((ml + 255) & ~(size_t)255);
+size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window, size_t max_bytes) {
+  const int problems = jobs * batch;
+  const int parts = choose_splits(problems, heads, top_k, window, max_bytes) + (window ? kWinSplits : 0);
+  return partial_bytes(problems, heads, parts);
 }
 
 hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsDev &S, int heads, int top_k,
-                              float scale, void *ws, hipStream_t st) {
+                              float scale, void *ws, size_t max_ws, hipStream_t st) {
   if (S.batch == 0 || n_jobs == 0) return hipSuccess;
   const bool window = jobs[0].win_codes != nullptr;
   const int problems = n_jobs * S.batch;
   const int hgsz = heads_per_group(problems, heads);
-  const int splits = choose_splits(problems, heads, top_k);
+  const int splits = choose_splits(problems, heads, top_k, window, max_ws);
   const int parts = splits + (window ? kWinSplits : 0);
   const int tiles = (top_k + kT - 1) / kT;
   AttnArgs a;

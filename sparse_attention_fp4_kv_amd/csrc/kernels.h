@@ -128,7 +128,10 @@ struct AttnLaunchJob {
   float *out;
   float *lse;
 };
-size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window);
+// Workspace of an attention launch; max_bytes bounds the split partials (the
+// split count is lowered to fit when it can be).
+size_t attn_workspace_bytes(int jobs, int batch, int heads, int top_k, bool window,
+                            size_t max_bytes = ~(size_t)0);
 // The library-held scratch of the allocation-free entry point (device memory
 // of this many bytes on every device it runs on) and its address on the
 // current device.
@@ -136,7 +139,7 @@ constexpr size_t kAttnScratchBytes = (size_t)32 << 20;
 hipError_t attn_scratch(void **ptr);
 
 hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsDev &S, int heads, int top_k,
-                              float scale, void *ws, hipStream_t st);
+                              float scale, void *ws, size_t max_ws, hipStream_t st);
 
 // ---- CED projection (ced.hip)
 // Latent finish (RMSNorm, RoPE, FP4 pack) and the FP4 indexer key projected

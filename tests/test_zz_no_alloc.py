@@ -1,7 +1,7 @@
 """The allocation-free attention entry point (csa2_sparse_fp4_decode_attn_layers_noalloc) called through the
 C ABI: two calls in a row, the second on a smaller problem, each equal to the workspace entry point's result
 on the same arguments (the same kernels and split choice, so the same bits) and within the attention bar of
-the oracle."""
+the oracle; a problem whose usual split count would overflow the scratch runs with fewer splits."""
 
 import ctypes
 import math
@@ -67,6 +67,27 @@ def test_noalloc_matches_workspace_entry_point_twice():
             for b, n in enumerate(seq_lens):
                 o_out, _ = oracle_attention_rows(lat[l][b], None, q[l][b], idx[b], n, sigma)
                 assert float(np.max(np.abs(outs[l].cpu().numpy()[b] - o_out))) <= ATTN_TOL, (seed, l, b)
+
+
+def test_noalloc_lowers_splits_to_fit_its_scratch():
+    """Batch 8 x 64 heads at K 2048: the workspace entry point's 32 splits need more than the 32 MiB scratch, so
+    the allocation-free call runs with fewer; same result within the rounding of a different split (each within
+    ~2e-5 of the exact one) and within the attention bar of the oracle."""
+    sigma = 1 / math.sqrt(512)
+    seq_lens, L, H, K = [2500 + 97 * b for b in range(8)], 1, 64, 2048
+    n = ctypes.c_size_t()
+    assert csa2.lib().csa2_attn_layers_workspace_size(L, len(seq_lens), H, K, 512, 0, ctypes.byref(n)) == csa2.OK
+    assert n.value > 32 << 20
+    batch, layers, lat, idx_d, idx, q = _case(902, seq_lens, L, H, K)
+    q_d = [to_dev(x) for x in q]
+    outs, lses = _noalloc(batch, layers, q_d, idx_d, sigma, H, K)
+    ref_o, ref_l = csa2.csa2_sparse_fp4_decode_attn_layers([(layers[0], q_d[0], idx_d)], batch, sigma)
+    torch.cuda.synchronize()
+    assert bool(((outs[0] - ref_o[0]).abs() <= 5e-5 * ref_o[0].abs().clamp(min=1.0)).all())
+    assert float((lses[0] - ref_l[0]).abs().max()) <= 1e-5
+    for b, n_b in enumerate(seq_lens):
+        o_out, _ = oracle_attention_rows(lat[0][b], None, q[0][b], idx[b], n_b, sigma)
+        assert float(np.max(np.abs(outs[0].cpu().numpy()[b] - o_out))) <= ATTN_TOL, b
 
 
 def test_noalloc_rejects_beyond_its_scratch():
