@@ -10,7 +10,7 @@
 // with c_s the dequantized 512-channel latent (K = V).
 //
 // Design (ours):
-//   * One workgroup (8 waves, two per SIMD) serves 16 or 64 heads of one
+//   * One workgroup (8 waves, two per SIMD) serves 16, 32 or 64 heads of one
 //     sequence, so each dequantized entry feeds all of them: QK^T and PV are
 //     MFMA contractions with M = heads (v_mfma_f32_16x16x32_f16, fp32
 //     accumulation).  QK^T splits each 16 x 16 logit tile's 512 (+64)
@@ -433,7 +433,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
   // One tile from buffer cq, with the next tile's dequantization into cq_next
   // (three buffers in turn) in the same phase.  Two barriers per tile: the
   // buffer a phase writes was last read two barriers earlier.
-  auto step = [&](int tile, f16 (*cq)[LD], const Raw *next, f16 (*cq_next)[LD]) {
+  auto step = [&](int tile, f16 (*cq)[LD], bool has_next, const Raw &next, f16 (*cq_next)[LD]) {
     // 1. partial logits S_kp = Q C^T over this wave's k-part; even and odd
     // k-steps of every N-tile accumulate separately (2 or 4 independent MFMA
     // chains), the B fragments of 4 k-steps read together ahead of them
@@ -478,7 +478,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) sm.s[qk_kp][16 * (qk_mt + i) + 4 * (lane >> 4) + rr][ent] = sa[rr];
       }
-    if (next != nullptr) dequant(*next, cq_next);
+    if (has_next) dequant(next, cq_next);
     __syncthreads();
     // 2. online softmax: logit = scale * (sum of the k-parts), masked entries -inf
     if (sm_on) {
@@ -597,7 +597,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
         *reinterpret_cast<f16x4 *>(&sm.cq[0][tile_entry][kLatent + 4 * tile_chunk]) = f16x4{};
       }
       __syncthreads();
-      step(0, sm.cq[0], nullptr, sm.cq[1]);
+      step(0, sm.cq[0], false, Raw{}, sm.cq[1]);
     }
   } else if (tile_begin < tile_end && J.L.num_blocks > 0) {
     const int last = tile_end - 1;
@@ -609,14 +609,14 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
     load_raw(min(tile_begin + 3, last), ra);
     __syncthreads();
     for (int tile = tile_begin; tile < tile_end; tile += 3) {
-      step(tile, sm.cq[0], tile + 1 < tile_end ? &rb : nullptr, sm.cq[1]);
+      step(tile, sm.cq[0], tile + 1 < tile_end, rb, sm.cq[1]);
       load_raw(min(tile + 4, last), rb);
       if (tile + 1 < tile_end) {
-        step(tile + 1, sm.cq[1], tile + 2 < tile_end ? &rc : nullptr, sm.cq[2]);
+        step(tile + 1, sm.cq[1], tile + 2 < tile_end, rc, sm.cq[2]);
         load_raw(min(tile + 5, last), rc);
       }
       if (tile + 2 < tile_end) {
-        step(tile + 2, sm.cq[2], tile + 3 < tile_end ? &ra : nullptr, sm.cq[0]);
+        step(tile + 2, sm.cq[2], tile + 3 < tile_end, ra, sm.cq[0]);
         load_raw(min(tile + 6, last), ra);
       }
     }
@@ -801,15 +801,21 @@ __global__ void __launch_bounds__(kWideThreads) attn_combine_wide_kernel(const f
 }
 
 // Heads per workgroup.  64 shares each dequantized tile (and each window
-// tile) among the most heads; with fewer than 8 (job, sequence) problems in
-// the launch 16 heads per workgroup give 4x the workgroups, each with a
-// quarter of the MFMA work per tile (the tile is then dequantized once per
-// head group, from L2), which measured faster for one sequence over 4
-// layers (73 against 79 us per step) while 64 heads won at 8 sequences (63
-// -> 58 us) and for 20 layers with their windows (99 -> 93 us).
+// tile) among the most heads; fewer heads per workgroup give more
+// workgroups, each with less MFMA work per tile (the tile is then
+// dequantized once per head group, from L2).  Measured per step (64 heads
+// per problem): one sequence over 4 layers 72 us with 16, 74 with 32, 78
+// with 64; 8 sequences of one layer 55 us with 32, 57 with 64, 62 with 16
+// (the 32-head groups take half as many splits, so the combine reads half
+// the partials); one sequence over 20 layers the same with 32 or 64, and 64
+// won over 16 with their windows (99 -> 93 us).
 // `problems` counts (job, sequence) pairs of the launch.
 int heads_per_group(int problems, int heads) {
-  if (heads % 64 == 0 && (int64_t)problems * (heads / 64) >= 8) return 64;
+  if (heads % 64 == 0) {
+    const int64_t groups64 = (int64_t)problems * (heads / 64);
+    if (groups64 >= 16) return 64;
+    if (groups64 >= 8) return 32;
+  }
   return 16;
 }
 
@@ -883,6 +889,9 @@ hipError_t launch_sparse_attn(const AttnLaunchJob *jobs, int n_jobs, const SeqsD
   if (hgsz == 64) {
     if (rope) sparse_attn_kernel<4, true><<<grid, dim3(kThreads), 0, st>>>(a);
     else sparse_attn_kernel<4, false><<<grid, dim3(kThreads), 0, st>>>(a);
+  } else if (hgsz == 32) {
+    if (rope) sparse_attn_kernel<2, true><<<grid, dim3(kThreads), 0, st>>>(a);
+    else sparse_attn_kernel<2, false><<<grid, dim3(kThreads), 0, st>>>(a);
   } else {
     if (rope) sparse_attn_kernel<1, true><<<grid, dim3(kThreads), 0, st>>>(a);
     else sparse_attn_kernel<1, false><<<grid, dim3(kThreads), 0, st>>>(a);

@@ -70,11 +70,12 @@ def test_noalloc_matches_workspace_entry_point_twice():
 
 
 def test_noalloc_lowers_splits_to_fit_its_scratch():
-    """Batch 8 x 64 heads at K 2048: the workspace entry point's 32 splits need more than the 32 MiB scratch, so
-    the allocation-free call runs with fewer; same result within the rounding of a different split (each within
-    ~2e-5 of the exact one) and within the attention bar of the oracle."""
+    """Batch 16 x 64 heads at K 2048: the workspace entry point's 16 splits need more than the 32 MiB scratch
+    (16 x 64 x 16 partial rows of 2 KB, plus their m and l), so the allocation-free call runs with fewer; same
+    result within the rounding of a different split (each within ~2e-5 of the exact one) and within the
+    attention bar of the oracle."""
     sigma = 1 / math.sqrt(512)
-    seq_lens, L, H, K = [2500 + 97 * b for b in range(8)], 1, 64, 2048
+    seq_lens, L, H, K = [2500 + 97 * b for b in range(16)], 1, 64, 2048
     n = ctypes.c_size_t()
     assert csa2.lib().csa2_attn_layers_workspace_size(L, len(seq_lens), H, K, 512, 0, ctypes.byref(n)) == csa2.OK
     assert n.value > 32 << 20
