@@ -114,7 +114,8 @@ def test_identity_vs_permuted_table_bitwise():
 
 
 def test_batch8_64k_rope_launch_shape():
-    """8 sequences x 65,536 tokens, 64 heads + rope, K 2048: the 16-head split launch of batched decode."""
+    """8 sequences x 65,536 tokens, 64 heads + rope, K 2048: the 32-heads-per-workgroup split launch of batched
+    decode."""
     _run_and_check([65536] * 8, 64, 2048, rope_dim=64, seed=51)
 
 
