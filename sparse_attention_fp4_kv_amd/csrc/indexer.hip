@@ -1222,6 +1222,7 @@ struct SelSmem {
   uint32_t seg_cnt[kMaxSeg];  // candidates a segment contributes
   uint32_t seg_off[kMaxSeg];  // where they start in ck/cp
   uint32_t red[80];  // scans (0..7), threshold search (16..18), per-wave values (16..23, 32..39, 48..55, 64..71), gather count (76)
+  unsigned long long best;  // largest (key, ~position) of a final bin from which one item is taken
 };
 
 // Threshold of a selection: an item (key k, position p) is selected when
@@ -1444,14 +1445,17 @@ __device__ __forceinline__ void items_key_range(SelSmem &sm, const Items &it, ui
   *kmax = mx;
 }
 
-// Zeroes the histogram and the gather counter for find_thresh_items.
+// Zeroes the histogram, the gather counter and the best-item word for find_thresh_items.
 __device__ __forceinline__ void clear_for_search(SelSmem &sm) {
   u32x4 *h4 = reinterpret_cast<u32x4 *>(sm.hist), *s4 = reinterpret_cast<u32x4 *>(sm.seg_cnt);
   for (int i = threadIdx.x; i < kBins / 4; i += kSelThreads) {
     h4[i] = u32x4{0u, 0u, 0u, 0u};
     s4[i] = u32x4{0u, 0u, 0u, 0u};  // second-level histogram
   }
-  if (threadIdx.x == 0) sm.red[76] = 0u;
+  if (threadIdx.x == 0) {
+    sm.red[76] = 0u;
+    sm.best = 0ull;
+  }
 }
 
 // Exact threshold for the top `need` of the items (at least `need` valid ones;
@@ -1461,9 +1465,10 @@ __device__ __forceinline__ void clear_for_search(SelSmem &sm) {
 // boundary bin is split the same way once more (second-level histogram in
 // seg_cnt).  At most 64 items left in the final bin are ranked by one wave
 // (gathered into seg_off); more send the items to LDS for the radix levels.
-// On entry hist, seg_cnt[0 .. 2048) and the gather counter red[76] are zero
-// and a barrier separates the call from earlier reads of red[16..17] and
-// seg_off.
+// When one item of a final bin of at most 64 is taken, an LDS maximum over
+// the items in place finds it instead.  On entry hist, seg_cnt[0 .. 2048), the gather
+// counter red[76] and best are zero and a barrier separates the call from
+// earlier reads of red[16..17], seg_off and best.
 __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it, int n, uint32_t need,
                                                     uint32_t kmin, uint32_t kmax) {
   const int t = threadIdx.x;
@@ -1513,6 +1518,22 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
     }
     __syncthreads();
     return find_thresh_lds(sm, n, need);
+  }
+  if (rem == 1u) {
+    // one item of the bin (<= 64 items) is taken: the threshold item is the
+    // bin's best by (key desc, position asc), one LDS maximum of
+    // (key, ~position) over the items in place (no gather, no rank; a larger
+    // bin of equal keys would serialize on the one word)
+#pragma unroll
+    for (int j = 0; j < kSelIPT; ++j)
+      if ((it.k[j] >= lo_key) & (((it.k[j] - lo_key) >> sub) == 0u))
+        atomicMax(&sm.best, ((unsigned long long)it.k[j] << 32) | (unsigned long long)(~it.p[j]));
+    __syncthreads();
+    const unsigned long long v = sm.best;
+    th.kt = (uint32_t)(v >> 32);
+    th.pinv = (uint32_t)v;
+    th.tie = true;
+    return th;
   }
   // gather the remaining bin (<= 64 items) and rank it in wave 0
   uint32_t *gk = sm.seg_off, *gp = sm.seg_off + 64, *gn = sm.red + 76;

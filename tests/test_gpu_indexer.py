@@ -56,6 +56,32 @@ def test_topk_exact_on_given_scores_with_ties():
             assert np.sum(idx[b] < 0) == max(0, K - n)
 
 
+def test_topk_boundary_pairs_over_a_wide_key_range():
+    """Scores spread over [-100, 100] (two histogram levels) with the K-th and (K+1)-th one ulp apart, exactly
+    equal (the lower position wins), or three equal values around the K-th (two of them taken): the final
+    bin holds two or three items and one or two are taken; the sets must match the oracle exactly."""
+    rng = np.random.default_rng(17)
+    B, M, K = 6, 5000, 1000
+    lens = np.full(B, M, dtype=np.int32)
+    sc = rng.uniform(-100.0, 100.0, size=(B, M)).astype(np.float32)
+    for b in range(B):
+        order = np.argsort(-sc[b].astype(np.float64), kind="stable")
+        kth, nxt, prv = order[K - 1], order[K], order[K - 2]
+        if b % 3 == 0:    # one ulp below the K-th
+            sc[b, nxt] = np.nextafter(sc[b, kth], np.float32(-np.inf))
+        elif b % 3 == 1:  # equal to the K-th, at a lower or a higher position
+            sc[b, nxt] = sc[b, kth]
+        else:             # three equal values around the K-th
+            sc[b, nxt] = sc[b, kth]
+            sc[b, prv] = sc[b, kth]
+    idx = csa2.csa2_topk(to_dev(sc), to_dev(lens), K)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for b in range(B):
+        ref = oracle.indexer.topk(sc[b].astype(np.float64), K)
+        assert set(idx[b].tolist()) == set(ref.tolist()), b
+
+
 def test_topk_narrow_key_range():
     """Scores within a few thousand ulps of each other: the histogram bins are single keys, so
     a partly taken bin is a group of equal scores ranked by position."""
