@@ -33,8 +33,10 @@
 //              into registers in position order and finds the exact threshold
 //              with a 2048-bin histogram over the candidates' own key range,
 //              a second one inside the boundary bin and an exact rank of the
-//              few items left (radix levels on key then position bits when
-//              heavy ties leave more; each threshold search runs in one wave).  A segment whose edge exceeds the threshold's key may
+//              few items left, or one LDS maximum when one of them is taken
+//              (radix levels on key then position bits when heavy ties leave
+//              more; each threshold search runs in one wave).  A segment
+//              whose edge exceeds the threshold's key may
 //              hold more winners: those segments are re-read in full from the
 //              stored keys (items at or above the threshold key only) and the
 //              threshold is recomputed, which is then exact.  If that would
@@ -1583,8 +1585,10 @@ __device__ __forceinline__ Thresh find_thresh_items(SelSmem &sm, const Items &it
 }
 
 // Ordered compaction of the selected items (all valid ones when `all`) to
-// out[0 .. need), padded with -1.  The kept positions are staged in ck and
-// written out with 16-byte stores.  Returns the number of kept items written
+// out[0 .. need), padded with -1.  Each kept position is stored from the
+// register that holds it (the kept items of one ballot land in consecutive
+// slots, so each store instruction writes one contiguous run; staging them in
+// LDS for 16-byte stores measured slower).  Returns the number of kept items written
 // (at most need).  A barrier separates the call from earlier reads of ck and
 // of red[0..7].
 __device__ __forceinline__ uint32_t compact_items(SelSmem &sm, const Items &it, bool all, const Thresh &th,
