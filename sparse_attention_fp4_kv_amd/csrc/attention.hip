@@ -133,9 +133,12 @@ template <int MT, int LD>
 struct __attribute__((aligned(16))) Smem {  // 16-byte aligned rows: every tile access is a 128-bit LDS op
   __attribute__((aligned(16))) f16 cq[3][kT][LD];   // row-major dequantized tiles (+ rope), used in turn
   float s[kKParts<MT>][16 * MT][kT + 1];             // partial logits of the k-parts (padded rows)
-  __attribute__((aligned(16))) f16 p_hi[16 * MT][kPLd];
-  __attribute__((aligned(16))) f16 p_lo[16 * MT][kPLd];
-  float m_run[16 * MT], l_run[16 * MT], alpha[16 * MT];
+  // P (hi + lo parts) and the accumulator factors of two tiles: a tile's
+  // softmax writes one while the previous tile's PV reads the other
+  __attribute__((aligned(16))) f16 p_hi[2][16 * MT][kPLd];
+  __attribute__((aligned(16))) f16 p_lo[2][16 * MT][kPLd];
+  float alpha[2][16 * MT];
+  float m_run[16 * MT], l_run[16 * MT];
   uint32_t slot[kSlotCap];       // physical rows of this workgroup's entries (kNoSlot: skipped)
   float wts[kT], wp[kT];         // window tile: token scales, and times the P normalization
   float unnorm;                  // window tile: the P normalization, inverted
@@ -430,57 +433,47 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
   const bool sm_on = tid < HG * TPH;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // One tile from buffer cq, with the next tile's dequantization into cq_next
-  // (three buffers in turn) in the same phase.  Two barriers per tile: the
-  // buffer a phase writes was last read two barriers earlier.
-  auto step = [&](int tile, f16 (*cq)[LD], bool has_next, const Raw &next, f16 (*cq_next)[LD]) {
-    // 1. partial logits S_kp = Q C^T over this wave's k-part; even and odd
-    // k-steps of every N-tile accumulate separately (2 or 4 independent MFMA
-    // chains), the B fragments of 4 k-steps read together ahead of them
-    f32x4 sacc[QMT][QNT][2];
-    const f16 *brow[QNT];
+  // O = alpha * O + P V for a tile whose softmax is done: tile buffer cq, P
+  // and alpha buffer pb (wave: channels 64*wave .. +63, all heads)
+  auto pv = [&](f16 (*cq)[LD], int pb) {
+    float al[MT][4];
+    bool rescale = false;
 #pragma unroll
-    for (int j = 0; j < QNT; ++j) {
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < QMT; ++i) {
-        sacc[i][j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sacc[i][j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < 4; ++rr) {
+        al[mt][rr] = sm.alpha[pb][16 * mt + 4 * (lane >> 4) + rr];
+        rescale |= al[mt][rr] != 1.f;
       }
-      brow[j] = &cq[16 * (qk_nt0 + j) + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
+    if (__ballot(rescale)) {  // the accumulators live in AGPRs: scale only when a reference moved
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) acc[mt][nt][rr] *= al[mt][rr];
+    }
+    f16x8 ph[MT], pl[MT], bv[4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      ph[mt] = lds_f16x8(&sm.p_hi[pb][16 * mt + (lane & 15)][8 * (lane >> 4)]);
+      pl[mt] = lds_f16x8(&sm.p_lo[pb][16 * mt + (lane & 15)][8 * (lane >> 4)]);
     }
 #pragma unroll
-    for (int k0 = 0; k0 < QKS; k0 += 4) {
-      f16x8 bq[QNT][4];
+    for (int nt = 0; nt < 4; ++nt)
+      bv[nt] = pv_operand<LD>(&cq[8 * (lane >> 4) + ((lane >> 2) & 3)][64 * wave + 16 * nt + 4 * (lane & 3)]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+    for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int j = 0; j < QNT; ++j)
-          if (k0 + kk < QKS)
-            bq[j][kk] = (kEvenParts || k0 + kk < qk_kn) ? lds_f16x8(brow[j] + 32 * (k0 + kk)) : f16x8{};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int j = 0; j < QNT; ++j)
-#pragma unroll
-          for (int i = 0; i < QMT; ++i)
-            if (k0 + kk < QKS)
-              sacc[i][j][kk & 1] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[i][k0 + kk], bq[j][kk], sacc[i][j][kk & 1], 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < QNT; ++j)
-#pragma unroll
-      for (int i = 0; i < QMT; ++i) {
-        const int nt = qk_nt0 + j;
-        const f32x4 sa = sacc[i][j][0] + sacc[i][j][1];
-        // lane holds S_kp[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
-        const int ent = 16 * nt + (lane & 15);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) sm.s[qk_kp][16 * (qk_mt + i) + 4 * (lane >> 4) + rr][ent] = sa[rr];
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv[nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[mt], bv[nt], acc[mt][nt], 0, 0, 0);
       }
-    if (has_next) dequant(next, cq_next);
-    __syncthreads();
-    // 2. online softmax: logit = scale * (sum of the k-parts), masked entries -inf
+  };
+
+  // online softmax of one tile: logit = scale * (sum of the k-parts), masked
+  // entries -inf; writes P and alpha buffer pb
+  auto softmax = [&](int tile, int pb) {
     if (sm_on) {
       float v[EPT];
       float mx = -INFINITY;
@@ -518,52 +511,79 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
         ph[i] = (f16)pw;
         pl[i] = (f16)(pw - (float)ph[i]);
       }
-      *reinterpret_cast<f16xE *>(&sm.p_hi[sm_h][sm_part * EPT]) = ph;
-      *reinterpret_cast<f16xE *>(&sm.p_lo[sm_h][sm_part * EPT]) = pl;
+      *reinterpret_cast<f16xE *>(&sm.p_hi[pb][sm_h][sm_part * EPT]) = ph;
+      *reinterpret_cast<f16xE *>(&sm.p_lo[pb][sm_h][sm_part * EPT]) = pl;
       sum = group_sum<TPH>(sum);
       // (from an empty state O and l are zero: no rescaling either)
       const float al = (m_new == m_run || m_run == -INFINITY) ? 1.f : exp2f(m_run - m_new);
       l_run = l_run * al + sum;
       m_run = m_new;
-      if (sm_part == 0) sm.alpha[sm_h] = al;
+      if (sm_part == 0) sm.alpha[pb][sm_h] = al;
     }
+  };
+
+  // One tile from buffer cq in two phases, each ended by a barrier:
+  //   1. its partial logits (QK^T, matrix cores) and the next tile's
+  //      dequantization into cq_next (vector ALU);
+  //   2. the previous tile's PV from cq_prev (matrix cores) beside this
+  //      tile's online softmax (vector ALU), which writes the other P buffer.
+  // The last tile's PV follows the loop.  Three tile buffers in turn: the one
+  // a phase writes was last read two barriers earlier.
+  auto step = [&](int tile, f16 (*cq)[LD], bool has_next, const Raw &next, f16 (*cq_next)[LD],
+                  f16 (*cq_prev)[LD]) {
+    const int pb = (tile - tile_begin) & 1;  // this tile's P buffer
+    auto qk = [&]() {
+      // 1. partial logits S_kp = Q C^T over this wave's k-part; even and odd
+      // k-steps of every N-tile accumulate separately (2 or 4 independent MFMA
+      // chains), the B fragments of 4 k-steps read together ahead of them
+      f32x4 sacc[QMT][QNT][2];
+      const f16 *brow[QNT];
+#pragma unroll
+      for (int j = 0; j < QNT; ++j) {
+#pragma unroll
+        for (int i = 0; i < QMT; ++i) {
+          sacc[i][j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+          sacc[i][j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        brow[j] = &cq[16 * (qk_nt0 + j) + (lane & 15)][32 * qk_k0 + 8 * (lane >> 4)];
+      }
+#pragma unroll
+      for (int k0 = 0; k0 < QKS; k0 += 4) {
+        f16x8 bq[QNT][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int j = 0; j < QNT; ++j)
+            if (k0 + kk < QKS)
+              bq[j][kk] = (kEvenParts || k0 + kk < qk_kn) ? lds_f16x8(brow[j] + 32 * (k0 + kk)) : f16x8{};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int j = 0; j < QNT; ++j)
+#pragma unroll
+            for (int i = 0; i < QMT; ++i)
+              if (k0 + kk < QKS)
+                sacc[i][j][kk & 1] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[i][k0 + kk], bq[j][kk], sacc[i][j][kk & 1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < QNT; ++j)
+#pragma unroll
+        for (int i = 0; i < QMT; ++i) {
+          const int nt = qk_nt0 + j;
+          const f32x4 sa = sacc[i][j][0] + sacc[i][j][1];
+          // lane holds S_kp[head 16*mt + 4*(lane/16) + r][entry 16*nt + lane%16]
+          const int ent = 16 * nt + (lane & 15);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) sm.s[qk_kp][16 * (qk_mt + i) + 4 * (lane >> 4) + rr][ent] = sa[rr];
+        }
+    };
+    qk();
+    if (has_next) dequant(next, cq_next);
     __syncthreads();
-    // 3. O = alpha * O + P V  (wave: channels 64*wave .. +63, all heads)
-    {
-      float al[MT][4];
-      bool rescale = false;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          al[mt][rr] = sm.alpha[16 * mt + 4 * (lane >> 4) + rr];
-          rescale |= al[mt][rr] != 1.f;
-        }
-      if (__ballot(rescale)) {  // the accumulators live in AGPRs: scale only when a reference moved
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) acc[mt][nt][rr] *= al[mt][rr];
-      }
-      f16x8 ph[MT], pl[MT], bv[4];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        ph[mt] = lds_f16x8(&sm.p_hi[16 * mt + (lane & 15)][8 * (lane >> 4)]);
-        pl[mt] = lds_f16x8(&sm.p_lo[16 * mt + (lane & 15)][8 * (lane >> 4)]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-        bv[nt] = pv_operand<LD>(&cq[8 * (lane >> 4) + ((lane >> 2) & 3)][64 * wave + 16 * nt + 4 * (lane & 3)]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[mt], bv[nt], acc[mt][nt], 0, 0, 0);
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[mt], bv[nt], acc[mt][nt], 0, 0, 0);
-        }
-    }
+    if (tile > tile_begin) pv(cq_prev, pb ^ 1);
+    softmax(tile, pb);
+    __syncthreads();
   };
 
   // ---- tiles: three register sets of raw rows (each tile's loads are issued
@@ -597,7 +617,8 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
         *reinterpret_cast<f16x4 *>(&sm.cq[0][tile_entry][kLatent + 4 * tile_chunk]) = f16x4{};
       }
       __syncthreads();
-      step(0, sm.cq[0], false, Raw{}, sm.cq[1]);
+      step(0, sm.cq[0], false, Raw{}, sm.cq[1], sm.cq[2]);
+      pv(sm.cq[0], 0);
     }
   } else if (tile_begin < tile_end && J.L.num_blocks > 0) {
     const int last = tile_end - 1;
@@ -609,17 +630,18 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
     load_raw(min(tile_begin + 3, last), ra);
     __syncthreads();
     for (int tile = tile_begin; tile < tile_end; tile += 3) {
-      step(tile, sm.cq[0], tile + 1 < tile_end, rb, sm.cq[1]);
+      step(tile, sm.cq[0], tile + 1 < tile_end, rb, sm.cq[1], sm.cq[2]);
       load_raw(min(tile + 4, last), rb);
       if (tile + 1 < tile_end) {
-        step(tile + 1, sm.cq[1], tile + 2 < tile_end, rc, sm.cq[2]);
+        step(tile + 1, sm.cq[1], tile + 2 < tile_end, rc, sm.cq[2], sm.cq[0]);
         load_raw(min(tile + 5, last), rc);
       }
       if (tile + 2 < tile_end) {
-        step(tile + 2, sm.cq[2], tile + 3 < tile_end, ra, sm.cq[0]);
+        step(tile + 2, sm.cq[2], tile + 3 < tile_end, ra, sm.cq[0], sm.cq[1]);
         load_raw(min(tile + 6, last), ra);
       }
     }
+    pv(sm.cq[(last - tile_begin) % 3], (last - tile_begin) & 1);  // the last tile's PV
   }
   if (sm_on && sm_part == 0) {
     sm.m_run[sm_h] = m_run;
