@@ -41,6 +41,12 @@ def test_window_positions_and_slots():
     w = swa.window_positions(1000)
     assert w[0] == 872 and w[-1] == 999 and w.size == 128
     assert sorted(swa.window_slot(w).tolist()) == list(range(128))  # a full ring holds every slot once
+    # hand values of the ring slot (position mod 128): a new token overwrites the entry 128 positions back
+    assert swa.window_slot([0, 1, 127, 128, 129, 999, 1000]).tolist() == [0, 1, 127, 0, 1, 103, 104]
+    assert swa.window_slot(1000) == swa.window_slot(1000 - 128)
+    # the window slides by one position per token: the oldest position leaves as the new one enters
+    assert np.array_equal(swa.window_positions(1001)[:-1], swa.window_positions(1000)[1:])
+    assert swa.window_positions(128).tolist() == list(range(128)) and swa.window_positions(129)[0] == 1
 
 
 def test_merge_equals_attention_over_the_union():
