@@ -240,3 +240,28 @@ def test_multi_layer_validation_rejects_before_launch():
     rows = (csa2.AppendRowC * 1)(row(kv, 16, None, 16))
     assert h(P(kv), P(sq), rows, 9, 16, None, 8, None, 0, 0, 16, 256, 1 << 30, None) == csa2.ERR_INVALID_ARG
     assert h(P(kv), P(sq), rows, 1, 16, None, 8, None, 0, 0, 16, 256, 1, None) == csa2.ERR_WORKSPACE
+
+
+@needs_lib
+def test_noalloc_attention_rejects_before_launch():
+    """The allocation-free layered attention checks its arguments and its fixed scratch bound on the host, before
+    it resolves the scratch's device address: every case here returns without touching a device."""
+    L = csa2.lib()
+    P = ctypes.byref
+    kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=None, num_blocks=1, block_tokens=64, latent_dim=512,
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
+    sq = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=1, max_seq_len=64)
+    f = L.csa2_sparse_fp4_decode_attn_layers_noalloc
+    arr = (csa2.AttnLayerC * 20)(*[csa2.AttnLayerC(ctypes.pointer(kv), 16, 16, 16, None, None, None)
+                                   for _ in range(20)])
+    assert f(None, 1, P(sq), 64, 64, 0.1, None) == csa2.ERR_INVALID_ARG
+    for n_layers, heads, top_k in ((0, 64, 64), (21, 64, 64), (1, 24, 64), (1, 144, 64), (1, 64, 0), (1, 64, 4097)):
+        assert f(arr, n_layers, P(sq), heads, top_k, 0.1, None) == csa2.ERR_INVALID_ARG, (n_layers, heads, top_k)
+    bad = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=1, max_seq_len=65)
+    assert f(arr, 1, P(bad), 64, 64, 0.1, None) == csa2.ERR_INVALID_ARG  # lengths beyond the table
+    # 20 layers x 64 sequences x 128 heads: one split's fp32 partials alone (~335 MB) exceed the 32 MiB scratch
+    big = csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=64, max_seq_len=64)
+    assert f(arr, 20, P(big), 128, 4096, 0.1, None) == csa2.ERR_WORKSPACE
+    # the caller-workspace entry point sizes the same problem without refusing it
+    n = ctypes.c_size_t()
+    assert L.csa2_attn_layers_workspace_size(20, 64, 128, 4096, 512, 0, P(n)) == csa2.OK and n.value > 32 << 20
