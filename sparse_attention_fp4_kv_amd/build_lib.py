@@ -35,9 +35,10 @@ def hipcc():
 
 
 # Per-source device flags.  The indexer's MFMA results feed VALU epilogues
-# (ReLU and head weights), so its MFMAs write VGPRs instead of AGPRs (no
-# v_accvgpr_read per result); the attention and CED kernels keep their
-# accumulators in AGPRs.
+# (ReLU and head weights), so its MFMAs are made to write VGPRs, never AGPRs
+# (no v_accvgpr_read per result).  Elsewhere the compiler picks the form: the
+# attention and CED accumulators land in VGPRs too (gfx950's register file is
+# unified), the finish kernel's key-projection accumulators in AGPRs.
 FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -445,7 +445,7 @@ __global__ void __launch_bounds__(kThreads) sparse_attn_kernel(AttnArgs a) {
         al[mt][rr] = sm.alpha[pb][16 * mt + 4 * (lane >> 4) + rr];
         rescale |= al[mt][rr] != 1.f;
       }
-    if (__ballot(rescale)) {  // the accumulators live in AGPRs: scale only when a reference moved
+    if (__ballot(rescale)) {  // 16 * MT multiplies per lane: skipped unless some row's reference moved
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
