@@ -23,6 +23,9 @@
  *     default stream).  Host-side argument validation happens before any
  *     launch; a rejected call launches nothing and returns a status.
  *   - Launch failures return CSA2_ERR_HIP.  No exception crosses the ABI.
+ *   - A call serves at most 65,535 sequences (csa2_seqs.batch and every
+ *     `batch` argument, workspace-size calls included); more return
+ *     CSA2_ERR_INVALID_ARG.
  *   - Device data is trusted only as far as stated: selected indices that are
  *     negative or >= the sequence length, and page ids outside
  *     [0, num_blocks), are skipped rather than read.
@@ -93,7 +96,8 @@ typedef struct {
   const int32_t *block_table; /* device [batch][max_blocks_per_seq]                 */
   int32_t max_blocks_per_seq;
   const int32_t *seq_lens;    /* device [batch]: visible tokens of each sequence     */
-  int32_t batch;
+  int32_t batch;              /* 0 .. 65,535 sequences per call (one grid
+                                 dimension spans them)                              */
   int32_t max_seq_len;        /* host upper bound of seq_lens (sizes the launches);
                                  0 means max_blocks_per_seq * 64                      */
 } csa2_seqs;
@@ -425,7 +429,9 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
  * csa2_sparse_fp4_decode_attn_swa defines it (its own ring; new_latent NULL
  * or that layer's current window entry).  All layers share seqs, heads,
  * top_k and softmax_scale; their pools have the same rope_dim; either every
- * layer has a window or none has.  1 <= n_layers <= 20.  Results equal those
+ * layer has a window or none has.  1 <= n_layers <= 20, and n_layers *
+ * seqs->batch at most 65,535 (the launch's (layer, sequence) grid dimension;
+ * larger calls fail with CSA2_ERR_INVALID_ARG).  Results equal those
  * of one call per layer (the same kernels; only the launch is shared), so the
  * layers' problems are independent: no output may alias another layer's
  * input.  Workspace from csa2_attn_layers_workspace_size (with_window: 1 when

@@ -84,6 +84,10 @@ namespace {
 constexpr int kMaxTopK = 4096;
 constexpr int kMaxPoolBlocks = 2048;  // pool positions must fit one 16,384-candidate select
 constexpr int64_t kMaxSelectLen = 4096LL * 2048;  // 8M positions per row
+// Sequences per call, and (layer, sequence) problems per layered attention
+// launch: each spans one grid dimension, which also keeps the host's int
+// products of these counts with heads and splits in range.
+constexpr int32_t kMaxBatch = 65535;
 
 hipStream_t as_stream(csa2_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -136,7 +140,8 @@ bool query_ok(const csa2_kv_layer *l, const void *q_idx, const float *w_idx) {
 }
 
 csa2_status check_seqs(const csa2_seqs *s, SeqsDev *out) {
-  if (s == nullptr || s->batch < 0 || s->max_blocks_per_seq < 0 || s->max_seq_len < 0) return CSA2_ERR_INVALID_ARG;
+  if (s == nullptr || s->batch < 0 || s->batch > kMaxBatch || s->max_blocks_per_seq < 0 || s->max_seq_len < 0)
+    return CSA2_ERR_INVALID_ARG;
   if (s->batch > 0 && (s->block_table == nullptr || s->seq_lens == nullptr)) return CSA2_ERR_INVALID_ARG;
   const int64_t cap = (int64_t)s->max_blocks_per_seq * 64;
   const int64_t ml = s->max_seq_len ? s->max_seq_len : cap;
@@ -361,7 +366,7 @@ csa2_status csa2_kv_append_finished(const csa2_kv_layer *layer, const csa2_seqs 
 csa2_status csa2_swa_append(const csa2_swa_window *win, const int32_t *positions, int32_t batch,
                             const float *latent, csa2_stream stream) {
   CSA2_TRACE;
-  if (win == nullptr || batch < 0 || batch > win->batch) return CSA2_ERR_INVALID_ARG;
+  if (win == nullptr || batch < 0 || batch > kMaxBatch || batch > win->batch) return CSA2_ERR_INVALID_ARG;
   if (batch == 0) return CSA2_OK;
   if (win->codes == nullptr || win->scales == nullptr || positions == nullptr || latent == nullptr)
     return CSA2_ERR_INVALID_ARG;
@@ -373,7 +378,7 @@ csa2_status csa2_swa_attn_merge(const csa2_swa_window *win, const int32_t *seq_l
                                 const uint16_t *q, int32_t heads, int32_t q_dim, float softmax_scale, float *out,
                                 float *lse, csa2_stream stream) {
   CSA2_TRACE;
-  if (win == nullptr || batch < 0 || batch > win->batch) return CSA2_ERR_INVALID_ARG;
+  if (win == nullptr || batch < 0 || batch > kMaxBatch || batch > win->batch) return CSA2_ERR_INVALID_ARG;
   if (heads < 16 || heads > 128 || heads % 16 != 0 || (q_dim != 512 && q_dim != 576)) return CSA2_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !(softmax_scale < 3.0e38f)) return CSA2_ERR_INVALID_ARG;
   if (batch == 0) return CSA2_OK;
@@ -415,7 +420,8 @@ csa2_status csa2_index_scores(const csa2_kv_layer *keys, const csa2_seqs *seqs, 
 }
 
 csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top_k, size_t *bytes) {
-  if (bytes == nullptr || batch < 0 || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 || top_k > kMaxTopK)
+  if (bytes == nullptr || batch < 0 || batch > kMaxBatch || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 ||
+      top_k > kMaxTopK)
     return CSA2_ERR_INVALID_ARG;
   *bytes = topk_workspace_bytes(batch, max_len, top_k);
   return CSA2_OK;
@@ -424,7 +430,8 @@ csa2_status csa2_topk_workspace_size(int32_t batch, int32_t max_len, int32_t top
 csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *lens, int32_t batch, int32_t max_len,
                       int32_t top_k, int32_t *indices, void *ws, size_t ws_bytes, csa2_stream stream) {
   CSA2_TRACE;
-  if (batch < 0 || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 || top_k > kMaxTopK || row_stride < max_len)
+  if (batch < 0 || batch > kMaxBatch || max_len < 0 || max_len > kMaxSelectLen || top_k < 1 || top_k > kMaxTopK ||
+      row_stride < max_len)
     return CSA2_ERR_INVALID_ARG;
   if (batch == 0) return CSA2_OK;
   if (scores == nullptr || lens == nullptr || indices == nullptr) return CSA2_ERR_INVALID_ARG;
@@ -435,8 +442,8 @@ csa2_status csa2_topk(const float *scores, int64_t row_stride, const int32_t *le
 
 csa2_status csa2_index_select_workspace_size(int32_t batch, int32_t max_seq_len, int32_t top_k, int32_t pool_blocks,
                                              int32_t pool_block_tokens, size_t *bytes) {
-  if (bytes == nullptr || batch < 0 || max_seq_len < 0 || max_seq_len > kMaxSelectLen || top_k < 1 ||
-      top_k > kMaxTopK)
+  if (bytes == nullptr || batch < 0 || batch > kMaxBatch || max_seq_len < 0 || max_seq_len > kMaxSelectLen ||
+      top_k < 1 || top_k > kMaxTopK)
     return CSA2_ERR_INVALID_ARG;
   if (pool_blocks < 0 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
   if (pool_blocks > 0 && pool_block_tokens != 8) return CSA2_ERR_INVALID_ARG;
@@ -535,7 +542,8 @@ csa2_status csa2_index_select_append(const csa2_kv_layer *keys, const csa2_seqs 
 
 csa2_status csa2_index_reindex_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t top_k,
                                                     int32_t pool_blocks, int32_t pool_block_tokens, size_t *bytes) {
-  if (bytes == nullptr || n_layers < 1 || n_layers > kMaxIdxLayers || batch < 0 || top_k < 1 || top_k > kMaxTopK)
+  if (bytes == nullptr || n_layers < 1 || n_layers > kMaxIdxLayers || batch < 0 || batch > kMaxBatch || top_k < 1 ||
+      top_k > kMaxTopK)
     return CSA2_ERR_INVALID_ARG;
   if (pool_block_tokens != 8 || pool_blocks < 1 || pool_blocks > kMaxPoolBlocks) return CSA2_ERR_INVALID_ARG;
   *bytes = reindex_layers_workspace_bytes(n_layers, batch);
@@ -571,8 +579,8 @@ csa2_status csa2_index_reindex_layers(const csa2_kv_layer *keys, const csa2_seqs
 }
 
 csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim, size_t *bytes) {
-  if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
-      top_k > kMaxTopK || latent_dim != 512)
+  if (bytes == nullptr || batch < 0 || batch > kMaxBatch || heads <= 0 || heads % 16 != 0 || heads > 128 ||
+      top_k < 1 || top_k > kMaxTopK || latent_dim != 512)
     return CSA2_ERR_INVALID_ARG;
   *bytes = attn_workspace_bytes(1, batch, heads, top_k, false);
   return CSA2_OK;
@@ -580,8 +588,8 @@ csa2_status csa2_attn_workspace_size(int32_t batch, int32_t heads, int32_t top_k
 
 csa2_status csa2_attn_swa_workspace_size(int32_t batch, int32_t heads, int32_t top_k, int32_t latent_dim,
                                          size_t *bytes) {
-  if (bytes == nullptr || batch < 0 || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
-      top_k > kMaxTopK || latent_dim != 512)
+  if (bytes == nullptr || batch < 0 || batch > kMaxBatch || heads <= 0 || heads % 16 != 0 || heads > 128 ||
+      top_k < 1 || top_k > kMaxTopK || latent_dim != 512)
     return CSA2_ERR_INVALID_ARG;
   *bytes = attn_workspace_bytes(1, batch, heads, top_k, true);
   return CSA2_OK;
@@ -634,8 +642,9 @@ csa2_status csa2_sparse_fp4_decode_attn_swa(const csa2_kv_layer *layer, const cs
 
 csa2_status csa2_attn_layers_workspace_size(int32_t n_layers, int32_t batch, int32_t heads, int32_t top_k,
                                             int32_t latent_dim, int32_t with_window, size_t *bytes) {
-  if (bytes == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs || batch < 0 || heads <= 0 || heads % 16 != 0 ||
-      heads > 128 || top_k < 1 || top_k > kMaxTopK || latent_dim != 512)
+  if (bytes == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs || batch < 0 ||
+      (int64_t)n_layers * batch > kMaxBatch || heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 ||
+      top_k > kMaxTopK || latent_dim != 512)
     return CSA2_ERR_INVALID_ARG;
   *bytes = attn_workspace_bytes(n_layers, batch, heads, top_k, with_window != 0);
   return CSA2_OK;
@@ -652,6 +661,7 @@ csa2_status attn_layers_impl(const csa2_attn_layer *layers, int32_t n_layers, co
   csa2_status st;
   if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
   if ((st = check_seqs(seqs, &S)) != CSA2_OK) return st;
+  if ((int64_t)n_layers * S.batch > kMaxBatch) return CSA2_ERR_INVALID_ARG;
   if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.0f) || !(softmax_scale < 1e30f)) return CSA2_ERR_INVALID_ARG;
   AttnLaunchJob jobs[kMaxAttnJobs];
@@ -704,6 +714,7 @@ csa2_status csa2_sparse_fp4_decode_attn_layers_noalloc(const csa2_attn_layer *la
   csa2_status st = check_seqs(seqs, &S);
   if (st != CSA2_OK) return st;
   if (layers == nullptr || n_layers < 1 || n_layers > kMaxAttnJobs) return CSA2_ERR_INVALID_ARG;
+  if ((int64_t)n_layers * S.batch > kMaxBatch) return CSA2_ERR_INVALID_ARG;
   if (heads <= 0 || heads % 16 != 0 || heads > 128 || top_k < 1 || top_k > kMaxTopK) return CSA2_ERR_INVALID_ARG;
   const bool window = layers[0].win != nullptr;
   if (attn_workspace_bytes(n_layers, S.batch, heads, top_k, window, kAttnScratchBytes) > kAttnScratchBytes)

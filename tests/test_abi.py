@@ -265,3 +265,37 @@ def test_noalloc_attention_rejects_before_launch():
     # the caller-workspace entry point sizes the same problem without refusing it
     n = ctypes.c_size_t()
     assert L.csa2_attn_layers_workspace_size(20, 64, 128, 4096, 512, 0, P(n)) == csa2.OK and n.value > 32 << 20
+
+
+@needs_lib
+def test_batch_bound_rejects_before_launch():
+    """At most 65,535 sequences per call (and per layered attention launch, layers x sequences): the largest
+    accepted batch passes validation (the call then stops at its missing workspace), one more is refused."""
+    L = csa2.lib()
+    P = ctypes.byref
+    n = ctypes.c_size_t()
+    top = 65535
+    kv = csa2.KvLayer(codes=16, scales=16, rope=None, idx_keys=16, num_blocks=1, block_tokens=64, latent_dim=512,
+                      rope_dim=0, idx_dim=64, idx_dtype=csa2.BF16, idx_heads=1)
+    seqs = lambda batch: csa2.Seqs(block_table=16, max_blocks_per_seq=1, seq_lens=16, batch=batch, max_seq_len=64)
+    for batch, want_sel, want_size in ((top, csa2.ERR_WORKSPACE, csa2.OK), (top + 1, csa2.ERR_INVALID_ARG,
+                                                                            csa2.ERR_INVALID_ARG)):
+        sq = seqs(batch)
+        assert L.csa2_index_select(P(kv), P(sq), 16, None, 8, csa2.FULL, None, None, 0, 0, 16, 256, 1,
+                                   None) == want_sel
+        assert L.csa2_sparse_fp4_decode_attn(P(kv), P(sq), 16, 64, 16, 64, 0.1, 16, None, 256, 1,
+                                             None) == want_sel
+        assert L.csa2_index_select_workspace_size(batch, 64, 8, 0, 8, P(n)) == want_size
+        assert L.csa2_attn_workspace_size(batch, 64, 64, 512, P(n)) == want_size
+        assert L.csa2_topk_workspace_size(batch, 64, 8, P(n)) == want_size
+        assert L.csa2_topk(16, 64, 16, batch, 64, 8, 16, 256, 1, None) == want_sel
+    # the layered attention: layers x sequences
+    arr = (csa2.AttnLayerC * 3)(*[csa2.AttnLayerC(ctypes.pointer(kv), 16, 16, 16, None, None, None)
+                                  for _ in range(3)])
+    f = L.csa2_sparse_fp4_decode_attn_layers
+    assert f(arr, 3, P(seqs(top // 3)), 64, 64, 0.1, 256, 1, None) == csa2.ERR_WORKSPACE
+    assert f(arr, 3, P(seqs(top // 3 + 1)), 64, 64, 0.1, 256, 1, None) == csa2.ERR_INVALID_ARG
+    assert L.csa2_attn_layers_workspace_size(3, top // 3, 64, 64, 512, 0, P(n)) == csa2.OK
+    assert L.csa2_attn_layers_workspace_size(3, top // 3 + 1, 64, 64, 512, 0, P(n)) == csa2.ERR_INVALID_ARG
+    g = L.csa2_sparse_fp4_decode_attn_layers_noalloc
+    assert g(arr, 3, P(seqs(top // 3 + 1)), 64, 64, 0.1, None) == csa2.ERR_INVALID_ARG
