@@ -37,6 +37,13 @@ static void validation() {
   CHECK(csa2_attn_workspace_size(1, 64, 2048, 512, &n) == CSA2_OK);
   CHECK(csa2_attn_layers_workspace_size(20, 32, 128, 4096, 512, 1, &n) == CSA2_OK && n > 0);
   CHECK(csa2_attn_layers_workspace_size(21, 1, 64, 2048, 512, 0, &n) == CSA2_ERR_INVALID_ARG);
+  // at most 65,535 sequences per call (layers x sequences for the layered attention)
+  CHECK(csa2_attn_workspace_size(65535, 128, 4096, 512, &n) == CSA2_OK && n > 0);
+  CHECK(csa2_attn_workspace_size(65536, 64, 2048, 512, &n) == CSA2_ERR_INVALID_ARG);
+  CHECK(csa2_attn_layers_workspace_size(20, 3276, 128, 4096, 512, 1, &n) == CSA2_OK && n > 0);
+  CHECK(csa2_attn_layers_workspace_size(20, 3277, 64, 2048, 512, 0, &n) == CSA2_ERR_INVALID_ARG);
+  CHECK(csa2_index_select_workspace_size(65535, 1 << 10, 2048, 2048, 8, &n) == CSA2_OK && n > 0);
+  CHECK(csa2_index_select_workspace_size(65536, 1 << 10, 2048, 0, 8, &n) == CSA2_ERR_INVALID_ARG);
   CHECK(csa2_workspace_clear(nullptr, 0, s) == CSA2_OK);
   CHECK(csa2_workspace_clear(nullptr, 64, s) == CSA2_ERR_INVALID_ARG);
 
