@@ -299,3 +299,22 @@ def test_batch_bound_rejects_before_launch():
     assert L.csa2_attn_layers_workspace_size(3, top // 3 + 1, 64, 64, 512, 0, P(n)) == csa2.ERR_INVALID_ARG
     g = L.csa2_sparse_fp4_decode_attn_layers_noalloc
     assert g(arr, 3, P(seqs(top // 3 + 1)), 64, 64, 0.1, None) == csa2.ERR_INVALID_ARG
+
+
+def test_header_is_plain_c():
+    """include/csa2.h is a C header: it compiles as strict C99 and as C++17 (extern "C"), and names no C++,
+    HIP or torch type."""
+    import shutil
+    import subprocess
+
+    hdr = os.path.join(ROOT, "include", "csa2.h")
+    for cc, lang, std in (("gcc", "c", "-std=c99"), ("g++", "c++", "-std=c++17")):
+        exe = shutil.which(cc)
+        if exe is None:
+            pytest.skip(f"{cc} not found")
+        r = subprocess.run([exe, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-x", lang, hdr],
+                           capture_output=True, text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    for word in ("torch", "at::", "std::", "hipStream_t", "hip_runtime", "class ", "template"):
+        assert word not in text, word
