@@ -318,3 +318,20 @@ def test_header_is_plain_c():
     text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
     for word in ("torch", "at::", "std::", "hipStream_t", "hip_runtime", "class ", "template"):
         assert word not in text, word
+
+
+def test_binding_signatures_match_the_header():
+    """Every function the header declares has a ctypes signature in the binding with the same number of
+    arguments (a missing or extra argument would shift every later one silently)."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "csa2.h")).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    protos = {}
+    for m in re.finditer(r"\b(csa2_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", text):
+        name, args = m.group(1), m.group(2).strip()
+        if name in protos:
+            continue
+        protos[name] = 0 if args in ("", "void") else args.count(",") + 1
+    assert len(protos) >= 25
+    for name, nargs in protos.items():
+        assert name in csa2.SIGNATURES, f"{name} has no ctypes signature"
+        assert len(csa2.SIGNATURES[name][1]) == nargs, (name, nargs, len(csa2.SIGNATURES[name][1]))
