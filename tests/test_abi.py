@@ -335,3 +335,36 @@ def test_binding_signatures_match_the_header():
     for name, nargs in protos.items():
         assert name in csa2.SIGNATURES, f"{name} has no ctypes signature"
         assert len(csa2.SIGNATURES[name][1]) == nargs, (name, nargs, len(csa2.SIGNATURES[name][1]))
+
+
+def _c_kind(arg):
+    """Kind of one C parameter declaration: pointer, 32- or 64-bit integer, size or float."""
+    a = arg.strip()
+    if "*" in a or re.match(r"(const\s+)?csa2_stream\b", a):
+        return "ptr"
+    t = a.split()[-2] if len(a.split()) > 1 else a
+    return {"int32_t": "i32", "int": "i32", "csa2_mode": "i32", "csa2_dtype": "i32", "csa2_status": "i32", "int64_t": "i64",
+            "size_t": "sz", "float": "f32", "uint32_t": "u32"}[t]
+
+
+def _ctypes_kind(t):
+    if t in (ctypes.c_void_p, ctypes.c_char_p) or hasattr(t, "_type_") and isinstance(t._type_, type):
+        return "ptr"
+    return {ctypes.c_int32: "i32", ctypes.c_int64: "i64", ctypes.c_size_t: "sz", ctypes.c_float: "f32",
+            ctypes.c_uint32: "u32"}[t]
+
+
+def test_binding_argument_kinds_match_the_header():
+    """Argument by argument, the ctypes type has the C parameter's kind (a float passed where the header
+    takes an int, or a 32-bit count where it takes a 64-bit one, would be read as garbage)."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "csa2.h")).read(), flags=re.S)
+    seen = set()
+    for m in re.finditer(r"\b(csa2_[a-z0-9_]+)\s*\(([^;{]*?)\)\s*;", text):
+        name, args = m.group(1), m.group(2).strip()
+        if name in seen or args in ("", "void"):
+            continue
+        seen.add(name)
+        c = [_c_kind(a) for a in args.split(",")]
+        py = [_ctypes_kind(t) for t in csa2.SIGNATURES[name][1]]
+        assert c == py, (name, c, py)
+    assert len(seen) >= 25
