@@ -368,3 +368,44 @@ def test_binding_argument_kinds_match_the_header():
         py = [_ctypes_kind(t) for t in csa2.SIGNATURES[name][1]]
         assert c == py, (name, c, py)
     assert len(seen) >= 25
+
+
+def test_binding_structs_match_the_header_layout():
+    """Each ctypes structure of the binding has the size and field offsets the C compiler gives the header's
+    struct (a C program built with the host compiler prints them)."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("gcc not found")
+    pairs = {"csa2_kv_layer": csa2.KvLayer, "csa2_seqs": csa2.Seqs, "csa2_kv_finish": csa2.KvFinish,
+             "csa2_swa_window": csa2.SwaWindow, "csa2_append": csa2.AppendRowC,
+             "csa2_reindex_query": csa2.ReindexQueryC, "csa2_attn_layer": csa2.AttnLayerC}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "csa2.h"', "int main(void) {"]
+    for cname, cls in pairs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    tmp = tempfile.mkdtemp(prefix="csa2_layout_")
+    try:
+        src, exe = os.path.join(tmp, "layout.c"), os.path.join(tmp, "layout")
+        with open(src, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        r = subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), "-o", exe, src], capture_output=True,
+                           text=True, timeout=120)
+        assert r.returncode == 0, r.stderr
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=60).stdout.split("\n")
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    got = {}
+    for line in out:
+        if line:
+            cname, key, val = line.split()
+            got[(cname, key)] = int(val)
+    for cname, cls in pairs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert got[(cname, field)] == getattr(cls, field).offset, (cname, field)
