@@ -409,3 +409,24 @@ def test_binding_structs_match_the_header_layout():
         assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for field, _ in cls._fields_:
             assert got[(cname, field)] == getattr(cls, field).offset, (cname, field)
+
+
+def test_launch_timer_accepts_every_documented_name():
+    """csa2_time_next_launch arms for each kernel name the header lists (and for every name bench.py times),
+    refuses others, and disarms with NULL; arming launches nothing."""
+    L = csa2.lib()
+    text = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    block = text[text.index("Profiling aid"):text.index("csa2_status csa2_time_next_launch")]
+    names = re.findall(r'"([a-z_0-9]+)"', block)
+    assert len(names) >= 8
+    bench = open(os.path.join(ROOT, "bench.py")).read()
+    timed = set(re.findall(r'kernel_ms\("([a-z_]+)"', bench)) | set(re.findall(r'"([a-z_]+)": "[a-z]+\.hip"', bench))
+    assert timed and timed <= set(names), timed - set(names)
+    ev = ctypes.c_void_p(16)
+    for name in names:
+        assert L.csa2_time_next_launch(name.encode(), ev, ev) == csa2.OK, name
+        assert L.csa2_timer_pending() == 1
+        assert L.csa2_time_next_launch(None, None, None) == csa2.OK
+        assert L.csa2_timer_pending() == 0
+    assert L.csa2_time_next_launch(b"no_such_kernel", ev, ev) == csa2.ERR_INVALID_ARG
+    assert L.csa2_timer_pending() == 0
