@@ -3,6 +3,7 @@ header declares, and its host-side validation and page allocator behave as
 documented (no GPU work is launched by any call here)."""
 
 import ctypes
+import glob
 import os
 import re
 
@@ -430,3 +431,12 @@ def test_launch_timer_accepts_every_documented_name():
         assert L.csa2_timer_pending() == 0
     assert L.csa2_time_next_launch(b"no_such_kernel", ev, ev) == csa2.ERR_INVALID_ARG
     assert L.csa2_timer_pending() == 0
+
+
+def test_build_compiles_every_hip_source():
+    """The build compiles every .hip file under csrc (a source left out of the list would drop its kernels
+    from the library without a compile error)."""
+    from sparse_attention_fp4_kv_amd import build_lib
+
+    on_disk = sorted(os.path.basename(p) for p in glob.glob(os.path.join(build_lib.CSRC, "*.hip")))
+    assert sorted(build_lib.SOURCES) == on_disk
